@@ -1,0 +1,219 @@
+"""Benchmark: one dropless MoE layer forward (route -> permute -> grouped SwiGLU MLP ->
+combine) on one MI355X, DeepSeek-V3-shaped bf16 by default.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is useful GEMM FLOPs (6*T*k*d*f + 6*T*d*f_shared, padding never
+counted, router projection excluded) divided by the whole step time, i.e. layer TFLOPS;
+`gemm_tflops` uses the two grouped-GEMM launches' own event time instead, `tokens_per_s` is
+T / step time. Inputs and weights are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialise-gather", action="store_true",
+                    help="write x_perm in the permute and read it in GEMM 1 (default: gather fused into GEMM 1)")
+    return ap.parse_args()
+
+
+def useful_flops(w, counts):
+    routed = 6.0 * w.T * w.k * w.d * w.f
+    shared = 6.0 * w.T * w.d * w.shared_f
+    return routed + shared
+
+
+def gemm1_bytes(w, counts, fused):
+    """Algorithmic HBM bytes of grouped GEMM 1 (gate/up + SwiGLU): the gate/up weights of
+    every non-empty group once, the A rows once (x itself when the gather is fused, else
+    x_perm), H written once, plus the index metadata."""
+    nonempty = int(np.count_nonzero(counts))
+    rows = w.T * w.k + (w.T if w.shared_f else 0)
+    wbytes = nonempty * 2 * w.f * w.d * 2
+    abytes = (w.T * w.d * 2) if fused else rows * w.d * 2
+    hbytes = rows * w.f * 2
+    return wbytes + abytes + hbytes + rows * 4
+
+
+def cpu_baseline(w, idx_np):
+    """The oracle's forward on a bounded sample of the same workload: routing and the
+    permutation for every token, then the SwiGLU experts of every 16th expert id (and the
+    shared expert's first 512 tokens). Reported in useful TFLOPS of the sampled experts."""
+    import torch
+    import moe_inputs as mi
+    from oracle import moe_oracle as O
+    try:
+        import threadpoolctl
+        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    sample_e = list(range(0, w.E, 16))
+    weights = {}
+    for e in sample_e + ([w.E] if w.shared_f else []):
+        gu = torch.empty((2 * w.f, w.d), dtype=torch.bfloat16)
+        dn = torch.empty((w.d, w.f), dtype=torch.bfloat16)
+        if e == w.E:
+            mi.randn_torch(w.seed, mi.SHARED, 0, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[:w.f])
+            mi.randn_torch(w.seed, mi.SHARED, 1, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[w.f:])
+            mi.randn_torch(w.seed, mi.SHARED, 2, w.d, w.f, w.sigma_w, w.dtype, "cpu", out=dn)
+        else:
+            mi.randn_torch(w.seed, mi.W_GATE, e, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[:w.f])
+            mi.randn_torch(w.seed, mi.W_UP, e, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[w.f:])
+            mi.randn_torch(w.seed, mi.W_DOWN, e, w.d, w.f, w.sigma_w, w.dtype, "cpu", out=dn)
+        weights[e] = (gu.float().numpy(), dn.float().numpy())
+    x = mi.x_np(w)
+    wr = mi.w_router_np(w)
+    bias = mi.expert_bias(w)
+    t0 = time.perf_counter()
+    idx, wt, _ = O.route(x, wr, bias, w.k, w.score)
+    off, row_of, src = O.permutation(idx, w.E)
+    flops = 0.0
+    for e in sample_e:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            O.expert_forward(x[src[lo:hi]], weights[e][0], weights[e][1], O.round_bf16)
+            flops += 6.0 * (hi - lo) * w.d * w.f
+    if w.shared_f:
+        O.expert_forward(x[:512], weights[w.E][0], weights[w.E][1], O.round_bf16)
+        flops += 6.0 * 512 * w.d * w.shared_f
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"fp64 numpy oracle: route + permutation of all {w.T} tokens, then the SwiGLU experts "
+                      f"of expert ids 0,16,...,{sample_e[-1]} ({len(sample_e)} of {w.E}) on their real rows"
+                      + (" and the shared expert on 512 tokens" if w.shared_f else "")
+                      + "; value = their useful FLOPs / wall time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import moe_inputs as mi
+    from dropless_mixture_experts_device_amd import _lib as L
+    from dropless_mixture_experts_device_amd import layer
+
+    w = mi.WORKLOADS[args.workload]
+    assert w.dtype == "bf16" and not w.mxfp8, "bench times the bf16 forward workloads"
+    torch.cuda.init()
+    dev = "cuda"
+    x = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.X, 0, w.T, w.d, w.sigma_x, w.dtype, dev, out=x)
+    wr = torch.empty((w.E, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.W_ROUTER, 0, w.E, w.d, w.sigma_w, w.dtype, dev, out=wr)
+    b = mi.expert_bias(w)
+    bias = None if b is None else torch.from_numpy(b).to(dev)
+    n = w.E + (1 if w.shared_f else 0)
+    w_gu = torch.empty((n, 2 * w.f, w.d), dtype=torch.bfloat16, device=dev)
+    w_down = torch.empty((n, w.d, w.f), dtype=torch.bfloat16, device=dev)
+    mi.fill_weights_torch(w, w_gu, w_down, dev)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    fused = not args.materialise_gather
+    buf = layer.LayerBuffers(s, dev, fused_gather=fused)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+
+    def step(evs=None):
+        if evs: evs[0].record(stream)
+        layer.route(x, wr, bias, s, buf)
+        if evs: evs[1].record(stream)
+        layer.permute(x, s, buf)
+        if evs: evs[2].record(stream)
+        if buf.fused_gather:
+            L.moe_grouped_gemm(x, w_gu, buf.H, buf.offsets, L.MOE_EPI_SWIGLU, a_rows=buf.src_token,
+                               workspace=buf.ws_gemm1)
+        else:
+            L.moe_grouped_gemm(buf.x_perm, w_gu, buf.H, buf.offsets, L.MOE_EPI_SWIGLU, workspace=buf.ws_gemm1)
+        if evs: evs[3].record(stream)
+        L.moe_grouped_gemm(buf.H, w_down, buf.Y, buf.offsets, L.MOE_EPI_NONE, workspace=buf.ws_gemm2)
+        if evs: evs[4].record(stream)
+        layer.combine(s, buf)
+        if evs: evs[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    parts = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(5)] for i in range(args.steps)])
+    pm = parts.mean(0)    # route, permute, gemm1, gemm2, combine (ms)
+
+    counts = np.diff(buf.offsets.cpu().numpy())[:w.E]
+    flops = useful_flops(w, counts)
+    rows = w.T * w.k + (w.T if w.shared_f else 0)
+    g1_flops = 2.0 * rows * w.d * 2 * w.f
+    g1_bytes = gemm1_bytes(w, counts, fused)
+    g1_ms = pm[2]
+    g1_tflops = g1_flops / (g1_ms * 1e-3) / 1e12
+    g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
+    t_hbm, t_mfma = g1_bytes / (HBM_PEAK_GBS * 1e9), g1_flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g1_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "moe_grouped_gemm gate/up+SwiGLU (schedule + main kernel)",
+                 "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops, "ms": round(g1_ms, 4),
+                 "tflops": round(g1_tflops, 1), "gbs": round(g1_gbs, 1)})
+    route_bytes = w.T * w.d * 2 + w.E * w.d * 2 + w.T * w.k * 8
+    perm_bytes = w.T * w.k * 4 * 4 + (0 if fused else (w.T * w.d * 2 + rows * w.d * 2))
+    comb_bytes = w.T * w.k * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2 + (w.T * w.d * 2 if w.shared_f else 0)
+    res = {
+        "metric": "MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped bf16",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded hash-table normal inputs, Zipf/linear expert-bias skew; random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "score": w.score,
+                   "shared_f": w.shared_f, "gather": "fused into GEMM 1" if fused else "materialised x_perm",
+                   "groups_nonempty": int(np.count_nonzero(counts)), "group_max": int(counts.max()),
+                   "group_min": int(counts.min()), "groups_empty": int((counts == 0).sum())},
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "gemm_tflops": round(flops / ((pm[2] + pm[3]) * 1e-3) / 1e12, 2),
+        "stage_ms": {"route": round(pm[0], 4), "permute": round(pm[1], 4), "gemm1_swiglu": round(pm[2], 4),
+                     "gemm2": round(pm[3], 4), "combine": round(pm[4], 4)},
+        "stage_gbs": {"route": round(route_bytes / (pm[0] * 1e-3) / 1e9, 1),
+                      "permute": round(perm_bytes / (pm[1] * 1e-3) / 1e9, 1),
+                      "combine": round(comb_bytes / (pm[4] * 1e-3) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, None)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+"""ctypes binding of libmoe.so: one Python function per C entry point, same names.
+
+Only argument marshalling lives here (tensor -> device pointer, the current HIP stream,
+status -> exception). Every step of the computation runs in the HIP library; there is no
+fallback: if libmoe.so is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run dropless_mixture_experts_device_amd.build.build()")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM = 0, 1, 2
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class MoeGemmArgs(ctypes.Structure):
+    """Mirror of moe_gemm_args_t (include/moe.h)."""
+    _fields_ = [
+        ("G", _i32), ("offsets", _vp), ("M", _i64), ("N", _i64), ("K", _i64),
+        ("A", _vp), ("a_dtype", _i32), ("lda", _i64), ("A_rows", _i64), ("a_rows", _vp),
+        ("B", _vp), ("b_dtype", _i32), ("ldb", _i64), ("b_group_stride", _i64),
+        ("C", _vp), ("c_dtype", _i32), ("ldc", _i64),
+        ("epilogue", _i32), ("aux", _vp), ("ld_aux", _i64),
+    ]
+
+
+_lib.moe_status_str.argtypes = [_i32]
+_lib.moe_status_str.restype = ctypes.c_char_p
+_lib.moe_workspace_bytes.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32]
+_lib.moe_workspace_bytes.restype = _sz
+_lib.moe_route.argtypes = [_vp, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_route.restype = _i32
+_lib.moe_permute.argtypes = [_vp, _i32, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_permute.restype = _i32
+_lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), _vp, _sz, _vp]
+_lib.moe_grouped_gemm.restype = _i32
+_lib.moe_combine.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+_lib.moe_combine.restype = _i32
+
+EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_str(status)}")
+        self.status = status
+
+
+def moe_status_str(status: int) -> str:
+    return _lib.moe_status_str(status).decode()
+
+
+def moe_workspace_bytes(op: int, T: int = 0, d: int = 0, E: int = 0, k: int = 0, G: int = 0) -> int:
+    return int(_lib.moe_workspace_bytes(op, T, d, E, k, G))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.uint8:
+        return MOE_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ws(ws):
+    return (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def moe_route(x, w_router, bias, k: int, score: int, topk_idx, topk_w, keys_out=None, stream=None):
+    """x [T,d], w_router [E,d] (bf16 or fp32), bias [E] fp32 or None -> topk_idx int32 [T,k],
+    topk_w fp32 [T,k], keys_out fp32 [T,E] (optional)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    _check("moe_route", _lib.moe_route(_ptr(x), _ptr(w_router), _dtype(x), _ptr(bias), T, d, E, k, score,
+                                       _ptr(topk_idx), _ptr(topk_w), _ptr(keys_out), None, 0, _stream(stream)))
+
+
+def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_token, x_perm, workspace,
+                stream=None, d: int | None = None, dtype: int | None = None):
+    """topk_idx int32 [T,k] -> offsets [E+1(+1)], row_of [T,k], src_token [T*k(+T)], and x_perm
+    [T*k(+T), d] = x[src_token] when x_perm is given."""
+    T, k = topk_idx.shape
+    if d is None:
+        d = x.shape[1] if x is not None else 0
+    if dtype is None:
+        dtype = _dtype(x) if x is not None else MOE_BF16
+    ws, wsb = _ws(workspace)
+    _check("moe_permute", _lib.moe_permute(_ptr(x), dtype, _ptr(topk_idx), T, d, E, k, 1 if shared_group else 0,
+                                           _ptr(offsets), _ptr(row_of), _ptr(src_token), _ptr(x_perm), ws, wsb,
+                                           _stream(stream)))
+
+
+def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None, aux=None, workspace=None,
+                     stream=None):
+    """C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate) * up), one launch.
+
+    A [A_rows, K]; B [G, N or 2N, K]; C [M, N]; offsets int32 [G+1] (device); a_rows int32 [M].
+    """
+    G = B.shape[0]
+    M, N = C.shape
+    K = A.shape[1]
+    args = MoeGemmArgs(
+        G=G, offsets=offsets.data_ptr(), M=M, N=N, K=K,
+        A=A.data_ptr(), a_dtype=_dtype(A), lda=A.stride(0), A_rows=A.shape[0],
+        a_rows=None if a_rows is None else a_rows.data_ptr(),
+        B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(1), b_group_stride=B.stride(0),
+        C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
+        epilogue=epilogue, aux=None if aux is None else aux.data_ptr(), ld_aux=0 if aux is None else aux.stride(0))
+    ws, wsb = _ws(workspace)
+    _check("moe_grouped_gemm", _lib.moe_grouped_gemm(ctypes.byref(args), ws, wsb, _stream(stream)))
+
+
+def moe_combine(y, topk_w, row_of, y_shared, out, stream=None):
+    """out[t] = sum_j topk_w[t,j] * y[row_of[t,j]] (+ y_shared[t])."""
+    T, k = row_of.shape
+    d = out.shape[1]
+    _check("moe_combine", _lib.moe_combine(_ptr(y), _dtype(out), _ptr(topk_w), _ptr(row_of), _ptr(y_shared), T, d, k,
+                                           _ptr(out), _stream(stream)))

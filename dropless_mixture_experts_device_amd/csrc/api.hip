@@ -1,0 +1,27 @@
+// Host-only parts of the C ABI: status strings and workspace sizes.
+#include "moe_internal.h"
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t E);
+size_t moe_gemm_workspace_bytes(int32_t G);
+
+extern "C" const char* moe_status_str(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_ENOTSUP: return "MOE_ENOTSUP: unsupported dtype or option";
+        case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
+        case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+        default: return "MOE_UNKNOWN_STATUS";
+    }
+}
+
+extern "C" size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G) {
+    (void)d;
+    (void)k;
+    switch (op) {
+        case MOE_OP_ROUTE: return 0;
+        case MOE_OP_PERMUTE: return moe_permute_workspace_bytes(T, E);
+        case MOE_OP_GROUPED_GEMM: return moe_gemm_workspace_bytes(G);
+        default: return 0;
+    }
+}

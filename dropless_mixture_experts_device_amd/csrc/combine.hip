@@ -1,0 +1,112 @@
+// moe_combine: return every expert output row to its token and sum them with the routing
+// weights (plus the always-on shared expert), in a fixed order with fp32 accumulation.
+//
+// [Blog] "Optimisation 2": combine brings each processed token back to its original
+// position and accumulates the experts' results. Written as a gather-reduce per token
+// rather than a scatter-add: every output element is produced by exactly one lane, so the
+// result is deterministic and needs no atomics or zero-initialised output.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCombThreads = 256;
+
+template <int ESIZE>
+__device__ __forceinline__ void load8(const char* p, float (&v)[8]) {
+    if (ESIZE == 2) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(q[i] << 16);
+            v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+        }
+    } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    }
+}
+
+template <int ESIZE>
+__device__ __forceinline__ void store8(char* p, const float (&v)[8]) {
+    if (ESIZE == 2) {
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        *reinterpret_cast<u32x4*>(p) = q;
+    } else {
+        u32x4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = __float_as_uint(v[i]);
+            b[i] = __float_as_uint(v[4 + i]);
+        }
+        *reinterpret_cast<u32x4*>(p) = a;
+        *reinterpret_cast<u32x4*>(p + 16) = b;
+    }
+}
+
+// One workgroup per token; each thread owns 8 consecutive columns at a time.
+template <int ESIZE>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __restrict__ y,
+                                                               const float* __restrict__ topk_w,
+                                                               const int32_t* __restrict__ row_of,
+                                                               const char* __restrict__ y_shared, int T, int d,
+                                                               int k, char* __restrict__ out) {
+    const int t = blockIdx.x;
+    __shared__ int rows[16];
+    __shared__ float wts[16];
+    const int TK = T * k;
+    if (threadIdx.x < k) {
+        rows[threadIdx.x] = min(max(row_of[(int64_t)t * k + threadIdx.x], 0), TK - 1);
+        wts[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const int ngroups = d / 8;
+    const int64_t rowbytes = (int64_t)d * ESIZE;
+    for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            float v[8];
+            load8<ESIZE>(y + rows[j] * rowbytes + c * 8 * ESIZE, v);
+            const float w = wts[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+        }
+        if (y_shared != nullptr) {
+            float v[8];
+            load8<ESIZE>(y_shared + t * rowbytes + c * 8 * ESIZE, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
+        store8<ESIZE>(out + t * rowbytes + c * 8 * ESIZE, acc);
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, const int32_t* row_of,
+                                    const void* y_shared, int64_t T, int64_t d, int32_t k, void* out,
+                                    void* stream) {
+    if (T < 0 || d <= 0 || d % 8 != 0 || k < 1 || k > 16) return MOE_EINVAL;
+    if (T * (int64_t)k > INT32_MAX || d > INT32_MAX / 16) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!y || !topk_w || !row_of || !out) return MOE_EINVAL;
+    if (!moe_aligned16(y) || !moe_aligned16(out) || (y_shared && !moe_aligned16(y_shared))) return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(moe::combine_kernel<2>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
+                           (const char*)y, topk_w, row_of, (const char*)y_shared, (int)T, (int)d, k, (char*)out);
+    else
+        hipLaunchKernelGGL(moe::combine_kernel<4>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
+                           (const char*)y, topk_w, row_of, (const char*)y_shared, (int)T, (int)d, k, (char*)out);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}

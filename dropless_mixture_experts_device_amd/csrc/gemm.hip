@@ -1,0 +1,462 @@
+// moe_grouped_gemm: one launch computes every group's product at its real row count.
+//
+// [Blog] "Optimisation 1": a grouped GEMM runs all experts' matmuls in one kernel call, each
+// at its actual token count, and computes only the regions that hold real tokens; the
+// alternatives (a host loop over experts after a device-to-host copy of the counts, or a
+// batched GEMM padded to the worst case) are what it replaces. [Blog] Figure 3 paragraph:
+// the grouped MLP is two such GEMMs, gate/up then down.
+//
+// Design (gfx950):
+//  * A one-workgroup schedule kernel turns the device-resident group offsets into a tile
+//    prefix (tiles of group g start at tile_start[g]); the host never sees group sizes.
+//  * Each group gets its own tile height BM in {16, 32, 64, 128} from its row count, so tiny
+//    groups do not pay for 128-row tiles and empty groups get no tile at all.
+//  * Persistent workgroups (one per CU, 4 waves) walk the tile list; tiles are ordered
+//    group by group, in supertiles of 4 column tiles x all row tiles, and handed out so the
+//    32 CUs of one XCD work on 32 consecutive tiles (shared A/B panels hit that XCD's L2).
+//  * Operands go global -> LDS with 16-byte DMA loads (no VGPR staging) through a 3-stage
+//    ring of 64-wide K slices; LDS rows are XOR-swizzled so the MFMA fragment reads are
+//    bank-conflict free; products use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//  * The epilogue (optional SwiGLU) goes through LDS so that C is written in 16-byte
+//    coalesced chunks.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBN = 256;            // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
+constexpr int kBK = 64;             // K elements per pipeline stage (128 bytes of bf16)
+constexpr int kStages = 3;
+constexpr int kMaxBM = 128;
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStageBytes = (kMaxBM + kBN) * kRowBytes;   // 48 KiB
+constexpr int kPipeBytes = kStages * kStageBytes;         // 144 KiB
+constexpr int kMaxGroups = 4095;
+constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;   // 160 KiB
+constexpr int kSuper = 4;           // column tiles per supertile
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ int bm_of_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
+
+// Rows [begin, end) of group g, clamped into [0, M] so that inconsistent offsets can never
+// send a load or store outside the buffers.
+__device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int M, int& begin, int& end) {
+    begin = min(max(offsets[g], 0), M);
+    end = min(max(offsets[g + 1], begin), M);
+}
+
+struct GemmParams {
+    const int32_t* offsets;
+    int G;
+    int M;          // rows of C (row indices are clamped to it)
+    int N;          // output columns
+    int K;
+    int NT;         // column tiles per group
+    const char* A;
+    int64_t lda;
+    int64_t A_rows;
+    const int32_t* a_rows;
+    const char* B;
+    int64_t ldb;
+    int64_t b_stride;
+    char* C;
+    int64_t ldc;
+    int c_f32;
+    char* aux;
+    int64_t ld_aux;
+    const int32_t* tile_start;   // [G+1] in workspace
+};
+
+// ---------------------------------------------------------------------------------------
+// schedule: tile_start[g] = sum over groups < g of ceil(m_g / BM_g) * NT
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
+                                                             int NT, int32_t* __restrict__ tile_start) {
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int g0 = 0; g0 < G; g0 += 1024) {
+        const int g = g0 + tid;
+        int tiles = 0;
+        if (g < G) {
+            int b, e;
+            group_rows(offsets, g, M, b, e);
+            const int m = e - b;
+            tiles = m > 0 ? cdiv(m, bm_of_rows(m)) * NT : 0;
+        }
+        int incl = tiles;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += o;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int wbase = carry_s;
+        for (int w = 0; w < wave; ++w) wbase += wsum[w];
+        if (g < G) tile_start[g] = wbase + incl - tiles;
+        __syncthreads();
+        if (tid == 1023) carry_s = wbase + incl;
+        __syncthreads();
+    }
+    if (tid == 0) tile_start[G] = carry_s;
+}
+
+// ---------------------------------------------------------------------------------------
+// one output tile of BM rows x (256 B-rows) for group g
+// ---------------------------------------------------------------------------------------
+template <int BM, bool SWIGLU>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
+    constexpr int WM = BM >= 128 ? 2 : 1;
+    constexpr int WN = 4 / WM;
+    constexpr int WTM = BM / WM;              // rows per wave
+    constexpr int WTN = kBN / WN;             // B rows (tile columns) per wave
+    constexpr int MI = WTM / 16;
+    constexpr int NI = WTN / 16;
+    constexpr int A_INSTR = BM / 8;           // 1 KiB DMA instructions for the A slice
+    constexpr int A_PER_WAVE = cdiv(A_INSTR, 4);
+    constexpr int B_PER_WAVE = kBN / 8 / 4;   // 8
+    constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    int row_begin, row_end;
+    group_rows(p.offsets, g, p.M, row_begin, row_end);
+    const int r0 = row_begin + mt * BM;                   // first C row of the tile
+    const int n0 = nt * BN_OUT;                           // first output column
+
+    // per-lane global source pointers for the DMA loads (fixed for the whole K loop)
+    const char* a_src[A_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+        const int instr = wave + 4 * i;
+        const int row = instr * 8 + lane / 8;
+        const int chunk = (lane % 8) ^ swz(row);
+        int r = min(r0 + row, row_end - 1);
+        int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
+        ar = ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
+        a_src[i] = p.A + (ar * p.lda + chunk * 8) * 2;
+    }
+    const char* b_src[B_PER_WAVE];
+    const char* bg = p.B + (int64_t)g * p.b_stride * 2;
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+        const int instr = wave * B_PER_WAVE + i;
+        const int rho = instr * 8 + lane / 8;             // LDS row of the B slice
+        const int chunk = (lane % 8) ^ swz(rho);
+        int grow;
+        if (SWIGLU) {
+            const int wnb = rho / WTN, within = rho % WTN;
+            const int half = within / (WTN / 2), idx = within % (WTN / 2);
+            const int col = min(n0 + wnb * (WTN / 2) + idx, p.N - 1);
+            grow = half * p.N + col;
+        } else {
+            grow = min(n0 + rho, p.N - 1);
+        }
+        b_src[i] = bg + ((int64_t)grow * p.ldb + chunk * 8) * 2;
+    }
+
+    auto issue = [&](int kt) {
+        char* st = lds + (kt % kStages) * kStageBytes;
+        const int64_t koff = (int64_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < A_PER_WAVE; ++i) {
+            const int instr = wave + 4 * i;
+            if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
+        }
+        char* stb = st + BM * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < B_PER_WAVE; ++i) load_lds16(b_src[i] + koff, stb + (wave * B_PER_WAVE + i) * 1024);
+    };
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = p.K / kBK;
+    // waves 2 and 3 issue fewer A loads when BM == 16; the wait count uses the smallest
+    // per-wave load count so that every wave is sure its own stage kt has landed
+    constexpr int LOADS_MIN = B_PER_WAVE + (A_INSTR >= 4 ? A_INSTR / 4 : 0);
+
+    lds_barrier();   // the previous tile's epilogue may still read LDS
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) wait_vm_lgkm0<LOADS_MIN>();
+        else wait_vm_lgkm0<0>();
+        lds_barrier();
+        if (kt + 2 < nk) issue(kt + 2);
+        const char* sa = lds + (kt % kStages) * kStageBytes;
+        const char* sb = sa + BM * kRowBytes;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int chunk = ks * 4 + lane / 16;
+            bf16x8 af[MI], bfr[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * WTM + i * 16 + lane % 16;
+                af[i] = *reinterpret_cast<const bf16x8*>(sa + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int row = wn * WTN + j * 16 + lane % 16;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    const int esize = p.c_f32 ? 4 : 2;
+    const int pitch = BN_OUT * esize + 16;
+    const int rows_valid = min(BM, row_end - r0);
+    constexpr int NO = SWIGLU ? NI / 2 : NI;       // output fragments per wave row block
+    constexpr int WOUT = SWIGLU ? WTN / 2 : WTN;   // output columns per wave
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int col = wn * WOUT + j * 16 + lane % 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * WTM + i * 16 + (lane / 16) * 4 + r;
+                float v;
+                if (SWIGLU) {
+                    const float gv = acc[i][j][r], uv = acc[i][j + NO][r];
+                    v = silu(gv) * uv;
+                    if (p.aux != nullptr && row < rows_valid && n0 + col < p.N) {
+                        char* ap = p.aux + ((int64_t)(r0 + row) * p.ld_aux + n0 + col) * esize;
+                        char* up = p.aux + ((int64_t)(r0 + row) * p.ld_aux + p.N + n0 + col) * esize;
+                        if (p.c_f32) {
+                            *reinterpret_cast<float*>(ap) = gv;
+                            *reinterpret_cast<float*>(up) = uv;
+                        } else {
+                            *reinterpret_cast<uint16_t*>(ap) = f32_to_bf16(gv);
+                            *reinterpret_cast<uint16_t*>(up) = f32_to_bf16(uv);
+                        }
+                    }
+                } else {
+                    v = acc[i][j][r];
+                }
+                char* dst = lds + row * pitch + col * esize;
+                if (p.c_f32) *reinterpret_cast<float*>(dst) = v;
+                else *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(v);
+            }
+        }
+    lds_barrier();
+    const int chunks_per_row = BN_OUT * esize / 16;
+    const int cols_per_chunk = 16 / esize;
+    for (int c = tid; c < BM * chunks_per_row; c += kThreads) {
+        const int row = c / chunks_per_row, ch = c % chunks_per_row;
+        const int col = n0 + ch * cols_per_chunk;
+        if (row < rows_valid && col < p.N) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + ch * 16);
+            *reinterpret_cast<u32x4*>(p.C + ((int64_t)(r0 + row) * p.ldc + col) * esize) = v;
+        }
+    }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
+    for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
+    __syncthreads();
+    const int total = ts[p.G];
+    // XCD-aware slot: the hardware deals workgroups round-robin over the 8 XCDs, so give the
+    // workgroups of one XCD consecutive slots (and hence consecutive tiles in each round)
+    const int nxcd = (gridDim.x % 8 == 0) ? 8 : 1;
+    const int per_xcd = gridDim.x / nxcd;
+    const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
+    for (int tile = slot; tile < total; tile += gridDim.x) {
+        // group = last g with ts[g] <= tile
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ts[mid] <= tile) lo = mid;
+            else hi = mid - 1;
+        }
+        const int g = lo;
+        const int L = tile - ts[g];
+        int gb, ge;
+        group_rows(p.offsets, g, p.M, gb, ge);
+        const int m = ge - gb;
+        const int bm = bm_of_rows(m);
+        const int MT = cdiv(m, bm);
+        const int NT = p.NT;
+        const int full = NT / kSuper;
+        int mt, nt;
+        if (L < full * MT * kSuper) {
+            const int s = L / (MT * kSuper), rem = L % (MT * kSuper);
+            mt = rem / kSuper;
+            nt = s * kSuper + rem % kSuper;
+        } else {
+            const int rem = L - full * MT * kSuper, w = NT - full * kSuper;
+            mt = rem / w;
+            nt = full * kSuper + rem % w;
+        }
+        switch (bm) {
+            case 16: gemm_tile<16, SWIGLU>(p, lds, g, mt, nt); break;
+            case 32: gemm_tile<32, SWIGLU>(p, lds, g, mt, nt); break;
+            case 64: gemm_tile<64, SWIGLU>(p, lds, g, mt, nt); break;
+            default: gemm_tile<128, SWIGLU>(p, lds, g, mt, nt); break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 grouped GEMM: one thread per output element, sequential fp32 dot products.
+// Meant for small fp32 layers (correctness, not speed).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p, int64_t M, int swiglu) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * p.N) return;
+    const int r = (int)(idx / p.N), n = (int)(idx % p.N);
+    int g = -1;
+    for (int q = 0; q < p.G; ++q) {     // small G only: a linear search is fine
+        int b, e;
+        group_rows(p.offsets, q, p.M, b, e);
+        if (r >= b && r < e) { g = q; break; }
+    }
+    if (g < 0) return;
+    int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
+    ar = ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
+    const float* a = reinterpret_cast<const float*>(p.A) + ar * p.lda;
+    const float* b = reinterpret_cast<const float*>(p.B) + (int64_t)g * p.b_stride;
+    float s = 0.f, u = 0.f;
+    for (int kk = 0; kk < p.K; ++kk) s = fmaf(a[kk], b[(int64_t)n * p.ldb + kk], s);
+    float v = s;
+    if (swiglu) {
+        for (int kk = 0; kk < p.K; ++kk) u = fmaf(a[kk], b[(int64_t)(p.N + n) * p.ldb + kk], u);
+        v = silu(s) * u;
+        if (p.aux) {
+            float* ax = reinterpret_cast<float*>(p.aux);
+            ax[(int64_t)r * p.ld_aux + n] = s;
+            ax[(int64_t)r * p.ld_aux + p.N + n] = u;
+        }
+    }
+    if (p.c_f32) reinterpret_cast<float*>(p.C)[(int64_t)r * p.ldc + n] = v;
+    else reinterpret_cast<uint16_t*>(p.C)[(int64_t)r * p.ldc + n] = f32_to_bf16(v);
+}
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+bool set_lds_attr() {
+    static bool done[2] = {false, false};
+    if (!done[0]) {
+        if (hipFuncSetAttribute((const void*)gemm_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsBytes) != hipSuccess)
+            return false;
+        done[0] = true;
+    }
+    if (!done[1]) {
+        if (hipFuncSetAttribute((const void*)gemm_bf16_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsBytes) != hipSuccess)
+            return false;
+        done[1] = true;
+    }
+    return true;
+}
+
+}  // namespace
+}  // namespace moe
+
+size_t moe_gemm_workspace_bytes(int32_t G) {
+    if (G < 1) G = 1;
+    return (((size_t)G + 1) * 4 + 255) & ~size_t(255);
+}
+
+extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    if (!a) return MOE_EINVAL;
+    if (a->G < 1 || a->G > moe::kMaxGroups || !a->offsets) return MOE_EINVAL;
+    if (a->M < 0 || a->N <= 0 || a->K <= 0 || a->N % 8 != 0 || a->N > (1 << 24) || a->K > (1 << 24))
+        return MOE_EINVAL;
+    if (a->M > INT32_MAX / 2) return MOE_EINVAL;
+    if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_EINVAL;
+    if (a->a_dtype != a->b_dtype) return MOE_ENOTSUP;
+    if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32) return MOE_ENOTSUP;
+    if (a->c_dtype != MOE_BF16 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
+    if (a->a_dtype == MOE_F32 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
+    if (a->M == 0) return MOE_OK;
+    if (!a->A || !a->B || !a->C || a->A_rows <= 0) return MOE_EINVAL;
+    const int64_t nb = a->epilogue == MOE_EPI_SWIGLU ? 2 * a->N : a->N;
+    if (a->lda < a->K || a->ldb < a->K || a->ldc < a->N || a->b_group_stride < nb * a->ldb) return MOE_EINVAL;
+    if (a->aux && (a->epilogue != MOE_EPI_SWIGLU || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
+    if (!workspace || workspace_bytes < moe_gemm_workspace_bytes(a->G)) return MOE_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+
+    moe::GemmParams p;
+    p.offsets = a->offsets;
+    p.G = a->G;
+    p.M = (int)a->M;
+    p.N = (int)a->N;
+    p.K = (int)a->K;
+    p.A = (const char*)a->A;
+    p.lda = a->lda;
+    p.A_rows = a->A_rows;
+    p.a_rows = a->a_rows;
+    p.B = (const char*)a->B;
+    p.ldb = a->ldb;
+    p.b_stride = a->b_group_stride;
+    p.C = (char*)a->C;
+    p.ldc = a->ldc;
+    p.c_f32 = a->c_dtype == MOE_F32 ? 1 : 0;
+    p.aux = (char*)a->aux;
+    p.ld_aux = a->ld_aux;
+    p.tile_start = (const int32_t*)workspace;
+    const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
+
+    if (a->a_dtype == MOE_F32) {
+        p.NT = 0;
+        const int64_t n = a->M * a->N;
+        hipLaunchKernelGGL(moe::gemm_f32_kernel, dim3((unsigned)moe::cdiv<int64_t>(n, 256)), dim3(256), 0, s, p,
+                           a->M, swiglu ? 1 : 0);
+        MOE_CHECK_LAUNCH();
+        return MOE_OK;
+    }
+    // bf16 MFMA path
+    if (a->K % moe::kBK != 0) return MOE_EINVAL;
+    if (!moe_aligned16(a->A) || !moe_aligned16(a->B) || !moe_aligned16(a->C)) return MOE_EINVAL;
+    if (a->lda % 8 || a->ldb % 8 || a->ldc % 8 || a->b_group_stride % 8) return MOE_EINVAL;
+    if (a->aux && (!moe_aligned16(a->aux) || a->ld_aux % 8)) return MOE_EINVAL;
+    const int bn_out = swiglu ? moe::kBN / 2 : moe::kBN;
+    p.NT = (int)moe::cdiv<int64_t>(a->N, bn_out);
+    if (!moe::set_lds_attr()) return MOE_EHIP;
+    hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
+                       (int32_t*)workspace);
+    MOE_CHECK_LAUNCH();
+    // enough persistent workgroups to fill every CU, never more than the tile bound
+    const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;
+    const int64_t grid = std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
+    if (swiglu)
+        hipLaunchKernelGGL(moe::gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(moe::kThreads), moe::kLdsBytes, s, p);
+    else
+        hipLaunchKernelGGL(moe::gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(moe::kThreads), moe::kLdsBytes, s, p);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}

@@ -1,0 +1,64 @@
+// Internal helpers shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt untouched). The gfx9 encoding keeps
+// vmcnt in bits [3:0] and [15:14], expcnt in [6:4], lgkmcnt in [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier that does NOT drain outstanding global->LDS loads (the fence inside
+// __syncthreads would wait for every one of them). Callers wait for exactly the loads they
+// need with wait_vm_lgkm0<N>() first. The empty asm statements stop the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes from global memory straight into LDS. Lane i of the wave writes LDS bytes
+// [lds_wave_base + 16 i, +16); lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gptr, MOE_LDS(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+template <typename T>
+__host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
+
+}  // namespace moe
+
+#define MOE_CHECK_LAUNCH()                                  \
+    do {                                                    \
+        if (hipGetLastError() != hipSuccess) return MOE_EHIP; \
+    } while (0)
+
+static inline bool moe_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -1,0 +1,234 @@
+// moe_route: router projection (bf16 MFMA, fp32 accumulate), expert bias, top-k selection
+// and normalised routing weights, fused in one kernel per 32-token tile.
+//
+// [Blog] opening section: a learnable router picks each token's top-K experts;
+// [Blog] "Optimisation 2": a single fused router kernel assigns the experts.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouteBT = 32;       // tokens per workgroup
+constexpr int kRouteThreads = 256; // 4 waves
+
+// Map a float to an unsigned key whose unsigned order is the float order (-0 folded to +0).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, s, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Top-k over keys held in LDS ([kRouteBT][pitch] floats, bias already added). Each wave
+// handles tokens wave, wave+4, ... of the tile. Selection order: larger key first, equal
+// keys -> lower expert id (the packed low word is ~e, so the larger packed value wins).
+template <int NQ>
+__device__ void topk_tile(const float* keys, int pitch, int t0, int T, int E, int k, int score,
+                          int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    for (int tl = wave; tl < kRouteBT; tl += kRouteThreads / kWave) {
+        const int t = t0 + tl;
+        if (t >= T) break;
+        uint64_t cand[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int e = q * kWave + lane;
+            cand[q] = (e < E) ? (((uint64_t)ordered_bits(keys[tl * pitch + e]) << 32) | (uint32_t)(~e)) : 0ull;
+        }
+        float sel_key[16];
+        int sel_e[16];
+        for (int j = 0; j < k; ++j) {
+            uint64_t best = 0;
+            int bq = 0;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (cand[q] > best) { best = cand[q]; bq = q; }
+            const uint64_t win = wave_max_u64(best);
+            const int e = (int)(~(uint32_t)win);
+            if (best == win) cand[bq] = 0ull;   // only the owner of e holds this packed value
+            sel_e[j] = e;
+            const uint32_t u = (uint32_t)(win >> 32);
+            sel_key[j] = __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+        }
+        // weights: every lane computes the same normaliser in the same order
+        float z[16];
+        float sum = 0.f;
+        for (int j = 0; j < k; ++j) {
+            z[j] = (score == MOE_SOFTMAX) ? expf(sel_key[j] - sel_key[0]) : 1.0f / (1.0f + expf(-sel_key[j]));
+            sum += z[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            if (lane == j) {
+                topk_idx[(int64_t)t * k + j] = sel_e[j];
+                topk_w[(int64_t)t * k + j] = z[j] / sum;
+            }
+        }
+    }
+}
+
+// bf16 router: each wave owns NTW*16 experts and all 32 tokens of the tile; A (tokens) and
+// B (router rows) fragments are loaded straight from global memory into registers (no LDS:
+// no operand is shared between waves except the small token tile, which stays in L1/L2).
+template <int NTW, int NQ>
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    int T, int d, int E, int k, int score, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ keys_out) {
+    constexpr int EPAD = NTW * 16 * 4;
+    constexpr int PITCH = EPAD + 4;
+    __shared__ float keys[kRouteBT * PITCH];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int t0 = blockIdx.x * kRouteBT;
+    const int ebase = wave * NTW * 16;
+    const int sub = lane / 16;   // which 8-element k chunk of the 32-wide step
+    const int r16 = lane % 16;
+
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int t = t0 + i * 16 + r16;
+        t = t < T ? t : T - 1;
+        arow[i] = x + (int64_t)t * d;
+    }
+    const uint16_t* brow[NTW];
+    bool bval[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        int e = ebase + j * 16 + r16;
+        bval[j] = e < E;
+        brow[j] = w + (int64_t)(e < E ? e : E - 1) * d;
+    }
+    f32x4 acc[2][NTW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int U = 4;   // k-steps of 32 issued together
+    const bf16x8 zero8 = {};
+    for (int k0 = 0; k0 < d; k0 += 32 * U) {
+        bf16x8 af[U][2], bfr[U][NTW];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * 32 + sub * 8;
+            const bool in = kk < d;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[u][i] = in ? *reinterpret_cast<const bf16x8*>(arow[i] + kk) : zero8;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+                bfr[u][j] = (in && bval[j]) ? *reinterpret_cast<const bf16x8*>(brow[j] + kk) : zero8;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][i], bfr[u][j], acc[i][j], 0, 0, 0);
+    }
+    // logits + bias -> LDS; the 16x16 output tile puts rows 4*(lane/16)+r, column lane%16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int e = ebase + j * 16 + r16;
+            const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) keys[(i * 16 + sub * 4 + r) * PITCH + e] = acc[i][j][r] + b;
+        }
+    __syncthreads();
+    if (keys_out != nullptr) {
+        for (int idx = threadIdx.x; idx < kRouteBT * E; idx += kRouteThreads) {
+            const int tl = idx / E, e = idx % E;
+            if (t0 + tl < T) keys_out[(int64_t)(t0 + tl) * E + e] = keys[tl * PITCH + e];
+        }
+    }
+    topk_tile<NQ>(keys, PITCH, t0, T, E, k, score, topk_idx, topk_w);
+}
+
+// fp32 router (small, correctness-oriented): plain fp32 FMA dot products, sequential in d.
+template <int NQ>
+__global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias, int T,
+    int d, int E, int k, int score, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ keys_out) {
+    constexpr int PITCH = NQ * kWave + 4;
+    __shared__ float keys[kRouteBT * PITCH];
+    const int t0 = blockIdx.x * kRouteBT;
+    for (int idx = threadIdx.x; idx < kRouteBT * E; idx += kRouteThreads) {
+        const int tl = idx / E, e = idx % E;
+        const int t = min(t0 + tl, T - 1);
+        const float* xr = x + (int64_t)t * d;
+        const float* wr = w + (int64_t)e * d;
+        float s = 0.f;
+        for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+        keys[tl * PITCH + e] = s + (bias != nullptr ? bias[e] : 0.f);
+    }
+    __syncthreads();
+    if (keys_out != nullptr) {
+        for (int idx = threadIdx.x; idx < kRouteBT * E; idx += kRouteThreads) {
+            const int tl = idx / E, e = idx % E;
+            if (t0 + tl < T) keys_out[(int64_t)(t0 + tl) * E + e] = keys[tl * PITCH + e];
+        }
+    }
+    topk_tile<NQ>(keys, PITCH, t0, T, E, k, score, topk_idx, topk_w);
+}
+
+template <int NTW>
+void launch_route_bf16(dim3 g, hipStream_t s, const void* x, const void* w, const float* b, int T, int d,
+                       int E, int k, int score, int32_t* ti, float* tw, float* ko) {
+    constexpr int NQ = (NTW * 64 + 63) / 64;
+    hipLaunchKernelGGL((route_bf16_kernel<NTW, NQ>), g, dim3(kRouteThreads), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)w, b, T, d, E, k, score, ti, tw, ko);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
+                                  int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
+                                  int32_t* topk_idx, float* topk_w, float* keys_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (T < 0 || d <= 0 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return MOE_EINVAL;
+    if (d % 8 != 0 || T > INT32_MAX / 16 || d > INT32_MAX / 16) return MOE_EINVAL;
+    if (score != MOE_SOFTMAX && score != MOE_SIGMOID) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_idx || !topk_w) return MOE_EINVAL;
+    if (!moe_aligned16(x) || !moe_aligned16(w_router)) return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    dim3 grid((unsigned)moe::cdiv<int64_t>(T, moe::kRouteBT));
+    const int Ti = (int)T, di = (int)d;
+    if (dtype == MOE_BF16) {
+        const int ntw = moe::cdiv(E, 64);   // 16-expert tiles per wave, 4 waves
+        switch (ntw) {
+            case 1: moe::launch_route_bf16<1>(grid, s, x, w_router, bias, Ti, di, E, k, score, topk_idx, topk_w, keys_out); break;
+            case 2: moe::launch_route_bf16<2>(grid, s, x, w_router, bias, Ti, di, E, k, score, topk_idx, topk_w, keys_out); break;
+            default: moe::launch_route_bf16<4>(grid, s, x, w_router, bias, Ti, di, E, k, score, topk_idx, topk_w, keys_out); break;
+        }
+    } else {
+        const int nq = moe::cdiv(E, 64);
+        if (nq <= 1)
+            hipLaunchKernelGGL((moe::route_f32_kernel<1>), grid, dim3(moe::kRouteThreads), 0, s, (const float*)x,
+                               (const float*)w_router, bias, Ti, di, E, k, score, topk_idx, topk_w, keys_out);
+        else
+            hipLaunchKernelGGL((moe::route_f32_kernel<4>), grid, dim3(moe::kRouteThreads), 0, s, (const float*)x,
+                               (const float*)w_router, bias, Ti, di, E, k, score, topk_idx, topk_w, keys_out);
+    }
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}

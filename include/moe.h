@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the dropless mixture-of-experts layer hot path on AMD Instinct MI355X
+ * (gfx950): routing, dispatch (histogram, offsets, permutation, gather), grouped GEMMs over
+ * ragged expert groups with a fused SwiGLU epilogue, weighted combine, and the MXFP8 group
+ * quantiser.
+ *
+ * Sources (cited by page and section; the pages describe the method in words only):
+ *   [Blog]    "Accelerating Dropless MoE Training in JAX with NVIDIA Transformer Engine",
+ *             Chinese rendering on zhiding.cn.
+ *   [Reading] paper-daily deep reading of arXiv 2603.07685.
+ *   [OCP-MX]  OCP Microscaling Formats (MX) Specification v1.0.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named in the signatures are DEVICE pointers unless a comment says "host".
+ *     The caller allocates and frees all device memory (inputs, outputs, workspace); the
+ *     library never allocates, frees or keeps per-call state, and is re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call only
+ *     enqueues work on it and returns: no host synchronisation, no device-to-host read, so
+ *     group sizes never reach the host and every call can be captured in a HIP graph
+ *     ([Blog] "Optimisations dropless MoE needs": kernels must work without the CPU knowing
+ *     the shapes; [Reading] contribution 4: sync-free kernels for full graph coverage).
+ *   - Matrices are row-major; a leading dimension is counted in elements.
+ *   - Errors the host can see (null pointers, negative or unsupported sizes, misaligned
+ *     pointers, workspace too small) return a status and enqueue nothing. A failed launch
+ *     returns MOE_EHIP. Bad device-side data (an expert id outside [0, E), inconsistent
+ *     offsets) gives unspecified results; every kernel clamps its indices, so it never
+ *     reads or writes outside the buffers described here.
+ *   - Sizes of zero (T = 0, every group empty) are valid and write only what is defined.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,      /* invalid argument (checked on the host; nothing enqueued) */
+    MOE_ENOTSUP = 2,     /* valid but unsupported combination (e.g. dtype pair)       */
+    MOE_EWORKSPACE = 3,  /* workspace pointer NULL or smaller than moe_workspace_bytes */
+    MOE_EHIP = 4         /* a HIP launch failed                                        */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
+typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue_t;
+typedef enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2 } moe_op_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(int32_t status);
+
+/* Device bytes of workspace an entry point needs (0 if none). Arguments that do not apply
+ * to `op` are ignored: ROUTE uses (T, E); PERMUTE uses (T, E); GROUPED_GEMM uses G (the
+ * group count). The result depends only on sizes, never on data. */
+size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G);
+
+/*
+ * moe_route -- the router: logits, expert bias, top-k selection and normalised weights.
+ * [Blog] opening section: a learnable router picks the top-K experts of every token;
+ * [Blog] "Optimisation 2": one fused router kernel assigns the experts.
+ *
+ *   L[t,e]   = sum_i x[t,i] * w_router[e,i]        (fp32 accumulation)
+ *   key[t,e] = L[t,e] + bias[e]                    (fp32; bias may be NULL = 0)
+ *   topk_idx[t,0..k-1] = the k experts with the largest keys, largest first; equal keys
+ *                        go to the lower expert id
+ *   topk_w[t,j]: score == MOE_SOFTMAX: exp(key_j - key_0) / sum_j' exp(key_j' - key_0)
+ *                score == MOE_SIGMOID: s_j / sum_j' s_j',  s_j = 1 / (1 + exp(-key_j))
+ *   keys_out (optional, may be NULL): key[t,e] as float32 [T, E].
+ *
+ *   x        [T, d] of dtype (MOE_BF16 or MOE_F32), leading dimension d
+ *   w_router [E, d] same dtype (row e is expert e's router vector)
+ *   1 <= k <= min(E, 16), 1 <= E <= 256, d % 8 == 0, x and w_router 16-byte aligned.
+ *   Workspace: none (workspace may be NULL).
+ */
+moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
+                       int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
+                       int32_t* topk_idx, float* topk_w, float* keys_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute -- dispatch on one GPU: per-expert histogram, group offsets, permutation and
+ * (optionally) the gather of token rows into expert-contiguous order.
+ * [Blog] "Optimisation 2": dispatch reorders tokens so each expert's tokens are contiguous
+ * and combine later restores the original order; [Blog] "Optimisation 1": group sizes are
+ * never copied to the host.
+ *
+ *   offsets[e]   = number of (token, slot) pairs routed to experts < e; offsets[E] = T*k.
+ *   row_of[t,j]  = the row of pair (t, j) in expert order; rows of one expert are
+ *                  contiguous and in ascending token order (a stable counting sort).
+ *   src_token[r] = the token of row r.
+ *   x_perm[r,:]  = x[src_token[r],:]   (only if x_perm != NULL; x may be NULL otherwise)
+ *   shared_group != 0 appends group E holding every token in order (the always-on shared
+ *   expert): offsets has E+2 entries with offsets[E+1] = T*k + T, src_token and x_perm have
+ *   T*k + T rows, rows T*k + t being token t.
+ *
+ *   topk_idx [T, k] int32 with distinct ids in [0, E) per token.
+ *   x, x_perm: dtype MOE_BF16 or MOE_F32, leading dimension d, d % 8 == 0, 16-byte aligned.
+ *   Workspace: moe_workspace_bytes(MOE_OP_PERMUTE, T, d, E, k, 0) bytes, 256-byte aligned.
+ *   The result is deterministic (no floating point, no order-dependent atomics).
+ */
+moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t* topk_idx,
+                         int64_t T, int64_t d, int32_t E, int32_t k, int32_t shared_group,
+                         int32_t* offsets, int32_t* row_of, int32_t* src_token, void* x_perm,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Arguments of a grouped GEMM over ragged row groups (the "grouped_gemm / ragged_dot"
+ * contract of [Blog] "Optimisation 1": one call runs every expert's product at its actual
+ * token count and computes only the rows that exist; [Blog] Figure 3 paragraph: two such
+ * GEMMs form the grouped MLP).
+ *
+ * For each group g with rows r in [offsets[g], offsets[g+1]):
+ *   epilogue NONE:   C[r, n] = sum_k A[a(r), k] * B_g[n, k]                  n < N
+ *   epilogue SWIGLU: G = sum_k A[a(r),k] B_g[n,k], U = sum_k A[a(r),k] B_g[N+n,k]
+ *                    C[r, n] = silu(G) * U,  silu(z) = z / (1 + exp(-z))     n < N
+ *                    (B_g has 2N rows: gate rows first, then up rows); when aux != NULL
+ *                    also aux[r, n] = G and aux[r, N+n] = U (in c_dtype).
+ * with a(r) = a_rows[r] if a_rows != NULL (a fused gather) else r, and
+ * B_g = B + g * b_group_stride elements. Accumulation is fp32; C is rounded once.
+ * Rows of C outside [offsets[0], offsets[G]) are not written. Empty groups cost nothing.
+ */
+typedef struct moe_gemm_args {
+    int32_t G;                  /* number of groups (>= 1)                                  */
+    const int32_t* offsets;     /* device [G+1], non-decreasing, offsets[G] <= M            */
+    int64_t M;                  /* rows of C (and of a_rows); a host-known capacity         */
+    int64_t N;                  /* output columns, N % 8 == 0                                */
+    int64_t K;                  /* contraction length, K % 64 == 0                           */
+    const void* A;              /* [A_rows, K], leading dimension lda                        */
+    int32_t a_dtype;            /* MOE_BF16 or MOE_F32 (MOE_E4M3 reserved for MXFP8)         */
+    int64_t lda;
+    int64_t A_rows;             /* rows of A (gather indices are clamped to it)              */
+    const int32_t* a_rows;      /* optional device [M] gather index                          */
+    const void* B;              /* group g: [N or 2N, K] at B + g*b_group_stride, ld = ldb   */
+    int32_t b_dtype;            /* must equal a_dtype                                        */
+    int64_t ldb;
+    int64_t b_group_stride;
+    void* C;                    /* [M, N], leading dimension ldc                             */
+    int32_t c_dtype;            /* MOE_BF16 or MOE_F32                                       */
+    int64_t ldc;
+    int32_t epilogue;           /* moe_epilogue_t                                            */
+    void* aux;                  /* SWIGLU only, optional [M, 2N] pre-activation save        */
+    int64_t ld_aux;
+} moe_gemm_args_t;
+
+/* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
+ * 0, 0, 0, 0, G) bytes (a device-built tile schedule). A, B, C, aux 16-byte aligned, and
+ * lda, ldb, ldc, ld_aux multiples of 8. The args struct is read on the host during the
+ * call only. */
+moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * moe_combine -- restore token order and accumulate the expert outputs.
+ * [Blog] "Optimisation 2": combine returns each processed token to its original position
+ * and sums the experts' results.
+ *
+ *   out[t,:] = sum_{j<k} topk_w[t,j] * y[row_of[t,j],:]  (+ y_shared[t,:] if not NULL)
+ * summed in fp32 in the fixed order j = 0..k-1 then the shared expert, rounded once.
+ *   y        [T*k, d] (rows in expert order), y_shared [T, d] or NULL, out [T, d];
+ *   dtype MOE_BF16 or MOE_F32 for y, y_shared and out; d % 8 == 0; 16-byte aligned.
+ */
+moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, const int32_t* row_of,
+                         const void* y_shared, int64_t T, int64_t d, int32_t k, void* out,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

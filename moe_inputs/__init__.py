@@ -120,6 +120,35 @@ def randn_torch(seed: int, tensor: int, slab: int, rows: int, cols: int, sigma: 
     return out
 
 
+def randint_np(seed: int, tensor: int, slab: int, rows, cols: int, lo: int, hi: int, scale_log2: int) -> np.ndarray:
+    """Integers uniform in [lo, hi] times 2**scale_log2 (float32), from the same hash as
+    `randn_np`; `randint_torch` gives the same values on the device."""
+    if isinstance(rows, (int, np.integer)):
+        rows = np.arange(int(rows), dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    counter = rows[:, None] * cols + np.arange(cols, dtype=np.int64)[None, :]
+    h = _hash_top16(counter, slab_key(seed, tensor, slab))
+    return ((h % (hi - lo + 1) + lo).astype(np.float64) * math.ldexp(1.0, scale_log2)).astype(np.float32)
+
+
+def randint_torch(seed: int, tensor: int, slab: int, rows: int, cols: int, lo: int, hi: int, scale_log2: int,
+                  dtype: str, device, out=None):
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    if out is None:
+        out = torch.empty((rows, cols), dtype=tdt, device=device)
+    flat = out.view(-1)
+    key = slab_key(seed, tensor, slab)
+    n = rows * cols
+    step = 1 << 25
+    for s in range(0, n, step):
+        e = min(n, s + step)
+        c = torch.arange(s, e, dtype=torch.int64, device=device)
+        v = (_hash_top16(c, key) % (hi - lo + 1) + lo).to(torch.float32) * math.ldexp(1.0, scale_log2)
+        flat[s:e] = v.to(tdt)
+    return out
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     """One MoE layer shape and its synthetic-input recipe."""

@@ -1,0 +1,95 @@
+"""The C ABI library loads, exports every entry point the header declares, and rejects bad
+arguments on the host (these calls return before touching the GPU, so they run on CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "dropless_mixture_experts_device_amd", "libmoe.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from dropless_mixture_experts_device_amd import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_symbol():
+    from dropless_mixture_experts_device_amd import _lib as L
+    assert set(_declared()) == set(L.EXPORTED)
+    for n in L.EXPORTED:
+        assert callable(getattr(L, n))
+
+
+def test_status_strings_and_workspace(lib):
+    from dropless_mixture_experts_device_amd import _lib as L
+    assert L.moe_status_str(0) == "MOE_OK"
+    assert "invalid" in L.moe_status_str(1)
+    assert L.moe_workspace_bytes(L.MOE_OP_ROUTE, 8192, 7168, 256, 8, 0) == 0
+    pb = L.moe_workspace_bytes(L.MOE_OP_PERMUTE, 8192, 7168, 256, 8, 0)
+    assert pb >= (8192 // 64) * 256 * 12
+    assert L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, 257) >= 258 * 4
+
+
+def test_host_argument_errors_enqueue_nothing(lib):
+    from dropless_mixture_experts_device_amd import _lib as L
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every call fails validation
+    # k > E
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 16, 64, 4, 5, 0, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    # E too large, bad score, bad dtype, d not a multiple of 8, null output
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 16, 64, 300, 2, 0, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 16, 64, 8, 2, 7, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    assert L._lib.moe_route(fake, fake, L.MOE_E4M3, None, 16, 64, 8, 2, 0, fake, fake, None, None, 0, None) == L.MOE_ENOTSUP
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 16, 60, 8, 2, 0, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 16, 64, 8, 2, 0, None, fake, None, None, 0, None) == L.MOE_EINVAL
+    # misaligned input
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L._lib.moe_route(odd, fake, L.MOE_BF16, None, 16, 64, 8, 2, 0, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    # T == 0 is a valid no-op
+    assert L._lib.moe_route(None, None, L.MOE_BF16, None, 0, 64, 8, 2, 0, None, None, None, None, 0, None) == L.MOE_OK
+    # permute: workspace missing / too small / misaligned
+    assert L._lib.moe_permute(None, L.MOE_BF16, fake, 64, 64, 8, 2, 0, fake, fake, fake, None, None, 0, None) == L.MOE_EWORKSPACE
+    assert L._lib.moe_permute(None, L.MOE_BF16, fake, 64, 64, 8, 2, 0, fake, fake, fake, None, fake, 16, None) == L.MOE_EWORKSPACE
+    assert L._lib.moe_permute(None, L.MOE_BF16, fake, 64, 64, 8, 9, 0, fake, fake, fake, None, fake, 1 << 20, None) == L.MOE_EINVAL
+    # combine
+    assert L._lib.moe_combine(fake, L.MOE_BF16, fake, fake, None, 16, 60, 2, fake, None) == L.MOE_EINVAL
+    assert L._lib.moe_combine(fake, L.MOE_BF16, fake, None, None, 16, 64, 2, fake, None) == L.MOE_EINVAL
+    # grouped GEMM
+    a = L.MoeGemmArgs(G=4, offsets=fake.value, M=128, N=64, K=64, A=fake.value, a_dtype=L.MOE_BF16, lda=64,
+                      A_rows=128, a_rows=None, B=fake.value, b_dtype=L.MOE_BF16, ldb=64, b_group_stride=64 * 64,
+                      C=fake.value, c_dtype=L.MOE_BF16, ldc=64, epilogue=L.MOE_EPI_NONE, aux=None, ld_aux=0)
+    assert L._lib.moe_grouped_gemm(ctypes.byref(a), None, 0, None) == L.MOE_EWORKSPACE
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.N = 60
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_EINVAL
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.b_dtype = L.MOE_F32
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_ENOTSUP
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.b_group_stride = 10
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_EINVAL
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.K = 96                                   # bf16 path needs K % 64 == 0
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_EINVAL
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.M = 0
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_OK
+    assert L._lib.moe_grouped_gemm(None, fake, 1 << 20, None) == L.MOE_EINVAL
