@@ -26,7 +26,8 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;     // 8 waves: two per SIMD, so one wave's MFMAs cover the other's waits
+constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 256;            // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
 constexpr int kBK = 64;             // K elements per pipeline stage (128 bytes of bf16)
 constexpr int kStages = 3;
@@ -38,7 +39,10 @@ constexpr int kMaxGroups = 4095;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;   // 160 KiB
 constexpr int kSuper = 4;           // column tiles per supertile
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Measured on gfx950 with 128-byte
+// rows: this XOR keeps ds_read_b128 of 16x16 and 32x32 MFMA fragments (16 or 32 rows at one
+// chunk) bank-conflict free (~230 B/clk/CU), where c ^ (r & 7) conflicts for 32-row reads.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ int bm_of_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
 
@@ -111,20 +115,64 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
 // ---------------------------------------------------------------------------------------
 // one output tile of BM rows x (256 B-rows) for group g
 // ---------------------------------------------------------------------------------------
+// The two bf16 MFMA shapes used: operand fragment = one 16-byte LDS chunk per lane; the
+// output tile is MS x MS with `out_row/out_col` giving the position of accumulator element r.
+// Measured on MI355X from registers: 32x32x16 sustains ~2.28 PFLOP/s with 8 accumulators,
+// 16x16x32 at most ~1.95, so the 64- and 128-row tiles use 32x32x16.
+template <int MS>
+struct Mfma;
+template <>
+struct Mfma<16> {
+    using acc_t = f32x4;
+    static constexpr int K = 32;         // contraction per instruction
+    static constexpr int NACC = 4;       // accumulator floats per lane
+    static __device__ __forceinline__ acc_t zero() { return acc_t{0.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 16; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
+};
+template <>
+struct Mfma<32> {
+    using acc_t = f32x16;
+    static constexpr int K = 16;
+    static constexpr int NACC = 16;
+    static __device__ __forceinline__ acc_t zero() {
+        acc_t z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0.f;
+        return z;
+    }
+    static __device__ __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 2 + lane / 32; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
+};
+
 template <int BM, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
-    constexpr int WM = BM >= 128 ? 2 : 1;
-    constexpr int WN = 4 / WM;
+    constexpr int WM = (BM == 16) ? 1 : 2;    // wave grid: WM x WN = 8 waves
+    constexpr int WN = kWaves / WM;
+    constexpr int MS = (BM / WM >= 32) ? 32 : 16;   // MFMA tile edge
+    using MF = Mfma<MS>;
+    constexpr int NKS = kBK / MF::K;          // MFMA k-steps per pipeline stage
     constexpr int WTM = BM / WM;              // rows per wave
     constexpr int WTN = kBN / WN;             // B rows (tile columns) per wave
-    constexpr int MI = WTM / 16;
-    constexpr int NI = WTN / 16;
+    constexpr int MI = WTM / MS;
+    constexpr int NI = WTN / MS;
     constexpr int A_INSTR = BM / 8;           // 1 KiB DMA instructions for the A slice
-    constexpr int A_PER_WAVE = cdiv(A_INSTR, 4);
-    constexpr int B_PER_WAVE = kBN / 8 / 4;   // 8
+    constexpr int A_PER_WAVE = cdiv(A_INSTR, kWaves);
+    constexpr int B_PER_WAVE = kBN / 8 / kWaves;   // 4
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     int row_begin, row_end;
     group_rows(p.offsets, g, p.M, row_begin, row_end);
@@ -135,7 +183,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const char* a_src[A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
-        const int instr = wave + 4 * i;
+        const int instr = wave + kWaves * i;
         const int row = instr * 8 + lane / 8;
         const int chunk = (lane % 8) ^ swz(row);
         int r = min(r0 + row, row_end - 1);
@@ -167,56 +215,86 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         const int64_t koff = (int64_t)kt * kRowBytes;
 #pragma unroll
         for (int i = 0; i < A_PER_WAVE; ++i) {
-            const int instr = wave + 4 * i;
-            if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
+            const int instr = wave + kWaves * i;
+            if constexpr (A_INSTR % kWaves == 0) load_lds16(a_src[i] + koff, st + instr * 1024);
+            else if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
         }
         char* stb = st + BM * kRowBytes;
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i) load_lds16(b_src[i] + koff, stb + (wave * B_PER_WAVE + i) * 1024);
     };
 
-    f32x4 acc[MI][NI];
+    typename MF::acc_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NI; ++j) acc[i][j] = MF::zero();
 
     const int nk = p.K / kBK;
-    // waves 2 and 3 issue fewer A loads when BM == 16; the wait count uses the smallest
+    // some waves issue no A load when BM < 64; the wait count uses the smallest
     // per-wave load count so that every wave is sure its own stage kt has landed
-    constexpr int LOADS_MIN = B_PER_WAVE + (A_INSTR >= 4 ? A_INSTR / 4 : 0);
+    constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / kWaves;
+
+    // per-lane LDS byte offsets of the MFMA fragments (fixed for the whole tile)
+    int a_off[NKS][MI], b_off[NKS][NI];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int chunk = MF::frag_chunk(lane, ks);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int row = wm * WTM + i * MS + MF::frag_row(lane);
+            a_off[ks][i] = row * kRowBytes + ((chunk ^ swz(row)) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int row = wn * WTN + j * MS + MF::frag_row(lane);
+            b_off[ks][j] = BM * kRowBytes + row * kRowBytes + ((chunk ^ swz(row)) << 4);
+        }
+    }
+    // Fragments are double-buffered in registers: the LDS reads of k-step ks+1 are issued
+    // before the MFMAs of k-step ks, so LDS latency overlaps matrix work.
+    auto compute = [&](int kt) {
+        const char* st = lds + (kt % kStages) * kStageBytes;
+        bf16x8 af[2][MI], bfr[2][NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(st + a_off[0][i]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(st + b_off[0][j]);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            if (ks + 1 < NKS) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i) af[nxt][i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks + 1][i]);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) bfr[nxt][j] = *reinterpret_cast<const bf16x8*>(st + b_off[ks + 1][j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] = MF::run(af[cur][i], bfr[cur][j], acc[i][j]);
+        }
+    };
 
     lds_barrier();   // the previous tile's epilogue may still read LDS
     issue(0);
     if (nk > 1) issue(1);
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) wait_vm_lgkm0<LOADS_MIN>();
-        else wait_vm_lgkm0<0>();
+    // steady state: stage kt is ready once at most LOADS_MIN loads (stage kt+1) are pending
+    for (int kt = 0; kt < nk - 2; ++kt) {
+        wait_vm_lgkm0<LOADS_MIN>();
         lds_barrier();
-        if (kt + 2 < nk) issue(kt + 2);
-        const char* sa = lds + (kt % kStages) * kStageBytes;
-        const char* sb = sa + BM * kRowBytes;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int chunk = ks * 4 + lane / 16;
-            bf16x8 af[MI], bfr[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm * WTM + i * 16 + lane % 16;
-                af[i] = *reinterpret_cast<const bf16x8*>(sa + row * kRowBytes + ((chunk ^ swz(row)) << 4));
-            }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int row = wn * WTN + j * 16 + lane % 16;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + row * kRowBytes + ((chunk ^ swz(row)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+        issue(kt + 2);
+        compute(kt);
     }
+    if (nk >= 2) {
+        wait_vm_lgkm0<LOADS_MIN>();
+        lds_barrier();
+        compute(nk - 2);
+    }
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    compute(nk - 1);
 
     // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
     wait_vm_lgkm0<0>();
@@ -230,10 +308,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
-            const int col = wn * WOUT + j * 16 + lane % 16;
+            const int col = wn * WOUT + j * MS + MF::out_col(lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wm * WTM + i * 16 + (lane / 16) * 4 + r;
+            for (int r = 0; r < MF::NACC; ++r) {
+                const int row = wm * WTM + i * MS + MF::out_row(lane, r);
                 float v;
                 if (SWIGLU) {
                     const float gv = acc[i][j][r], uv = acc[i][j + NO][r];
