@@ -29,22 +29,42 @@ namespace {
 constexpr int kThreads = 512;     // 8 waves: two per SIMD, so one wave's MFMAs cover the other's waits
 constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 256;            // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
-constexpr int kBK = 64;             // K elements per pipeline stage (128 bytes of bf16)
-constexpr int kStages = 3;
-constexpr int kMaxBM = 128;
-constexpr int kRowBytes = kBK * 2;
-constexpr int kStageBytes = (kMaxBM + kBN) * kRowBytes;   // 48 KiB
-constexpr int kPipeBytes = kStages * kStageBytes;         // 144 KiB
+constexpr int kBK = 64;             // K granularity the launch requires (K % 64 == 0)
+// LDS pipeline geometry per tile height. The global->LDS path streams at ~53 B/clk per CU
+// (measured on MI355X), so the largest tiles matter most: 256x256 tiles need ~31 B/clk at
+// full MFMA rate against ~47 B/clk for 128x256. 256-row tiles use K slices of 32 (64-byte
+// LDS rows) in a 4-deep ring of 32 KiB; smaller tiles use K slices of 64 (128-byte rows) in a
+// 3-deep ring of up to 48 KiB. Stage = (BM rows of A + 256 rows of B) x row bytes.
+template <int BM>
+struct Pipe {
+    static constexpr int BK = BM >= 256 ? 32 : 64;
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per LDS row
+    static constexpr int kStages = BM >= 256 ? 4 : 3;
+    static constexpr int kStageBytes = (BM + kBN) * kRowBytes;
+};
+constexpr int kPipeBytes = 3 * (128 + kBN) * 128;           // 144 KiB (>= 4 x 32 KiB)
 constexpr int kMaxGroups = 4095;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;   // 160 KiB
 constexpr int kSuper = 4;           // column tiles per supertile
 
-// 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Measured on gfx950 with 128-byte
-// rows: this XOR keeps ds_read_b128 of 16x16 and 32x32 MFMA fragments (16 or 32 rows at one
-// chunk) bank-conflict free (~230 B/clk/CU), where c ^ (r & 7) conflicts for 32-row reads.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Chosen from measurements on gfx950
+// of ds_read_b128 fragment reads (16 or 32 rows at one chunk): with 128-byte rows,
+// (r >> 1) & 7 is conflict free (~230 B/clk/CU) for both 16x16 and 32x32 fragments (r & 7
+// conflicts 2-way for 32 rows); with 64-byte rows, 32x32 fragments need (r >> 2) & 3 and
+// 16x16 fragments (r >> 1) & 3 (each alternative conflicts 2-way).
+template <int CHUNKS, int MS>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (CHUNKS == 8) return (row >> 1) & 7;
+    else if constexpr (MS == 32) return (row >> 2) & 3;
+    else return (row >> 1) & 3;
+}
 
-__device__ __forceinline__ int bm_of_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
+// Tile height of a group with m rows. 256-row tiles need a bf16 C (their fp32 staging tile
+// would not fit in LDS), so `max_bm` is 128 for fp32 output.
+__device__ __forceinline__ int bm_of_rows(int m, int max_bm) {
+    return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : (m <= 192 || max_bm < 256) ? 128 : 256;
+}
 
 // Rows [begin, end) of group g, clamped into [0, M] so that inconsistent offsets can never
 // send a load or store outside the buffers.
@@ -70,6 +90,7 @@ struct GemmParams {
     char* C;
     int64_t ldc;
     int c_f32;
+    int max_bm;     // largest tile height used (128 when C is fp32)
     char* aux;
     int64_t ld_aux;
     const int32_t* tile_start;   // [G+1] in workspace
@@ -79,7 +100,7 @@ struct GemmParams {
 // schedule: tile_start[g] = sum over groups < g of ceil(m_g / BM_g) * NT
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
-                                                             int NT, int32_t* __restrict__ tile_start) {
+                                                             int NT, int max_bm, int32_t* __restrict__ tile_start) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -92,7 +113,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
             int b, e;
             group_rows(offsets, g, M, b, e);
             const int m = e - b;
-            tiles = m > 0 ? cdiv(m, bm_of_rows(m)) * NT : 0;
+            tiles = m > 0 ? cdiv(m, bm_of_rows(m, max_bm)) * NT : 0;
         }
         int incl = tiles;
 #pragma unroll
@@ -157,19 +178,27 @@ struct Mfma<32> {
 
 template <int BM, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
+    using PG = Pipe<BM>;
     constexpr int WM = (BM == 16) ? 1 : 2;    // wave grid: WM x WN = 8 waves
     constexpr int WN = kWaves / WM;
     constexpr int MS = (BM / WM >= 32) ? 32 : 16;   // MFMA tile edge
     using MF = Mfma<MS>;
-    constexpr int NKS = kBK / MF::K;          // MFMA k-steps per pipeline stage
+    constexpr int RB = PG::kRowBytes;
+    constexpr int CH = PG::kChunks;
+    constexpr int ROWS_PER_INSTR = 1024 / RB;     // LDS rows filled by one 1 KiB DMA instruction
+    constexpr int NKS = PG::BK / MF::K;          // MFMA k-steps per pipeline stage
     constexpr int WTM = BM / WM;              // rows per wave
     constexpr int WTN = kBN / WN;             // B rows (tile columns) per wave
     constexpr int MI = WTM / MS;
     constexpr int NI = WTN / MS;
-    constexpr int A_INSTR = BM / 8;           // 1 KiB DMA instructions for the A slice
+    constexpr int A_INSTR = BM / ROWS_PER_INSTR;        // 1 KiB DMA instructions for the A slice
     constexpr int A_PER_WAVE = cdiv(A_INSTR, kWaves);
-    constexpr int B_PER_WAVE = kBN / 8 / kWaves;   // 4
+    constexpr int B_PER_WAVE = kBN / ROWS_PER_INSTR / kWaves;
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
+    constexpr int kStages = PG::kStages;
+    constexpr int kStageBytes = PG::kStageBytes;
+    static_assert(kStages * kStageBytes <= kPipeBytes, "pipeline exceeds its LDS budget");
+    static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -179,13 +208,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int r0 = row_begin + mt * BM;                   // first C row of the tile
     const int n0 = nt * BN_OUT;                           // first output column
 
-    // per-lane global source pointers for the DMA loads (fixed for the whole K loop)
+    // per-lane global source pointers for the DMA loads (fixed for the whole K loop);
+    // lane l of an instruction fills LDS row (instr * ROWS_PER_INSTR + l / CH), slot l % CH
     const char* a_src[A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
         const int instr = wave + kWaves * i;
-        const int row = instr * 8 + lane / 8;
-        const int chunk = (lane % 8) ^ swz(row);
+        const int row = instr * ROWS_PER_INSTR + lane / CH;
+        const int chunk = (lane % CH) ^ swz<CH, MS>(row);
         int r = min(r0 + row, row_end - 1);
         int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
         ar = ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
@@ -196,8 +226,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
         const int instr = wave * B_PER_WAVE + i;
-        const int rho = instr * 8 + lane / 8;             // LDS row of the B slice
-        const int chunk = (lane % 8) ^ swz(rho);
+        const int rho = instr * ROWS_PER_INSTR + lane / CH;   // LDS row of the B slice
+        const int chunk = (lane % CH) ^ swz<CH, MS>(rho);
         int grow;
         if (SWIGLU) {
             const int wnb = rho / WTN, within = rho % WTN;
@@ -212,14 +242,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 
     auto issue = [&](int kt) {
         char* st = lds + (kt % kStages) * kStageBytes;
-        const int64_t koff = (int64_t)kt * kRowBytes;
+        const int64_t koff = (int64_t)kt * RB;
 #pragma unroll
         for (int i = 0; i < A_PER_WAVE; ++i) {
             const int instr = wave + kWaves * i;
             if constexpr (A_INSTR % kWaves == 0) load_lds16(a_src[i] + koff, st + instr * 1024);
             else if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
         }
-        char* stb = st + BM * kRowBytes;
+        char* stb = st + BM * RB;
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i) load_lds16(b_src[i] + koff, stb + (wave * B_PER_WAVE + i) * 1024);
     };
@@ -230,10 +260,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
         for (int j = 0; j < NI; ++j) acc[i][j] = MF::zero();
 
-    const int nk = p.K / kBK;
+    const int nk = p.K / PG::BK;
     // some waves issue no A load when BM < 64; the wait count uses the smallest
     // per-wave load count so that every wave is sure its own stage kt has landed
     constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / kWaves;
+    static_assert((kStages - 2) * LOADS_MIN < 64, "vmcnt range");
 
     // per-lane LDS byte offsets of the MFMA fragments (fixed for the whole tile)
     int a_off[NKS][MI], b_off[NKS][NI];
@@ -243,12 +274,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int row = wm * WTM + i * MS + MF::frag_row(lane);
-            a_off[ks][i] = row * kRowBytes + ((chunk ^ swz(row)) << 4);
+            a_off[ks][i] = row * RB + ((chunk ^ swz<CH, MS>(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int row = wn * WTN + j * MS + MF::frag_row(lane);
-            b_off[ks][j] = BM * kRowBytes + row * kRowBytes + ((chunk ^ swz(row)) << 4);
+            b_off[ks][j] = BM * RB + row * RB + ((chunk ^ swz<CH, MS>(row)) << 4);
         }
     }
     // Fragments are double-buffered in registers: the LDS reads of k-step ks+1 are issued
@@ -277,24 +308,35 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         }
     };
 
+    // Ring of kStages LDS stages: stages kt+1 .. kt+kStages-2 stream in while stage kt is
+    // multiplied. Before stage kt is read, this wave's loads of the later stages may still be
+    // pending (LOADS_MIN each); the barrier then makes every wave's loads of stage kt visible
+    // and guarantees the buffer refilled next (read in iteration kt-1) is no longer in use.
     lds_barrier();   // the previous tile's epilogue may still read LDS
-    issue(0);
-    if (nk > 1) issue(1);
-    // steady state: stage kt is ready once at most LOADS_MIN loads (stage kt+1) are pending
-    for (int kt = 0; kt < nk - 2; ++kt) {
-        wait_vm_lgkm0<LOADS_MIN>();
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) issue(s);
+    int kt = 0;
+    for (; kt + kStages - 1 < nk; ++kt) {
+        wait_vm_lgkm0<(kStages - 2) * LOADS_MIN>();
         lds_barrier();
-        issue(kt + 2);
+        issue(kt + kStages - 1);
         compute(kt);
     }
-    if (nk >= 2) {
-        wait_vm_lgkm0<LOADS_MIN>();
+    // tail: no more stages to issue; stages after kt still in flight = nk - 1 - kt
+    for (; kt < nk; ++kt) {
+        const int pending = nk - 1 - kt;
+        if constexpr (kStages >= 4) {
+            if (pending >= 2) wait_vm_lgkm0<2 * LOADS_MIN>();
+            else if (pending == 1) wait_vm_lgkm0<LOADS_MIN>();
+            else wait_vm_lgkm0<0>();
+        } else {
+            if (pending >= 1) wait_vm_lgkm0<LOADS_MIN>();
+            else wait_vm_lgkm0<0>();
+        }
         lds_barrier();
-        compute(nk - 2);
+        compute(kt);
     }
-    wait_vm_lgkm0<0>();
-    lds_barrier();
-    compute(nk - 1);
 
     // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
     wait_vm_lgkm0<0>();
@@ -373,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
         int gb, ge;
         group_rows(p.offsets, g, p.M, gb, ge);
         const int m = ge - gb;
-        const int bm = bm_of_rows(m);
+        const int bm = bm_of_rows(m, p.max_bm);
         const int MT = cdiv(m, bm);
         const int NT = p.NT;
         const int full = NT / kSuper;
@@ -504,6 +546,9 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.C = (char*)a->C;
     p.ldc = a->ldc;
     p.c_f32 = a->c_dtype == MOE_F32 ? 1 : 0;
+    // 256-row tiles (4-stage, 32-wide K slices) measured faster on a square 8192^3 product but
+    // slower on the DeepSeek-V3 and Mixtral expert shapes, so the launch stops at 128 rows.
+    p.max_bm = 128;
     p.aux = (char*)a->aux;
     p.ld_aux = a->ld_aux;
     p.tile_start = (const int32_t*)workspace;
@@ -525,7 +570,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     const int bn_out = swiglu ? moe::kBN / 2 : moe::kBN;
     p.NT = (int)moe::cdiv<int64_t>(a->N, bn_out);
     if (!moe::set_lds_attr()) return MOE_EHIP;
-    hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
+    hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT, p.max_bm,
                        (int32_t*)workspace);
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
