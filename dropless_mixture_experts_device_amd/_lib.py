@@ -94,13 +94,15 @@ def _ws(ws):
     return (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
 
 
-def moe_route(x, w_router, bias, k: int, score: int, topk_idx, topk_w, keys_out=None, stream=None):
+def moe_route(x, w_router, bias, k: int, score: int, topk_idx, topk_w, keys_out=None, workspace=None, stream=None):
     """x [T,d], w_router [E,d] (bf16 or fp32), bias [E] fp32 or None -> topk_idx int32 [T,k],
-    topk_w fp32 [T,k], keys_out fp32 [T,E] (optional)."""
+    topk_w fp32 [T,k], keys_out fp32 [T,E] (optional). `workspace`: a uint8 device tensor of
+    moe_workspace_bytes(MOE_OP_ROUTE, T, d, E) bytes (None when that is zero)."""
     T, d = x.shape
     E = w_router.shape[0]
+    ws, wsb = _ws(workspace)
     _check("moe_route", _lib.moe_route(_ptr(x), _ptr(w_router), _dtype(x), _ptr(bias), T, d, E, k, score,
-                                       _ptr(topk_idx), _ptr(topk_w), _ptr(keys_out), None, 0, _stream(stream)))
+                                       _ptr(topk_idx), _ptr(topk_w), _ptr(keys_out), ws, wsb, _stream(stream)))
 
 
 def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_token, x_perm, workspace,

@@ -17,26 +17,40 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One DPP step of a 64-bit max: lanes outside `row_mask` keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+// Wave-wide max of a 64-bit value, returned to every lane. DPP lane moves stay in the VALU
+// (no LDS round trip): pairs, quads, then rotations inside each 16-lane row give every lane
+// its row's max; two row broadcasts fold rows so lane 63 holds the wave max.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, s, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x124, 0xF>(v);   // row_ror:4
+    v = dpp_max_step<0x128, 0xF>(v);   // row_ror:8
+    v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Top-k over keys held in LDS ([kRouteBT][pitch] floats, bias already added). Each wave
 // handles tokens wave, wave+4, ... of the tile. Selection order: larger key first, equal
 // keys -> lower expert id (the packed low word is ~e, so the larger packed value wins).
-template <int NQ>
+template <int NQ, int BT = kRouteBT>
 __device__ void topk_tile(const float* keys, int pitch, int t0, int T, int E, int k, int score,
                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    for (int tl = wave; tl < kRouteBT; tl += kRouteThreads / kWave) {
+    for (int tl = wave; tl < BT; tl += kRouteThreads / kWave) {
         const int t = t0 + tl;
         if (t >= T) break;
         uint64_t cand[NQ];
@@ -186,6 +200,101 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
     topk_tile<NQ>(keys, PITCH, t0, T, E, k, score, topk_idx, topk_w);
 }
 
+// ---- split-K router for large layers -------------------------------------------------------
+// The projection x[T,d] . w_router[E,d]^T is a skinny GEMM (E <= 256 columns): with one
+// 128-token tile per workgroup it fills only T/128 CUs. It is therefore run on the tuned
+// grouped-GEMM kernel as KS groups, group s multiplying the s-th K slice: x is viewed as
+// [KS*T, d/KS] (row t*KS+s is x[t, s*d/KS : (s+1)*d/KS]) through a gather index, and group
+// s's B is w_router[:, s*d/KS : ...] (leading dimension d). The fp32 partial logits are
+// then summed in the fixed order s = 0..KS-1, the bias added, and the top-k taken.
+constexpr int kRouteKS = 4;
+
+__host__ __device__ inline size_t ralign(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct RouteWs {
+    float* partial;     // [KS*T, E]
+    int32_t* a_rows;    // [KS*T]
+    int32_t* offsets;   // [KS+1]
+    char* gemm_ws;
+};
+
+inline RouteWs route_ws(void* ws, int64_t T, int E) {
+    char* p = (char*)ws;
+    RouteWs r;
+    r.partial = (float*)p;
+    p += ralign((size_t)kRouteKS * T * E * 4);
+    r.a_rows = (int32_t*)p;
+    p += ralign((size_t)kRouteKS * T * 4);
+    r.offsets = (int32_t*)p;
+    p += ralign((kRouteKS + 1) * 4);
+    r.gemm_ws = p;
+    return r;
+}
+
+inline bool route_uses_split(int64_t T, int64_t d, int E) {
+    return T >= 256 && E % 8 == 0 && d % (64 * kRouteKS) == 0;
+}
+
+__global__ void route_split_init_kernel(int T, int32_t* __restrict__ a_rows, int32_t* __restrict__ offsets) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < kRouteKS * T) {
+        const int s = i / T, t = i % T;
+        a_rows[i] = t * kRouteKS + s;
+    }
+    if (i <= kRouteKS) offsets[i] = i * T;
+}
+
+constexpr int kTopkBT = 8;   // tokens per workgroup of the split-K top-k pass (2 per wave)
+
+template <int NQ>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ partial,
+                                                                   const float* __restrict__ bias, int T, int E,
+                                                                   int k, int score, int32_t* __restrict__ topk_idx,
+                                                                   float* __restrict__ topk_w,
+                                                                   float* __restrict__ keys_out) {
+    constexpr int PITCH = NQ * kWave + 4;
+    __shared__ float keys[kTopkBT * PITCH];
+    const int t0 = blockIdx.x * kTopkBT;
+    // 4 consecutive experts per lane-load (E % 8 == 0 here); every partial of a chunk is
+    // loaded before any is summed so the loads overlap, then summed in the order q = 0..KS-1
+    const int e4 = E / 4;
+    constexpr int PER = cdiv(kTopkBT * NQ * kWave / 4, kRouteThreads);   // chunks per thread (upper bound)
+    f32x4 v[PER][kRouteKS];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int c = threadIdx.x + u * kRouteThreads;
+        const int tl = c / e4, e = (c % e4) * 4;
+        const int t = min(t0 + tl, T - 1);
+        if (tl < kTopkBT) {
+#pragma unroll
+            for (int q = 0; q < kRouteKS; ++q)
+                v[u][q] = *reinterpret_cast<const f32x4*>(partial + ((int64_t)q * T + t) * E + e);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int c = threadIdx.x + u * kRouteThreads;
+        const int tl = c / e4, e = (c % e4) * 4;
+        if (tl < kTopkBT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int q = 0; q < kRouteKS; ++q) s += v[u][q][i];
+                keys[tl * PITCH + e + i] = s + (bias != nullptr ? bias[e + i] : 0.f);
+            }
+        }
+    }
+    __syncthreads();
+    if (keys_out != nullptr) {
+        for (int idx = threadIdx.x; idx < kTopkBT * E; idx += kRouteThreads) {
+            const int tl = idx / E, e = idx % E;
+            if (t0 + tl < T) keys_out[(int64_t)(t0 + tl) * E + e] = keys[tl * PITCH + e];
+        }
+    }
+    topk_tile<NQ, kTopkBT>(keys, PITCH, t0, T, E, k, score, topk_idx, topk_w);
+}
+
 template <int NTW>
 void launch_route_bf16(dim3 g, hipStream_t s, const void* x, const void* w, const float* b, int T, int d,
                        int E, int k, int score, int32_t* ti, float* tw, float* ko) {
@@ -197,12 +306,16 @@ void launch_route_bf16(dim3 g, hipStream_t s, const void* x, const void* w, cons
 }  // namespace
 }  // namespace moe
 
+size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E) {
+    if (T <= 0 || E <= 0 || !moe::route_uses_split(T, d, E)) return 0;
+    return moe::ralign((size_t)moe::kRouteKS * T * E * 4) + moe::ralign((size_t)moe::kRouteKS * T * 4) +
+           moe::ralign((moe::kRouteKS + 1) * 4) + 256;
+}
+
 extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
                                   int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
                                   int32_t* topk_idx, float* topk_w, float* keys_out, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (T < 0 || d <= 0 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return MOE_EINVAL;
     if (d % 8 != 0 || T > INT32_MAX / 16 || d > INT32_MAX / 16) return MOE_EINVAL;
     if (score != MOE_SOFTMAX && score != MOE_SIGMOID) return MOE_EINVAL;
@@ -210,9 +323,53 @@ extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t d
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !topk_idx || !topk_w) return MOE_EINVAL;
     if (!moe_aligned16(x) || !moe_aligned16(w_router)) return MOE_EINVAL;
+    const bool split = dtype == MOE_BF16 && moe::route_uses_split(T, d, E);
+    if (split && (!workspace || workspace_bytes < moe_route_workspace_bytes(T, d, E))) return MOE_EWORKSPACE;
+    if (split && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)moe::cdiv<int64_t>(T, moe::kRouteBT));
     const int Ti = (int)T, di = (int)d;
+    if (split) {
+        moe::RouteWs ws = moe::route_ws(workspace, T, E);
+        const int n = moe::kRouteKS * Ti;
+        hipLaunchKernelGGL(moe::route_split_init_kernel, dim3(moe::cdiv(n + 1, 256)), dim3(256), 0, s, Ti, ws.a_rows,
+                           ws.offsets);
+        MOE_CHECK_LAUNCH();
+        moe_gemm_args_t g{};
+        g.G = moe::kRouteKS;
+        g.offsets = ws.offsets;
+        g.M = (int64_t)moe::kRouteKS * T;
+        g.N = E;
+        g.K = d / moe::kRouteKS;
+        g.A = x;
+        g.a_dtype = MOE_BF16;
+        g.lda = d / moe::kRouteKS;
+        g.A_rows = (int64_t)moe::kRouteKS * T;
+        g.a_rows = ws.a_rows;
+        g.B = w_router;
+        g.b_dtype = MOE_BF16;
+        g.ldb = d;
+        g.b_group_stride = d / moe::kRouteKS;
+        g.C = ws.partial;
+        g.c_dtype = MOE_F32;
+        g.ldc = E;
+        g.epilogue = MOE_EPI_NONE;
+        const moe_status_t st = moe_grouped_gemm(&g, ws.gemm_ws, 256, stream);
+        if (st != MOE_OK) return st;
+        const int nq = moe::cdiv(E, 64);
+        const dim3 tgrid((unsigned)moe::cdiv<int64_t>(T, moe::kTopkBT));
+        if (nq <= 1)
+            hipLaunchKernelGGL((moe::route_topk_kernel<1>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+                               k, score, topk_idx, topk_w, keys_out);
+        else if (nq <= 2)
+            hipLaunchKernelGGL((moe::route_topk_kernel<2>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+                               k, score, topk_idx, topk_w, keys_out);
+        else
+            hipLaunchKernelGGL((moe::route_topk_kernel<4>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+                               k, score, topk_idx, topk_w, keys_out);
+        MOE_CHECK_LAUNCH();
+        return MOE_OK;
+    }
     if (dtype == MOE_BF16) {
         const int ntw = moe::cdiv(E, 64);   // 16-expert tiles per wave, 4 waves
         switch (ntw) {

@@ -57,13 +57,15 @@ class LayerBuffers:
         self.out = torch.empty((s.T, s.d), dtype=s.dtype, device=dev)
         pb = L.moe_workspace_bytes(L.MOE_OP_PERMUTE, s.T, s.d, s.E, s.k, 0)
         gb = L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, s.groups)
+        rb = L.moe_workspace_bytes(L.MOE_OP_ROUTE, s.T, s.d, s.E, s.k, 0)
+        self.ws_route = torch.empty((max(rb, 256),), dtype=torch.uint8, device=dev)
         self.ws_permute = torch.empty((max(pb, 256),), dtype=torch.uint8, device=dev)
         self.ws_gemm1 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
         self.ws_gemm2 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
 
 
 def route(x, w_router, bias, s: LayerShape, b: LayerBuffers, keys_out=None):
-    L.moe_route(x, w_router, bias, s.k, s.score, b.topk_idx, b.topk_w, keys_out)
+    L.moe_route(x, w_router, bias, s.k, s.score, b.topk_idx, b.topk_w, keys_out, workspace=b.ws_route)
 
 
 def permute(x, s: LayerShape, b: LayerBuffers):

@@ -54,7 +54,7 @@ typedef enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2 } m
 const char* moe_status_str(int32_t status);
 
 /* Device bytes of workspace an entry point needs (0 if none). Arguments that do not apply
- * to `op` are ignored: ROUTE uses (T, E); PERMUTE uses (T, E); GROUPED_GEMM uses G (the
+ * to `op` are ignored: ROUTE uses (T, d, E); PERMUTE uses (T, E); GROUPED_GEMM uses G (the
  * group count). The result depends only on sizes, never on data. */
 size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G);
 
@@ -74,7 +74,9 @@ size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t 
  *   x        [T, d] of dtype (MOE_BF16 or MOE_F32), leading dimension d
  *   w_router [E, d] same dtype (row e is expert e's router vector)
  *   1 <= k <= min(E, 16), 1 <= E <= 256, d % 8 == 0, x and w_router 16-byte aligned.
- *   Workspace: none (workspace may be NULL).
+ *   Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, d, E, k, 0) bytes, 256-byte aligned (it
+ *   is non-zero for large bf16 layers, whose projection runs as a K-split grouped GEMM with
+ *   fp32 partial logits summed in a fixed order; workspace may be NULL when it is zero).
  */
 moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
                        int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
@@ -120,7 +122,8 @@ moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t* topk_idx,
  *                    (B_g has 2N rows: gate rows first, then up rows); when aux != NULL
  *                    also aux[r, n] = G and aux[r, N+n] = U (in c_dtype).
  * with a(r) = a_rows[r] if a_rows != NULL (a fused gather) else r, and
- * B_g = B + g * b_group_stride elements. Accumulation is fp32; C is rounded once.
+ * B_g = B + g * b_group_stride elements (groups may share or overlap B: it is only read).
+ * Accumulation is fp32; C is rounded once.
  * Rows of C outside [offsets[0], offsets[G]) are not written. Empty groups cost nothing.
  */
 typedef struct moe_gemm_args {

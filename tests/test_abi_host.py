@@ -43,7 +43,8 @@ def test_status_strings_and_workspace(lib):
     from dropless_mixture_experts_device_amd import _lib as L
     assert L.moe_status_str(0) == "MOE_OK"
     assert "invalid" in L.moe_status_str(1)
-    assert L.moe_workspace_bytes(L.MOE_OP_ROUTE, 8192, 7168, 256, 8, 0) == 0
+    assert L.moe_workspace_bytes(L.MOE_OP_ROUTE, 8192, 7168, 256, 8, 0) >= 4 * 8192 * 256 * 4
+    assert L.moe_workspace_bytes(L.MOE_OP_ROUTE, 64, 128, 8, 2, 0) == 0
     pb = L.moe_workspace_bytes(L.MOE_OP_PERMUTE, 8192, 7168, 256, 8, 0)
     assert pb >= (8192 // 64) * 256 * 12
     assert L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, 257) >= 258 * 4
@@ -63,6 +64,8 @@ def test_host_argument_errors_enqueue_nothing(lib):
     # misaligned input
     odd = ctypes.c_void_p((1 << 20) + 2)
     assert L._lib.moe_route(odd, fake, L.MOE_BF16, None, 16, 64, 8, 2, 0, fake, fake, None, None, 0, None) == L.MOE_EINVAL
+    # a large bf16 layer needs the split-K workspace
+    assert L._lib.moe_route(fake, fake, L.MOE_BF16, None, 8192, 7168, 256, 8, 1, fake, fake, None, None, 0, None) == L.MOE_EWORKSPACE
     # T == 0 is a valid no-op
     assert L._lib.moe_route(None, None, L.MOE_BF16, None, 0, 64, 8, 2, 0, None, None, None, None, 0, None) == L.MOE_OK
     # permute: workspace missing / too small / misaligned
@@ -84,7 +87,7 @@ def test_host_argument_errors_enqueue_nothing(lib):
     bad.b_dtype = L.MOE_F32
     assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_ENOTSUP
     bad = L.MoeGemmArgs.from_buffer_copy(a)
-    bad.b_group_stride = 10
+    bad.b_group_stride = -64
     assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_EINVAL
     bad = L.MoeGemmArgs.from_buffer_copy(a)
     bad.K = 96                                   # bf16 path needs K % 64 == 0

@@ -23,7 +23,9 @@ def _run(L, x, w, bias, k, score, want_keys=True):
     idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
     wt = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
     keys = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda") if want_keys else None
-    L.moe_route(x, w, bias, k, score, idx, wt, keys)
+    nb = L.moe_workspace_bytes(L.MOE_OP_ROUTE, T, x.shape[1], E, k, 0)
+    ws = torch.empty((max(nb, 256),), dtype=torch.uint8, device="cuda")
+    L.moe_route(x, w, bias, k, score, idx, wt, keys, workspace=ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), wt.cpu().numpy().astype(np.float64), None if keys is None else keys.cpu().numpy()
 
@@ -31,7 +33,9 @@ def _run(L, x, w, bias, k, score, want_keys=True):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d,E,k,score", [(300, 512, 8, 2, "softmax"), (77, 256, 64, 8, "sigmoid"),
                                            (130, 1024, 256, 8, "sigmoid"), (33, 64, 128, 1, "softmax"),
-                                           (5, 128, 16, 16, "softmax"), (64, 7168, 256, 8, "sigmoid")])
+                                           (5, 128, 16, 16, "softmax"), (64, 7168, 256, 8, "sigmoid"),
+                                           (1000, 2048, 128, 8, "softmax"), (777, 7168, 256, 8, "sigmoid"),
+                                           (300, 1024, 64, 4, "sigmoid")])
 def test_route_exact_inputs_bit_exact(L, dtype, T, d, E, k, score):
     # small integers times powers of two: every partial sum is exact in fp32, so the GPU's
     # keys must equal the oracle's bit for bit and many keys tie (pins the tie-break)
