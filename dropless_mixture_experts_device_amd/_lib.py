@@ -20,7 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM = 0, 1, 2
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT = 0, 1, 2, 3
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -48,8 +48,12 @@ _lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), _vp, _sz, _vp]
 _lib.moe_grouped_gemm.restype = _i32
 _lib.moe_combine.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 _lib.moe_combine.restype = _i32
+_lib.moe_group_quant_mxfp8.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _i64, _vp, _i64, _vp, _vp,
+                                       _sz, _vp]
+_lib.moe_group_quant_mxfp8.restype = _i32
 
-EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine")
+EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
+            "moe_group_quant_mxfp8")
 
 
 class MoeError(RuntimeError):
@@ -146,3 +150,17 @@ def moe_combine(y, topk_w, row_of, y_shared, out, stream=None):
     d = out.shape[1]
     _check("moe_combine", _lib.moe_combine(_ptr(y), _dtype(out), _ptr(topk_w), _ptr(row_of), _ptr(y_shared), T, d, k,
                                            _ptr(out), _stream(stream)))
+
+
+def moe_group_quant_mxfp8(x, q, scales, axis: int = 0, group_offsets=None, block_start=None, workspace=None,
+                          stream=None):
+    """MXFP8 quantisation of x [rows, cols] (bf16 or fp32) into E4M3 codes q (uint8) and E8M0
+    scale bytes (uint8). axis 0: q [rows, >=cols], scales [rows, >=cols/32]. axis 1 (blocks of
+    32 rows inside each group of group_offsets, transposed output): q [cols, >=32*(ceil(rows/32)+G)],
+    scales [cols, >=ceil(rows/32)+G], block_start int32 [G+1] (optional output)."""
+    rows, cols = x.shape
+    G = 0 if group_offsets is None else group_offsets.numel() - 1
+    ws, wsb = _ws(workspace)
+    _check("moe_group_quant_mxfp8", _lib.moe_group_quant_mxfp8(
+        _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(group_offsets), G, axis, _ptr(q), q.stride(0),
+        _ptr(scales), scales.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))

@@ -48,14 +48,14 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
 typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue_t;
-typedef enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2 } moe_op_t;
+typedef enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2, MOE_OP_QUANT = 3 } moe_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_str(int32_t status);
 
 /* Device bytes of workspace an entry point needs (0 if none). Arguments that do not apply
- * to `op` are ignored: ROUTE uses (T, d, E); PERMUTE uses (T, E); GROUPED_GEMM uses G (the
- * group count). The result depends only on sizes, never on data. */
+ * to `op` are ignored: ROUTE uses (T, d, E); PERMUTE uses (T, E); GROUPED_GEMM and QUANT use
+ * G (the group count). The result depends only on sizes, never on data. */
 size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G);
 
 /*
@@ -169,6 +169,39 @@ moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size
 moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, const int32_t* row_of,
                          const void* y_shared, int64_t T, int64_t d, int32_t k, void* out,
                          void* stream);
+
+/*
+ * moe_group_quant_mxfp8 -- MXFP8 quantisation: E4M3 element codes plus one E8M0 scale byte
+ * per block of 32 elements taken along a GEMM's contraction axis.
+ * [Blog] "Optimisations dropless MoE needs": group-aware MXFP8 quantisation for the expert
+ * GEMMs; [Reading] contribution 3: MoE low precision needs group quantisation.
+ * Rule ([OCP-MX]): for a block with largest magnitude amax, scale byte
+ *   s = clamp(floor(log2 amax) - 8 + 127, 0, 254)   (s = 0 for an all-zero block)
+ * and each element x becomes the E4M3 code of x / 2^(s-127) rounded to nearest-even,
+ * saturating at +-448 (bias 7, 3 mantissa bits, subnormal step 2^-9; the sign of zero kept).
+ *
+ *   in [rows, cols] (MOE_BF16 or MOE_F32, leading dimension ld_in), cols % 32 == 0.
+ *   axis 0 (row-wise, for operands contracted along their rows' length):
+ *     q [rows, ld_q >= cols] codes, scales [rows, ld_scales >= cols/32] bytes;
+ *     group_offsets, G, block_start and workspace are ignored.
+ *   axis 1 (group-aware column-wise, for the weight-gradient operands, contracted over
+ *     the tokens of each group): rows are partitioned into G groups by group_offsets
+ *     (device, [G+1]); each column is cut into blocks of 32 consecutive rows inside one
+ *     group, the last block of a group possibly partial (its missing rows count as zero);
+ *     blocks never straddle groups. Output is TRANSPOSED so the blocked axis is
+ *     contiguous: block j of column c has codes q[c, 32j .. 32j+31] (zero codes for the
+ *     missing rows of a partial block) and scale scales[c, j]; group g's blocks are
+ *     j = block_start[g] .. block_start[g+1]-1 (block_start[g] = sum over g' < g of
+ *     ceil(m_g'/32)), so each group starts on a 32-element boundary.
+ *     block_start (device, [G+1]) is written when not NULL, else kept in workspace
+ *     (moe_workspace_bytes(MOE_OP_QUANT, 0, 0, 0, 0, G) bytes). Capacities:
+ *     ld_q >= 32 * (ceil(rows/32) + G), ld_scales >= ceil(rows/32) + G.
+ *   q 16-byte aligned, ld_q % 16 == 0. Deterministic; no floating-point atomics.
+ */
+moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                   const int32_t* group_offsets, int32_t G, int32_t axis,
+                                   uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
+                                   int32_t* block_start, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

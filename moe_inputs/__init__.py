@@ -85,13 +85,16 @@ def normal_table(sigma: float, dtype: str) -> np.ndarray:
     return v.numpy().copy()
 
 
-def randn_np(seed: int, tensor: int, slab: int, rows, cols: int, sigma: float, dtype: str) -> np.ndarray:
-    """Rows `rows` (an int count, or an index array) of a [*, cols] slab, as float32."""
+def randn_np(seed: int, tensor: int, slab: int, rows, cols: int, sigma: float, dtype: str,
+             col_index=None) -> np.ndarray:
+    """Rows `rows` (an int count, or an index array) of a [*, cols] slab, as float32; with
+    `col_index`, only those columns."""
     if isinstance(rows, (int, np.integer)):
         rows = np.arange(int(rows), dtype=np.int64)
     rows = np.asarray(rows, dtype=np.int64)
     assert rows.size == 0 or (int(rows.max()) + 1) * cols <= 2 ** 32
-    counter = rows[:, None] * cols + np.arange(cols, dtype=np.int64)[None, :]
+    cidx = np.arange(cols, dtype=np.int64) if col_index is None else np.asarray(col_index, dtype=np.int64)
+    counter = rows[:, None] * cols + cidx[None, :]
     idx = _hash_top16(counter, slab_key(seed, tensor, slab))
     return normal_table(sigma, dtype)[idx]
 

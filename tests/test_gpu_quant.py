@@ -1,0 +1,123 @@
+"""moe_group_quant_mxfp8 on the GPU vs the oracle: E4M3 codes and E8M0 scale bytes must match
+bit for bit (the quantiser is a deterministic function), row-wise and group-aware
+column-wise, including saturating blocks, all-zero and signed-zero blocks, partial, empty
+and one-row groups, and sampled rows/columns at the DeepSeek-V3 shapes."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+from tests.gpu_util import dev, dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from dropless_mixture_experts_device_amd import _lib
+    return _lib
+
+
+def _nasty(rows, cols, seed, dtype="bf16"):
+    """bf16-exact values with a different power-of-two range per row, plus special blocks."""
+    a = mi.randn_np(seed, mi.X, 0, rows, cols, 1.0, dtype).astype(np.float64)
+    g = np.random.Generator(np.random.PCG64(seed))
+    a *= np.ldexp(1.0, g.integers(-20, 21, rows))[:, None]
+    if rows >= 4 and cols >= 64:
+        a[0, :32] = 0.0                                  # all-zero block
+        a[1, :32] = -0.0                                 # signed zeros
+        a[2, 5] = 1.875 * 2.0 ** 3                       # amax mantissa 1.875 -> 448 saturation
+        a[2, :32] = np.clip(a[2, :32], -15.0, 15.0)
+        a[2, 5] = 1.875 * 2.0 ** 3
+        a[3, 32:64] = 2.0 ** -7                          # constant block on an exact power of two
+    return a
+
+
+def _rowwise(L, a, dtype="bf16"):
+    x = dev(a, dtype)
+    rows, cols = a.shape
+    q = torch.full((rows, cols), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, cols // 32), 0xAB, dtype=torch.uint8, device="cuda")
+    L.moe_group_quant_mxfp8(x, q, s, axis=0)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(64, 128, "bf16"), (300, 7168, "bf16"), (7, 32, "bf16"),
+                                             (50, 96, "f32")])
+def test_quant_rowwise_bit_exact(L, rows, cols, dtype):
+    a = _nasty(rows, cols, rows + cols, dtype)
+    q, s = _rowwise(L, a, dtype)
+    wq, ws, _ = O.mx_quantize_rowwise(a)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(q, wq)
+
+
+def _colwise(L, a, offsets, dtype="bf16"):
+    rows, cols = a.shape
+    G = len(offsets) - 1
+    nblk = -(-rows // 32) + G
+    x = dev(a, dtype)
+    q = torch.full((cols, 32 * nblk), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((cols, nblk), 0xAB, dtype=torch.uint8, device="cuda")
+    bs = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8(x, q, s, axis=1, group_offsets=dev_i32(offsets), block_start=bs)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy(), bs.cpu().numpy()
+
+
+def _check_colwise(a, offsets, q, s, bs):
+    off = np.asarray(offsets, np.int64)
+    nb = -(-np.diff(off) // 32)
+    np.testing.assert_array_equal(bs, np.concatenate([[0], np.cumsum(nb)]))
+    codes, scales, _ = O.mx_quantize_colwise_grouped(a, off)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        m = hi - lo
+        for i in range(int(nb[g])):
+            j = int(bs[g]) + i
+            n = min(32, m - 32 * i)
+            np.testing.assert_array_equal(s[:, j], scales[g][i], err_msg=f"group {g} block {i}")
+            blk = q[:, 32 * j:32 * j + 32]
+            np.testing.assert_array_equal(blk[:, :n], codes[lo + 32 * i:lo + 32 * i + n].T)
+            assert np.all(blk[:, n:] == 0), "padding rows of a partial block must be zero codes"
+
+
+@pytest.mark.parametrize("sizes,cols", [([0, 1, 33, 0, 100, 64, 31], 96), ([5], 64), ([300, 0, 0], 320)])
+def test_quant_colwise_grouped_bit_exact(L, sizes, cols):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    a = _nasty(int(off[-1]), cols, cols + len(sizes))
+    q, s, bs = _colwise(L, a, off)
+    _check_colwise(a, off, q, s, bs)
+
+
+def test_quant_dsv3_shapes_sampled(L):
+    """Row-wise quantisation of a [73728, 7168] activation and group-wise column quantisation
+    with the DeepSeek-V3 routing's 257 groups, checked on sampled rows and columns."""
+    w = mi.WORKLOADS["dsv3"]
+    idx, _, _ = O.route(mi.x_np(w), mi.w_router_np(w), mi.expert_bias(w), w.k, w.score)
+    off, _, _ = O.permutation(idx, w.E, w.T)
+    rows, cols = int(off[-1]), w.d
+    x = mi.randn_torch(w.seed, mi.D_OUT, 9, rows, cols, 1.0, "bf16", "cuda")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    L.moe_group_quant_mxfp8(x, q, s, axis=0)
+    G = len(off) - 1
+    nblk = -(-rows // 32) + G
+    qc = torch.empty((cols, 32 * nblk), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((cols, nblk), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8(x, qc, sc, axis=1, group_offsets=dev_i32(off), block_start=bs)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(5))
+    r_s = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 30)]))
+    a_rows = mi.randn_np(w.seed, mi.D_OUT, 9, r_s, cols, 1.0, "bf16").astype(np.float64)
+    wq, ws, _ = O.mx_quantize_rowwise(a_rows)
+    rs_t = torch.from_numpy(r_s).cuda()
+    np.testing.assert_array_equal(s[rs_t].cpu().numpy(), ws)
+    np.testing.assert_array_equal(q[rs_t].cpu().numpy(), wq)
+    c_s = np.unique(np.concatenate([[0, cols - 1], rng.integers(0, cols, 6)]))
+    full_cols = mi.randn_np(w.seed, mi.D_OUT, 9, rows, cols, 1.0, "bf16", col_index=c_s).astype(np.float64)
+    cs_t = torch.from_numpy(c_s).cuda()
+    _check_colwise(full_cols, off, qc[cs_t].cpu().numpy(), sc[cs_t].cpu().numpy(), bs.cpu().numpy())
