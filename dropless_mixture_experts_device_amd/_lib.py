@@ -33,6 +33,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("B", _vp), ("b_dtype", _i32), ("ldb", _i64), ("b_group_stride", _i64),
         ("C", _vp), ("c_dtype", _i32), ("ldc", _i64),
         ("epilogue", _i32), ("aux", _vp), ("ld_aux", _i64),
+        ("a_scale", _vp), ("lda_scale", _i64), ("b_scale", _vp), ("ldb_scale", _i64), ("b_scale_group_stride", _i64),
     ]
 
 
@@ -125,10 +126,12 @@ def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_to
 
 
 def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None, aux=None, workspace=None,
-                     stream=None):
+                     stream=None, a_scale=None, b_scale=None):
     """C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate) * up), one launch.
 
     A [A_rows, K]; B [G, N or 2N, K]; C [M, N]; offsets int32 [G+1] (device); a_rows int32 [M].
+    MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale [G, N_B, K/32]
+    uint8 E8M0 bytes.
     """
     G = B.shape[0]
     M, N = C.shape
@@ -139,7 +142,10 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
         a_rows=None if a_rows is None else a_rows.data_ptr(),
         B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(1), b_group_stride=B.stride(0),
         C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
-        epilogue=epilogue, aux=None if aux is None else aux.data_ptr(), ld_aux=0 if aux is None else aux.stride(0))
+        epilogue=epilogue, aux=None if aux is None else aux.data_ptr(), ld_aux=0 if aux is None else aux.stride(0),
+        a_scale=None if a_scale is None else a_scale.data_ptr(), lda_scale=0 if a_scale is None else a_scale.stride(0),
+        b_scale=None if b_scale is None else b_scale.data_ptr(), ldb_scale=0 if b_scale is None else b_scale.stride(1),
+        b_scale_group_stride=0 if b_scale is None else b_scale.stride(0))
     ws, wsb = _ws(workspace)
     _check("moe_grouped_gemm", _lib.moe_grouped_gemm(ctypes.byref(args), ws, wsb, _stream(stream)))
 

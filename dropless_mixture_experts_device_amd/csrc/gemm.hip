@@ -4,67 +4,57 @@
 // at its actual token count, and computes only the regions that hold real tokens; the
 // alternatives (a host loop over experts after a device-to-host copy of the counts, or a
 // batched GEMM padded to the worst case) are what it replaces. [Blog] Figure 3 paragraph:
-// the grouped MLP is two such GEMMs, gate/up then down.
+// the grouped MLP is two such GEMMs, gate/up then down. [Blog] "Optimisations dropless MoE
+// needs": the expert GEMMs also run in MXFP8 ([OCP-MX] block-scaled E4M3).
 //
 // Design (gfx950):
 //  * A one-workgroup schedule kernel turns the device-resident group offsets into a tile
 //    prefix (tiles of group g start at tile_start[g]); the host never sees group sizes.
 //  * Each group gets its own tile height BM in {16, 32, 64, 128} from its row count, so tiny
 //    groups do not pay for 128-row tiles and empty groups get no tile at all.
-//  * Persistent workgroups (one per CU, 4 waves) walk the tile list; tiles are ordered
-//    group by group, in supertiles of 4 column tiles x all row tiles, and handed out so the
-//    32 CUs of one XCD work on 32 consecutive tiles (shared A/B panels hit that XCD's L2).
-//  * Operands go global -> LDS with 16-byte DMA loads (no VGPR staging) through a 3-stage
-//    ring of 64-wide K slices; LDS rows are XOR-swizzled so the MFMA fragment reads are
-//    bank-conflict free; products use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
-//  * The epilogue (optional SwiGLU) goes through LDS so that C is written in 16-byte
-//    coalesced chunks.
+//  * Persistent workgroups (one per CU, 8 waves) walk the tile list; tiles are ordered group
+//    by group, in supertiles of 4 column tiles x all row tiles, and handed out so the 32 CUs
+//    of one XCD work on consecutive tiles (shared A/B panels hit that XCD's L2).
+//  * Operands stream global -> LDS with 16-byte DMA loads (no VGPR staging) through a 3-stage
+//    ring of K slices (64 bf16 or 128 fp8 = 128 bytes per row); LDS rows are XOR-swizzled so
+//    MFMA fragment reads are bank-conflict free; fragments are double-buffered in registers.
+//  * bf16: v_mfma_f32_32x32x16_bf16 (16x16x32 for 16/32-row tiles). MXFP8: E4M3 codes with one
+//    E8M0 scale per 32 K-elements; each stage also brings one dword (4 block scales) per row,
+//    and v_mfma_scale_f32_32x32x64_f8f6f4 (16x16x128) applies per-(row, 32-block) scales (the
+//    lane-to-block layout was measured; see the Mfma traits). Accumulation is fp32 in both.
+//  * The epilogue (optional SwiGLU) goes through LDS so that C is written in 16-byte chunks.
 #include <algorithm>
 
 #include "moe_internal.h"
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 512;     // 8 waves: two per SIMD, so one wave's MFMAs cover the other's waits
 constexpr int kWaves = kThreads / 64;
-constexpr int kBN = 256;            // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
-constexpr int kBK = 64;             // K granularity the launch requires (K % 64 == 0)
-// LDS pipeline geometry per tile height. The global->LDS path streams at ~53 B/clk per CU
-// (measured on MI355X), so the largest tiles matter most: 256x256 tiles need ~31 B/clk at
-// full MFMA rate against ~47 B/clk for 128x256. 256-row tiles use K slices of 32 (64-byte
-// LDS rows) in a 4-deep ring of 32 KiB; smaller tiles use K slices of 64 (128-byte rows) in a
-// 3-deep ring of up to 48 KiB. Stage = (BM rows of A + 256 rows of B) x row bytes.
-template <int BM>
-struct Pipe {
-    static constexpr int BK = BM >= 256 ? 32 : 64;
-    static constexpr int kRowBytes = BK * 2;
-    static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per LDS row
-    static constexpr int kStages = BM >= 256 ? 4 : 3;
-    static constexpr int kStageBytes = (BM + kBN) * kRowBytes;
-};
-constexpr int kPipeBytes = 3 * (128 + kBN) * 128;           // 144 KiB (>= 4 x 32 KiB)
-constexpr int kMaxGroups = 4095;
-constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;   // 160 KiB
-constexpr int kSuper = 4;           // column tiles per supertile
+constexpr int kBN = 256;          // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
+constexpr int kRowBytes = 128;    // one LDS row per stage: 64 bf16 or 128 fp8 of K
+constexpr int kChunks = kRowBytes / 16;
+constexpr int kStages = 3;
+constexpr int kMaxBM = 128;
+constexpr int kStageData = (kMaxBM + kBN) * kRowBytes;   // 48 KiB of operands
+constexpr int kScaleOffA = kStageData;                   // MXFP8: one dword per A row ...
+constexpr int kScaleOffB = kStageData + kMaxBM * 4;      // ... and per B row
+constexpr int kStageBytes = kStageData + (kMaxBM + kBN) * 4;
+constexpr int kPipeBytes = kStages * kStageBytes;        // 148.5 KiB
+constexpr int kMaxGroups = 2047;
+constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+constexpr int kSuper = 4;         // column tiles per supertile
 
-// 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Chosen from measurements on gfx950
-// of ds_read_b128 fragment reads (16 or 32 rows at one chunk): with 128-byte rows,
-// (r >> 1) & 7 is conflict free (~230 B/clk/CU) for both 16x16 and 32x32 fragments (r & 7
-// conflicts 2-way for 32 rows); with 64-byte rows, 32x32 fragments need (r >> 2) & 3 and
-// 16x16 fragments (r >> 1) & 3 (each alternative conflicts 2-way).
-template <int CHUNKS, int MS>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (CHUNKS == 8) return (row >> 1) & 7;
-    else if constexpr (MS == 32) return (row >> 2) & 3;
-    else return (row >> 1) & 3;
-}
+// 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Measured on gfx950 with 128-byte
+// rows: this XOR keeps ds_read_b128 of 16x16 and 32x32 MFMA fragments (16 or 32 rows at one
+// chunk) bank-conflict free (~230 B/clk/CU), where c ^ (r & 7) conflicts 2-way for 32 rows.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Tile height of a group with m rows. 256-row tiles need a bf16 C (their fp32 staging tile
-// would not fit in LDS), so `max_bm` is 128 for fp32 output.
-__device__ __forceinline__ int bm_of_rows(int m, int max_bm) {
-    return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : (m <= 192 || max_bm < 256) ? 128 : 256;
-}
+__device__ __forceinline__ int bm_of_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
 
 // Rows [begin, end) of group g, clamped into [0, M] so that inconsistent offsets can never
 // send a load or store outside the buffers.
@@ -78,9 +68,9 @@ struct GemmParams {
     int G;
     int M;          // rows of C (row indices are clamped to it)
     int N;          // output columns
-    int K;
+    int K;          // contraction length (elements)
     int NT;         // column tiles per group
-    const char* A;
+    const char* A;  // all strides below are in elements of the operand's dtype
     int64_t lda;
     int64_t A_rows;
     const int32_t* a_rows;
@@ -90,9 +80,13 @@ struct GemmParams {
     char* C;
     int64_t ldc;
     int c_f32;
-    int max_bm;     // largest tile height used (128 when C is fp32)
     char* aux;
     int64_t ld_aux;
+    const uint8_t* a_scale;   // MXFP8 only: E8M0 bytes [A_rows, K/32]
+    int64_t lda_scale;
+    const uint8_t* b_scale;   // group g: [N_B, K/32] at b_scale + g * b_scale_stride
+    int64_t ldb_scale;
+    int64_t b_scale_stride;
     const int32_t* tile_start;   // [G+1] in workspace
 };
 
@@ -100,7 +94,7 @@ struct GemmParams {
 // schedule: tile_start[g] = sum over groups < g of ceil(m_g / BM_g) * NT
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
-                                                             int NT, int max_bm, int32_t* __restrict__ tile_start) {
+                                                             int NT, int32_t* __restrict__ tile_start) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -113,7 +107,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
             int b, e;
             group_rows(offsets, g, M, b, e);
             const int m = e - b;
-            tiles = m > 0 ? cdiv(m, bm_of_rows(m, max_bm)) * NT : 0;
+            tiles = m > 0 ? cdiv(m, bm_of_rows(m)) * NT : 0;
         }
         int incl = tiles;
 #pragma unroll
@@ -134,71 +128,137 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------------------
-// one output tile of BM rows x (256 B-rows) for group g
+// MFMA shapes. A lane's operand fragment is 16 bytes (bf16) or 32 bytes (fp8) of one row at
+// consecutive K; `out_row/out_col` give the position of accumulator element r in the
+// MS x MS output tile. Measured on MI355X from registers: 32x32x16 bf16 sustains ~2.28
+// PFLOP/s with 8 accumulators, 16x16x32 at most ~1.95, so 64/128-row tiles use 32x32.
 // ---------------------------------------------------------------------------------------
-// The two bf16 MFMA shapes used: operand fragment = one 16-byte LDS chunk per lane; the
-// output tile is MS x MS with `out_row/out_col` giving the position of accumulator element r.
-// Measured on MI355X from registers: 32x32x16 sustains ~2.28 PFLOP/s with 8 accumulators,
-// 16x16x32 at most ~1.95, so the 64- and 128-row tiles use 32x32x16.
-template <int MS>
+template <int MS, bool MX>
 struct Mfma;
+
 template <>
-struct Mfma<16> {
+struct Mfma<16, false> {
     using acc_t = f32x4;
-    static constexpr int K = 32;         // contraction per instruction
-    static constexpr int NACC = 4;       // accumulator floats per lane
-    static __device__ __forceinline__ acc_t zero() { return acc_t{0.f, 0.f, 0.f, 0.f}; }
-    static __device__ __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
+    static constexpr int KS = 2;                                    // k-steps per stage
+    static constexpr int NACC = 4;
+    static constexpr int kChunk2 = 0;                               // one 16-byte chunk
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 16; }
     static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
 };
 template <>
-struct Mfma<32> {
+struct Mfma<32, false> {
     using acc_t = f32x16;
-    static constexpr int K = 16;
+    static constexpr int KS = 4;
     static constexpr int NACC = 16;
-    static __device__ __forceinline__ acc_t zero() {
-        acc_t z;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = 0.f;
-        return z;
-    }
-    static __device__ __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
+    static constexpr int kChunk2 = 0;
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 2 + lane / 32; }
     static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
 };
+// fp8 (measured on gfx950 with one-hot operands and distinct per-lane scales): a lane's 32
+// bytes are two 16-byte K chunks that belong to two different MX blocks, and the scale a lane
+// passes is applied to block `frag_block` of its row, whose two halves sit in this lane's
+// and a partner lane's chunks. 32x32x64: lanes 32h+r hold K [16h, 16h+16) and [32+16h, ...),
+// scale lane 32b+r owns block b. 16x16x128: lanes 16g+r hold K [16g, 16g+16) and
+// [64+16g, ...), scale lane 16b+r owns block b. frag_chunk is the first chunk, the second
+// follows kChunk2 chunks later.
+template <>
+struct Mfma<16, true> {
+    using acc_t = f32x4;
+    static constexpr int KS = 1;                                    // 16x16x128
+    static constexpr int NACC = 4;
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
+    static constexpr int kChunk2 = 4;
+    static __device__ __forceinline__ int frag_block(int lane, int ks) { return ks * 4 + lane / 16; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 8 + lane / 16; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
+};
+template <>
+struct Mfma<32, true> {
+    using acc_t = f32x16;
+    static constexpr int KS = 2;                                    // 32x32x64
+    static constexpr int NACC = 16;
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
+    static constexpr int kChunk2 = 2;
+    static __device__ __forceinline__ int frag_block(int lane, int ks) { return ks * 2 + lane / 32; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 32; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
+};
 
-template <int BM, bool SWIGLU>
+template <int MS, bool MX>
+struct Frag {
+    using t = bf16x8;
+};
+template <int MS>
+struct Frag<MS, true> {
+    using t = i32x8;
+};
+
+template <int MS, bool MX>
+__device__ __forceinline__ typename Frag<MS, MX>::t load_frag(const char* st, int off0, int off1) {
+    if constexpr (MX) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(st + off0);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(st + off1);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+        (void)off1;
+        return *reinterpret_cast<const bf16x8*>(st + off0);
+    }
+}
+
+template <int MS, bool MX>
+__device__ __forceinline__ typename Mfma<MS, MX>::acc_t mfma(typename Frag<MS, MX>::t a, typename Frag<MS, MX>::t b,
+                                                             typename Mfma<MS, MX>::acc_t c, int sa, int sb) {
+    if constexpr (!MX) {
+        (void)sa;
+        (void)sb;
+        if constexpr (MS == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+        else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    } else {
+        // format 0 = E4M3 for both operands; scale bytes in bits [7:0] (opsel 0)
+        if constexpr (MS == 32) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+        else return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    }
+}
+
+template <int MS, bool MX>
+__device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
+    typename Mfma<MS, MX>::acc_t z;
+#pragma unroll
+    for (int r = 0; r < Mfma<MS, MX>::NACC; ++r) z[r] = 0.f;
+    return z;
+}
+
+// ---------------------------------------------------------------------------------------
+// one output tile of BM rows x (256 B-rows) for group g
+// ---------------------------------------------------------------------------------------
+template <int BM, bool SWIGLU, bool MX>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
-    using PG = Pipe<BM>;
-    constexpr int WM = (BM == 16) ? 1 : 2;    // wave grid: WM x WN = 8 waves
+    constexpr int EB = MX ? 1 : 2;                      // operand element bytes
+    constexpr int WM = (BM == 16) ? 1 : 2;              // wave grid: WM x WN = 8 waves
     constexpr int WN = kWaves / WM;
-    constexpr int MS = (BM / WM >= 32) ? 32 : 16;   // MFMA tile edge
-    using MF = Mfma<MS>;
-    constexpr int RB = PG::kRowBytes;
-    constexpr int CH = PG::kChunks;
-    constexpr int ROWS_PER_INSTR = 1024 / RB;     // LDS rows filled by one 1 KiB DMA instruction
-    constexpr int NKS = PG::BK / MF::K;          // MFMA k-steps per pipeline stage
-    constexpr int WTM = BM / WM;              // rows per wave
-    constexpr int WTN = kBN / WN;             // B rows (tile columns) per wave
+    constexpr int MS = (BM / WM >= 32) ? 32 : 16;       // MFMA tile edge
+    using MF = Mfma<MS, MX>;
+    using FragT = typename Frag<MS, MX>::t;
+    constexpr int NKS = MF::KS;                          // MFMA k-steps per stage
+    constexpr int ROWS_PER_INSTR = 1024 / kRowBytes;     // LDS rows filled by one 1 KiB DMA instruction
+    constexpr int WTM = BM / WM;                         // rows per wave
+    constexpr int WTN = kBN / WN;                        // B rows (tile columns) per wave
     constexpr int MI = WTM / MS;
     constexpr int NI = WTN / MS;
-    constexpr int A_INSTR = BM / ROWS_PER_INSTR;        // 1 KiB DMA instructions for the A slice
+    constexpr int A_INSTR = BM / ROWS_PER_INSTR;         // 1 KiB DMA instructions for the A slice
     constexpr int A_PER_WAVE = cdiv(A_INSTR, kWaves);
     constexpr int B_PER_WAVE = kBN / ROWS_PER_INSTR / kWaves;
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
-    constexpr int kStages = PG::kStages;
-    constexpr int kStageBytes = PG::kStageBytes;
-    static_assert(kStages * kStageBytes <= kPipeBytes, "pipeline exceeds its LDS budget");
+    constexpr int AS_INSTR = cdiv(BM, 64);               // MXFP8: scale dwords, 64 rows per instruction
+    constexpr int BS_INSTR = kBN / 64;
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
+    static_assert(AS_INSTR + BS_INSTR <= kWaves, "one scale load per wave at most");
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -208,135 +268,175 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int r0 = row_begin + mt * BM;                   // first C row of the tile
     const int n0 = nt * BN_OUT;                           // first output column
 
+    auto a_row_of = [&](int row) -> int64_t {             // A row feeding tile row `row`
+        const int r = min(r0 + row, row_end - 1);
+        int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
+        return ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
+    };
+    auto b_row_of = [&](int rho) -> int {                 // B row feeding LDS B-row `rho`
+        if (SWIGLU) {
+            // wave wn's WTN rows: first half gate rows, second half the matching up rows
+            const int wnb = rho / WTN, within = rho % WTN;
+            const int half = within / (WTN / 2), idx = within % (WTN / 2);
+            return half * p.N + min(n0 + wnb * (WTN / 2) + idx, p.N - 1);
+        }
+        return min(n0 + rho, p.N - 1);
+    };
+
     // per-lane global source pointers for the DMA loads (fixed for the whole K loop);
-    // lane l of an instruction fills LDS row (instr * ROWS_PER_INSTR + l / CH), slot l % CH
+    // lane l of an instruction fills LDS row (instr * ROWS_PER_INSTR + l / kChunks)
     const char* a_src[A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
         const int instr = wave + kWaves * i;
-        const int row = instr * ROWS_PER_INSTR + lane / CH;
-        const int chunk = (lane % CH) ^ swz<CH, MS>(row);
-        int r = min(r0 + row, row_end - 1);
-        int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
-        ar = ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
-        a_src[i] = p.A + (ar * p.lda + chunk * 8) * 2;
+        const int row = instr * ROWS_PER_INSTR + lane / kChunks;
+        const int chunk = (lane % kChunks) ^ swz(row);
+        a_src[i] = p.A + a_row_of(row) * p.lda * EB + chunk * 16;
     }
     const char* b_src[B_PER_WAVE];
-    const char* bg = p.B + (int64_t)g * p.b_stride * 2;
+    const char* bg = p.B + (int64_t)g * p.b_stride * EB;
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
         const int instr = wave * B_PER_WAVE + i;
-        const int rho = instr * ROWS_PER_INSTR + lane / CH;   // LDS row of the B slice
-        const int chunk = (lane % CH) ^ swz<CH, MS>(rho);
-        int grow;
-        if (SWIGLU) {
-            const int wnb = rho / WTN, within = rho % WTN;
-            const int half = within / (WTN / 2), idx = within % (WTN / 2);
-            const int col = min(n0 + wnb * (WTN / 2) + idx, p.N - 1);
-            grow = half * p.N + col;
-        } else {
-            grow = min(n0 + rho, p.N - 1);
+        const int rho = instr * ROWS_PER_INSTR + lane / kChunks;
+        const int chunk = (lane % kChunks) ^ swz(rho);
+        b_src[i] = bg + (int64_t)b_row_of(rho) * p.ldb * EB + chunk * 16;
+    }
+    // MXFP8 scale rows: waves 0..AS_INSTR-1 load A-scale dwords, the next BS_INSTR waves B's
+    const uint8_t* s_src = nullptr;
+    int s_lds = 0;
+    if constexpr (MX) {
+        if (wave < AS_INSTR) {
+            s_src = p.a_scale + a_row_of(wave * 64 + lane) * p.lda_scale;
+            s_lds = kScaleOffA + wave * 256;
+        } else if (wave < AS_INSTR + BS_INSTR) {
+            const int rho = (wave - AS_INSTR) * 64 + lane;
+            s_src = p.b_scale + (int64_t)g * p.b_scale_stride + (int64_t)b_row_of(rho) * p.ldb_scale;
+            s_lds = kScaleOffB + (wave - AS_INSTR) * 256;
         }
-        b_src[i] = bg + ((int64_t)grow * p.ldb + chunk * 8) * 2;
     }
 
     auto issue = [&](int kt) {
         char* st = lds + (kt % kStages) * kStageBytes;
-        const int64_t koff = (int64_t)kt * RB;
+        const int64_t koff = (int64_t)kt * kRowBytes;
 #pragma unroll
         for (int i = 0; i < A_PER_WAVE; ++i) {
             const int instr = wave + kWaves * i;
             if constexpr (A_INSTR % kWaves == 0) load_lds16(a_src[i] + koff, st + instr * 1024);
             else if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
         }
-        char* stb = st + BM * RB;
+        char* stb = st + BM * kRowBytes;
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i) load_lds16(b_src[i] + koff, stb + (wave * B_PER_WAVE + i) * 1024);
+        if constexpr (MX) {
+            // 4 scale bytes (the stage's 4 blocks of 32) per row
+            if (wave < AS_INSTR + BS_INSTR) load_lds4(s_src + kt * 4, st + s_lds);
+        }
     };
 
     typename MF::acc_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = MF::zero();
+        for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, MX>();
 
-    const int nk = p.K / PG::BK;
-    // some waves issue no A load when BM < 64; the wait count uses the smallest
-    // per-wave load count so that every wave is sure its own stage kt has landed
+    const int nk = p.K / (kRowBytes / EB);
+    // Per-wave loads per stage differ (some waves issue no A or scale load); the wait count
+    // uses the smallest, so every wave is sure its own loads of stage kt have landed.
     constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / kWaves;
-    static_assert((kStages - 2) * LOADS_MIN < 64, "vmcnt range");
 
     // per-lane LDS byte offsets of the MFMA fragments (fixed for the whole tile)
-    int a_off[NKS][MI], b_off[NKS][NI];
+    int a_off[NKS][MI][2], b_off[NKS][NI][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         const int chunk = MF::frag_chunk(lane, ks);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int row = wm * WTM + i * MS + MF::frag_row(lane);
-            a_off[ks][i] = row * RB + ((chunk ^ swz<CH, MS>(row)) << 4);
+            a_off[ks][i][0] = row * kRowBytes + ((chunk ^ swz(row)) << 4);
+            a_off[ks][i][1] = row * kRowBytes + (((chunk + MF::kChunk2) ^ swz(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int row = wn * WTN + j * MS + MF::frag_row(lane);
-            b_off[ks][j] = BM * RB + row * RB + ((chunk ^ swz<CH, MS>(row)) << 4);
+            b_off[ks][j][0] = BM * kRowBytes + row * kRowBytes + ((chunk ^ swz(row)) << 4);
+            b_off[ks][j][1] = BM * kRowBytes + row * kRowBytes + (((chunk + MF::kChunk2) ^ swz(row)) << 4);
         }
     }
     // Fragments are double-buffered in registers: the LDS reads of k-step ks+1 are issued
     // before the MFMAs of k-step ks, so LDS latency overlaps matrix work.
     auto compute = [&](int kt) {
         const char* st = lds + (kt % kStages) * kStageBytes;
-        bf16x8 af[2][MI], bfr[2][NI];
+        int sa_w[MI], sb_w[NI];   // MXFP8: this lane's rows' 4 scale bytes of the stage
+        if constexpr (MX) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(st + a_off[0][i]);
+            for (int i = 0; i < MI; ++i)
+                sa_w[i] = *reinterpret_cast<const int*>(st + kScaleOffA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(st + b_off[0][j]);
+            for (int j = 0; j < NI; ++j)
+                sb_w[j] = *reinterpret_cast<const int*>(st + kScaleOffB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
+        }
+        FragT af[2][MI], bfr[2][NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, MX>(st, a_off[0][i][0], a_off[0][i][1]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, MX>(st, b_off[0][j][0], b_off[0][j][1]);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;
             if (ks + 1 < NKS) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i) af[nxt][i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks + 1][i]);
+                for (int i = 0; i < MI; ++i)
+                    af[nxt][i] = load_frag<MS, MX>(st, a_off[ks + 1][i][0], a_off[ks + 1][i][1]);
 #pragma unroll
-                for (int j = 0; j < NI; ++j) bfr[nxt][j] = *reinterpret_cast<const bf16x8*>(st + b_off[ks + 1][j]);
+                for (int j = 0; j < NI; ++j)
+                    bfr[nxt][j] = load_frag<MS, MX>(st, b_off[ks + 1][j][0], b_off[ks + 1][j][1]);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
+            int sa[MI], sb[NI];
+            if constexpr (MX) {
+                const int sh = 8 * MF::frag_block(lane, ks);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) sa[i] = (sa_w[i] >> sh) & 0xFF;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) sb[j] = (sb_w[j] >> sh) & 0xFF;
+            } else {
+#pragma unroll
+                for (int i = 0; i < MI; ++i) sa[i] = 0;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) sb[j] = 0;
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = MF::run(af[cur][i], bfr[cur][j], acc[i][j]);
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = mfma<MS, MX>(af[cur][i], bfr[cur][j], acc[i][j], sa[i], sb[j]);
         }
     };
 
     // Ring of kStages LDS stages: stages kt+1 .. kt+kStages-2 stream in while stage kt is
-    // multiplied. Before stage kt is read, this wave's loads of the later stages may still be
-    // pending (LOADS_MIN each); the barrier then makes every wave's loads of stage kt visible
-    // and guarantees the buffer refilled next (read in iteration kt-1) is no longer in use.
+    // multiplied. Before stage kt is read, this wave's loads of the later stage may still be
+    // pending (LOADS_MIN); the barrier then makes every wave's loads of stage kt visible and
+    // guarantees the buffer refilled next (read in iteration kt-1) is no longer in use.
     lds_barrier();   // the previous tile's epilogue may still read LDS
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < nk) issue(s);
+    issue(0);
+    if (nk > 1) issue(1);
     int kt = 0;
-    for (; kt + kStages - 1 < nk; ++kt) {
-        wait_vm_lgkm0<(kStages - 2) * LOADS_MIN>();
+    for (; kt + 2 < nk; ++kt) {
+        wait_vm_lgkm0<LOADS_MIN>();
         lds_barrier();
-        issue(kt + kStages - 1);
+        issue(kt + 2);
         compute(kt);
     }
-    // tail: no more stages to issue; stages after kt still in flight = nk - 1 - kt
-    for (; kt < nk; ++kt) {
-        const int pending = nk - 1 - kt;
-        if constexpr (kStages >= 4) {
-            if (pending >= 2) wait_vm_lgkm0<2 * LOADS_MIN>();
-            else if (pending == 1) wait_vm_lgkm0<LOADS_MIN>();
-            else wait_vm_lgkm0<0>();
-        } else {
-            if (pending >= 1) wait_vm_lgkm0<LOADS_MIN>();
-            else wait_vm_lgkm0<0>();
-        }
+    if (kt + 1 < nk) {
+        wait_vm_lgkm0<LOADS_MIN>();
         lds_barrier();
         compute(kt);
+        ++kt;
     }
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    compute(kt);
 
     // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
     wait_vm_lgkm0<0>();
@@ -390,8 +490,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     }
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
+template <bool SWIGLU, bool MX>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
     for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
@@ -415,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
         int gb, ge;
         group_rows(p.offsets, g, p.M, gb, ge);
         const int m = ge - gb;
-        const int bm = bm_of_rows(m, p.max_bm);
+        const int bm = bm_of_rows(m);
         const int MT = cdiv(m, bm);
         const int NT = p.NT;
         const int full = NT / kSuper;
@@ -430,10 +530,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
             nt = full * kSuper + rem % w;
         }
         switch (bm) {
-            case 16: gemm_tile<16, SWIGLU>(p, lds, g, mt, nt); break;
-            case 32: gemm_tile<32, SWIGLU>(p, lds, g, mt, nt); break;
-            case 64: gemm_tile<64, SWIGLU>(p, lds, g, mt, nt); break;
-            default: gemm_tile<128, SWIGLU>(p, lds, g, mt, nt); break;
+            case 16: gemm_tile<16, SWIGLU, MX>(p, lds, g, mt, nt); break;
+            case 32: gemm_tile<32, SWIGLU, MX>(p, lds, g, mt, nt); break;
+            case 64: gemm_tile<64, SWIGLU, MX>(p, lds, g, mt, nt); break;
+            default: gemm_tile<128, SWIGLU, MX>(p, lds, g, mt, nt); break;
         }
     }
 }
@@ -485,21 +585,24 @@ int num_cus() {
     return cached[dev];
 }
 
+template <bool SWIGLU, bool MX>
 bool set_lds_attr() {
-    static bool done[2] = {false, false};
-    if (!done[0]) {
-        if (hipFuncSetAttribute((const void*)gemm_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    static bool done = false;
+    if (!done) {
+        if (hipFuncSetAttribute((const void*)gemm_mfma_kernel<SWIGLU, MX>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 kLdsBytes) != hipSuccess)
             return false;
-        done[0] = true;
-    }
-    if (!done[1]) {
-        if (hipFuncSetAttribute((const void*)gemm_bf16_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsBytes) != hipSuccess)
-            return false;
-        done[1] = true;
+        done = true;
     }
     return true;
+}
+
+template <bool SWIGLU, bool MX>
+moe_status_t launch(const GemmParams& p, int grid, hipStream_t s) {
+    if (!set_lds_attr<SWIGLU, MX>()) return MOE_EHIP;
+    hipLaunchKernelGGL((gemm_mfma_kernel<SWIGLU, MX>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, p);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
 }
 
 }  // namespace
@@ -510,6 +613,8 @@ size_t moe_gemm_workspace_bytes(int32_t G) {
     return (((size_t)G + 1) * 4 + 255) & ~size_t(255);
 }
 
+static inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspace, size_t workspace_bytes,
                                          void* stream) {
     if (!a) return MOE_EINVAL;
@@ -519,7 +624,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->M > INT32_MAX / 2) return MOE_EINVAL;
     if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_EINVAL;
     if (a->a_dtype != a->b_dtype) return MOE_ENOTSUP;
-    if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32) return MOE_ENOTSUP;
+    if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3) return MOE_ENOTSUP;
     if (a->c_dtype != MOE_BF16 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->a_dtype == MOE_F32 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->M == 0) return MOE_OK;
@@ -529,8 +634,9 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->aux && (a->epilogue != MOE_EPI_SWIGLU || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
     if (!workspace || workspace_bytes < moe_gemm_workspace_bytes(a->G)) return MOE_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    const bool mx = a->a_dtype == MOE_E4M3;
 
-    moe::GemmParams p;
+    moe::GemmParams p{};
     p.offsets = a->offsets;
     p.G = a->G;
     p.M = (int)a->M;
@@ -546,11 +652,13 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.C = (char*)a->C;
     p.ldc = a->ldc;
     p.c_f32 = a->c_dtype == MOE_F32 ? 1 : 0;
-    // 256-row tiles (4-stage, 32-wide K slices) measured faster on a square 8192^3 product but
-    // slower on the DeepSeek-V3 and Mixtral expert shapes, so the launch stops at 128 rows.
-    p.max_bm = 128;
     p.aux = (char*)a->aux;
     p.ld_aux = a->ld_aux;
+    p.a_scale = a->a_scale;
+    p.lda_scale = a->lda_scale;
+    p.b_scale = a->b_scale;
+    p.ldb_scale = a->ldb_scale;
+    p.b_scale_stride = a->b_scale_group_stride;
     p.tile_start = (const int32_t*)workspace;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
@@ -562,24 +670,26 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         MOE_CHECK_LAUNCH();
         return MOE_OK;
     }
-    // bf16 MFMA path
-    if (a->K % moe::kBK != 0) return MOE_EINVAL;
+    // MFMA paths: 128-byte K slices (64 bf16 or 128 fp8)
+    const int64_t eb = mx ? 1 : 2;
+    if (a->K % (moe::kRowBytes / eb) != 0) return MOE_EINVAL;
     if (!moe_aligned16(a->A) || !moe_aligned16(a->B) || !moe_aligned16(a->C)) return MOE_EINVAL;
-    if (a->lda % 8 || a->ldb % 8 || a->ldc % 8 || a->b_group_stride % 8) return MOE_EINVAL;
+    if ((a->lda * eb) % 16 || (a->ldb * eb) % 16 || a->ldc % 8 || (a->b_group_stride * eb) % 16) return MOE_EINVAL;
     if (a->aux && (!moe_aligned16(a->aux) || a->ld_aux % 8)) return MOE_EINVAL;
+    if (mx) {
+        if (!a->a_scale || !a->b_scale || !aligned4(a->a_scale) || !aligned4(a->b_scale)) return MOE_EINVAL;
+        if (a->lda_scale < a->K / 32 || a->ldb_scale < a->K / 32 || a->lda_scale % 4 || a->ldb_scale % 4 ||
+            a->b_scale_group_stride < 0 || a->b_scale_group_stride % 4)
+            return MOE_EINVAL;
+    }
     const int bn_out = swiglu ? moe::kBN / 2 : moe::kBN;
     p.NT = (int)moe::cdiv<int64_t>(a->N, bn_out);
-    if (!moe::set_lds_attr()) return MOE_EHIP;
-    hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT, p.max_bm,
+    hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
                        (int32_t*)workspace);
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;
-    const int64_t grid = std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
-    if (swiglu)
-        hipLaunchKernelGGL(moe::gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(moe::kThreads), moe::kLdsBytes, s, p);
-    else
-        hipLaunchKernelGGL(moe::gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(moe::kThreads), moe::kLdsBytes, s, p);
-    MOE_CHECK_LAUNCH();
-    return MOE_OK;
+    const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
+    if (swiglu) return mx ? moe::launch<true, true>(p, grid, s) : moe::launch<true, false>(p, grid, s);
+    return mx ? moe::launch<false, true>(p, grid, s) : moe::launch<false, false>(p, grid, s);
 }

@@ -41,6 +41,11 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base
     __builtin_amdgcn_global_load_lds(gptr, MOE_LDS(lds_wave_base), 16, 0, 0);
 }
 
+// 4 bytes from global memory into LDS: lane i writes LDS bytes [lds_wave_base + 4 i, +4).
+__device__ __forceinline__ void load_lds4(const void* gptr, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gptr, MOE_LDS(lds_wave_base), 4, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // float -> bfloat16, round to nearest even (NaN stays NaN).

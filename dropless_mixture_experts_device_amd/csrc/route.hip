@@ -335,7 +335,7 @@ extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t d
         hipLaunchKernelGGL(moe::route_split_init_kernel, dim3(moe::cdiv(n + 1, 256)), dim3(256), 0, s, Ti, ws.a_rows,
                            ws.offsets);
         MOE_CHECK_LAUNCH();
-        moe_gemm_args_t g{};
+        moe_gemm_args_t g{};   // zero-initialised: no MXFP8 scales
         g.G = moe::kRouteKS;
         g.offsets = ws.offsets;
         g.M = (int64_t)moe::kRouteKS * T;

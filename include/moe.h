@@ -131,9 +131,9 @@ typedef struct moe_gemm_args {
     const int32_t* offsets;     /* device [G+1], non-decreasing, offsets[G] <= M            */
     int64_t M;                  /* rows of C (and of a_rows); a host-known capacity         */
     int64_t N;                  /* output columns, N % 8 == 0                                */
-    int64_t K;                  /* contraction length, K % 64 == 0                           */
+    int64_t K;                  /* contraction length: K % 64 == 0 (bf16), K % 128 == 0 (E4M3) */
     const void* A;              /* [A_rows, K], leading dimension lda                        */
-    int32_t a_dtype;            /* MOE_BF16 or MOE_F32 (MOE_E4M3 reserved for MXFP8)         */
+    int32_t a_dtype;            /* MOE_BF16, MOE_F32 or MOE_E4M3 (MXFP8, with scales below)  */
     int64_t lda;
     int64_t A_rows;             /* rows of A (gather indices are clamped to it)              */
     const int32_t* a_rows;      /* optional device [M] gather index                          */
@@ -147,12 +147,21 @@ typedef struct moe_gemm_args {
     int32_t epilogue;           /* moe_epilogue_t                                            */
     void* aux;                  /* SWIGLU only, optional [M, 2N] pre-activation save        */
     int64_t ld_aux;
+    /* MXFP8 operands (a_dtype = b_dtype = MOE_E4M3, K % 128 == 0): A and B hold E4M3 codes and
+     * every 32 consecutive K elements of a row share one E8M0 scale byte s, the element value
+     * being code_value * 2^(s-127) ([OCP-MX]); products are exact and summed in fp32. */
+    const uint8_t* a_scale;     /* [A_rows, K/32], leading dimension lda_scale (a_rows applies) */
+    int64_t lda_scale;
+    const uint8_t* b_scale;     /* group g: [N or 2N, K/32] at b_scale + g*b_scale_group_stride  */
+    int64_t ldb_scale;
+    int64_t b_scale_group_stride;
 } moe_gemm_args_t;
 
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
- * 0, 0, 0, 0, G) bytes (a device-built tile schedule). A, B, C, aux 16-byte aligned, and
- * lda, ldb, ldc, ld_aux multiples of 8. The args struct is read on the host during the
- * call only. */
+ * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047. A, B, C, aux 16-byte
+ * aligned; A and B rows (lda, ldb, b_group_stride) 16-byte multiples; ldc, ld_aux multiples
+ * of 8; MXFP8 scale pointers and their strides 4-byte multiples. The args struct is read on
+ * the host during the call only. */
 moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size_t workspace_bytes,
                               void* stream);
 

@@ -1,0 +1,91 @@
+"""MXFP8 grouped GEMM on the GPU vs the oracle.
+
+On-grid inputs (E4M3 codes of small integers, per-block scale bytes within +-2 of 127) make
+every product and partial sum exact in fp32, so the GPU result must equal the oracle's fp64
+product of the dequantised operands bit for bit: this pins the scaled-MFMA operand layout,
+the per-lane scale selection and the fp8 tile geometry. Random bf16 inputs quantised by the
+oracle's own quantiser then check the plain and SwiGLU epilogues within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+from tests.gpu_util import assert_close, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from dropless_mixture_experts_device_amd import _lib
+    return _lib
+
+
+def _ws(L, G):
+    return torch.empty((L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, G),), dtype=torch.uint8,
+                       device="cuda")
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _dequant(codes, scales):
+    """value = decode(code) * 2^(scale - 127), blocks of 32 along the last axis."""
+    v = O.e4m3_decode(codes)
+    s = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+    return v * s
+
+
+def _grid_operand(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    vals = g.integers(-2, 3, size=shape).astype(np.float64) * 0.25      # exact E4M3 values
+    codes = O.e4m3_encode(O.e4m3_round(vals))
+    scales = g.integers(125, 130, size=shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return codes, scales
+
+
+def _run(L, A, As, B, Bs, off, M, N, epi, c_dtype, a_rows=None):
+    C = torch.full((M, N), float("nan"), dtype=c_dtype, device="cuda")
+    L.moe_grouped_gemm(_u8(A), _u8(B), C, dev_i32(off), epi, a_rows=None if a_rows is None else dev_i32(a_rows),
+                       workspace=_ws(L, B.shape[0]), a_scale=_u8(As), b_scale=_u8(Bs))
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 1, 17, 33, 65, 129, 300, 2], 256, 512), ([700], 192, 128),
+                                       ([5, 0, 90], 520, 2048)])
+@pytest.mark.parametrize("gather", [False, True])
+def test_mx_gemm_on_grid_bit_exact(L, sizes, N, K, gather):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G = int(off[-1]) + 2, len(sizes)
+    A, As = _grid_operand((M + 5, K), N + K)
+    B, Bs = _grid_operand((G, N, K), G + K)
+    a_rows = np.random.Generator(np.random.PCG64(2)).integers(0, M + 5, M).astype(np.int32) if gather else None
+    C = host(_run(L, A, As, B, Bs, off, M, N, L.MOE_EPI_NONE, torch.float32, a_rows))
+    want = O.grouped_gemm(_dequant(A, As), _dequant(B, Bs), off, a_row_index=a_rows)
+    np.testing.assert_array_equal(C[:off[-1]], want)
+    assert np.all(np.isnan(C[off[-1]:]))
+
+
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_mx_gemm_quantised_random_within_tolerance(L, epi):
+    sizes = [40, 0, 1, 200, 7, 129, 513]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G, N, K = int(off[-1]), len(sizes), 384, 1024
+    nb = 2 * N if epi == "swiglu" else N
+    x = mi.randn_np(7, mi.X, 0, M, K, 1.0, "bf16").astype(np.float64)
+    W = np.stack([mi.randn_np(7, mi.W_GATE, g, nb, K, 0.02, "bf16") for g in range(G)]).astype(np.float64)
+    A, As, Aq = O.mx_quantize_rowwise(x)
+    Bq_parts = [O.mx_quantize_rowwise(W[g]) for g in range(G)]
+    B = np.stack([p[0] for p in Bq_parts])
+    Bs = np.stack([p[1] for p in Bq_parts])
+    Wq = np.stack([p[2] for p in Bq_parts])
+    if epi == "none":
+        C = _run(L, A, As, B, Bs, off, M, N, L.MOE_EPI_NONE, torch.bfloat16)
+        want = O.grouped_gemm(Aq, Wq, off, rnd=O.round_bf16)
+    else:
+        C = _run(L, A, As, B, Bs, off, M, N, L.MOE_EPI_SWIGLU, torch.bfloat16)
+        want = O.grouped_swiglu(Aq, Wq, off, rnd=O.round_bf16)
+    assert_close(host(C), want, "bf16", f"mx {epi}")
