@@ -34,7 +34,45 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialise-gather", action="store_true",
                     help="write x_perm in the permute and read it in GEMM 1 (default: gather fused into GEMM 1)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a 1 GiB device copy (torch.neg into a second buffer) three "
+                         "times, so a counter pass of this same command sees the HBM bytes of a copy of known size")
     return ap.parse_args()
+
+
+COPY_CAL_BYTES = 1 << 30
+GEMM_SOURCES = ("dropless_mixture_experts_device_amd/csrc/gemm.hip",
+                "dropless_mixture_experts_device_amd/csrc/moe_internal.h")
+
+
+def gemm_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, each scaled by the same counter's reading for a copy
+    of known size). None when no summary exists or the GEMM sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_swiglu_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                key, val = line[2:].split(":", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != gemm_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def useful_flops(w, counts):
@@ -55,11 +93,16 @@ def gemm1_bytes(w, counts, fused):
     return wbytes + abytes + hbytes + rows * 4
 
 
-def cpu_baseline(w, idx_np):
-    """The oracle's forward on a bounded sample of the same workload: routing and the
-    permutation for every token, then the SwiGLU experts of every 16th expert id (and the
-    shared expert's first 512 tokens). Reported in useful TFLOPS of the sampled experts."""
-    import torch
+CPU_BUDGET_S = 25.0
+
+
+def cpu_baseline(w, w_gu_dev, w_down_dev):
+    """The oracle's forward (fp64 numpy, as it stands) on the host cores: routing, the
+    permutation and gather of all T tokens, then the SwiGLU experts one group at a time in a
+    spread order (0, 16, 32, ..., then 8, 24, ...), the shared expert on all tokens, and the
+    combine, until about CPU_BUDGET_S seconds of oracle time are spent. Each expert's weights
+    are copied off the GPU (same generator, same values) outside the timed region. Reported
+    in useful TFLOPS of the groups it finished."""
     import moe_inputs as mi
     from oracle import moe_oracle as O
     try:
@@ -67,42 +110,43 @@ def cpu_baseline(w, idx_np):
         cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:
         cores = os.cpu_count() or 1
-    sample_e = list(range(0, w.E, 16))
-    weights = {}
-    for e in sample_e + ([w.E] if w.shared_f else []):
-        gu = torch.empty((2 * w.f, w.d), dtype=torch.bfloat16)
-        dn = torch.empty((w.d, w.f), dtype=torch.bfloat16)
-        if e == w.E:
-            mi.randn_torch(w.seed, mi.SHARED, 0, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[:w.f])
-            mi.randn_torch(w.seed, mi.SHARED, 1, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[w.f:])
-            mi.randn_torch(w.seed, mi.SHARED, 2, w.d, w.f, w.sigma_w, w.dtype, "cpu", out=dn)
-        else:
-            mi.randn_torch(w.seed, mi.W_GATE, e, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[:w.f])
-            mi.randn_torch(w.seed, mi.W_UP, e, w.f, w.d, w.sigma_w, w.dtype, "cpu", out=gu[w.f:])
-            mi.randn_torch(w.seed, mi.W_DOWN, e, w.d, w.f, w.sigma_w, w.dtype, "cpu", out=dn)
-        weights[e] = (gu.float().numpy(), dn.float().numpy())
     x = mi.x_np(w)
     wr = mi.w_router_np(w)
     bias = mi.expert_bias(w)
+    spent = 0.0
     t0 = time.perf_counter()
     idx, wt, _ = O.route(x, wr, bias, w.k, w.score)
-    off, row_of, src = O.permutation(idx, w.E)
-    flops = 0.0
-    for e in sample_e:
-        lo, hi = int(off[e]), int(off[e + 1])
-        if hi > lo:
-            O.expert_forward(x[src[lo:hi]], weights[e][0], weights[e][1], O.round_bf16)
-            flops += 6.0 * (hi - lo) * w.d * w.f
-    if w.shared_f:
-        O.expert_forward(x[:512], weights[w.E][0], weights[w.E][1], O.round_bf16)
-        flops += 6.0 * 512 * w.d * w.shared_f
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"fp64 numpy oracle: route + permutation of all {w.T} tokens, then the SwiGLU experts "
-                      f"of expert ids 0,16,...,{sample_e[-1]} ({len(sample_e)} of {w.E}) on their real rows"
-                      + (" and the shared expert on 512 tokens" if w.shared_f else "")
-                      + "; value = their useful FLOPs / wall time"}
+    off, row_of, src = O.permutation(idx, w.E, w.T if w.shared_f else 0)
+    xp = O.gather_rows(x, src)
+    spent += time.perf_counter() - t0
+    Y = np.zeros((int(off[-1]), w.d))
+    groups = ([w.E] if w.shared_f else []) + [e for r in range(16) for e in range(int(f"{r:04b}"[::-1], 2), w.E, 16)]
+    flops, done = 0.0, 0
+    for g in groups:
+        if spent >= CPU_BUDGET_S:
+            break
+        lo, hi = int(off[g]), int(off[g + 1])
+        done += 1
+        if hi == lo:
+            continue
+        gu = w_gu_dev[g].float().cpu().numpy()
+        dn = w_down_dev[g].float().cpu().numpy()
+        t0 = time.perf_counter()
+        _, Y[lo:hi] = O.expert_forward(xp[lo:hi], gu, dn, O.round_bf16)
+        spent += time.perf_counter() - t0
+        flops += 6.0 * (hi - lo) * w.d * (gu.shape[0] // 2)
+    whole = done == len(groups)
+    if whole:
+        t0 = time.perf_counter()
+        O.combine(Y[:w.T * w.k], wt, row_of, Y[w.T * w.k:] if w.shared_f else None, O.round_bf16)
+        spent += time.perf_counter() - t0
+    what = ("the whole layer forward" if whole else
+            f"routing, permutation and gather of all {w.T} tokens, then {done} of {len(groups)} expert groups "
+            f"(shared first, then ids in the order 0,16,32,...,8,24,...) on their real rows, stopped at "
+            f"{CPU_BUDGET_S:.0f} s; no combine")
+    return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "seconds": round(spent, 2),
+            "sample": f"fp64 numpy oracle on {what}; value = useful FLOPs of the finished groups / oracle time"}
 
 
 def main():
@@ -179,10 +223,11 @@ def main():
     t_hbm, t_mfma = g1_bytes / (HBM_PEAK_GBS * 1e9), g1_flops / (BF16_PEAK_TFLOPS * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(g1_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = pmc_traffic(w.name) if fused else None
     roof.update({"kernel": "moe_grouped_gemm gate/up+SwiGLU (schedule + main kernel)",
                  "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops, "ms": round(g1_ms, 4),
                  "tflops": round(g1_tflops, 1), "gbs": round(g1_gbs, 1)})
@@ -210,8 +255,15 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.calibrate_copy:
+        src = torch.zeros((COPY_CAL_BYTES // 2,), dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, None)
+        res["cpu_baseline"] = cpu_baseline(w, w_gu, w_down)
     print(json.dumps(res), flush=True)
 
 
