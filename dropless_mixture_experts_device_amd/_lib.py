@@ -34,6 +34,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("C", _vp), ("c_dtype", _i32), ("ldc", _i64),
         ("epilogue", _i32), ("aux", _vp), ("ld_aux", _i64),
         ("a_scale", _vp), ("lda_scale", _i64), ("b_scale", _vp), ("ldb_scale", _i64), ("b_scale_group_stride", _i64),
+        ("ragged_k", _i32), ("c_group_stride", _i64),
     ]
 
 
@@ -49,12 +50,17 @@ _lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), _vp, _sz, _vp]
 _lib.moe_grouped_gemm.restype = _i32
 _lib.moe_combine.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 _lib.moe_combine.restype = _i32
-_lib.moe_group_quant_mxfp8.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _i64, _vp, _i64, _vp, _vp,
-                                       _sz, _vp]
+_lib.moe_group_quant_mxfp8.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _i32, _vp, _i64, _vp, _i64,
+                                       _vp, _vp, _sz, _vp]
 _lib.moe_group_quant_mxfp8.restype = _i32
 
+_lib.moe_combine_backward.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]
+_lib.moe_combine_backward.restype = _i32
+_lib.moe_swiglu_backward.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i64, _vp]
+_lib.moe_swiglu_backward.restype = _i32
+
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
-            "moe_group_quant_mxfp8")
+            "moe_group_quant_mxfp8", "moe_combine_backward", "moe_swiglu_backward")
 
 
 class MoeError(RuntimeError):
@@ -126,47 +132,96 @@ def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_to
 
 
 def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None, aux=None, workspace=None,
-                     stream=None, a_scale=None, b_scale=None):
-    """C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate) * up), one launch.
+                     stream=None, a_scale=None, b_scale=None, ragged_k: bool = False):
+    """One launch over all groups.
 
-    A [A_rows, K]; B [G, N or 2N, K]; C [M, N]; offsets int32 [G+1] (device); a_rows int32 [M].
-    MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale [G, N_B, K/32]
-    uint8 E8M0 bytes.
+    Ragged rows (default): C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate)
+    * up). A [A_rows, K]; B [G, N or 2N, K] (any strides with unit inner stride, e.g. a
+    permuted view of transposed weights); C [M, N]; offsets int32 [G+1] (device); a_rows
+    int32 [M]. MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale
+    [G, N_B, K/32] uint8 E8M0 bytes.
+    ragged_k: C [G, M, N], C[g] = A[:, Kg] @ B[:, Kg]^T over the K range of group g given by
+    offsets in 32-element blocks; A [M, K], B [N, K], a_scale [M, K/32], b_scale [N, K/32].
     """
-    G = B.shape[0]
-    M, N = C.shape
-    K = A.shape[1]
-    args = MoeGemmArgs(
-        G=G, offsets=offsets.data_ptr(), M=M, N=N, K=K,
-        A=A.data_ptr(), a_dtype=_dtype(A), lda=A.stride(0), A_rows=A.shape[0],
-        a_rows=None if a_rows is None else a_rows.data_ptr(),
-        B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(1), b_group_stride=B.stride(0),
-        C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
-        epilogue=epilogue, aux=None if aux is None else aux.data_ptr(), ld_aux=0 if aux is None else aux.stride(0),
-        a_scale=None if a_scale is None else a_scale.data_ptr(), lda_scale=0 if a_scale is None else a_scale.stride(0),
-        b_scale=None if b_scale is None else b_scale.data_ptr(), ldb_scale=0 if b_scale is None else b_scale.stride(1),
-        b_scale_group_stride=0 if b_scale is None else b_scale.stride(0))
+    if ragged_k:
+        G, M, N = C.shape
+        K = A.shape[1]
+        args = MoeGemmArgs(
+            G=G, offsets=offsets.data_ptr(), M=M, N=N, K=K,
+            A=A.data_ptr(), a_dtype=_dtype(A), lda=A.stride(0), A_rows=A.shape[0], a_rows=None,
+            B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(0), b_group_stride=0,
+            C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(1), epilogue=epilogue, aux=None, ld_aux=0,
+            a_scale=None if a_scale is None else a_scale.data_ptr(),
+            lda_scale=0 if a_scale is None else a_scale.stride(0),
+            b_scale=None if b_scale is None else b_scale.data_ptr(),
+            ldb_scale=0 if b_scale is None else b_scale.stride(0), b_scale_group_stride=0,
+            ragged_k=1, c_group_stride=C.stride(0))
+    else:
+        G = B.shape[0]
+        M, N = C.shape
+        K = A.shape[1]
+        args = MoeGemmArgs(
+            G=G, offsets=offsets.data_ptr(), M=M, N=N, K=K,
+            A=A.data_ptr(), a_dtype=_dtype(A), lda=A.stride(0), A_rows=A.shape[0],
+            a_rows=None if a_rows is None else a_rows.data_ptr(),
+            B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(1), b_group_stride=B.stride(0),
+            C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
+            epilogue=epilogue, aux=None if aux is None else aux.data_ptr(),
+            ld_aux=0 if aux is None else aux.stride(0),
+            a_scale=None if a_scale is None else a_scale.data_ptr(),
+            lda_scale=0 if a_scale is None else a_scale.stride(0),
+            b_scale=None if b_scale is None else b_scale.data_ptr(),
+            ldb_scale=0 if b_scale is None else b_scale.stride(1),
+            b_scale_group_stride=0 if b_scale is None else b_scale.stride(0), ragged_k=0, c_group_stride=0)
     ws, wsb = _ws(workspace)
     _check("moe_grouped_gemm", _lib.moe_grouped_gemm(ctypes.byref(args), ws, wsb, _stream(stream)))
 
 
 def moe_combine(y, topk_w, row_of, y_shared, out, stream=None):
-    """out[t] = sum_j topk_w[t,j] * y[row_of[t,j]] (+ y_shared[t])."""
+    """out[t] = sum_j topk_w[t,j] * y[row_of[t,j]] (+ y_shared[t]); topk_w None: weights one
+    (the transpose of the permutation's gather)."""
     T, k = row_of.shape
     d = out.shape[1]
     _check("moe_combine", _lib.moe_combine(_ptr(y), _dtype(out), _ptr(topk_w), _ptr(row_of), _ptr(y_shared), T, d, k,
                                            _ptr(out), _stream(stream)))
 
 
+def quant_col_blocks(rows: int, G: int) -> int:
+    """Capacity in 32-row blocks of the column-wise (axis 1) output: 4 * (ceil(rows/128) + G)."""
+    return 4 * (-(-rows // 128) + G)
+
+
+def moe_combine_backward(d_out, topk_w, row_of, dy, y=None, dy_shared=None, dw=None, stream=None):
+    """dy[row_of[t,j]] = topk_w[t,j] * d_out[t]; dy_shared[t] = d_out[t]; dw[t,j] = <d_out[t], y[row_of[t,j]]>."""
+    T, k = row_of.shape
+    d = d_out.shape[1]
+    _check("moe_combine_backward", _lib.moe_combine_backward(
+        _ptr(d_out), _dtype(d_out), _ptr(topk_w), _ptr(row_of), _ptr(y), T, d, k, _ptr(dy), _ptr(dy_shared),
+        _ptr(dw), _stream(stream)))
+
+
+def moe_swiglu_backward(dh, gu, dgu, stream=None):
+    """dgu = [dh * u * silu'(g), dh * silu(g)] from gu = [g, u] (all row-major, rows x f / 2f)."""
+    rows, f = dh.shape
+    _check("moe_swiglu_backward", _lib.moe_swiglu_backward(
+        _ptr(dh), dh.stride(0), _ptr(gu), gu.stride(0), _dtype(dh), rows, f, _ptr(dgu), dgu.stride(0),
+        _stream(stream)))
+
+
 def moe_group_quant_mxfp8(x, q, scales, axis: int = 0, group_offsets=None, block_start=None, workspace=None,
-                          stream=None):
-    """MXFP8 quantisation of x [rows, cols] (bf16 or fp32) into E4M3 codes q (uint8) and E8M0
-    scale bytes (uint8). axis 0: q [rows, >=cols], scales [rows, >=cols/32]. axis 1 (blocks of
-    32 rows inside each group of group_offsets, transposed output): q [cols, >=32*(ceil(rows/32)+G)],
-    scales [cols, >=ceil(rows/32)+G], block_start int32 [G+1] (optional output)."""
-    rows, cols = x.shape
+                          stream=None, row_index=None, rows=None):
+    """MXFP8 quantisation of x (bf16 or fp32, [in_rows, cols]) into E4M3 codes q (uint8) and
+    E8M0 scale bytes (uint8). Logical row r reads x[row_index[r]] when row_index is given
+    (then `rows` defaults to row_index's length), else x[r]. axis 0: q [rows, >=cols],
+    scales [rows, >=cols/32]. axis 1 (blocks of 32 rows inside each group of group_offsets,
+    each group starting on a multiple of 4 blocks; transposed output):
+    q [cols, >=32*quant_col_blocks(rows, G)], scales [cols, >=quant_col_blocks(rows, G)],
+    block_start int32 [G+1] (optional output)."""
+    in_rows, cols = x.shape
+    if rows is None:
+        rows = in_rows if row_index is None else row_index.numel()
     G = 0 if group_offsets is None else group_offsets.numel() - 1
     ws, wsb = _ws(workspace)
     _check("moe_group_quant_mxfp8", _lib.moe_group_quant_mxfp8(
-        _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(group_offsets), G, axis, _ptr(q), q.stride(0),
-        _ptr(scales), scales.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
+        _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(row_index), in_rows, _ptr(group_offsets), G, axis,
+        _ptr(q), q.stride(0), _ptr(scales), scales.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))

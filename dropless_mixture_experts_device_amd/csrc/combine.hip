@@ -1,5 +1,8 @@
 // moe_combine: return every expert output row to its token and sum them with the routing
 // weights (plus the always-on shared expert), in a fixed order with fp32 accumulation.
+// With no weights it is the transpose of the permutation (dx[t] = sum_j dX_perm[row_of[t,j]]).
+// moe_combine_backward: the transpose of the weighted combine (dY rows and the routing
+// weights' gradient).
 //
 // [Blog] "Optimisation 2": combine brings each processed token back to its original
 // position and accumulates the experts' results. Written as a gather-reduce per token
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __res
     const int TK = T * k;
     if (threadIdx.x < k) {
         rows[threadIdx.x] = min(max(row_of[(int64_t)t * k + threadIdx.x], 0), TK - 1);
-        wts[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
+        wts[threadIdx.x] = topk_w ? topk_w[(int64_t)t * k + threadIdx.x] : 1.f;   // NULL: plain sum
     }
     __syncthreads();
     const int ngroups = d / 8;
@@ -88,8 +91,114 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __res
     }
 }
 
+// x * w rounded once to the storage type: the product of an fp32 weight and a bf16/fp32
+// value is exact in double; round-to-odd to fp32 keeps enough bits that the final
+// nearest-even rounding to bf16 equals a single rounding of the exact product.
+__device__ __forceinline__ float mul_round_odd(float w, float x) {
+    const double p = (double)w * (double)x;
+    float f = (float)p;
+    if ((double)f != p) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(p)) u -= 1;   // truncate toward zero ...
+        f = __uint_as_float(u | 1u);             // ... and mark inexact in the last bit
+    }
+    return f;
+}
+
+// Transpose of the combine, one workgroup per token:
+//   dy[row_of[t,j]] = w[t,j] * d_out[t]       (every routed row is written exactly once)
+//   dy_shared[t]    = d_out[t]                (the shared expert's output gradient)
+//   dw[t,j]         = <d_out[t], y[row_of[t,j]]>   (fp32, fixed reduction order)
+template <int ESIZE>
+__global__ __launch_bounds__(kCombThreads) void combine_bwd_kernel(const char* __restrict__ d_out,
+                                                                   const float* __restrict__ topk_w,
+                                                                   const int32_t* __restrict__ row_of,
+                                                                   const char* __restrict__ y, int T, int d, int k,
+                                                                   char* __restrict__ dy, char* __restrict__ dy_shared,
+                                                                   float* __restrict__ dw) {
+    const int t = blockIdx.x;
+    __shared__ int rows[16];
+    __shared__ float wts[16];
+    __shared__ float red[kCombThreads / kWave][16];
+    const int TK = T * k;
+    if (threadIdx.x < k) {
+        rows[threadIdx.x] = min(max(row_of[(int64_t)t * k + threadIdx.x], 0), TK - 1);
+        wts[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const int ngroups = d / 8;
+    const int64_t rowbytes = (int64_t)d * ESIZE;
+    float part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = 0.f;
+    for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
+        float g[8];
+        load8<ESIZE>(d_out + t * rowbytes + c * 8 * ESIZE, g);
+        if (dy_shared != nullptr) store8<ESIZE>(dy_shared + t * rowbytes + c * 8 * ESIZE, g);
+        for (int j = 0; j < k; ++j) {
+            float o[8];
+            const float w = wts[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = ESIZE == 2 ? mul_round_odd(w, g[i]) : w * g[i];
+            store8<ESIZE>(dy + rows[j] * rowbytes + c * 8 * ESIZE, o);
+            if (dw != nullptr) {
+                float v[8];
+                load8<ESIZE>(y + rows[j] * rowbytes + c * 8 * ESIZE, v);
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc = fmaf(g[i], v[i], acc);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (q == j) part[q] += acc;
+            }
+        }
+    }
+    if (dw == nullptr) return;
+    // fixed-order reduction: wave butterfly, then the 4 waves in order
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j >= k) break;
+        float v = part[j];
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if (lane == 0) red[wave][j] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCombThreads / kWave; ++w) v += red[w][threadIdx.x];
+        dw[(int64_t)t * k + threadIdx.x] = v;
+    }
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" moe_status_t moe_combine_backward(const void* d_out, int32_t dtype, const float* topk_w,
+                                             const int32_t* row_of, const void* y, int64_t T, int64_t d, int32_t k,
+                                             void* dy, void* dy_shared, float* dw, void* stream) {
+    if (T < 0 || d <= 0 || d % 8 != 0 || k < 1 || k > 16) return MOE_EINVAL;
+    if (T * (int64_t)k > INT32_MAX || d > INT32_MAX / 16) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!d_out || !topk_w || !row_of || !dy || (dw && !y)) return MOE_EINVAL;
+    if (!moe_aligned16(d_out) || !moe_aligned16(dy) || (dy_shared && !moe_aligned16(dy_shared)) ||
+        (dw && !moe_aligned16(y)))
+        return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(moe::combine_bwd_kernel<2>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
+                           (const char*)d_out, topk_w, row_of, (const char*)y, (int)T, (int)d, k, (char*)dy,
+                           (char*)dy_shared, dw);
+    else
+        hipLaunchKernelGGL(moe::combine_bwd_kernel<4>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
+                           (const char*)d_out, topk_w, row_of, (const char*)y, (int)T, (int)d, k, (char*)dy,
+                           (char*)dy_shared, dw);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
 
 extern "C" moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, const int32_t* row_of,
                                     const void* y_shared, int64_t T, int64_t d, int32_t k, void* out,
@@ -98,7 +207,7 @@ extern "C" moe_status_t moe_combine(const void* y, int32_t dtype, const float* t
     if (T * (int64_t)k > INT32_MAX || d > INT32_MAX / 16) return MOE_EINVAL;
     if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
-    if (!y || !topk_w || !row_of || !out) return MOE_EINVAL;
+    if (!y || !row_of || !out) return MOE_EINVAL;
     if (!moe_aligned16(y) || !moe_aligned16(out) || (y_shared && !moe_aligned16(y_shared))) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (dtype == MOE_BF16)

@@ -87,7 +87,9 @@ struct GemmParams {
     const uint8_t* b_scale;   // group g: [N_B, K/32] at b_scale + g * b_scale_stride
     int64_t ldb_scale;
     int64_t b_scale_stride;
-    const int32_t* tile_start;   // [G+1] in workspace
+    const int32_t* tile_start;   // [G+1] in workspace (ragged rows)
+    int64_t c_stride;            // ragged K: elements between groups' C
+    int MT;                      // ragged K: row tiles per group
 };
 
 // ---------------------------------------------------------------------------------------
@@ -237,7 +239,9 @@ __device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
 // ---------------------------------------------------------------------------------------
 // one output tile of BM rows x (256 B-rows) for group g
 // ---------------------------------------------------------------------------------------
-template <int BM, bool SWIGLU, bool MX>
+// RK (ragged K): every group computes the full M x N output over its own K range
+// [32 offsets[g], 32 offsets[g+1]) and writes it at C + g * c_stride.
+template <int BM, bool SWIGLU, bool MX, bool RK>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
     constexpr int EB = MX ? 1 : 2;                      // operand element bytes
     constexpr int WM = (BM == 16) ? 1 : 2;              // wave grid: WM x WN = 8 waves
@@ -264,7 +268,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     int row_begin, row_end;
-    group_rows(p.offsets, g, p.M, row_begin, row_end);
+    int64_t kbase = 0;                                    // first K element (ragged K)
+    int nk = p.K / (kRowBytes / EB);                      // K slices
+    char* Cg = p.C;
+    if constexpr (RK) {
+        row_begin = 0;
+        row_end = p.M;
+        // clamp the block range into [0, K/32] and round to whole 128-element slices, so
+        // inconsistent offsets can never move a load outside A or B
+        const int kb_max = p.K / 32;
+        const int kb0 = min(max(p.offsets[g], 0), kb_max) & ~3;
+        const int kb1 = max(min(p.offsets[g + 1], kb_max), kb0);
+        kbase = (int64_t)kb0 * 32;
+        nk = (kb1 - kb0) / 4;
+        Cg = p.C + (int64_t)g * p.c_stride * (p.c_f32 ? 4 : 2);
+    } else {
+        group_rows(p.offsets, g, p.M, row_begin, row_end);
+    }
     const int r0 = row_begin + mt * BM;                   // first C row of the tile
     const int n0 = nt * BN_OUT;                           // first output column
 
@@ -291,10 +311,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         const int instr = wave + kWaves * i;
         const int row = instr * ROWS_PER_INSTR + lane / kChunks;
         const int chunk = (lane % kChunks) ^ swz(row);
-        a_src[i] = p.A + a_row_of(row) * p.lda * EB + chunk * 16;
+        a_src[i] = p.A + (a_row_of(row) * p.lda + kbase) * EB + chunk * 16;
     }
     const char* b_src[B_PER_WAVE];
-    const char* bg = p.B + (int64_t)g * p.b_stride * EB;
+    const char* bg = p.B + ((RK ? 0 : (int64_t)g * p.b_stride) + kbase) * EB;
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
         const int instr = wave * B_PER_WAVE + i;
@@ -307,11 +327,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     int s_lds = 0;
     if constexpr (MX) {
         if (wave < AS_INSTR) {
-            s_src = p.a_scale + a_row_of(wave * 64 + lane) * p.lda_scale;
+            s_src = p.a_scale + a_row_of(wave * 64 + lane) * p.lda_scale + kbase / 32;
             s_lds = kScaleOffA + wave * 256;
         } else if (wave < AS_INSTR + BS_INSTR) {
             const int rho = (wave - AS_INSTR) * 64 + lane;
-            s_src = p.b_scale + (int64_t)g * p.b_scale_stride + (int64_t)b_row_of(rho) * p.ldb_scale;
+            s_src = p.b_scale + (RK ? 0 : (int64_t)g * p.b_scale_stride) + (int64_t)b_row_of(rho) * p.ldb_scale +
+                    kbase / 32;
             s_lds = kScaleOffB + (wave - AS_INSTR) * 256;
         }
     }
@@ -340,7 +361,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
         for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, MX>();
 
-    const int nk = p.K / (kRowBytes / EB);
     // Per-wave loads per stage differ (some waves issue no A or scale load); the wait count
     // uses the smallest, so every wave is sure its own loads of stage kt have landed.
     constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / kWaves;
@@ -418,25 +438,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     // multiplied. Before stage kt is read, this wave's loads of the later stage may still be
     // pending (LOADS_MIN); the barrier then makes every wave's loads of stage kt visible and
     // guarantees the buffer refilled next (read in iteration kt-1) is no longer in use.
-    lds_barrier();   // the previous tile's epilogue may still read LDS
-    issue(0);
-    if (nk > 1) issue(1);
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) {
-        wait_vm_lgkm0<LOADS_MIN>();
+    if (nk > 0) {    // only a ragged-K group with an empty range has no slice (C_g = 0)
+        lds_barrier();   // the previous tile's epilogue may still read LDS
+        issue(0);
+        if (nk > 1) issue(1);
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) {
+            wait_vm_lgkm0<LOADS_MIN>();
+            lds_barrier();
+            issue(kt + 2);
+            compute(kt);
+        }
+        if (kt + 1 < nk) {
+            wait_vm_lgkm0<LOADS_MIN>();
+            lds_barrier();
+            compute(kt);
+            ++kt;
+        }
+        wait_vm_lgkm0<0>();
         lds_barrier();
-        issue(kt + 2);
         compute(kt);
     }
-    if (kt + 1 < nk) {
-        wait_vm_lgkm0<LOADS_MIN>();
-        lds_barrier();
-        compute(kt);
-        ++kt;
-    }
-    wait_vm_lgkm0<0>();
-    lds_barrier();
-    compute(kt);
 
     // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
     wait_vm_lgkm0<0>();
@@ -485,23 +507,49 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         const int col = n0 + ch * cols_per_chunk;
         if (row < rows_valid && col < p.N) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + ch * 16);
-            *reinterpret_cast<u32x4*>(p.C + ((int64_t)(r0 + row) * p.ldc + col) * esize) = v;
+            *reinterpret_cast<u32x4*>(Cg + ((int64_t)(r0 + row) * p.ldc + col) * esize) = v;
         }
     }
 }
 
-template <bool SWIGLU, bool MX>
+// Ordering of the tiles of one group: supertiles of kSuper column tiles x all MT row tiles,
+// row-major inside a supertile, so consecutive tiles share B panels and A panels.
+__device__ __forceinline__ void tile_coords(int L, int MT, int NT, int& mt, int& nt) {
+    const int full = NT / kSuper;
+    if (L < full * MT * kSuper) {
+        const int s = L / (MT * kSuper), rem = L % (MT * kSuper);
+        mt = rem / kSuper;
+        nt = s * kSuper + rem % kSuper;
+    } else {
+        const int rem = L - full * MT * kSuper, w = NT - full * kSuper;
+        mt = rem / w;
+        nt = full * kSuper + rem % w;
+    }
+}
+
+template <bool SWIGLU, bool MX, bool RK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
-    for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
-    __syncthreads();
-    const int total = ts[p.G];
     // XCD-aware slot: the hardware deals workgroups round-robin over the 8 XCDs, so give the
     // workgroups of one XCD consecutive slots (and hence consecutive tiles in each round)
     const int nxcd = (gridDim.x % 8 == 0) ? 8 : 1;
     const int per_xcd = gridDim.x / nxcd;
     const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
+    if constexpr (RK) {
+        const int per_group = p.MT * p.NT;
+        const int total = p.G * per_group;
+        for (int tile = slot; tile < total; tile += gridDim.x) {
+            const int g = tile / per_group;
+            int mt, nt;
+            tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
+            gemm_tile<128, false, true, true>(p, lds, g, mt, nt);
+        }
+        return;
+    }
+    int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
+    for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
+    __syncthreads();
+    const int total = ts[p.G];
     for (int tile = slot; tile < total; tile += gridDim.x) {
         // group = last g with ts[g] <= tile
         int lo = 0, hi = p.G - 1;
@@ -516,24 +564,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
         group_rows(p.offsets, g, p.M, gb, ge);
         const int m = ge - gb;
         const int bm = bm_of_rows(m);
-        const int MT = cdiv(m, bm);
-        const int NT = p.NT;
-        const int full = NT / kSuper;
         int mt, nt;
-        if (L < full * MT * kSuper) {
-            const int s = L / (MT * kSuper), rem = L % (MT * kSuper);
-            mt = rem / kSuper;
-            nt = s * kSuper + rem % kSuper;
-        } else {
-            const int rem = L - full * MT * kSuper, w = NT - full * kSuper;
-            mt = rem / w;
-            nt = full * kSuper + rem % w;
-        }
+        tile_coords(L, cdiv(m, bm), p.NT, mt, nt);
         switch (bm) {
-            case 16: gemm_tile<16, SWIGLU, MX>(p, lds, g, mt, nt); break;
-            case 32: gemm_tile<32, SWIGLU, MX>(p, lds, g, mt, nt); break;
-            case 64: gemm_tile<64, SWIGLU, MX>(p, lds, g, mt, nt); break;
-            default: gemm_tile<128, SWIGLU, MX>(p, lds, g, mt, nt); break;
+            case 16: gemm_tile<16, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
+            case 32: gemm_tile<32, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
+            case 64: gemm_tile<64, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
+            default: gemm_tile<128, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
         }
     }
 }
@@ -585,22 +622,22 @@ int num_cus() {
     return cached[dev];
 }
 
-template <bool SWIGLU, bool MX>
+template <bool SWIGLU, bool MX, bool RK>
 bool set_lds_attr() {
     static bool done = false;
     if (!done) {
-        if (hipFuncSetAttribute((const void*)gemm_mfma_kernel<SWIGLU, MX>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsBytes) != hipSuccess)
+        if (hipFuncSetAttribute((const void*)gemm_mfma_kernel<SWIGLU, MX, RK>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
             return false;
         done = true;
     }
     return true;
 }
 
-template <bool SWIGLU, bool MX>
+template <bool SWIGLU, bool MX, bool RK = false>
 moe_status_t launch(const GemmParams& p, int grid, hipStream_t s) {
-    if (!set_lds_attr<SWIGLU, MX>()) return MOE_EHIP;
-    hipLaunchKernelGGL((gemm_mfma_kernel<SWIGLU, MX>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, p);
+    if (!set_lds_attr<SWIGLU, MX, RK>()) return MOE_EHIP;
+    hipLaunchKernelGGL((gemm_mfma_kernel<SWIGLU, MX, RK>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, p);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
@@ -627,6 +664,13 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3) return MOE_ENOTSUP;
     if (a->c_dtype != MOE_BF16 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->a_dtype == MOE_F32 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
+    if (a->ragged_k != 0 && a->ragged_k != 1) return MOE_EINVAL;
+    if (a->ragged_k) {
+        // weight-gradient form: MXFP8 only, plain epilogue, A is [M, K] and B is [N, K]
+        if (a->a_dtype != MOE_E4M3 || a->epilogue != MOE_EPI_NONE) return MOE_ENOTSUP;
+        if (a->a_rows || a->aux || a->b_group_stride != 0 || a->b_scale_group_stride != 0) return MOE_EINVAL;
+        if (a->A_rows != a->M || a->c_group_stride < a->M * a->ldc) return MOE_EINVAL;
+    }
     if (a->M == 0) return MOE_OK;
     if (!a->A || !a->B || !a->C || a->A_rows <= 0) return MOE_EINVAL;
     // groups' B matrices are only read, so they may overlap (e.g. K slices of one matrix)
@@ -660,6 +704,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.ldb_scale = a->ldb_scale;
     p.b_scale_stride = a->b_scale_group_stride;
     p.tile_start = (const int32_t*)workspace;
+    p.c_stride = a->c_group_stride;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
     if (a->a_dtype == MOE_F32) {
@@ -684,6 +729,15 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     }
     const int bn_out = swiglu ? moe::kBN / 2 : moe::kBN;
     p.NT = (int)moe::cdiv<int64_t>(a->N, bn_out);
+    if (a->ragged_k) {
+        // every group: MT x NT tiles of 128 x 256 over its own K range; no schedule needed
+        if (a->ldc % 8 || (a->c_group_stride % 8)) return MOE_EINVAL;
+        p.MT = (int)moe::cdiv<int64_t>(a->M, 128);
+        const int64_t tiles = (int64_t)p.MT * p.NT * a->G;
+        if (tiles > INT32_MAX) return MOE_EINVAL;
+        const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), tiles);
+        return moe::launch<false, true, true>(p, grid, s);
+    }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
                        (int32_t*)workspace);
     MOE_CHECK_LAUNCH();

@@ -12,6 +12,14 @@ namespace moe {
 namespace {
 
 constexpr int kBlock = 32;
+constexpr int kGroupAlign = 4;   // column-wise: each group's blocks start on a multiple of 4 blocks (128 rows)
+
+// Row of `in` that feeds logical row r: row_index[r] (clamped into the input) or r itself.
+__device__ __forceinline__ int64_t in_row(const int32_t* row_index, int64_t in_rows, int64_t r) {
+    if (!row_index) return r;
+    const int64_t v = row_index[r];
+    return v < 0 ? 0 : (v >= in_rows ? in_rows - 1 : v);
+}
 
 // E8M0 byte for a block whose largest magnitude is `amax` (0 for an all-zero block).
 __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
@@ -50,14 +58,15 @@ __device__ __forceinline__ float load_val(const char* p, int esize) {
 // blocks of a row so loads and code stores are contiguous.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict__ in, int64_t rows, int cols,
-                                                         int64_t ld_in, uint8_t* __restrict__ q, int64_t ld_q,
+                                                         int64_t ld_in, const int32_t* __restrict__ row_index,
+                                                         int64_t in_rows, uint8_t* __restrict__ q, int64_t ld_q,
                                                          uint8_t* __restrict__ sc, int64_t ld_sc) {
     const int nb = cols / kBlock;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= rows * nb) return;
     const int64_t r = idx / nb;
     const int b = (int)(idx % nb);
-    const char* src = in + (r * ld_in + (int64_t)b * kBlock) * ESIZE;
+    const char* src = in + (in_row(row_index, in_rows, r) * ld_in + (int64_t)b * kBlock) * ESIZE;
     float v[kBlock];
     if (ESIZE == 2) {
 #pragma unroll
@@ -101,6 +110,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict_
 // Group-aware column-wise, transposed output: block j (a global index over all groups'
 // 32-row blocks) of column c covers rows [offsets[g] + 32 i, +32) of group g, where
 // j = block_start[g] + i; its 32 codes go to q[c, 32 j ...] and its scale to sc[c, j].
+// Group g owns 4 * ceil(m_g / 128) blocks, so every group starts on a 128-element boundary
+// of the transposed rows (one K slice of the MXFP8 GEMM, with its 4 scale bytes in one
+// aligned dword); blocks past the group's last row are all-zero (codes 0, scale byte 0).
 __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t* __restrict__ offsets, int G,
                                                                   int64_t rows, int32_t* __restrict__ block_start) {
     __shared__ int wsum[16];
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
         if (g < G) {
             const int b = (int)min<int64_t>(max(offsets[g], 0), rows);
             const int e = (int)min<int64_t>(max(offsets[g + 1], b), rows);
-            nb = cdiv(e - b, kBlock);
+            nb = kGroupAlign * cdiv(e - b, kGroupAlign * kBlock);
         }
         int incl = nb;
 #pragma unroll
@@ -138,7 +150,8 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
 // reads of a wave is one contiguous segment.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict__ in, int64_t rows, int cols,
-                                                         int64_t ld_in, const int32_t* __restrict__ offsets, int G,
+                                                         int64_t ld_in, const int32_t* __restrict__ row_index,
+                                                         int64_t in_rows, const int32_t* __restrict__ offsets, int G,
                                                          const int32_t* __restrict__ block_start,
                                                          uint8_t* __restrict__ q, int64_t ld_q,
                                                          uint8_t* __restrict__ sc, int64_t ld_sc) {
@@ -155,12 +168,12 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     const int gb = (int)min<int64_t>(max(offsets[g], 0), rows);
     const int ge = (int)min<int64_t>(max(offsets[g + 1], gb), rows);
     const int r0 = gb + (j - block_start[g]) * kBlock;
-    const int n = min(kBlock, ge - r0);              // rows of this block (last one may be partial)
+    const int n = max(0, min(kBlock, ge - r0));      // rows of this block (partial or none at a group's end)
     float v[kBlock];
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) {
-        v[i] = (i < n) ? load_val(in + ((int64_t)(r0 + i) * ld_in + c) * ESIZE, ESIZE) : 0.f;
+        v[i] = (i < n) ? load_val(in + (in_row(row_index, in_rows, r0 + i) * ld_in + c) * ESIZE, ESIZE) : 0.f;
         amax = fmaxf(amax, fabsf(v[i]));
     }
     const uint32_t byte = mx_scale_byte(amax);
@@ -187,13 +200,16 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
 size_t moe_quant_workspace_bytes(int32_t G) { return ((size_t)(G < 1 ? 1 : G) + 1) * 4 + 255 & ~size_t(255); }
 
 extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, int64_t cols,
-                                              int64_t ld_in, const int32_t* group_offsets, int32_t G, int32_t axis,
+                                              int64_t ld_in, const int32_t* row_index, int64_t in_rows,
+                                              const int32_t* group_offsets, int32_t G, int32_t axis,
                                               uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                               int32_t* block_start, void* workspace, size_t workspace_bytes,
                                               void* stream) {
     if (rows < 0 || cols <= 0 || cols % moe::kBlock != 0 || cols > INT32_MAX / 2 || ld_in < cols) return MOE_EINVAL;
     if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
     if (axis != 0 && axis != 1) return MOE_EINVAL;
+    if (!row_index) in_rows = rows;
+    else if (in_rows <= 0 && rows > 0) return MOE_EINVAL;
     const int esize = dtype == MOE_BF16 ? 2 : 4;
     hipStream_t s = (hipStream_t)stream;
     if (axis == 0) {
@@ -204,16 +220,17 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
         const dim3 grid((unsigned)moe::cdiv<int64_t>(n, 256));
         if (esize == 2)
             hipLaunchKernelGGL(moe::quant_rows_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                               q, ld_q, scales, ld_scales);
+                               row_index, in_rows, q, ld_q, scales, ld_scales);
         else
             hipLaunchKernelGGL(moe::quant_rows_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                               q, ld_q, scales, ld_scales);
+                               row_index, in_rows, q, ld_q, scales, ld_scales);
         MOE_CHECK_LAUNCH();
         return MOE_OK;
     }
     // axis 1: group-aware blocks of rows, transposed output
     if (G < 1 || !group_offsets || rows > INT32_MAX / 2) return MOE_EINVAL;
-    const int64_t nblk_cap = moe::cdiv<int64_t>(rows, moe::kBlock) + G;      // blocks over all groups, upper bound
+    // blocks over all groups, upper bound: sum_g 4 ceil(m_g / 128) <= 4 (ceil(rows / 128) + G)
+    const int64_t nblk_cap = moe::kGroupAlign * (moe::cdiv<int64_t>(rows, moe::kGroupAlign * moe::kBlock) + G);
     if (!workspace && !block_start) return MOE_EWORKSPACE;
     if (!block_start && workspace_bytes < moe_quant_workspace_bytes(G)) return MOE_EWORKSPACE;
     if (!q || !scales || ld_q < nblk_cap * moe::kBlock || ld_scales < nblk_cap) return MOE_EINVAL;
@@ -226,10 +243,10 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
     const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, 256), (unsigned)nblk_cap);
     if (esize == 2)
         hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           group_offsets, G, bs, q, ld_q, scales, ld_scales);
+                           row_index, in_rows, group_offsets, G, bs, q, ld_q, scales, ld_scales);
     else
         hipLaunchKernelGGL(moe::quant_cols_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           group_offsets, G, bs, q, ld_q, scales, ld_scales);
+                           row_index, in_rows, group_offsets, G, bs, q, ld_q, scales, ld_scales);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }

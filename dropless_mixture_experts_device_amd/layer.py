@@ -95,3 +95,150 @@ def forward(x, w_router, bias, w_gu, w_down, s: LayerShape, b: LayerBuffers):
     experts(x, w_gu, w_down, s, b)
     combine(s, b)
     return b.out
+
+
+# --------------------------------------------------------------------------------------
+# MXFP8 training step (forward + backward of the experts, the permutation and the combine)
+#
+# [Blog] "Optimisations dropless MoE needs": the expert GEMMs run in MXFP8 with group-aware
+# quantisation; [Reading] contribution 3: MoE low precision needs group quantisation.
+# Every GEMM operand is quantised along that GEMM's contraction axis: row-wise for the
+# forward and data-gradient GEMMs, in 32-row blocks inside each group (column-wise, output
+# transposed) for the weight gradients, whose contraction runs over the group's tokens.
+# --------------------------------------------------------------------------------------
+
+def _u8(shape, dev):
+    return torch.empty(shape, dtype=torch.uint8, device=dev)
+
+
+class MxWeights:
+    """The step's quantised weights, both axis copies (quantised once per step):
+    gu / dn     row-wise along d (W_gu [G, 2f, d]) and along f (W_down [G, d, f]) for the forward;
+    guT / dnT   along 2f and along d (column-wise over the stacked weights, transposed) for
+                the data gradients, viewed per group as [G, d, 2f] and [G, f, d]."""
+
+    def __init__(self, s: LayerShape, device):
+        dev = torch.device(device)
+        G, d, f = s.groups, s.d, s.f
+        for n, k in (("d", d), ("f", f), ("2f", 2 * f)):
+            if k % 128:
+                raise ValueError(f"MXFP8 GEMMs need {n} % 128 == 0 (got {k})")
+        self.shape = s
+        self.q_gu, self.s_gu = _u8((G, 2 * f, d), dev), _u8((G, 2 * f, d // 32), dev)
+        self.q_dn, self.s_dn = _u8((G, d, f), dev), _u8((G, d, f // 32), dev)
+        cgu = L.quant_col_blocks(G * 2 * f, G)
+        cdn = L.quant_col_blocks(G * d, G)
+        self.q_guT, self.s_guT = _u8((d, 32 * cgu), dev), _u8((d, cgu), dev)
+        self.q_dnT, self.s_dnT = _u8((f, 32 * cdn), dev), _u8((f, cdn), dev)
+        self.off_gu = (torch.arange(G + 1, dtype=torch.int32, device=dev) * (2 * f)).contiguous()
+        self.off_dn = (torch.arange(G + 1, dtype=torch.int32, device=dev) * d).contiguous()
+        self.bs = torch.empty((G + 1,), dtype=torch.int32, device=dev)
+
+    def quantise(self, w_gu, w_down):
+        s = self.shape
+        G, d, f = s.groups, s.d, s.f
+        L.moe_group_quant_mxfp8(w_gu.view(G * 2 * f, d), self.q_gu.view(G * 2 * f, d),
+                                self.s_gu.view(G * 2 * f, d // 32), axis=0)
+        L.moe_group_quant_mxfp8(w_down.view(G * d, f), self.q_dn.view(G * d, f), self.s_dn.view(G * d, f // 32),
+                                axis=0)
+        # 2f and d are multiples of 128, so group g's transposed blocks start at g*2f/32 (g*d/32)
+        L.moe_group_quant_mxfp8(w_gu.view(G * 2 * f, d), self.q_guT, self.s_guT, axis=1, group_offsets=self.off_gu,
+                                block_start=self.bs)
+        L.moe_group_quant_mxfp8(w_down.view(G * d, f), self.q_dnT, self.s_dnT, axis=1, group_offsets=self.off_dn,
+                                block_start=self.bs)
+
+    def gu_T(self):
+        s = self.shape
+        G, d, f2 = s.groups, s.d, 2 * s.f
+        return (self.q_guT.as_strided((G, d, f2), (f2, self.q_guT.stride(0), 1)),
+                self.s_guT.as_strided((G, d, f2 // 32), (f2 // 32, self.s_guT.stride(0), 1)))
+
+    def dn_T(self):
+        s = self.shape
+        G, d, f = s.groups, s.d, s.f
+        return (self.q_dnT.as_strided((G, f, d), (d, self.q_dnT.stride(0), 1)),
+                self.s_dnT.as_strided((G, f, d // 32), (d // 32, self.s_dnT.stride(0), 1)))
+
+
+class MxBuffers(LayerBuffers):
+    """Everything the MXFP8 forward and backward write, allocated once."""
+
+    def __init__(self, s: LayerShape, device):
+        super().__init__(s, device, fused_gather=True, save_gu=True)
+        dev = torch.device(device)
+        R, G, d, f = s.rows, s.groups, s.d, s.f
+        cap = L.quant_col_blocks(R, G)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.q_x, self.s_x = _u8((s.T, d), dev), _u8((s.T, d // 32), dev)
+        self.q_h, self.s_h = _u8((R, f), dev), _u8((R, f // 32), dev)
+        # backward
+        self.dY = torch.empty((R, d), **bf)
+        self.dw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+        self.q_dy, self.s_dy = _u8((R, d), dev), _u8((R, d // 32), dev)
+        self.dH = torch.empty((R, f), **bf)
+        self.dGU = torch.empty((R, 2 * f), **bf)
+        self.q_dgu, self.s_dgu = _u8((R, 2 * f), dev), _u8((R, 2 * f // 32), dev)
+        self.dXp = torch.empty((R, d), **bf)
+        self.dx = torch.empty((s.T, d), **bf)
+        # column-wise (weight-gradient) operands, transposed, groups on 128-row boundaries
+        self.qc_dy, self.sc_dy = _u8((d, 32 * cap), dev), _u8((d, cap), dev)
+        self.qc_h, self.sc_h = _u8((f, 32 * cap), dev), _u8((f, cap), dev)
+        self.qc_dgu, self.sc_dgu = _u8((2 * f, 32 * cap), dev), _u8((2 * f, cap), dev)
+        self.qc_x, self.sc_x = _u8((d, 32 * cap), dev), _u8((d, cap), dev)
+        self.bs = torch.empty((G + 1,), dtype=torch.int32, device=dev)
+        self.dW_gu = torch.empty((G, 2 * f, d), **bf)
+        self.dW_down = torch.empty((G, d, f), **bf)
+        gb = L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, G)
+        self.ws_gemm3 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
+
+
+def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False):
+    """MXFP8 forward: route and permute as in bf16, x quantised row-wise once per token (the
+    GEMM gathers codes and scale rows through src_token), GEMM 1 + SwiGLU saving G and U,
+    H quantised row-wise, GEMM 2, combine. mw must hold this step's quantised weights.
+    routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment."""
+    if not routed:
+        route(x, w_router, bias, s, b)
+    permute(x, s, b)
+    L.moe_group_quant_mxfp8(x, b.q_x, b.s_x, axis=0)
+    L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, aux=b.GU,
+                       workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu)
+    L.moe_group_quant_mxfp8(b.H, b.q_h, b.s_h, axis=0)
+    L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
+                       b_scale=mw.s_dn)
+    combine(s, b)
+    return b.out
+
+
+def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers):
+    """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down.
+
+    combine^T -> dY; dgrad 2 (dH = dY W_down, contracted over d) and wgrad 2 (dW_down[g] =
+    dY_g^T H_g over the group's tokens); SwiGLU backward from the saved G, U; dgrad 1
+    (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx.
+    The router's own backward is not part of this step."""
+    tk = s.T * s.k
+    L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
+                           dy_shared=b.dY[tk:] if s.shared else None, dw=b.dw)
+    # dgrad 2 and wgrad 2
+    L.moe_group_quant_mxfp8(b.dY, b.q_dy, b.s_dy, axis=0)
+    q_dnT, s_dnT = mw.dn_T()
+    L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
+                       b_scale=s_dnT)
+    L.moe_group_quant_mxfp8(b.dY, b.qc_dy, b.sc_dy, axis=1, group_offsets=b.offsets, block_start=b.bs)
+    L.moe_group_quant_mxfp8(b.H, b.qc_h, b.sc_h, axis=1, group_offsets=b.offsets, block_start=b.bs)
+    L.moe_grouped_gemm(b.qc_dy, b.qc_h, b.dW_down, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
+                       a_scale=b.sc_dy, b_scale=b.sc_h, ragged_k=True)
+    # SwiGLU backward, dgrad 1 and wgrad 1
+    L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
+    L.moe_group_quant_mxfp8(b.dGU, b.q_dgu, b.s_dgu, axis=0)
+    q_guT, s_guT = mw.gu_T()
+    L.moe_grouped_gemm(b.q_dgu, q_guT, b.dXp, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_dgu,
+                       b_scale=s_guT)
+    L.moe_group_quant_mxfp8(b.dGU, b.qc_dgu, b.sc_dgu, axis=1, group_offsets=b.offsets, block_start=b.bs)
+    L.moe_group_quant_mxfp8(x, b.qc_x, b.sc_x, axis=1, group_offsets=b.offsets, block_start=b.bs,
+                            row_index=b.src_token)
+    L.moe_grouped_gemm(b.qc_dgu, b.qc_x, b.dW_gu, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
+                       a_scale=b.sc_dgu, b_scale=b.sc_x, ragged_k=True)
+    # permute^T: each token's rows summed back (plus the shared expert's row)
+    L.moe_combine(b.dXp[:tk], None, b.row_of, b.dXp[tk:] if s.shared else None, b.dx)

@@ -125,6 +125,17 @@ moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t* topk_idx,
  * B_g = B + g * b_group_stride elements (groups may share or overlap B: it is only read).
  * Accumulation is fp32; C is rounded once.
  * Rows of C outside [offsets[0], offsets[G]) are not written. Empty groups cost nothing.
+ *
+ * Ragged-K mode (ragged_k = 1; the weight gradients, whose contraction runs over the tokens
+ * of each group: [Reading] contribution 3 on group-wise low precision, [Blog]
+ * "Optimisations dropless MoE needs" on group-aware MXFP8). Every group has the same
+ * M x N output and its own K range, given in 32-element MX blocks:
+ *   C_g[m, n] = sum over k in [32*offsets[g], 32*offsets[g+1]) of A[m, k] * B[n, k]
+ * for m < M, n < N, with C_g = C + g * c_group_stride elements. offsets is non-decreasing
+ * with offsets[G] <= K/32 and every entry a multiple of 4 (128 elements), as the
+ * column-wise quantiser's block_start is; a group with an empty range gets C_g = 0 written.
+ * Only MXFP8 operands and epilogue NONE; a_rows must be NULL, A is [M, K] and B is [N, K]
+ * (b_group_stride and b_scale_group_stride must be 0), c_group_stride >= M * ldc.
  */
 typedef struct moe_gemm_args {
     int32_t G;                  /* number of groups (>= 1)                                  */
@@ -155,6 +166,8 @@ typedef struct moe_gemm_args {
     const uint8_t* b_scale;     /* group g: [N or 2N, K/32] at b_scale + g*b_scale_group_stride  */
     int64_t ldb_scale;
     int64_t b_scale_group_stride;
+    int32_t ragged_k;           /* 0: groups partition the rows of A and C; 1: ragged-K mode  */
+    int64_t c_group_stride;     /* ragged-K mode: elements between consecutive groups' C      */
 } moe_gemm_args_t;
 
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
@@ -173,11 +186,42 @@ moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size
  *   out[t,:] = sum_{j<k} topk_w[t,j] * y[row_of[t,j],:]  (+ y_shared[t,:] if not NULL)
  * summed in fp32 in the fixed order j = 0..k-1 then the shared expert, rounded once.
  *   y        [T*k, d] (rows in expert order), y_shared [T, d] or NULL, out [T, d];
+ *   topk_w   [T, k] fp32, or NULL for weights of one: then the call is the transpose of the
+ *            permutation's gather, dx[t] = sum_j dX_perm[row_of[t,j]] (+ the shared rows),
+ *            which the backward uses to return the permuted input gradient to its tokens;
  *   dtype MOE_BF16 or MOE_F32 for y, y_shared and out; d % 8 == 0; 16-byte aligned.
  */
 moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, const int32_t* row_of,
                          const void* y_shared, int64_t T, int64_t d, int32_t k, void* out,
                          void* stream);
+
+/*
+ * moe_combine_backward -- the transpose of moe_combine (the backward of [Blog]
+ * "Optimisation 2"'s weighted combine):
+ *   dy[row_of[t,j],:] = topk_w[t,j] * d_out[t,:]           exact product rounded once
+ *   dy_shared[t,:]    = d_out[t,:]                         (if dy_shared != NULL)
+ *   dw[t,j]           = sum_c d_out[t,c] * y[row_of[t,j],c] (if dw != NULL; fp32, fixed order)
+ *   d_out [T, d], y [T*k, d] (the forward's expert outputs; read only when dw != NULL),
+ *   dy [T*k, d] (every row written once, since row_of is a permutation), dy_shared [T, d],
+ *   topk_w and dw [T, k] fp32; dtype MOE_BF16 or MOE_F32; d % 8 == 0; 16-byte aligned.
+ */
+moe_status_t moe_combine_backward(const void* d_out, int32_t dtype, const float* topk_w, const int32_t* row_of,
+                                  const void* y, int64_t T, int64_t d, int32_t k, void* dy, void* dy_shared,
+                                  float* dw, void* stream);
+
+/*
+ * moe_swiglu_backward -- gradient of the SwiGLU product h = silu(g) * u with respect to the
+ * gate and up pre-activations the forward saved ([Blog] Figure 3 paragraph: the experts
+ * are SwiGLU MLPs). With s = 1 / (1 + exp(-g)):
+ *   dgu[r, c]     = dh[r,c] * u * s * (1 + g * (1 - s))    (gate part, c < f)
+ *   dgu[r, f + c] = dh[r,c] * g * s                         (up part)
+ * where g = gu[r, c] and u = gu[r, f + c] (the layout moe_grouped_gemm's SWIGLU aux writes).
+ *   dh [rows, f] (ld_dh), gu [rows, 2f] (ld_gu), dgu [rows, 2f] (ld_dgu); dtype MOE_BF16 or
+ *   MOE_F32; f and every leading dimension multiples of 8; 16-byte aligned. Math in fp32,
+ *   one rounding per output.
+ */
+moe_status_t moe_swiglu_backward(const void* dh, int64_t ld_dh, const void* gu, int64_t ld_gu, int32_t dtype,
+                                 int64_t rows, int64_t f, void* dgu, int64_t ld_dgu, void* stream);
 
 /*
  * moe_group_quant_mxfp8 -- MXFP8 quantisation: E4M3 element codes plus one E8M0 scale byte
@@ -190,6 +234,10 @@ moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, cons
  * saturating at +-448 (bias 7, 3 mantissa bits, subnormal step 2^-9; the sign of zero kept).
  *
  *   in [rows, cols] (MOE_BF16 or MOE_F32, leading dimension ld_in), cols % 32 == 0.
+ *   row_index (device, [rows] int32, or NULL): logical row r is read from in row
+ *     row_index[r] (clamped into [0, in_rows)), e.g. the permutation's src_token so that
+ *     the permuted activations are quantised straight from the token-ordered input;
+ *     in_rows is the number of rows of `in` (ignored when row_index is NULL).
  *   axis 0 (row-wise, for operands contracted along their rows' length):
  *     q [rows, ld_q >= cols] codes, scales [rows, ld_scales >= cols/32] bytes;
  *     group_offsets, G, block_start and workspace are ignored.
@@ -199,15 +247,18 @@ moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, cons
  *     group, the last block of a group possibly partial (its missing rows count as zero);
  *     blocks never straddle groups. Output is TRANSPOSED so the blocked axis is
  *     contiguous: block j of column c has codes q[c, 32j .. 32j+31] (zero codes for the
- *     missing rows of a partial block) and scale scales[c, j]; group g's blocks are
- *     j = block_start[g] .. block_start[g+1]-1 (block_start[g] = sum over g' < g of
- *     ceil(m_g'/32)), so each group starts on a 32-element boundary.
+ *     missing rows of a partial block) and scale scales[c, j]. Group g owns
+ *     nb_g = 4 * ceil(m_g/128) blocks j = block_start[g] .. block_start[g+1]-1
+ *     (block_start[g] = sum over g' < g of nb_g'), so every group starts on a 128-element
+ *     boundary (one MXFP8 GEMM K slice); the blocks past a group's last row are all zero
+ *     (codes 0, scale byte 0) and add nothing to a product.
  *     block_start (device, [G+1]) is written when not NULL, else kept in workspace
  *     (moe_workspace_bytes(MOE_OP_QUANT, 0, 0, 0, 0, G) bytes). Capacities:
- *     ld_q >= 32 * (ceil(rows/32) + G), ld_scales >= ceil(rows/32) + G.
+ *     ld_q >= 32 * nblk, ld_scales >= nblk with nblk = 4 * (ceil(rows/128) + G).
  *   q 16-byte aligned, ld_q % 16 == 0. Deterministic; no floating-point atomics.
  */
 moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                   const int32_t* row_index, int64_t in_rows,
                                    const int32_t* group_offsets, int32_t G, int32_t axis,
                                    uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                    int32_t* block_start, void* workspace, size_t workspace_bytes, void* stream);

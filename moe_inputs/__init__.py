@@ -184,6 +184,9 @@ WORKLOADS = {
     # one-row groups, one hot group
     "small_softmax": Workload("small_softmax", 1000, 256, 384, 16, 4, "bf16", "softmax", ("zipf", 1.0, 1.0), 0, seed=11),
     "small_sigmoid": Workload("small_sigmoid", 777, 320, 192, 24, 6, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 192, seed=12),
+    # the MXFP8 training step at a reduced shape (d, f multiples of 128 as its GEMMs need)
+    "small_mxfp8": Workload("small_mxfp8", 600, 384, 256, 12, 3, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 256,
+                            seed=13, mxfp8=True, backward=True),
 }
 
 

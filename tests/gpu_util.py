@@ -14,6 +14,14 @@ TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 BF16_MAX_REL, BF16_MEAN_REL = 2e-2, 2e-3
 # fp32 storage: the only differences are fp32 accumulation order and fp32 expf/silu
 F32_MAX_REL, F32_MEAN_REL = 1e-4, 1e-5
+# MXFP8 pipelines against the MX-mirroring oracle: an intermediate that lands on the other
+# side of an E4M3 rounding boundary moves one element by up to one E4M3 step (1/16 relative)
+MX_MAX_REL, MX_MEAN_REL = 6e-2, 6e-3
+# A whole MXFP8 step against the fully independent oracle: every bf16 intermediate the GPU
+# rounds one ulp differently can flip the E4M3 code of a block maximum by a whole step (up to
+# 1/8 relative), which moves single outputs by ~2/sqrt(K) of the output rms; the mean stays
+# at the bf16 level. Stage-wise checks (each stage on the GPU's own inputs) use the bf16 gate.
+MX_E2E_MAX_REL, MX_E2E_MEAN_REL = 0.25, 2e-3
 
 
 def rel_err(y, r):
@@ -27,7 +35,8 @@ def rel_err(y, r):
 
 def assert_close(y, r, dtype: str, what: str = ""):
     mx, mean = rel_err(y, r)
-    lim = (BF16_MAX_REL, BF16_MEAN_REL) if dtype == "bf16" else (F32_MAX_REL, F32_MEAN_REL)
+    lim = {"bf16": (BF16_MAX_REL, BF16_MEAN_REL), "mx": (MX_MAX_REL, MX_MEAN_REL),
+           "mx_e2e": (MX_E2E_MAX_REL, MX_E2E_MEAN_REL)}.get(dtype, (F32_MAX_REL, F32_MEAN_REL))
     assert mx <= lim[0] and mean <= lim[1], f"{what}: max rel {mx:.3e} mean rel {mean:.3e} (limits {lim})"
     return mx, mean
 

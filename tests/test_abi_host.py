@@ -96,3 +96,44 @@ def test_host_argument_errors_enqueue_nothing(lib):
     bad.M = 0
     assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_OK
     assert L._lib.moe_grouped_gemm(None, fake, 1 << 20, None) == L.MOE_EINVAL
+
+
+def test_host_argument_errors_backward_and_quant(lib):
+    from dropless_mixture_experts_device_amd import _lib as L
+    fake = ctypes.c_void_p(1 << 20)
+    # ragged-K GEMM: MXFP8 only, no gather, no aux, C groups must not overlap
+    a = L.MoeGemmArgs(G=4, offsets=fake.value, M=128, N=64, K=512, A=fake.value, a_dtype=L.MOE_E4M3, lda=512,
+                      A_rows=128, a_rows=None, B=fake.value, b_dtype=L.MOE_E4M3, ldb=512, b_group_stride=0,
+                      C=fake.value, c_dtype=L.MOE_BF16, ldc=64, epilogue=L.MOE_EPI_NONE, aux=None, ld_aux=0,
+                      a_scale=fake.value, lda_scale=16, b_scale=fake.value, ldb_scale=16, b_scale_group_stride=0,
+                      ragged_k=1, c_group_stride=128 * 64)
+    assert L._lib.moe_grouped_gemm(ctypes.byref(a), None, 0, None) == L.MOE_EWORKSPACE
+    for field, value, want in (("a_dtype", L.MOE_BF16, L.MOE_ENOTSUP), ("epilogue", L.MOE_EPI_SWIGLU, L.MOE_ENOTSUP),
+                               ("a_rows", fake.value, L.MOE_EINVAL), ("c_group_stride", 64 * 64, L.MOE_EINVAL),
+                               ("b_group_stride", 512, L.MOE_EINVAL), ("ragged_k", 2, L.MOE_EINVAL),
+                               ("K", 480, L.MOE_EINVAL), ("lda_scale", 14, L.MOE_EINVAL)):
+        bad = L.MoeGemmArgs.from_buffer_copy(a)
+        setattr(bad, field, value)
+        if field == "a_dtype":
+            bad.b_dtype = value
+        assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, field
+    # combine backward: dw needs y; d % 8; T == 0 is a no-op
+    assert L._lib.moe_combine_backward(fake, L.MOE_BF16, fake, fake, None, 16, 64, 2, fake, None, fake, None) == L.MOE_EINVAL
+    assert L._lib.moe_combine_backward(fake, L.MOE_BF16, fake, fake, fake, 16, 60, 2, fake, None, None, None) == L.MOE_EINVAL
+    assert L._lib.moe_combine_backward(fake, L.MOE_E4M3, fake, fake, fake, 16, 64, 2, fake, None, None, None) == L.MOE_ENOTSUP
+    assert L._lib.moe_combine_backward(None, L.MOE_BF16, None, None, None, 0, 64, 2, None, None, None, None) == L.MOE_OK
+    # SwiGLU backward: f % 8, leading dimensions
+    assert L._lib.moe_swiglu_backward(fake, 64, fake, 128, L.MOE_BF16, 16, 60, fake, 128, None) == L.MOE_EINVAL
+    assert L._lib.moe_swiglu_backward(fake, 64, fake, 96, L.MOE_BF16, 16, 64, fake, 128, None) == L.MOE_EINVAL
+    assert L._lib.moe_swiglu_backward(None, 64, None, 128, L.MOE_BF16, 0, 64, None, 128, None) == L.MOE_OK
+    # quantiser: cols % 32, axis, gather without the input's row count, column-wise capacity
+    q = L._lib.moe_group_quant_mxfp8
+    assert q(fake, L.MOE_BF16, 64, 48, 48, None, 0, None, 0, 0, fake, 48, fake, 2, None, None, 0, None) == L.MOE_EINVAL
+    assert q(fake, L.MOE_BF16, 64, 64, 64, None, 0, None, 0, 2, fake, 64, fake, 2, None, None, 0, None) == L.MOE_EINVAL
+    assert q(fake, L.MOE_BF16, 64, 64, 64, fake, 0, None, 0, 0, fake, 64, fake, 2, None, None, 0, None) == L.MOE_EINVAL
+    cap = L.quant_col_blocks(64, 3)
+    assert cap == 4 * (1 + 3)
+    assert q(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, 1, fake, 32 * cap - 16, fake, cap, fake, None, 0,
+             None) == L.MOE_EINVAL
+    assert q(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, 1, fake, 32 * cap, fake, cap, None, None, 0,
+             None) == L.MOE_EWORKSPACE

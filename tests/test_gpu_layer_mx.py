@@ -1,0 +1,149 @@
+"""The MXFP8 training step (forward + backward of the experts, the permutation and the
+combine) on the GPU vs the MX-mirroring oracle, on the GPU's own routing so the expert path
+is compared on identical groups (routing parity is covered by the route tests). dY is one
+rounding of an exact product and must match bit for bit. Every other stage is checked
+against the oracle's functions applied to the GPU's own inputs of that stage (bf16
+tolerance: one rounding apart), and the whole step against the independent MX oracle with
+the end-to-end MXFP8 gate. A forced routing with an empty group checks that its weight
+gradients come back as zeros."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+from tests.gpu_util import DeviceWorkload, assert_close, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def LY():
+    from dropless_mixture_experts_device_amd import _lib, layer
+    return _lib, layer
+
+
+def _step(L, layer, w, topk=None):
+    dw = DeviceWorkload(w)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.MxWeights(s, "cuda")
+    mw.quantise(dw.w_gu, dw.w_down)
+    b = layer.MxBuffers(s, "cuda")
+    if topk is not None:
+        b.topk_idx.copy_(torch.from_numpy(topk[0]).cuda())
+        b.topk_w.copy_(torch.from_numpy(topk[1]).cuda())
+    layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, routed=topk is not None)
+    d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
+    layer.backward_mx(dw.x, d_out, mw, s, b)
+    torch.cuda.synchronize()
+    return b
+
+
+def _oracle(w, b):
+    idx = b.topk_idx.cpu().numpy()
+    wt = b.topk_w.cpu().numpy().astype(np.float64)
+    gu = lambda e: mi.w_gate_up_np(w, e)
+    dn = lambda e: mi.w_down_np(w, e)
+    fwd = O.layer_forward(mi.x_np(w), mi.w_router_np(w), mi.expert_bias(w), w.k, w.score, gu, dn, w.E,
+                          shared=bool(w.shared_f), rnd=O.round_bf16, topk=(idx, wt), mx=True)
+    d_out = mi.randn_np(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16").astype(np.float64)
+    bwd = O.layer_backward(fwd, d_out, gu, dn, w.E, shared=bool(w.shared_f), rnd=O.round_bf16, mx=True)
+    return fwd, bwd
+
+
+def _stage_refs(w, b, x, d_out):
+    """Each stage of the step recomputed by the oracle's functions from the GPU's own inputs
+    to that stage, so a mismatch points at one kernel."""
+    f64 = lambda t: host(t)
+    off = b.offsets.cpu().numpy().astype(np.int64)
+    src = b.src_token.cpu().numpy()
+    ro = b.row_of.cpu().numpy()
+    wt = b.topk_w.cpu().numpy().astype(np.float64)
+    H, GU, Y, dY, dH, dGU, dXp = (f64(t) for t in (b.H, b.GU, b.Y, b.dY, b.dH, b.dGU, b.dXp))
+    tk, f = w.T * w.k, w.f
+    xq, Hq, dYq, dGUq = O.mx_q_rows(x), O.mx_q_rows(H), O.mx_q_rows(dY), O.mx_q_rows(dGU)
+    ref = {n: np.zeros_like(a) for n, a in (("H", H), ("GU", GU), ("Y", Y), ("dH", dH), ("dX_perm", dXp))}
+    ref["dW_gu"] = {}
+    ref["dW_down"] = {}
+    for g in range(len(off) - 1):
+        lo, hi = off[g], off[g + 1]
+        if hi == lo:
+            continue
+        Wgu, Wd = mi.w_gate_up_np(w, g).astype(np.float64), mi.w_down_np(w, g).astype(np.float64)
+        Gm, Um = O.expert_gate_up(xq[src[lo:hi]], O.mx_q_rows(Wgu))
+        ref["GU"][lo:hi] = O.round_bf16(np.concatenate([Gm, Um], 1))
+        ref["H"][lo:hi] = O.round_bf16(O.silu(Gm) * Um)
+        ref["Y"][lo:hi] = O.round_bf16(Hq[lo:hi] @ O.mx_q_rows(Wd).T)
+        ref["dH"][lo:hi] = O.round_bf16(dYq[lo:hi] @ O.mx_q_rows(Wd.T).T)
+        ref["dX_perm"][lo:hi] = O.round_bf16(dGUq[lo:hi] @ O.mx_q_rows(Wgu.T).T)
+        one = np.array([0, hi - lo])
+        col = lambda a: O.mx_quantize_colwise_grouped(a, one)[2]
+        ref["dW_down"][g] = O.round_bf16(col(dY[lo:hi]).T @ col(H[lo:hi]))
+        ref["dW_gu"][g] = O.round_bf16(col(dGU[lo:hi]).T @ col(x[src[lo:hi]]))
+    Gs, Us = GU[:, :f], GU[:, f:]
+    ref["dGU"] = np.concatenate([O.round_bf16(dH * Us * O.silu_grad(Gs)), O.round_bf16(dH * O.silu(Gs))], 1)
+    shared = len(off) - 1 > w.E
+    ref["out"] = O.combine(Y[:tk], wt, ro, Y[tk:] if shared else None, O.round_bf16)
+    ref["dY"], ref["dw"] = O.combine_backward(d_out, Y[:tk], wt, ro, O.round_bf16)
+    ref["dx"] = O.permute_backward(dXp[:tk], ro, dXp[tk:] if shared else None, O.round_bf16)
+    return ref
+
+
+def _compare(w, b, fwd, bwd):
+    tk = w.T * w.k
+    np.testing.assert_array_equal(b.offsets.cpu().numpy(), fwd["offsets"])
+    np.testing.assert_array_equal(b.row_of.cpu().numpy(), fwd["row_of"])
+    np.testing.assert_array_equal(b.src_token.cpu().numpy(), fwd["src_token"])
+    counts = np.diff(fwd["offsets"])
+    live = np.flatnonzero(counts)
+    x = mi.x_np(w).astype(np.float64)
+    d_out = mi.randn_np(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16").astype(np.float64)
+    # stage by stage, each kernel on the GPU's own inputs
+    st = _stage_refs(w, b, x, d_out)
+    got = {"H": host(b.H), "GU": host(b.GU), "Y": host(b.Y), "out": host(b.out), "dH": host(b.dH),
+           "dGU": host(b.dGU), "dX_perm": host(b.dXp), "dx": host(b.dx)}
+    dWgu, dWd = host(b.dW_gu), host(b.dW_down)
+    np.testing.assert_array_equal(host(b.dY[:tk]), st["dY"])            # w * d_out, one rounding
+    assert_close(host(b.dw), st["dw"], "f32", "dw (stage)")
+    worst = 0.0
+    for n, a in got.items():
+        worst = max(worst, assert_close(a, st[n], "bf16", f"{n} (stage)")[0])
+    for g in range(len(counts)):
+        if counts[g] == 0:
+            assert np.all(dWgu[g] == 0) and np.all(dWd[g] == 0), f"empty group {g}: weight gradients must be zero"
+            continue
+        worst = max(worst, assert_close(dWgu[g], st["dW_gu"][g], "bf16", f"dW_gu[{g}] (stage)")[0])
+        worst = max(worst, assert_close(dWd[g], st["dW_down"][g], "bf16", f"dW_down[{g}] (stage)")[0])
+    # end to end against the independent MX oracle
+    e2e = {"H": (got["H"], fwd["H"]), "Y": (got["Y"], fwd["Y"]), "out": (got["out"], fwd["out"]),
+           "dw": (host(b.dw), bwd["dw"]), "dX_perm": (got["dX_perm"], bwd["dX_perm"]), "dx": (got["dx"], bwd["dx"]),
+           "dW_gu": (dWgu[live], np.stack([bwd["dW_gu"][g] for g in live])),
+           "dW_down": (dWd[live], np.stack([bwd["dW_down"][g] for g in live]))}
+    msg = []
+    for n, (a, r) in e2e.items():
+        mx, mean = assert_close(a, r, "mx_e2e", f"{n} (end to end)")
+        msg.append(f"{n} {mx:.1e}/{mean:.1e}")
+    print(f"stage-wise worst max rel {worst:.2e}; end to end " + " ".join(msg))
+
+
+def test_mx_step_small(LY):
+    L, layer = LY
+    w = mi.WORKLOADS["small_mxfp8"]
+    b = _step(L, layer, w)
+    fwd, bwd = _oracle(w, b)
+    _compare(w, b, fwd, bwd)
+
+
+def test_mx_step_forced_routing_with_empty_group(LY):
+    """Experts 0..3 of 12 take every token (expert 5 and others stay empty)."""
+    L, layer = LY
+    w = mi.WORKLOADS["small_mxfp8"]
+    g = np.random.Generator(np.random.PCG64(8))
+    idx = np.stack([g.permutation(4)[:w.k] for _ in range(w.T)]).astype(np.int32)
+    wt = g.random((w.T, w.k)).astype(np.float32)
+    wt /= wt.sum(1, keepdims=True)
+    b = _step(L, layer, w, topk=(idx, wt))
+    fwd, bwd = _oracle(w, b)
+    assert np.diff(fwd["offsets"])[5] == 0
+    _compare(w, b, fwd, bwd)

@@ -89,3 +89,56 @@ def test_mx_gemm_quantised_random_within_tolerance(L, epi):
         C = _run(L, A, As, B, Bs, off, M, N, L.MOE_EPI_SWIGLU, torch.bfloat16)
         want = O.grouped_swiglu(Aq, Wq, off, rnd=O.round_bf16)
     assert_close(host(C), want, "bf16", f"mx {epi}")
+
+
+def test_mx_gemm_ragged_k_on_grid_bit_exact(L):
+    """Weight-gradient form: C[g] = A[:, K_g] @ B[:, K_g]^T over each group's own block range
+    (multiples of 4 blocks, as the column-wise quantiser lays them out), with an empty range
+    whose C[g] must come back as zeros, and M, N that leave partial tiles."""
+    blocks = np.array([0, 4, 4, 12, 16, 28], np.int32)          # group K ranges in 32-element blocks
+    G, M, N, K = len(blocks) - 1, 192, 320, 32 * int(blocks[-1])
+    A, As = _grid_operand((M, K), 11)
+    B, Bs = _grid_operand((N, K), 12)
+    C = torch.full((G, M, N), float("nan"), dtype=torch.float32, device="cuda")
+    L.moe_grouped_gemm(_u8(A), _u8(B), C, dev_i32(blocks), L.MOE_EPI_NONE, workspace=_ws(L, G),
+                       a_scale=_u8(As), b_scale=_u8(Bs), ragged_k=True)
+    torch.cuda.synchronize()
+    Ad, Bd = _dequant(A, As), _dequant(B, Bs)
+    got = host(C)
+    for g in range(G):
+        lo, hi = 32 * int(blocks[g]), 32 * int(blocks[g + 1])
+        np.testing.assert_array_equal(got[g], Ad[:, lo:hi] @ Bd[:, lo:hi].T, err_msg=f"group {g}")
+
+
+def test_mx_wgrad_quantised_within_tolerance(L):
+    """The column-wise quantiser feeding the ragged-K GEMM reproduces the oracle's MXFP8
+    weight gradient dW_g = Qcol(dY_g)^T Qcol(H_g) per group, bf16 output."""
+    sizes = [37, 0, 1, 160, 128, 300]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows, G, d, f = int(off[-1]), len(sizes), 256, 384
+    dY = mi.randn_np(9, mi.D_OUT, 0, rows, d, 1.0, "bf16").astype(np.float64)
+    H = mi.randn_np(9, mi.X, 1, rows, f, 0.5, "bf16").astype(np.float64)
+    nblk = L.quant_col_blocks(rows, G)
+    qa = torch.zeros((d, 32 * nblk), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((d, nblk), dtype=torch.uint8, device="cuda")
+    qb = torch.zeros((f, 32 * nblk), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((f, nblk), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
+    offs = dev_i32(off)
+    L.moe_group_quant_mxfp8(torch.from_numpy(dY).to(torch.bfloat16).cuda(), qa, sa, axis=1, group_offsets=offs,
+                            block_start=bs)
+    L.moe_group_quant_mxfp8(torch.from_numpy(H).to(torch.bfloat16).cuda(), qb, sb, axis=1, group_offsets=offs,
+                            block_start=bs)
+    C = torch.full((G, d, f), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_grouped_gemm(qa, qb, C, bs, L.MOE_EPI_NONE, workspace=_ws(L, G), a_scale=sa, b_scale=sb, ragged_k=True)
+    torch.cuda.synchronize()
+    got = host(C)
+    _, _, dYq = O.mx_quantize_colwise_grouped(dY, off)
+    _, _, Hq = O.mx_quantize_colwise_grouped(H, off)
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        want = O.round_bf16(dYq[lo:hi].T @ Hq[lo:hi])
+        if hi == lo:
+            assert np.all(got[g] == 0), "an empty group's weight gradient is written as zeros"
+        else:
+            assert_close(got[g], want, "bf16", f"wgrad group {g}")

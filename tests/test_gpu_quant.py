@@ -1,7 +1,9 @@
 """moe_group_quant_mxfp8 on the GPU vs the oracle: E4M3 codes and E8M0 scale bytes must match
 bit for bit (the quantiser is a deterministic function), row-wise and group-aware
 column-wise, including saturating blocks, all-zero and signed-zero blocks, partial, empty
-and one-row groups, and sampled rows/columns at the DeepSeek-V3 shapes."""
+and one-row groups, rows read through a gather index, and sampled rows/columns at the
+DeepSeek-V3 shapes. In the column-wise layout every group starts on a multiple of four
+blocks; the blocks between a group's last row and the next group are checked to be zero."""
 import numpy as np
 import pytest
 import torch
@@ -54,22 +56,25 @@ def test_quant_rowwise_bit_exact(L, rows, cols, dtype):
     np.testing.assert_array_equal(q, wq)
 
 
-def _colwise(L, a, offsets, dtype="bf16"):
-    rows, cols = a.shape
+def _colwise(L, a, offsets, dtype="bf16", row_index=None):
+    """Column-wise quantisation of a (or of a[row_index] read through the gather)."""
     G = len(offsets) - 1
-    nblk = -(-rows // 32) + G
+    rows = a.shape[0] if row_index is None else len(row_index)
+    cols = a.shape[1]
+    nblk = L.quant_col_blocks(rows, G)
     x = dev(a, dtype)
     q = torch.full((cols, 32 * nblk), 0xAB, dtype=torch.uint8, device="cuda")
     s = torch.full((cols, nblk), 0xAB, dtype=torch.uint8, device="cuda")
     bs = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
-    L.moe_group_quant_mxfp8(x, q, s, axis=1, group_offsets=dev_i32(offsets), block_start=bs)
+    L.moe_group_quant_mxfp8(x, q, s, axis=1, group_offsets=dev_i32(offsets), block_start=bs,
+                            row_index=None if row_index is None else dev_i32(row_index))
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy(), bs.cpu().numpy()
 
 
 def _check_colwise(a, offsets, q, s, bs):
     off = np.asarray(offsets, np.int64)
-    nb = -(-np.diff(off) // 32)
+    nb = 4 * (-(-np.diff(off) // 128))
     np.testing.assert_array_equal(bs, np.concatenate([[0], np.cumsum(nb)]))
     codes, scales, _ = O.mx_quantize_colwise_grouped(a, off)
     for g in range(len(off) - 1):
@@ -77,9 +82,12 @@ def _check_colwise(a, offsets, q, s, bs):
         m = hi - lo
         for i in range(int(nb[g])):
             j = int(bs[g]) + i
+            blk = q[:, 32 * j:32 * j + 32]
+            if 32 * i >= m:      # alignment block past the group's rows
+                assert np.all(s[:, j] == 0) and np.all(blk == 0), f"group {g} block {i} must be all zero"
+                continue
             n = min(32, m - 32 * i)
             np.testing.assert_array_equal(s[:, j], scales[g][i], err_msg=f"group {g} block {i}")
-            blk = q[:, 32 * j:32 * j + 32]
             np.testing.assert_array_equal(blk[:, :n], codes[lo + 32 * i:lo + 32 * i + n].T)
             assert np.all(blk[:, n:] == 0), "padding rows of a partial block must be zero codes"
 
@@ -90,6 +98,23 @@ def test_quant_colwise_grouped_bit_exact(L, sizes, cols):
     a = _nasty(int(off[-1]), cols, cols + len(sizes))
     q, s, bs = _colwise(L, a, off)
     _check_colwise(a, off, q, s, bs)
+
+
+def test_quant_gather_rows_bit_exact(L):
+    """row_index reads logical row r from x[row_index[r]] in both layouts (repeats included)."""
+    a = _nasty(90, 96, 4)
+    ri = np.random.Generator(np.random.PCG64(6)).integers(0, 90, 200).astype(np.int32)
+    x = dev(a, "bf16")
+    q = torch.full((200, 96), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((200, 3), 0xAB, dtype=torch.uint8, device="cuda")
+    L.moe_group_quant_mxfp8(x, q, s, axis=0, row_index=dev_i32(ri))
+    torch.cuda.synchronize()
+    wq, ws, _ = O.mx_quantize_rowwise(a[ri])
+    np.testing.assert_array_equal(s.cpu().numpy(), ws)
+    np.testing.assert_array_equal(q.cpu().numpy(), wq)
+    off = np.array([0, 70, 70, 71, 200], np.int32)
+    qc, sc, bs = _colwise(L, a, off, row_index=ri)
+    _check_colwise(a[ri], off, qc, sc, bs)
 
 
 def test_quant_dsv3_shapes_sampled(L):
@@ -104,7 +129,7 @@ def test_quant_dsv3_shapes_sampled(L):
     s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
     L.moe_group_quant_mxfp8(x, q, s, axis=0)
     G = len(off) - 1
-    nblk = -(-rows // 32) + G
+    nblk = L.quant_col_blocks(rows, G)
     qc = torch.empty((cols, 32 * nblk), dtype=torch.uint8, device="cuda")
     sc = torch.empty((cols, nblk), dtype=torch.uint8, device="cuda")
     bs = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
