@@ -7,6 +7,11 @@ Prints ONE JSON line. `value` is useful GEMM FLOPs (6*T*k*d*f + 6*T*d*f_shared, 
 counted, router projection excluded) divided by the whole step time, i.e. layer TFLOPS;
 `gemm_tflops` uses the two grouped-GEMM launches' own event time instead, `tokens_per_s` is
 T / step time. Inputs and weights are resident in HBM before timing starts.
+
+--workload dsv3_mxfp8 times the MXFP8 training step instead: the per-step quantisation of
+the weights (both axis copies), the forward and the backward of the experts, permutation and
+combine (18*(T*k + T)*d*f useful FLOPs); `value` covers the whole step, `ms_without_weight_quant`
+and `value_without_weight_quant` leave the weight quantisation out.
 """
 from __future__ import annotations
 
@@ -23,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def parse():
@@ -149,6 +155,163 @@ def cpu_baseline(w, w_gu_dev, w_down_dev):
             "sample": f"fp64 numpy oracle on {what}; value = useful FLOPs of the finished groups / oracle time"}
 
 
+def mx_gemm_work(w, rows, nonempty):
+    """Algorithmic HBM bytes and FLOPs of each MXFP8 GEMM of the step: E4M3 operands with one
+    scale byte per 32 elements read once (weights of non-empty groups only), bf16 outputs
+    written once (GEMM 1 also writes the saved gate/up pre-activations)."""
+    d, f, G = w.d, w.f, w.E + (1 if w.shared_f else 0)
+    q = 33.0 / 32.0
+    return {
+        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + rows * f * 2 + rows * 2 * f * 2 + rows * 4,
+                         2.0 * rows * d * 2 * f),
+        "gemm2": (nonempty * d * f * q + rows * f * q + rows * d * 2, 2.0 * rows * f * d),
+        "dgrad2": (nonempty * f * d * q + rows * d * q + rows * f * 2, 2.0 * rows * d * f),
+        "wgrad2": ((d + f) * rows * q + G * d * f * 2, 2.0 * rows * d * f),
+        "dgrad1": (nonempty * d * 2 * f * q + rows * 2 * f * q + rows * d * 2, 2.0 * rows * 2 * f * d),
+        "wgrad1": ((2 * f + d) * rows * q + G * 2 * f * d * 2, 2.0 * rows * 2 * f * d),
+    }
+
+
+def cpu_baseline_mx(w, w_gu_dev, w_down_dev):
+    """The oracle's MXFP8 step (fp64 numpy on dequantised MX operands, as it stands): routing
+    and the permutation of all tokens, then each group's MX forward and backward in the same
+    spread order as the bf16 baseline until about CPU_BUDGET_S seconds of oracle time."""
+    import moe_inputs as mi
+    from oracle import moe_oracle as O
+    try:
+        import threadpoolctl
+        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    x = mi.x_np(w)
+    spent = 0.0
+    t0 = time.perf_counter()
+    idx, wt, _ = O.route(x, mi.w_router_np(w), mi.expert_bias(w), w.k, w.score)
+    off, row_of, src = O.permutation(idx, w.E, w.T if w.shared_f else 0)
+    spent += time.perf_counter() - t0
+    groups = ([w.E] if w.shared_f else []) + [e for r in range(16) for e in range(int(f"{r:04b}"[::-1], 2), w.E, 16)]
+    flops, done = 0.0, 0
+    for g in groups:
+        if spent >= CPU_BUDGET_S:
+            break
+        lo, hi = int(off[g]), int(off[g + 1])
+        done += 1
+        if hi == lo:
+            continue
+        gu = w_gu_dev[g].float().cpu().numpy()
+        dn = w_down_dev[g].float().cpu().numpy()
+        dY = mi.randn_np(w.seed, mi.D_OUT, 0, src[lo:hi], w.d, 1.0, "bf16")
+        t0 = time.perf_counter()
+        O.expert_backward(x[src[lo:hi]], gu, dn, dY, O.round_bf16, mx=True)   # recomputes the forward
+        spent += time.perf_counter() - t0
+        flops += 18.0 * (hi - lo) * w.d * (gu.shape[0] // 2)
+    return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "seconds": round(spent, 2),
+            "sample": f"fp64 numpy MX oracle: routing and permutation of all {w.T} tokens, then the MXFP8 forward "
+                      f"and backward of {done} of {len(groups)} expert groups (shared first, then ids "
+                      f"0,16,32,...,8,24,...) on their real rows, stopped at {CPU_BUDGET_S:.0f} s; value = useful "
+                      f"FLOPs (18 m d f per group) of the finished groups / oracle time"}
+
+
+def main_mx(args, w):
+    import torch
+    import moe_inputs as mi
+    from dropless_mixture_experts_device_amd import _lib as L
+    from dropless_mixture_experts_device_amd import layer
+
+    torch.cuda.init()
+    dev = "cuda"
+    x = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.X, 0, w.T, w.d, w.sigma_x, w.dtype, dev, out=x)
+    wr = torch.empty((w.E, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.W_ROUTER, 0, w.E, w.d, w.sigma_w, w.dtype, dev, out=wr)
+    b0 = mi.expert_bias(w)
+    bias = None if b0 is None else torch.from_numpy(b0).to(dev)
+    n = w.E + (1 if w.shared_f else 0)
+    w_gu = torch.empty((n, 2 * w.f, w.d), dtype=torch.bfloat16, device=dev)
+    w_down = torch.empty((n, w.d, w.f), dtype=torch.bfloat16, device=dev)
+    mi.fill_weights_torch(w, w_gu, w_down, dev)
+    d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", dev)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.MxWeights(s, dev)
+    b = layer.MxBuffers(s, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(rec=None):
+        mark = None
+        if rec is not None:
+            def mark(name):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                rec.append((name, e))
+            mark("start")
+        mw.quantise(w_gu, w_down)
+        if mark:
+            mark("weight_quant")
+        layer.forward_mx(x, wr, bias, mw, s, b, mark=mark)
+        layer.backward_mx(x, d_out, mw, s, b, mark=mark)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = [[] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(recs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = [n for n, _ in recs[0][1:]]
+    per = np.array([[r[j][1].elapsed_time(r[j + 1][1]) for j in range(len(r) - 1)] for r in recs])
+    pm = dict(zip(names, per.mean(0)))
+    counts = np.diff(b.offsets.cpu().numpy())[:w.E]
+    rows = s.rows
+    flops = 18.0 * rows * w.d * w.f
+    nonempty = int(np.count_nonzero(counts)) + (1 if w.shared_f else 0)
+    work = mx_gemm_work(w, rows, nonempty)
+    dom = max(work, key=lambda k: pm[k])
+    by, fl = work[dom]
+    t = pm[dom] * 1e-3
+    t_hbm, t_mfma = by / (HBM_PEAK_GBS * 1e9), fl / (FP8_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(by / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fl / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": f"moe_grouped_gemm MXFP8 {dom}", "algorithmic_bytes": int(by),
+                 "algorithmic_flops": fl, "ms": round(pm[dom], 4)})
+    step_ms = float(per.sum(1).mean())
+    no_wq = step_ms - pm["weight_quant"]
+    gemm_ms = sum(pm[k] for k in work)
+    res = {
+        "metric": "MoE layer fwd+bwd TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped MXFP8 training step",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3 (MXFP8, E8M0/32)",
+        "data": "synthetic (seeded hash-table normal inputs and output gradient, Zipf expert-bias skew; "
+                "random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "score": w.score,
+                   "shared_f": w.shared_f, "groups_nonempty": int(np.count_nonzero(counts)),
+                   "group_max": int(counts.max()), "group_min": int(counts.min()),
+                   "groups_empty": int((counts == 0).sum())},
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "ms_without_weight_quant": round(no_wq, 4),
+        "value_without_weight_quant": round(flops / (no_wq * 1e-3) / 1e12, 2),
+        "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in pm.items()},
+        "gemm_tflops_by_stage": {k: round(work[k][1] / (pm[k] * 1e-3) / 1e12, 1) for k in work},
+        "gemm_gbs_by_stage": {k: round(work[k][0] / (pm[k] * 1e-3) / 1e9, 1) for k in work},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mx(w, w_gu, w_down)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -161,7 +324,9 @@ def main():
     from dropless_mixture_experts_device_amd import layer
 
     w = mi.WORKLOADS[args.workload]
-    assert w.dtype == "bf16" and not w.mxfp8, "bench times the bf16 forward workloads"
+    if w.mxfp8:
+        return main_mx(args, w)
+    assert w.dtype == "bf16", "bench times the bf16 layer workloads"
     torch.cuda.init()
     dev = "cuda"
     x = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)

@@ -192,53 +192,78 @@ class MxBuffers(LayerBuffers):
         self.ws_gemm3 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
 
 
-def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False):
+def _nomark(name):
+    pass
+
+
+def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False, mark=None):
     """MXFP8 forward: route and permute as in bf16, x quantised row-wise once per token (the
     GEMM gathers codes and scale rows through src_token), GEMM 1 + SwiGLU saving G and U,
     H quantised row-wise, GEMM 2, combine. mw must hold this step's quantised weights.
-    routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment."""
+    routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment.
+    mark(name), if given, is called after each stage (e.g. to record a timing event)."""
+    mark = mark or _nomark
     if not routed:
         route(x, w_router, bias, s, b)
+    mark("route")
     permute(x, s, b)
+    mark("permute")
     L.moe_group_quant_mxfp8(x, b.q_x, b.s_x, axis=0)
+    mark("quant_x")
     L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, aux=b.GU,
                        workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu)
+    mark("gemm1_swiglu")
     L.moe_group_quant_mxfp8(b.H, b.q_h, b.s_h, axis=0)
+    mark("quant_h")
     L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
                        b_scale=mw.s_dn)
+    mark("gemm2")
     combine(s, b)
+    mark("combine")
     return b.out
 
 
-def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers):
+def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None):
     """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down.
 
     combine^T -> dY; dgrad 2 (dH = dY W_down, contracted over d) and wgrad 2 (dW_down[g] =
     dY_g^T H_g over the group's tokens); SwiGLU backward from the saved G, U; dgrad 1
     (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx.
     The router's own backward is not part of this step."""
+    mark = mark or _nomark
     tk = s.T * s.k
     L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
                            dy_shared=b.dY[tk:] if s.shared else None, dw=b.dw)
+    mark("combine_bwd")
     # dgrad 2 and wgrad 2
     L.moe_group_quant_mxfp8(b.dY, b.q_dy, b.s_dy, axis=0)
+    mark("quant_dy")
     q_dnT, s_dnT = mw.dn_T()
     L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
                        b_scale=s_dnT)
+    mark("dgrad2")
     L.moe_group_quant_mxfp8(b.dY, b.qc_dy, b.sc_dy, axis=1, group_offsets=b.offsets, block_start=b.bs)
     L.moe_group_quant_mxfp8(b.H, b.qc_h, b.sc_h, axis=1, group_offsets=b.offsets, block_start=b.bs)
+    mark("quant_cols_dy_h")
     L.moe_grouped_gemm(b.qc_dy, b.qc_h, b.dW_down, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dy, b_scale=b.sc_h, ragged_k=True)
+    mark("wgrad2")
     # SwiGLU backward, dgrad 1 and wgrad 1
     L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
+    mark("swiglu_bwd")
     L.moe_group_quant_mxfp8(b.dGU, b.q_dgu, b.s_dgu, axis=0)
+    mark("quant_dgu")
     q_guT, s_guT = mw.gu_T()
     L.moe_grouped_gemm(b.q_dgu, q_guT, b.dXp, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_dgu,
                        b_scale=s_guT)
+    mark("dgrad1")
     L.moe_group_quant_mxfp8(b.dGU, b.qc_dgu, b.sc_dgu, axis=1, group_offsets=b.offsets, block_start=b.bs)
     L.moe_group_quant_mxfp8(x, b.qc_x, b.sc_x, axis=1, group_offsets=b.offsets, block_start=b.bs,
                             row_index=b.src_token)
+    mark("quant_cols_dgu_x")
     L.moe_grouped_gemm(b.qc_dgu, b.qc_x, b.dW_gu, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dgu, b_scale=b.sc_x, ragged_k=True)
+    mark("wgrad1")
     # permute^T: each token's rows summed back (plus the shared expert's row)
     L.moe_combine(b.dXp[:tk], None, b.row_of, b.dXp[tk:] if s.shared else None, b.dx)
+    mark("unpermute")

@@ -147,3 +147,62 @@ def test_mx_step_forced_routing_with_empty_group(LY):
     fwd, bwd = _oracle(w, b)
     assert np.diff(fwd["offsets"])[5] == 0
     _compare(w, b, fwd, bwd)
+
+
+def test_mx_step_dsv3_sampled(LY):
+    """The full DeepSeek-V3-shaped MXFP8 step (T=8192, d=7168, f=2048, 256 experts + shared,
+    k=8) in the configuration the benchmark times, checked stage by stage on sampled rows of
+    a large, a small and the shared group, whole weight gradients of the smallest group and
+    sampled gradient rows of the largest, and sampled tokens of out, dw and dx."""
+    L, layer = LY
+    w = mi.WORKLOADS["dsv3_mxfp8"]
+    b = _step(L, layer, w)
+    off = b.offsets.cpu().numpy().astype(np.int64)
+    src = b.src_token.cpu().numpy()
+    counts = np.diff(off)
+    tk, f, d = w.T * w.k, w.f, w.d
+    rng = np.random.Generator(np.random.PCG64(17))
+    big, small = int(np.argmax(counts[:w.E])), int(np.argmin(counts[:w.E]))
+    groups = [big, small, w.E]
+    rows = {g: np.unique(np.concatenate([[off[g], off[g + 1] - 1], rng.integers(off[g], off[g + 1], 4)]))
+            for g in groups}
+    pick = lambda t, r: host(t[torch.from_numpy(np.asarray(r)).cuda()])
+    for g in groups:
+        r = rows[g]
+        Wgu, Wd = mi.w_gate_up_np(w, g).astype(np.float64), mi.w_down_np(w, g).astype(np.float64)
+        xr = mi.randn_np(w.seed, mi.X, 0, src[r], d, w.sigma_x, "bf16").astype(np.float64)
+        Gm, Um = O.expert_gate_up(O.mx_q_rows(xr), O.mx_q_rows(Wgu))
+        assert_close(pick(b.GU, r), O.round_bf16(np.concatenate([Gm, Um], 1)), "bf16", f"GU group {g}")
+        assert_close(pick(b.H, r), O.round_bf16(O.silu(Gm) * Um), "bf16", f"H group {g}")
+        assert_close(pick(b.Y, r), O.round_bf16(O.mx_q_rows(pick(b.H, r)) @ O.mx_q_rows(Wd).T), "bf16",
+                     f"Y group {g}")
+        assert_close(pick(b.dH, r), O.round_bf16(O.mx_q_rows(pick(b.dY, r)) @ O.mx_q_rows(Wd.T).T), "bf16",
+                     f"dH group {g}")
+        assert_close(pick(b.dXp, r), O.round_bf16(O.mx_q_rows(pick(b.dGU, r)) @ O.mx_q_rows(Wgu.T).T), "bf16",
+                     f"dX_perm group {g}")
+    # weight gradients: all of the smallest group, sampled output rows of the largest
+    for g, sel_d, sel_f in ((small, np.arange(d), np.arange(2 * f)),
+                            (big, rng.integers(0, d, 16), rng.integers(0, 2 * f, 16))):
+        lo, hi = off[g], off[g + 1]
+        one = np.array([0, hi - lo])
+        col = lambda a: O.mx_quantize_colwise_grouped(a, one)[2]
+        dY_g, H_g, dGU_g = host(b.dY[lo:hi]), host(b.H[lo:hi]), host(b.dGU[lo:hi])
+        x_g = mi.randn_np(w.seed, mi.X, 0, src[lo:hi], d, w.sigma_x, "bf16").astype(np.float64)
+        want_dn = O.round_bf16(col(dY_g[:, sel_d]).T @ col(H_g))
+        want_gu = O.round_bf16(col(dGU_g[:, sel_f]).T @ col(x_g))
+        assert_close(host(b.dW_down[g][torch.from_numpy(sel_d).cuda()]), want_dn, "bf16", f"dW_down[{g}]")
+        assert_close(host(b.dW_gu[g][torch.from_numpy(sel_f).cuda()]), want_gu, "bf16", f"dW_gu[{g}]")
+    # per-token steps: combine, its transpose and the permutation's transpose on sampled tokens
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.integers(0, w.T, 30)]))
+    ro = b.row_of.cpu().numpy()[toks]
+    wt = b.topk_w.cpu().numpy()[toks].astype(np.float64)
+    need = ro.reshape(-1)
+    local = np.arange(need.size).reshape(len(toks), w.k)
+    Y_r, dXp_r = pick(b.Y, need), pick(b.dXp, need)
+    d_out = mi.randn_np(w.seed, mi.D_OUT, 0, toks, d, 1.0, "bf16").astype(np.float64)
+    assert_close(pick(b.out, toks), O.combine(Y_r, wt, local, pick(b.Y, tk + toks), O.round_bf16), "bf16", "out")
+    want_dy, want_dw = O.combine_backward(d_out, Y_r, wt, local, O.round_bf16)
+    np.testing.assert_array_equal(pick(b.dY, need), want_dy[local.reshape(-1)])
+    assert_close(pick(b.dw, toks), want_dw, "f32", "dw")
+    assert_close(pick(b.dx, toks), O.permute_backward(dXp_r, local, pick(b.dXp, tk + toks), O.round_bf16), "bf16",
+                 "dx")
