@@ -24,6 +24,7 @@
 //    lane-to-block layout was measured; see the Mfma traits). Accumulation is fp32 in both.
 //  * The epilogue (optional SwiGLU) goes through LDS so that C is written in 16-byte chunks.
 #include <algorithm>
+#include <utility>
 
 #include "moe_internal.h"
 
@@ -37,13 +38,27 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 256;          // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
 constexpr int kRowBytes = 128;    // one LDS row per stage: 64 bf16 or 128 fp8 of K
 constexpr int kChunks = kRowBytes / 16;
-constexpr int kStages = 3;
-constexpr int kMaxBM = 128;
-constexpr int kStageData = (kMaxBM + kBN) * kRowBytes;   // 48 KiB of operands
-constexpr int kScaleOffA = kStageData;                   // MXFP8: one dword per A row ...
-constexpr int kScaleOffB = kStageData + kMaxBM * 4;      // ... and per B row
-constexpr int kStageBytes = kStageData + (kMaxBM + kBN) * 4;
-constexpr int kPipeBytes = kStages * kStageBytes;        // 148.5 KiB
+#ifndef MOE_GEMM_TILE256
+#define MOE_GEMM_TILE256 0        // 256-row tiles for bf16 groups of >= 256 rows with a bf16 output (measured
+                                  // slower on the DeepSeek-V3 and Mixtral shapes: longer tiles, worse tail)
+#endif
+
+// One LDS pipeline stage of a BM-row tile: BM A rows then kBN B rows of kRowBytes each, then
+// (MXFP8) one scale dword per A row and per B row. A scale rows are loaded 64 per wave
+// instruction, so their slot is rounded up to a multiple of 64 rows (a 16-row tile's scale
+// load still writes 64 dwords and must not reach the B scales). Tiles up to 128 rows keep a
+// 3-stage ring; 256-row tiles (64 KiB of operands per stage) fit two.
+template <int BM>
+struct Stage {
+    static constexpr int kScaleRowsA = (BM + 63) / 64 * 64;
+    static constexpr int kData = (BM + kBN) * kRowBytes;
+    static constexpr int kScaleA = kData;
+    static constexpr int kScaleB = kData + kScaleRowsA * 4;
+    static constexpr int kBytes = kData + (kScaleRowsA + kBN) * 4;
+    static constexpr int kCount = BM == 256 ? 2 : 3;
+};
+constexpr int kPipeBytes = 3 * Stage<128>::kBytes > 2 * Stage<256>::kBytes ? 3 * Stage<128>::kBytes
+                                                                             : 2 * Stage<256>::kBytes;   // 148.5 KiB
 constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
@@ -55,6 +70,45 @@ constexpr int kSuper = 4;         // column tiles per supertile
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ int bm_of_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
+
+// Row tiles of a group of m rows: groups of up to 128 rows get one tile of 16/32/64/128 rows;
+// larger groups get full 256-row tiles (when allowed), then full 128-row tiles, then one tile
+// of 16/32/64/128 rows for what is left, so only the last tile carries padding rows.
+struct RowTiles {
+    int n256, n128, last;   // last: height of the final partial tile (0 = none)
+    __device__ int count() const { return n256 + n128 + (last > 0 ? 1 : 0); }
+};
+
+__device__ __forceinline__ RowTiles row_tiles(int m, bool allow256) {
+    RowTiles t{0, 0, 0};
+    if (m <= 128) {
+        t.last = m > 0 ? bm_of_rows(m) : 0;
+        return t;
+    }
+    int rest = m;
+    if (allow256 && m >= 256) {
+        t.n256 = m / 256;
+        rest -= 256 * t.n256;
+    }
+    t.n128 = rest / 128;
+    rest -= 128 * t.n128;
+    t.last = rest > 0 ? bm_of_rows(rest) : 0;
+    return t;
+}
+
+// row tile mt of the decomposition -> first row inside the group and tile height
+__device__ __forceinline__ void row_tile(const RowTiles& t, int mt, int& r_off, int& bm) {
+    if (mt < t.n256) {
+        r_off = 256 * mt;
+        bm = 256;
+    } else if (mt < t.n256 + t.n128) {
+        r_off = 256 * t.n256 + 128 * (mt - t.n256);
+        bm = 128;
+    } else {
+        r_off = 256 * t.n256 + 128 * t.n128;
+        bm = t.last;
+    }
+}
 
 // Rows [begin, end) of group g, clamped into [0, M] so that inconsistent offsets can never
 // send a load or store outside the buffers.
@@ -88,15 +142,16 @@ struct GemmParams {
     int64_t ldb_scale;
     int64_t b_scale_stride;
     const int32_t* tile_start;   // [G+1] in workspace (ragged rows)
+    int allow256;                // ragged rows: 256-row tiles allowed (not for fp32 C)
     int64_t c_stride;            // ragged K: elements between groups' C
     int MT;                      // ragged K: row tiles per group
 };
 
 // ---------------------------------------------------------------------------------------
-// schedule: tile_start[g] = sum over groups < g of ceil(m_g / BM_g) * NT
+// schedule: tile_start[g] = sum over groups < g of (row tiles of g) * NT
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
-                                                             int NT, int32_t* __restrict__ tile_start) {
+                                                             int NT, int allow256, int32_t* __restrict__ tile_start) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -109,7 +164,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
             int b, e;
             group_rows(offsets, g, M, b, e);
             const int m = e - b;
-            tiles = m > 0 ? cdiv(m, bm_of_rows(m)) * NT : 0;
+            tiles = row_tiles(m, allow256 != 0).count() * NT;
         }
         int incl = tiles;
 #pragma unroll
@@ -135,6 +190,12 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
 // MS x MS output tile. Measured on MI355X from registers: 32x32x16 bf16 sustains ~2.28
 // PFLOP/s with 8 accumulators, 16x16x32 at most ~1.95, so 64/128-row tiles use 32x32.
 // ---------------------------------------------------------------------------------------
+// f(integral_constant<L0 + i>) for i = 0 .. n-1, unrolled at compile time
+template <int L0, int... Is, class F>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, L0 + Is>{}), ...);
+}
+
 template <int MS, bool MX>
 struct Mfma;
 
@@ -239,10 +300,11 @@ __device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
 // ---------------------------------------------------------------------------------------
 // one output tile of BM rows x (256 B-rows) for group g
 // ---------------------------------------------------------------------------------------
+// Rows [r_off, r_off + BM) of group g's output (fewer at the group's end), columns of tile nt.
 // RK (ragged K): every group computes the full M x N output over its own K range
 // [32 offsets[g], 32 offsets[g+1]) and writes it at C + g * c_stride.
 template <int BM, bool SWIGLU, bool MX, bool RK>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int mt, int nt) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int r_off, int nt) {
     constexpr int EB = MX ? 1 : 2;                      // operand element bytes
     constexpr int WM = (BM == 16) ? 1 : 2;              // wave grid: WM x WN = 8 waves
     constexpr int WN = kWaves / WM;
@@ -261,9 +323,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
     constexpr int AS_INSTR = cdiv(BM, 64);               // MXFP8: scale dwords, 64 rows per instruction
     constexpr int BS_INSTR = kBN / 64;
+    constexpr int NST = Stage<BM>::kCount;
+    constexpr int SB = Stage<BM>::kBytes;
+    static_assert(NST * SB <= kPipeBytes, "pipeline stages exceed the LDS ring");
+    static_assert(BM < 256 || (BM * (kBN * 2 + 16) <= kPipeBytes), "bf16 epilogue tile must fit in LDS");
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
     static_assert(AS_INSTR + BS_INSTR <= kWaves, "one scale load per wave at most");
 
+    if constexpr (BM == 256) {
+        if (p.c_f32) return;   // never scheduled: 256-row tiles are only chosen for 2-byte outputs
+    }
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
@@ -285,7 +354,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     } else {
         group_rows(p.offsets, g, p.M, row_begin, row_end);
     }
-    const int r0 = row_begin + mt * BM;                   // first C row of the tile
+    const int r0 = row_begin + r_off;                     // first C row of the tile
     const int n0 = nt * BN_OUT;                           // first output column
 
     auto a_row_of = [&](int row) -> int64_t {             // A row feeding tile row `row`
@@ -328,31 +397,36 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     if constexpr (MX) {
         if (wave < AS_INSTR) {
             s_src = p.a_scale + a_row_of(wave * 64 + lane) * p.lda_scale + kbase / 32;
-            s_lds = kScaleOffA + wave * 256;
+            s_lds = Stage<BM>::kScaleA + wave * 256;
         } else if (wave < AS_INSTR + BS_INSTR) {
             const int rho = (wave - AS_INSTR) * 64 + lane;
             s_src = p.b_scale + (RK ? 0 : (int64_t)g * p.b_scale_stride) + (int64_t)b_row_of(rho) * p.ldb_scale +
                     kbase / 32;
-            s_lds = kScaleOffB + (wave - AS_INSTR) * 256;
+            s_lds = Stage<BM>::kScaleB + (wave - AS_INSTR) * 256;
         }
     }
 
-    auto issue = [&](int kt) {
-        char* st = lds + (kt % kStages) * kStageBytes;
+    // This wave's DMA loads of one stage, numbered 0 .. NLOADS-1: its A instructions, its B
+    // instructions, then (MXFP8) its scale dword. issue_one(kt, l) issues load l of stage kt.
+    constexpr int NLOADS = A_PER_WAVE + B_PER_WAVE + (MX ? 1 : 0);
+    auto issue_one = [&](int kt, auto l_tag) {
+        constexpr int l = decltype(l_tag)::value;
+        char* st = lds + (kt % NST) * SB;
         const int64_t koff = (int64_t)kt * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < A_PER_WAVE; ++i) {
-            const int instr = wave + kWaves * i;
-            if constexpr (A_INSTR % kWaves == 0) load_lds16(a_src[i] + koff, st + instr * 1024);
-            else if (instr < A_INSTR) load_lds16(a_src[i] + koff, st + instr * 1024);
-        }
-        char* stb = st + BM * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < B_PER_WAVE; ++i) load_lds16(b_src[i] + koff, stb + (wave * B_PER_WAVE + i) * 1024);
-        if constexpr (MX) {
+        if constexpr (l < A_PER_WAVE) {
+            const int instr = wave + kWaves * l;
+            if constexpr (A_INSTR % kWaves == 0) load_lds16(a_src[l] + koff, st + instr * 1024);
+            else if (instr < A_INSTR) load_lds16(a_src[l] + koff, st + instr * 1024);
+        } else if constexpr (l < A_PER_WAVE + B_PER_WAVE) {
+            constexpr int i = l - A_PER_WAVE;
+            load_lds16(b_src[i] + koff, st + BM * kRowBytes + (wave * B_PER_WAVE + i) * 1024);
+        } else {
             // 4 scale bytes (the stage's 4 blocks of 32) per row
             if (wave < AS_INSTR + BS_INSTR) load_lds4(s_src + kt * 4, st + s_lds);
         }
+    };
+    auto issue = [&](int kt) {
+        static_for<0>([&](auto l) { issue_one(kt, l); }, std::make_integer_sequence<int, NLOADS>{});
     };
 
     typename MF::acc_t acc[MI][NI];
@@ -385,16 +459,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     }
     // Fragments are double-buffered in registers: the LDS reads of k-step ks+1 are issued
     // before the MFMAs of k-step ks, so LDS latency overlaps matrix work.
-    auto compute = [&](int kt) {
-        const char* st = lds + (kt % kStages) * kStageBytes;
+    // compute(kt, kn): multiply stage kt; when kn >= 0 also issue this wave's loads of stage kn,
+    // a share after the first MFMA of every k-step, so the DMA instructions queue while the
+    // matrix core works instead of all waves issuing them back to back after the barrier.
+    auto compute = [&](int kt, int kn) {
+        const char* st = lds + (kt % NST) * SB;
         int sa_w[MI], sb_w[NI];   // MXFP8: this lane's rows' 4 scale bytes of the stage
         if constexpr (MX) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                sa_w[i] = *reinterpret_cast<const int*>(st + kScaleOffA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4);
+                sa_w[i] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4);
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                sb_w[j] = *reinterpret_cast<const int*>(st + kScaleOffB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
+                sb_w[j] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
         }
         FragT af[2][MI], bfr[2][NI];
 #pragma unroll
@@ -426,38 +503,61 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
                 for (int j = 0; j < NI; ++j) sb[j] = 0;
             }
+            acc[0][0] = mfma<MS, MX>(af[cur][0], bfr[cur][0], acc[0][0], sa[0], sb[0]);
+            if (kn >= 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0>(
+                    [&](auto l) {
+                        // k-step ks issues loads [ks*NLOADS/NKS, (ks+1)*NLOADS/NKS)
+                        constexpr int lo = decltype(l)::value;
+                        if (lo * NKS >= ks * NLOADS && lo * NKS < (ks + 1) * NLOADS) issue_one(kn, l);
+                    },
+                    std::make_integer_sequence<int, NLOADS>{});
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = mfma<MS, MX>(af[cur][i], bfr[cur][j], acc[i][j], sa[i], sb[j]);
+                    if (i != 0 || j != 0) acc[i][j] = mfma<MS, MX>(af[cur][i], bfr[cur][j], acc[i][j], sa[i], sb[j]);
         }
     };
 
-    // Ring of kStages LDS stages: stages kt+1 .. kt+kStages-2 stream in while stage kt is
-    // multiplied. Before stage kt is read, this wave's loads of the later stage may still be
-    // pending (LOADS_MIN); the barrier then makes every wave's loads of stage kt visible and
-    // guarantees the buffer refilled next (read in iteration kt-1) is no longer in use.
+    // Ring of NST LDS stages. Three stages (tiles up to 128 rows): stage kt+1 may still be
+    // streaming in when stage kt is read, so each wave waits until at most its own loads of
+    // that later stage are pending (LOADS_MIN); the barrier then makes every wave's loads of
+    // stage kt visible and guarantees the buffer refilled next (read in iteration kt-1) is
+    // no longer in use.
     if (nk > 0) {    // only a ragged-K group with an empty range has no slice (C_g = 0)
         lds_barrier();   // the previous tile's epilogue may still read LDS
-        issue(0);
-        if (nk > 1) issue(1);
-        int kt = 0;
-        for (; kt + 2 < nk; ++kt) {
-            wait_vm_lgkm0<LOADS_MIN>();
+        if constexpr (NST == 3) {
+            issue(0);
+            if (nk > 1) issue(1);
+            int kt = 0;
+            for (; kt + 2 < nk; ++kt) {
+                wait_vm_lgkm0<LOADS_MIN>();
+                lds_barrier();
+                compute(kt, kt + 2);
+            }
+            if (kt + 1 < nk) {
+                wait_vm_lgkm0<LOADS_MIN>();
+                lds_barrier();
+                compute(kt, -1);
+                ++kt;
+            }
+            wait_vm_lgkm0<0>();
             lds_barrier();
-            issue(kt + 2);
-            compute(kt);
+            compute(kt, -1);
+        } else {
+            // two stages: stage kt+1 streams in while stage kt is multiplied; the barrier
+            // after the wait also guarantees stage kt-1's buffer is no longer being read
+            issue(0);
+            for (int kt = 0; kt < nk; ++kt) {
+                wait_vm_lgkm0<0>();
+                lds_barrier();
+                compute(kt, kt + 1 < nk ? kt + 1 : -1);
+            }
         }
-        if (kt + 1 < nk) {
-            wait_vm_lgkm0<LOADS_MIN>();
-            lds_barrier();
-            compute(kt);
-            ++kt;
-        }
-        wait_vm_lgkm0<0>();
-        lds_barrier();
-        compute(kt);
     }
 
     // ---- epilogue: values -> LDS (output dtype) -> 16-byte coalesced global stores ----
@@ -542,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
             const int g = tile / per_group;
             int mt, nt;
             tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
-            gemm_tile<128, false, true, true>(p, lds, g, mt, nt);
+            gemm_tile<128, false, true, true>(p, lds, g, mt * 128, nt);
         }
         return;
     }
@@ -562,15 +662,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
         const int L = tile - ts[g];
         int gb, ge;
         group_rows(p.offsets, g, p.M, gb, ge);
-        const int m = ge - gb;
-        const int bm = bm_of_rows(m);
-        int mt, nt;
-        tile_coords(L, cdiv(m, bm), p.NT, mt, nt);
+        const RowTiles rt = row_tiles(ge - gb, p.allow256 != 0);
+        int mt, nt, r_off, bm;
+        tile_coords(L, rt.count(), p.NT, mt, nt);
+        row_tile(rt, mt, r_off, bm);
         switch (bm) {
-            case 16: gemm_tile<16, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
-            case 32: gemm_tile<32, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
-            case 64: gemm_tile<64, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
-            default: gemm_tile<128, SWIGLU, MX, false>(p, lds, g, mt, nt); break;
+            case 16: gemm_tile<16, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
+            case 32: gemm_tile<32, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
+            case 64: gemm_tile<64, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
+            case 128: gemm_tile<128, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
+            default:
+                // 256-row tiles are bf16 only (the fp8 fragments of a 256-row tile do not fit
+                // the register budget next to its accumulators); never chosen for MXFP8
+                if constexpr (!MX) gemm_tile<256, SWIGLU, MX, false>(p, lds, g, r_off, nt);
+                break;
         }
     }
 }
@@ -705,6 +810,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.b_scale_stride = a->b_scale_group_stride;
     p.tile_start = (const int32_t*)workspace;
     p.c_stride = a->c_group_stride;
+    p.allow256 = (MOE_GEMM_TILE256 && a->c_dtype != MOE_F32 && a->a_dtype == MOE_BF16) ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
     if (a->a_dtype == MOE_F32) {
@@ -739,7 +845,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         return moe::launch<false, true, true>(p, grid, s);
     }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
-                       (int32_t*)workspace);
+                       p.allow256, (int32_t*)workspace);
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;
