@@ -140,8 +140,9 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
     permuted view of transposed weights); C [M, N]; offsets int32 [G+1] (device); a_rows
     int32 [M]. MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale
     [G, N_B, K/32] uint8 E8M0 bytes.
-    ragged_k: C [G, M, N], C[g] = A[:, Kg] @ B[:, Kg]^T over the K range of group g given by
-    offsets in 32-element blocks; A [M, K], B [N, K], a_scale [M, K/32], b_scale [N, K/32].
+    ragged_k: C [G, M, N], C[g] = A_g @ B_g^T over group g's offsets[g] .. offsets[g+1]-1
+    blocks of 32 K elements, A, B, a_scale, b_scale being the column-wise quantiser's
+    group-major output buffers (capacities [M, K], [N, K], [M, K/32], [N, K/32]).
     """
     if ragged_k:
         G, M, N = C.shape
@@ -214,9 +215,10 @@ def moe_group_quant_mxfp8(x, q, scales, axis: int = 0, group_offsets=None, block
     E8M0 scale bytes (uint8). Logical row r reads x[row_index[r]] when row_index is given
     (then `rows` defaults to row_index's length), else x[r]. axis 0: q [rows, >=cols],
     scales [rows, >=cols/32]. axis 1 (blocks of 32 rows inside each group of group_offsets,
-    each group starting on a multiple of 4 blocks; transposed output):
-    q [cols, >=32*quant_col_blocks(rows, G)], scales [cols, >=quant_col_blocks(rows, G)],
-    block_start int32 [G+1] (optional output)."""
+    each group starting on a multiple of 4 blocks; transposed group-major output, group g's
+    [cols, 32 n_g] codes at byte 32*cols*block_start[g] of q): q [cols, 32*nb] and scales
+    [cols, nb] buffers with nb >= quant_col_blocks(rows, G), block_start int32 [G+1]
+    (optional output)."""
     in_rows, cols = x.shape
     if rows is None:
         rows = in_rows if row_index is None else row_index.numel()

@@ -33,8 +33,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 namespace moe {
 namespace {
 
-constexpr int kThreads = 512;     // 8 waves: two per SIMD, so one wave's MFMAs cover the other's waits
-constexpr int kWaves = kThreads / 64;
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+// 8 waves: two per SIMD, 64x64-ish wave tiles; 4 waves: one per SIMD with twice the wave tile
+// (half the LDS fragment reads per MFMA), accumulators in the accumulation registers
+constexpr int kWaves = MOE_GEMM_WAVES;
+constexpr int kThreads = kWaves * 64;
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 constexpr int kBN = 256;          // B rows per tile (SwiGLU: 128 gate rows + 128 up rows)
 constexpr int kRowBytes = 128;    // one LDS row per stage: 64 bf16 or 128 fp8 of K
 constexpr int kChunks = kRowBytes / 16;
@@ -47,7 +53,8 @@ constexpr int kChunks = kRowBytes / 16;
 // (MXFP8) one scale dword per A row and per B row. A scale rows are loaded 64 per wave
 // instruction, so their slot is rounded up to a multiple of 64 rows (a 16-row tile's scale
 // load still writes 64 dwords and must not reach the B scales). Tiles up to 128 rows keep a
-// 3-stage ring; 256-row tiles (64 KiB of operands per stage) fit two.
+// 3-stage ring (a 4th stage for the 16/32-row tiles measured no faster on the expert
+// shapes); 256-row tiles (64 KiB of operands per stage) fit two.
 template <int BM>
 struct Stage {
     static constexpr int kScaleRowsA = (BM + 63) / 64 * 64;
@@ -57,8 +64,8 @@ struct Stage {
     static constexpr int kBytes = kData + (kScaleRowsA + kBN) * 4;
     static constexpr int kCount = BM == 256 ? 2 : 3;
 };
-constexpr int kPipeBytes = 3 * Stage<128>::kBytes > 2 * Stage<256>::kBytes ? 3 * Stage<128>::kBytes
-                                                                             : 2 * Stage<256>::kBytes;   // 148.5 KiB
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kPipeBytes = cmax(3 * Stage<128>::kBytes, 2 * Stage<256>::kBytes);   // 148.5 KiB
 constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
@@ -141,47 +148,125 @@ struct GemmParams {
     const uint8_t* b_scale;   // group g: [N_B, K/32] at b_scale + g * b_scale_stride
     int64_t ldb_scale;
     int64_t b_scale_stride;
-    const int32_t* tile_start;   // [G+1] in workspace (ragged rows)
+    const int32_t* tile_start;   // [G+1] in workspace (ragged rows): first tile of schedule position p
+    const int32_t* order;        // [G] in workspace: group at schedule position p
     int allow256;                // ragged rows: 256-row tiles allowed (not for fp32 C)
     int64_t c_stride;            // ragged K: elements between groups' C
     int MT;                      // ragged K: row tiles per group
 };
 
 // ---------------------------------------------------------------------------------------
-// schedule: tile_start[g] = sum over groups < g of (row tiles of g) * NT
+// schedule: the order in which the persistent workgroups take the groups' tiles.
+//
+// Groups of up to 128 rows are one row of tiles that stream their weights once (HBM-bound);
+// larger groups are MFMA-bound. Taking them in expert order makes the chip alternate between
+// phases that saturate HBM and phases that leave it idle, so the two classes are merged in
+// proportion instead: every non-empty group gets the fraction of its class's tiles completed
+// at its midpoint, and groups are taken in that order (ties: the larger class first, then by
+// id). order[p] is the group at position p, tile_start[p] the first tile of that position;
+// empty groups go last with no tiles. G <= 2047, one workgroup.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
-                                                             int NT, int allow256, int32_t* __restrict__ tile_start) {
-    __shared__ int wsum[16];
-    __shared__ int carry_s;
+                                                             int NT, int allow256, int32_t* __restrict__ tile_start,
+                                                             int32_t* __restrict__ order) {
+    __shared__ unsigned long long key[2048];
+    __shared__ int tiles_of[2048];
+    __shared__ unsigned long long wsum[16];
+    __shared__ unsigned long long carry_s;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // tiles per group, and each group's exclusive prefix of tiles within its class: one scan of
+    // (small-class tiles << 32 | large-class tiles)
+    unsigned long long pre[2];
     if (tid == 0) carry_s = 0;
     __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += 1024) {
-        const int g = g0 + tid;
-        int tiles = 0;
+    for (int h = 0; h < 2; ++h) {
+        const int g = h * 1024 + tid;
+        int t = 0, small = 0;
         if (g < G) {
             int b, e;
             group_rows(offsets, g, M, b, e);
-            const int m = e - b;
-            tiles = row_tiles(m, allow256 != 0).count() * NT;
+            t = row_tiles(e - b, allow256 != 0).count() * NT;
+            small = (e - b) <= 128;
         }
-        int incl = tiles;
+        if (g < 2048) tiles_of[g] = t;
+        const unsigned long long v = small ? ((unsigned long long)t << 32) : (unsigned long long)t;
+        unsigned long long incl = v;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const unsigned long long o = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += o;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        unsigned long long base = carry_s;
+        for (int w = 0; w < wave; ++w) base += wsum[w];
+        pre[h] = base + incl - v;
+        __syncthreads();
+        if (tid == 1023) carry_s = base + incl;
+        __syncthreads();
+    }
+    const unsigned long long tot = carry_s;
+    const unsigned long long tot_small = tot >> 32, tot_large = tot & 0xFFFFFFFFull;
+    for (int h = 0; h < 2; ++h) {
+        const int g = h * 1024 + tid;
+        unsigned long long k = ~0ull;   // padding and empty groups sort last
+        if (g < G && tiles_of[g] > 0) {
+            int b, e;
+            group_rows(offsets, g, M, b, e);
+            const bool small = (e - b) <= 128;
+            const unsigned long long p = small ? (pre[h] >> 32) : (pre[h] & 0xFFFFFFFFull);
+            const unsigned long long total = small ? tot_small : tot_large;
+            // midpoint fraction of the class's tiles in 2^-24 units
+            const unsigned long long frac = ((2 * p + (unsigned long long)tiles_of[g]) << 23) / total;
+            const bool first = small ? (tot_small >= tot_large) : (tot_large > tot_small);
+            k = (frac << 32) | ((unsigned long long)(first ? 0 : 1) << 16) | (unsigned long long)g;
+        } else if (g < G) {
+            k = (0xFFFFFFFFull << 32) | (unsigned long long)g;   // empty group: last, by id
+        }
+        key[g] = k;
+    }
+    __syncthreads();
+    // bitonic sort of the 2048 keys, ascending
+    for (int size = 2; size <= 2048; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int i = 2 * tid - (tid & (stride - 1));   // lower index of the pair
+            const int j = i + stride;
+            const bool up = (i & size) == 0;
+            const unsigned long long a = key[i], c = key[j];
+            if ((a > c) == up) {
+                key[i] = c;
+                key[j] = a;
+            }
+            __syncthreads();
+        }
+    }
+    // order and the tile prefix in schedule order
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int h = 0; h < 2; ++h) {
+        const int p = h * 1024 + tid;
+        int t = 0, g = 0;
+        if (p < G) {
+            g = (int)(key[p] & 0xFFFF);
+            t = tiles_of[g];
+            order[p] = g;
+        }
+        int incl = t;
 #pragma unroll
         for (int s = 1; s < kWave; s <<= 1) {
             const int o = __shfl_up(incl, s, kWave);
             if (lane >= s) incl += o;
         }
-        if (lane == kWave - 1) wsum[wave] = incl;
+        if (lane == kWave - 1) wsum[wave] = (unsigned long long)incl;
         __syncthreads();
-        int wbase = carry_s;
-        for (int w = 0; w < wave; ++w) wbase += wsum[w];
-        if (g < G) tile_start[g] = wbase + incl - tiles;
+        int base = (int)carry_s;
+        for (int w = 0; w < wave; ++w) base += (int)wsum[w];
+        if (p < G) tile_start[p] = base + incl - t;
         __syncthreads();
-        if (tid == 1023) carry_s = wbase + incl;
+        if (tid == 1023) carry_s = (unsigned long long)(base + incl);
         __syncthreads();
     }
-    if (tid == 0) tile_start[G] = carry_s;
+    if (tid == 0) tile_start[G] = (int)carry_s;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -301,12 +386,15 @@ __device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
 // one output tile of BM rows x (256 B-rows) for group g
 // ---------------------------------------------------------------------------------------
 // Rows [r_off, r_off + BM) of group g's output (fewer at the group's end), columns of tile nt.
-// RK (ragged K): every group computes the full M x N output over its own K range
-// [32 offsets[g], 32 offsets[g+1]) and writes it at C + g * c_stride.
+// RK (ragged K): every group computes the full M x N output over its own blocks
+// offsets[g] .. offsets[g+1]-1 of 32 K elements, read from the group-major column-wise
+// layout (group g's A block [M, 32 n_g] at A + 32 M offsets[g], row stride 32 n_g; likewise
+// B with N rows and both scale blocks), and writes it at C + g * c_stride.
 template <int BM, bool SWIGLU, bool MX, bool RK>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int r_off, int nt) {
     constexpr int EB = MX ? 1 : 2;                      // operand element bytes
-    constexpr int WM = (BM == 16) ? 1 : 2;              // wave grid: WM x WN = 8 waves
+    // wave grid WM x WN: 8 waves: 1x8 for 16 rows, else 2x4; 4 waves: 2x2 from 128 rows, else 1x4
+    constexpr int WM = kWaves == 8 ? ((BM == 16) ? 1 : 2) : ((BM >= 128) ? 2 : 1);
     constexpr int WN = kWaves / WM;
     constexpr int MS = (BM / WM >= 32) ? 32 : 16;       // MFMA tile edge
     using MF = Mfma<MS, MX>;
@@ -323,12 +411,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
     constexpr int AS_INSTR = cdiv(BM, 64);               // MXFP8: scale dwords, 64 rows per instruction
     constexpr int BS_INSTR = kBN / 64;
+    constexpr int SC_PER_WAVE = MX ? cdiv(AS_INSTR + BS_INSTR, kWaves) : 0;   // scale instructions per wave
     constexpr int NST = Stage<BM>::kCount;
     constexpr int SB = Stage<BM>::kBytes;
     static_assert(NST * SB <= kPipeBytes, "pipeline stages exceed the LDS ring");
+    static_assert(NST <= 4, "the wait counts cover at most two later stages in flight");
     static_assert(BM < 256 || (BM * (kBN * 2 + 16) <= kPipeBytes), "bf16 epilogue tile must fit in LDS");
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
-    static_assert(AS_INSTR + BS_INSTR <= kWaves, "one scale load per wave at most");
+    static_assert(SC_PER_WAVE <= 2, "at most two scale loads per wave");
 
     if constexpr (BM == 256) {
         if (p.c_f32) return;   // never scheduled: 256-row tiles are only chosen for 2-byte outputs
@@ -337,19 +427,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     int row_begin, row_end;
-    int64_t kbase = 0;                                    // first K element (ragged K)
     int nk = p.K / (kRowBytes / EB);                      // K slices
     char* Cg = p.C;
+    // operand bases and row strides (bytes); scale bases and row strides (scale bytes)
+    const char* a_base = p.A;
+    int64_t a_ld = p.lda * EB;
+    const char* b_base = p.B + (RK ? 0 : (int64_t)g * p.b_stride * EB);
+    int64_t b_ld = p.ldb * EB;
+    const uint8_t* as_base = p.a_scale;
+    int64_t as_ld = p.lda_scale;
+    const uint8_t* bs_base = p.b_scale ? p.b_scale + (RK ? 0 : (int64_t)g * p.b_scale_stride) : nullptr;
+    int64_t bs_ld = p.ldb_scale;
     if constexpr (RK) {
         row_begin = 0;
         row_end = p.M;
-        // clamp the block range into [0, K/32] and round to whole 128-element slices, so
-        // inconsistent offsets can never move a load outside A or B
+        // clamp the block range into [0, K/32] and keep whole 128-element slices (both ends on
+        // multiples of 4 blocks), so inconsistent offsets can never move a load outside A or B
         const int kb_max = p.K / 32;
         const int kb0 = min(max(p.offsets[g], 0), kb_max) & ~3;
-        const int kb1 = max(min(p.offsets[g + 1], kb_max), kb0);
-        kbase = (int64_t)kb0 * 32;
-        nk = (kb1 - kb0) / 4;
+        const int nbe = (max(min(p.offsets[g + 1], kb_max), kb0) - kb0) & ~3;   // blocks used
+        nk = nbe / 4;
+        a_base = p.A + (int64_t)32 * p.M * kb0;
+        a_ld = (int64_t)32 * nbe;
+        b_base = p.B + (int64_t)32 * p.N * kb0;
+        b_ld = (int64_t)32 * nbe;
+        as_base = p.a_scale + (int64_t)p.M * kb0;
+        as_ld = nbe;
+        bs_base = p.b_scale + (int64_t)p.N * kb0;
+        bs_ld = nbe;
         Cg = p.C + (int64_t)g * p.c_stride * (p.c_f32 ? 4 : 2);
     } else {
         group_rows(p.offsets, g, p.M, row_begin, row_end);
@@ -380,35 +485,39 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         const int instr = wave + kWaves * i;
         const int row = instr * ROWS_PER_INSTR + lane / kChunks;
         const int chunk = (lane % kChunks) ^ swz(row);
-        a_src[i] = p.A + (a_row_of(row) * p.lda + kbase) * EB + chunk * 16;
+        a_src[i] = a_base + a_row_of(row) * a_ld + chunk * 16;
     }
     const char* b_src[B_PER_WAVE];
-    const char* bg = p.B + ((RK ? 0 : (int64_t)g * p.b_stride) + kbase) * EB;
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
         const int instr = wave * B_PER_WAVE + i;
         const int rho = instr * ROWS_PER_INSTR + lane / kChunks;
         const int chunk = (lane % kChunks) ^ swz(rho);
-        b_src[i] = bg + (int64_t)b_row_of(rho) * p.ldb * EB + chunk * 16;
+        b_src[i] = b_base + (int64_t)b_row_of(rho) * b_ld + chunk * 16;
     }
-    // MXFP8 scale rows: waves 0..AS_INSTR-1 load A-scale dwords, the next BS_INSTR waves B's
-    const uint8_t* s_src = nullptr;
-    int s_lds = 0;
+    // MXFP8 scale rows: scale instruction q (0 .. AS_INSTR+BS_INSTR-1) is issued by wave q % kWaves
+    // as its (q / kWaves)-th scale load; instructions below AS_INSTR bring 64 A rows' scale
+    // dwords, the others 64 B rows'
+    const uint8_t* s_src[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
+    int s_lds[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
     if constexpr (MX) {
-        if (wave < AS_INSTR) {
-            s_src = p.a_scale + a_row_of(wave * 64 + lane) * p.lda_scale + kbase / 32;
-            s_lds = Stage<BM>::kScaleA + wave * 256;
-        } else if (wave < AS_INSTR + BS_INSTR) {
-            const int rho = (wave - AS_INSTR) * 64 + lane;
-            s_src = p.b_scale + (RK ? 0 : (int64_t)g * p.b_scale_stride) + (int64_t)b_row_of(rho) * p.ldb_scale +
-                    kbase / 32;
-            s_lds = Stage<BM>::kScaleB + (wave - AS_INSTR) * 256;
+#pragma unroll
+        for (int u = 0; u < SC_PER_WAVE; ++u) {
+            const int q = wave + kWaves * u;
+            if (q < AS_INSTR) {
+                s_src[u] = as_base + a_row_of(q * 64 + lane) * as_ld;
+                s_lds[u] = Stage<BM>::kScaleA + q * 256;
+            } else if (q < AS_INSTR + BS_INSTR) {
+                const int rho = (q - AS_INSTR) * 64 + lane;
+                s_src[u] = bs_base + (int64_t)b_row_of(rho) * bs_ld;
+                s_lds[u] = Stage<BM>::kScaleB + (q - AS_INSTR) * 256;
+            }
         }
     }
 
     // This wave's DMA loads of one stage, numbered 0 .. NLOADS-1: its A instructions, its B
     // instructions, then (MXFP8) its scale dword. issue_one(kt, l) issues load l of stage kt.
-    constexpr int NLOADS = A_PER_WAVE + B_PER_WAVE + (MX ? 1 : 0);
+    constexpr int NLOADS = A_PER_WAVE + B_PER_WAVE + SC_PER_WAVE;
     auto issue_one = [&](int kt, auto l_tag) {
         constexpr int l = decltype(l_tag)::value;
         char* st = lds + (kt % NST) * SB;
@@ -422,7 +531,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
             load_lds16(b_src[i] + koff, st + BM * kRowBytes + (wave * B_PER_WAVE + i) * 1024);
         } else {
             // 4 scale bytes (the stage's 4 blocks of 32) per row
-            if (wave < AS_INSTR + BS_INSTR) load_lds4(s_src + kt * 4, st + s_lds);
+            constexpr int u = l - A_PER_WAVE - B_PER_WAVE;
+            if (wave + kWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4, st + s_lds[u]);
         }
     };
     auto issue = [&](int kt) {
@@ -523,40 +633,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         }
     };
 
-    // Ring of NST LDS stages. Three stages (tiles up to 128 rows): stage kt+1 may still be
-    // streaming in when stage kt is read, so each wave waits until at most its own loads of
-    // that later stage are pending (LOADS_MIN); the barrier then makes every wave's loads of
-    // stage kt visible and guarantees the buffer refilled next (read in iteration kt-1) is
-    // no longer in use.
+    // Ring of NST LDS stages: stages kt+1 .. kt+NST-2 may still be streaming in when stage kt
+    // is read, so each wave first waits until at most its own loads of those later stages are
+    // pending (LOADS_MIN per stage); the barrier then makes every wave's loads of stage kt
+    // visible and guarantees that the buffer refilled during compute(kt) (stage kt+NST-1,
+    // last read in iteration kt-1) is no longer in use.
     if (nk > 0) {    // only a ragged-K group with an empty range has no slice (C_g = 0)
         lds_barrier();   // the previous tile's epilogue may still read LDS
-        if constexpr (NST == 3) {
-            issue(0);
-            if (nk > 1) issue(1);
-            int kt = 0;
-            for (; kt + 2 < nk; ++kt) {
-                wait_vm_lgkm0<LOADS_MIN>();
-                lds_barrier();
-                compute(kt, kt + 2);
-            }
-            if (kt + 1 < nk) {
-                wait_vm_lgkm0<LOADS_MIN>();
-                lds_barrier();
-                compute(kt, -1);
-                ++kt;
-            }
-            wait_vm_lgkm0<0>();
+#pragma unroll
+        for (int s0 = 0; s0 < NST - 1; ++s0)
+            if (s0 < nk) issue(s0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int ahead = min(NST - 2, nk - 1 - kt);   // later stages possibly in flight
+            if (ahead >= 2) wait_vm_lgkm0<2 * LOADS_MIN>();
+            else if (ahead == 1) wait_vm_lgkm0<LOADS_MIN>();
+            else wait_vm_lgkm0<0>();
             lds_barrier();
-            compute(kt, -1);
-        } else {
-            // two stages: stage kt+1 streams in while stage kt is multiplied; the barrier
-            // after the wait also guarantees stage kt-1's buffer is no longer being read
-            issue(0);
-            for (int kt = 0; kt < nk; ++kt) {
-                wait_vm_lgkm0<0>();
-                lds_barrier();
-                compute(kt, kt + 1 < nk ? kt + 1 : -1);
-            }
+            compute(kt, kt + NST - 1 < nk ? kt + NST - 1 : -1);
         }
     }
 
@@ -651,15 +744,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     __syncthreads();
     const int total = ts[p.G];
     for (int tile = slot; tile < total; tile += gridDim.x) {
-        // group = last g with ts[g] <= tile
+        // schedule position = last q with ts[q] <= tile; its group from the order table
         int lo = 0, hi = p.G - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (ts[mid] <= tile) lo = mid;
             else hi = mid - 1;
         }
-        const int g = lo;
-        const int L = tile - ts[g];
+        const int g = min(max(p.order[lo], 0), p.G - 1);
+        const int L = tile - ts[lo];
         int gb, ge;
         group_rows(p.offsets, g, p.M, gb, ge);
         const RowTiles rt = row_tiles(ge - gb, p.allow256 != 0);
@@ -674,7 +767,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
             default:
                 // 256-row tiles are bf16 only (the fp8 fragments of a 256-row tile do not fit
                 // the register budget next to its accumulators); never chosen for MXFP8
-                if constexpr (!MX) gemm_tile<256, SWIGLU, MX, false>(p, lds, g, r_off, nt);
+                if constexpr (!MX && MOE_GEMM_TILE256) gemm_tile<256, SWIGLU, MX, false>(p, lds, g, r_off, nt);
                 break;
         }
     }
@@ -752,7 +845,7 @@ moe_status_t launch(const GemmParams& p, int grid, hipStream_t s) {
 
 size_t moe_gemm_workspace_bytes(int32_t G) {
     if (G < 1) G = 1;
-    return (((size_t)G + 1) * 4 + 255) & ~size_t(255);
+    return ((2 * (size_t)G + 1) * 4 + 255) & ~size_t(255);   // tile_start [G+1], order [G]
 }
 
 static inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -775,6 +868,10 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         if (a->a_dtype != MOE_E4M3 || a->epilogue != MOE_EPI_NONE) return MOE_ENOTSUP;
         if (a->a_rows || a->aux || a->b_group_stride != 0 || a->b_scale_group_stride != 0) return MOE_EINVAL;
         if (a->A_rows != a->M || a->c_group_stride < a->M * a->ldc) return MOE_EINVAL;
+        // the operands are the column-wise quantiser's group-major blocks: the leading
+        // dimensions state the capacity, [M, K] and [N, K] codes, [M, K/32] and [N, K/32] scales
+        if (a->lda != a->K || a->ldb != a->K || a->lda_scale != a->K / 32 || a->ldb_scale != a->K / 32)
+            return MOE_EINVAL;
     }
     if (a->M == 0) return MOE_OK;
     if (!a->A || !a->B || !a->C || a->A_rows <= 0) return MOE_EINVAL;
@@ -809,6 +906,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.ldb_scale = a->ldb_scale;
     p.b_scale_stride = a->b_scale_group_stride;
     p.tile_start = (const int32_t*)workspace;
+    p.order = (const int32_t*)workspace + (a->G + 1);
     p.c_stride = a->c_group_stride;
     p.allow256 = (MOE_GEMM_TILE256 && a->c_dtype != MOE_F32 && a->a_dtype == MOE_BF16) ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
@@ -845,7 +943,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         return moe::launch<false, true, true>(p, grid, s);
     }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
-                       p.allow256, (int32_t*)workspace);
+                       p.allow256, (int32_t*)workspace, (int32_t*)workspace + (a->G + 1));
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;

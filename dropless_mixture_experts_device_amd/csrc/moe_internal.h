@@ -67,5 +67,6 @@ __host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
     } while (0)
 
 size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E);
+size_t moe_gemm_workspace_bytes(int32_t G);
 
 static inline bool moe_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

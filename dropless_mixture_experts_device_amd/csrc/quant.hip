@@ -34,20 +34,18 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
 // finite bf16/fp32 amax, so the result is a normal float.
 __device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
 
-// Round a (scaled) value to E4M3 (OCP "FN": bias 7, 3 mantissa bits, subnormal step 2^-9,
-// max 448, no infinities), nearest-even, saturating; returns the byte code (sign kept).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    if (a >= 448.f) return sign | 0x7Eu;
-    if (a < 0.015625f) {                       // below 2^-6: subnormal grid of step 2^-9
-        return sign | (uint32_t)rintf(a * 512.f);   // 8 maps to 0x08, the smallest normal
-    }
-    // normal: round the 23-bit mantissa to 3 bits, nearest-even; a carry bumps the exponent
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    const uint32_t e = (u >> 23) - 127u + 7u;
-    return sign | (e << 3) | ((u >> 20) & 7u);
+// Four scaled values -> four E4M3 codes (OCP "FN": bias 7, 3 mantissa bits, subnormal step
+// 2^-9, max 448, no infinities), packed little-endian into one word. gfx950's v_cvt_pk_fp8_f32
+// converts to OCP E4M3 with round-to-nearest-even; clamping to +-448 first gives the MX rule's
+// saturation (the sign of zero passes through).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    c = fminf(fmaxf(c, -448.f), 448.f);
+    d = fminf(fmaxf(d, -448.f), 448.f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);         // bytes 2, 3
+    return (uint32_t)w;
 }
 
 __device__ __forceinline__ float load_val(const char* p, int esize) {
@@ -96,10 +94,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict_
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) word |= e4m3_code(v[h * 16 + w * 4 + i] * inv) << (8 * i);
-            out[h][w] = word;
+            const float* e = v + h * 16 + w * 4;
+            out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
         }
     uint8_t* dst = q + r * ld_q + (int64_t)b * kBlock;
     *reinterpret_cast<u32x4*>(dst) = out[0];
@@ -107,12 +103,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict_
     sc[r * ld_sc + b] = (uint8_t)byte;
 }
 
-// Group-aware column-wise, transposed output: block j (a global index over all groups'
-// 32-row blocks) of column c covers rows [offsets[g] + 32 i, +32) of group g, where
-// j = block_start[g] + i; its 32 codes go to q[c, 32 j ...] and its scale to sc[c, j].
-// Group g owns 4 * ceil(m_g / 128) blocks, so every group starts on a 128-element boundary
-// of the transposed rows (one K slice of the MXFP8 GEMM, with its 4 scale bytes in one
-// aligned dword); blocks past the group's last row are all-zero (codes 0, scale byte 0).
+// Group-aware column-wise, transposed, group-major output: group g owns nb_g = 4 ceil(m_g/128)
+// blocks j = block_start[g] + i (i < nb_g) of 32 of its rows; its codes form a [cols, 32 nb_g]
+// matrix at q + 32 cols block_start[g] (block i of column c at column offset 32 i) and its
+// scales a [cols, nb_g] matrix at sc + cols block_start[g]. Each group thus starts on a
+// 128-element boundary (one K slice of the MXFP8 GEMM, its 4 scale bytes one aligned dword),
+// and one group's transposed block is contiguous in memory; blocks past the group's last row
+// are all-zero (codes 0, scale byte 0).
 __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t* __restrict__ offsets, int G,
                                                                   int64_t rows, int32_t* __restrict__ block_start) {
     __shared__ int wsum[16];
@@ -146,19 +143,27 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
     if (tid == 0) block_start[G] = carry_s;
 }
 
-// One thread per (column, block); 64 consecutive columns per wave, so each of the 32 row
-// reads of a wave is one contiguous segment.
+// Column-wise tile: one workgroup quantises a 4-block chunk (128 rows of one group: every
+// group starts on a multiple of 4 blocks) by kColTile columns. The rows are loaded with
+// coalesced 16-byte loads into LDS (read through row_index when given); then two threads own
+// each column, two blocks each: their maxima, scale bytes and codes, written as contiguous
+// 64-byte code segments and 2-byte scale pairs of the group's transposed block. A 32 KiB tile
+// keeps several workgroups resident per CU, so one's loads overlap another's arithmetic.
+constexpr int kColTile = 128;        // columns per workgroup (bf16; 64 for fp32)
 template <int ESIZE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, const int32_t* __restrict__ row_index,
                                                          int64_t in_rows, const int32_t* __restrict__ offsets, int G,
                                                          const int32_t* __restrict__ block_start,
-                                                         uint8_t* __restrict__ q, int64_t ld_q,
-                                                         uint8_t* __restrict__ sc, int64_t ld_sc) {
-    const int j = blockIdx.y;                       // global block index
-    const int c = blockIdx.x * 256 + threadIdx.x;   // column
-    if (j >= block_start[G] || c >= cols) return;
-    int lo = 0, hi = G - 1;                          // group = last g with block_start[g] <= j
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+    constexpr int TC = ESIZE == 2 ? kColTile : kColTile / 2;    // columns of this tile
+    constexpr int PITCH = TC * ESIZE;                            // LDS bytes per row (256)
+    __shared__ __attribute__((aligned(16))) char tile[kGroupAlign * kBlock * PITCH];   // 32 KiB
+    const int j = blockIdx.y * kGroupAlign;                      // first block of the chunk
+    const int c0 = blockIdx.x * TC;
+    const int t = threadIdx.x;
+    if (j >= block_start[G]) return;                             // uniform over the workgroup
+    int lo = 0, hi = G - 1;                                      // group = last g with block_start[g] <= j
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (block_start[mid] <= j) lo = mid;
@@ -167,31 +172,57 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     const int g = lo;
     const int gb = (int)min<int64_t>(max(offsets[g], 0), rows);
     const int ge = (int)min<int64_t>(max(offsets[g + 1], gb), rows);
-    const int r0 = gb + (j - block_start[g]) * kBlock;
-    const int n = max(0, min(kBlock, ge - r0));      // rows of this block (partial or none at a group's end)
-    float v[kBlock];
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) {
-        v[i] = (i < n) ? load_val(in + (in_row(row_index, in_rows, r0 + i) * ld_in + c) * ESIZE, ESIZE) : 0.f;
-        amax = fmaxf(amax, fabsf(v[i]));
-    }
-    const uint32_t byte = mx_scale_byte(amax);
-    const float inv = mx_inv_scale(byte);
-    u32x4 out[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) word |= e4m3_code(v[h * 16 + w * 4 + i] * inv) << (8 * i);
-            out[h][w] = word;
+    const int jb = j - block_start[g];                          // block index inside the group
+    const int nbg = block_start[g + 1] - block_start[g];        // the group's blocks (row stride / 32)
+    const int r0 = gb + jb * kBlock;
+    const int n = max(0, min(kGroupAlign * kBlock, ge - r0));   // valid rows of the chunk
+    // load: 128 rows x PITCH bytes in 16-byte pieces (rows past n read as zero)
+    constexpr int PIECES = PITCH / 16;
+    const int ncols = min(TC, cols - c0);
+    for (int idx = t; idx < kGroupAlign * kBlock * PIECES; idx += 256) {
+        const int i = idx / PIECES, pc = idx % PIECES;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (i < n && pc * 16 < ncols * ESIZE) {
+            const int64_t r = in_row(row_index, in_rows, r0 + i);
+            v = *reinterpret_cast<const u32x4*>(in + (r * ld_in + c0) * ESIZE + pc * 16);
         }
-    uint8_t* dst = q + (int64_t)c * ld_q + (int64_t)j * kBlock;
-    *reinterpret_cast<u32x4*>(dst) = out[0];
-    *reinterpret_cast<u32x4*>(dst + 16) = out[1];
-    sc[(int64_t)c * ld_sc + j] = (uint8_t)byte;
+        *reinterpret_cast<u32x4*>(tile + i * PITCH + pc * 16) = v;
+    }
+    __syncthreads();
+    constexpr int TPC = 256 / TC;                                // threads per column (2 bf16, 4 fp32)
+    constexpr int BPT = kGroupAlign / TPC;                       // blocks per thread (2 bf16, 1 fp32)
+    const int col = t % TC, part = t / TC;
+    if (col >= ncols) return;
+    const int c = c0 + col;
+    const int64_t gbase = (int64_t)cols * block_start[g];      // the group's transposed block
+    uint8_t* dst = q + (gbase + (int64_t)c * nbg + jb + BPT * part) * kBlock;
+    uint8_t* sdst = sc + gbase + (int64_t)c * nbg + jb + BPT * part;
+#pragma unroll
+    for (int bb = 0; bb < BPT; ++bb) {
+        const int b = BPT * part + bb;
+        float v[kBlock];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) {
+            const char* e = tile + (b * kBlock + i) * PITCH + col * ESIZE;
+            v[i] = ESIZE == 2 ? __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(e) << 16)
+                              : *reinterpret_cast<const float*>(e);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+        const uint32_t byte = mx_scale_byte(amax);
+        const float inv = mx_inv_scale(byte);
+        sdst[bb] = (uint8_t)byte;
+        u32x4 out[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float* e = v + h * 16 + w * 4;
+                out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+            }
+        *reinterpret_cast<u32x4*>(dst + bb * kBlock) = out[0];
+        *reinterpret_cast<u32x4*>(dst + bb * kBlock + 16) = out[1];
+    }
 }
 
 }  // namespace
@@ -205,7 +236,8 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
                                               uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                               int32_t* block_start, void* workspace, size_t workspace_bytes,
                                               void* stream) {
-    if (rows < 0 || cols <= 0 || cols % moe::kBlock != 0 || cols > INT32_MAX / 2 || ld_in < cols) return MOE_EINVAL;
+    if (rows < 0 || cols <= 0 || cols > INT32_MAX / 2 || ld_in < cols) return MOE_EINVAL;
+    if (axis == 0 && cols % moe::kBlock != 0) return MOE_EINVAL;   // row-wise blocks run along cols
     if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
     if (axis != 0 && axis != 1) return MOE_EINVAL;
     if (!row_index) in_rows = rows;
@@ -233,20 +265,26 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
     const int64_t nblk_cap = moe::kGroupAlign * (moe::cdiv<int64_t>(rows, moe::kGroupAlign * moe::kBlock) + G);
     if (!workspace && !block_start) return MOE_EWORKSPACE;
     if (!block_start && workspace_bytes < moe_quant_workspace_bytes(G)) return MOE_EWORKSPACE;
-    if (!q || !scales || ld_q < nblk_cap * moe::kBlock || ld_scales < nblk_cap) return MOE_EINVAL;
+    // group-major output: the caller passes the capacity in blocks as ld_scales (and 32 times
+    // it as ld_q): q holds 32 * cols * nblk bytes, scales cols * nblk bytes
+    if (!q || !scales || ld_scales < nblk_cap || ld_q != 32 * ld_scales) return MOE_EINVAL;
     if (rows > 0 && !in) return MOE_EINVAL;
-    if (!moe_aligned16(q) || ld_q % 16 != 0) return MOE_EINVAL;
+    if (!moe_aligned16(q)) return MOE_EINVAL;
+    // 16-byte row loads and 4-byte scale words
+    if ((reinterpret_cast<uintptr_t>(in) & 15) || (ld_in * esize) % 16 || (cols * esize) % 16) return MOE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(scales) & 3) return MOE_EINVAL;
     int32_t* bs = block_start ? block_start : (int32_t*)workspace;
     hipLaunchKernelGGL(moe::quant_block_prefix_kernel, dim3(1), dim3(1024), 0, s, group_offsets, G, rows, bs);
     MOE_CHECK_LAUNCH();
     if (rows == 0) return MOE_OK;
-    const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, 256), (unsigned)nblk_cap);
+    const int tc = esize == 2 ? moe::kColTile : moe::kColTile / 2;
+    const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, tc), (unsigned)(nblk_cap / moe::kGroupAlign));
     if (esize == 2)
         hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, ld_q, scales, ld_scales);
+                           row_index, in_rows, group_offsets, G, bs, q, scales);
     else
         hipLaunchKernelGGL(moe::quant_cols_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, ld_q, scales, ld_scales);
+                           row_index, in_rows, group_offsets, G, bs, q, scales);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }

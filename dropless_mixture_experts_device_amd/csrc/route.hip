@@ -309,7 +309,7 @@ void launch_route_bf16(dim3 g, hipStream_t s, const void* x, const void* w, cons
 size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E) {
     if (T <= 0 || E <= 0 || !moe::route_uses_split(T, d, E)) return 0;
     return moe::ralign((size_t)moe::kRouteKS * T * E * 4) + moe::ralign((size_t)moe::kRouteKS * T * 4) +
-           moe::ralign((moe::kRouteKS + 1) * 4) + 256;
+           moe::ralign((moe::kRouteKS + 1) * 4) + moe_gemm_workspace_bytes(moe::kRouteKS);
 }
 
 extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
@@ -354,7 +354,7 @@ extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t d
         g.c_dtype = MOE_F32;
         g.ldc = E;
         g.epilogue = MOE_EPI_NONE;
-        const moe_status_t st = moe_grouped_gemm(&g, ws.gemm_ws, 256, stream);
+        const moe_status_t st = moe_grouped_gemm(&g, ws.gemm_ws, moe_gemm_workspace_bytes(moe::kRouteKS), stream);
         if (st != MOE_OK) return st;
         const int nq = moe::cdiv(E, 64);
         const dim3 tgrid((unsigned)moe::cdiv<int64_t>(T, moe::kTopkBT));

@@ -147,17 +147,19 @@ class MxWeights:
         L.moe_group_quant_mxfp8(w_down.view(G * d, f), self.q_dnT, self.s_dnT, axis=1, group_offsets=self.off_dn,
                                 block_start=self.bs)
 
+    # The column-wise quantiser writes each group's transposed block contiguously (group-major);
+    # with 2f and d multiples of 128 there is no padding, so the copies are plain [G, ., .] arrays.
     def gu_T(self):
         s = self.shape
         G, d, f2 = s.groups, s.d, 2 * s.f
-        return (self.q_guT.as_strided((G, d, f2), (f2, self.q_guT.stride(0), 1)),
-                self.s_guT.as_strided((G, d, f2 // 32), (f2 // 32, self.s_guT.stride(0), 1)))
+        return (self.q_guT.view(-1)[:G * d * f2].view(G, d, f2),
+                self.s_guT.view(-1)[:G * d * f2 // 32].view(G, d, f2 // 32))
 
     def dn_T(self):
         s = self.shape
         G, d, f = s.groups, s.d, s.f
-        return (self.q_dnT.as_strided((G, f, d), (d, self.q_dnT.stride(0), 1)),
-                self.s_dnT.as_strided((G, f, d // 32), (d // 32, self.s_dnT.stride(0), 1)))
+        return (self.q_dnT.view(-1)[:G * f * d].view(G, f, d),
+                self.s_dnT.view(-1)[:G * f * d // 32].view(G, f, d // 32))
 
 
 class MxBuffers(LayerBuffers):

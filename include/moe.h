@@ -129,13 +129,18 @@ moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t* topk_idx,
  * Ragged-K mode (ragged_k = 1; the weight gradients, whose contraction runs over the tokens
  * of each group: [Reading] contribution 3 on group-wise low precision, [Blog]
  * "Optimisations dropless MoE needs" on group-aware MXFP8). Every group has the same
- * M x N output and its own K range, given in 32-element MX blocks:
- *   C_g[m, n] = sum over k in [32*offsets[g], 32*offsets[g+1]) of A[m, k] * B[n, k]
- * for m < M, n < N, with C_g = C + g * c_group_stride elements. offsets is non-decreasing
- * with offsets[G] <= K/32 and every entry a multiple of 4 (128 elements), as the
- * column-wise quantiser's block_start is; a group with an empty range gets C_g = 0 written.
- * Only MXFP8 operands and epilogue NONE; a_rows must be NULL, A is [M, K] and B is [N, K]
- * (b_group_stride and b_scale_group_stride must be 0), c_group_stride >= M * ldc.
+ * M x N output and its own K range of n_g = offsets[g+1] - offsets[g] blocks of 32:
+ *   C_g[m, n] = sum over k < 32 n_g of A_g[m, k] * B_g[n, k]
+ * for m < M, n < N, with C_g = C + g * c_group_stride elements. The operands are the
+ * group-major output of moe_group_quant_mxfp8's column-wise mode: A_g is the row-major
+ * [M, 32 n_g] matrix at A + 32*M*offsets[g], B_g the [N, 32 n_g] matrix at
+ * B + 32*N*offsets[g], their scales [M, n_g] at a_scale + M*offsets[g] and [N, n_g] at
+ * b_scale + N*offsets[g]. offsets is non-decreasing with offsets[G] <= K/32 and every entry
+ * a multiple of 4 (128 elements), as the quantiser's block_start is; a group with an empty
+ * range gets C_g = 0 written. The leading dimensions state the capacity: lda = ldb = K,
+ * lda_scale = ldb_scale = K/32 (A holds M*K codes, B N*K). Only MXFP8 operands and epilogue
+ * NONE; a_rows must be NULL, A_rows = M, b_group_stride and b_scale_group_stride 0,
+ * c_group_stride >= M * ldc.
  */
 typedef struct moe_gemm_args {
     int32_t G;                  /* number of groups (>= 1)                                  */
@@ -233,7 +238,7 @@ moe_status_t moe_swiglu_backward(const void* dh, int64_t ld_dh, const void* gu, 
  * and each element x becomes the E4M3 code of x / 2^(s-127) rounded to nearest-even,
  * saturating at +-448 (bias 7, 3 mantissa bits, subnormal step 2^-9; the sign of zero kept).
  *
- *   in [rows, cols] (MOE_BF16 or MOE_F32, leading dimension ld_in), cols % 32 == 0.
+ *   in [rows, cols] (MOE_BF16 or MOE_F32, leading dimension ld_in); axis 0 needs cols % 32 == 0.
  *   row_index (device, [rows] int32, or NULL): logical row r is read from in row
  *     row_index[r] (clamped into [0, in_rows)), e.g. the permutation's src_token so that
  *     the permuted activations are quantised straight from the token-ordered input;
@@ -245,17 +250,22 @@ moe_status_t moe_swiglu_backward(const void* dh, int64_t ld_dh, const void* gu, 
  *     the tokens of each group): rows are partitioned into G groups by group_offsets
  *     (device, [G+1]); each column is cut into blocks of 32 consecutive rows inside one
  *     group, the last block of a group possibly partial (its missing rows count as zero);
- *     blocks never straddle groups. Output is TRANSPOSED so the blocked axis is
- *     contiguous: block j of column c has codes q[c, 32j .. 32j+31] (zero codes for the
- *     missing rows of a partial block) and scale scales[c, j]. Group g owns
- *     nb_g = 4 * ceil(m_g/128) blocks j = block_start[g] .. block_start[g+1]-1
- *     (block_start[g] = sum over g' < g of nb_g'), so every group starts on a 128-element
- *     boundary (one MXFP8 GEMM K slice); the blocks past a group's last row are all zero
- *     (codes 0, scale byte 0) and add nothing to a product.
+ *     blocks never straddle groups. Output is TRANSPOSED per group so the blocked axis is
+ *     contiguous, and GROUP-MAJOR: group g owns nb_g = 4 * ceil(m_g/128) blocks, numbered
+ *     block_start[g] .. block_start[g+1]-1 (block_start[g] = sum over g' < g of nb_g'), so
+ *     every group starts on a 128-element boundary (one MXFP8 GEMM K slice); its codes are a
+ *     row-major [cols, 32*nb_g] matrix at q + 32*cols*block_start[g] (block i of column c in
+ *     columns 32i .. 32i+31; zero codes for the missing rows of a partial block) and its
+ *     scales a [cols, nb_g] matrix at scales + cols*block_start[g]. Blocks past a group's
+ *     last row are all zero (codes 0, scale byte 0) and add nothing to a product.
  *     block_start (device, [G+1]) is written when not NULL, else kept in workspace
- *     (moe_workspace_bytes(MOE_OP_QUANT, 0, 0, 0, 0, G) bytes). Capacities:
- *     ld_q >= 32 * nblk, ld_scales >= nblk with nblk = 4 * (ceil(rows/128) + G).
- *   q 16-byte aligned, ld_q % 16 == 0. Deterministic; no floating-point atomics.
+ *     (moe_workspace_bytes(MOE_OP_QUANT, 0, 0, 0, 0, G) bytes). Capacity: ld_scales is the
+ *     capacity in blocks, nblk <= ld_scales with nblk = 4 * (ceil(rows/128) + G), and
+ *     ld_q == 32 * ld_scales; q holds 32 * cols * ld_scales bytes and scales
+ *     cols * ld_scales bytes (the sizes of [cols, 32*nblk] and [cols, nblk] matrices);
+ *     in 16-byte aligned with ld_in and cols spanning multiples of 16 bytes, scales 4-byte
+ *     aligned.
+ *   q 16-byte aligned (axis 0 also ld_q % 16 == 0). Deterministic; no floating-point atomics.
  */
 moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
                                    const int32_t* row_index, int64_t in_rows,

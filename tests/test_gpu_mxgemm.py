@@ -92,22 +92,27 @@ def test_mx_gemm_quantised_random_within_tolerance(L, epi):
 
 
 def test_mx_gemm_ragged_k_on_grid_bit_exact(L):
-    """Weight-gradient form: C[g] = A[:, K_g] @ B[:, K_g]^T over each group's own block range
-    (multiples of 4 blocks, as the column-wise quantiser lays them out), with an empty range
-    whose C[g] must come back as zeros, and M, N that leave partial tiles."""
+    """Weight-gradient form: C[g] = A_g @ B_g^T over each group's own blocks (multiples of 4
+    blocks), the operands in the column-wise quantiser's group-major layout (group g's
+    [M, 32 n_g] block at 32*M*offsets[g]), with an empty range whose C[g] must come back as
+    zeros, and M, N that leave partial tiles."""
     blocks = np.array([0, 4, 4, 12, 16, 28], np.int32)          # group K ranges in 32-element blocks
     G, M, N, K = len(blocks) - 1, 192, 320, 32 * int(blocks[-1])
-    A, As = _grid_operand((M, K), 11)
-    B, Bs = _grid_operand((N, K), 12)
+    parts = [(_grid_operand((M, 32 * int(blocks[g + 1] - blocks[g])), 11 + g),
+              _grid_operand((N, 32 * int(blocks[g + 1] - blocks[g])), 31 + g)) for g in range(G)]
+    flat = lambda arrs, rows, width: np.concatenate([x.reshape(-1) for x in arrs]).reshape(rows, width)
+    A = flat([p[0][0] for p in parts], M, K)
+    As = flat([p[0][1] for p in parts], M, K // 32)
+    B = flat([p[1][0] for p in parts], N, K)
+    Bs = flat([p[1][1] for p in parts], N, K // 32)
     C = torch.full((G, M, N), float("nan"), dtype=torch.float32, device="cuda")
     L.moe_grouped_gemm(_u8(A), _u8(B), C, dev_i32(blocks), L.MOE_EPI_NONE, workspace=_ws(L, G),
                        a_scale=_u8(As), b_scale=_u8(Bs), ragged_k=True)
     torch.cuda.synchronize()
-    Ad, Bd = _dequant(A, As), _dequant(B, Bs)
     got = host(C)
     for g in range(G):
-        lo, hi = 32 * int(blocks[g]), 32 * int(blocks[g + 1])
-        np.testing.assert_array_equal(got[g], Ad[:, lo:hi] @ Bd[:, lo:hi].T, err_msg=f"group {g}")
+        (Ag, Ags), (Bg, Bgs) = parts[g]
+        np.testing.assert_array_equal(got[g], _dequant(Ag, Ags) @ _dequant(Bg, Bgs).T, err_msg=f"group {g}")
 
 
 def test_mx_wgrad_quantised_within_tolerance(L):

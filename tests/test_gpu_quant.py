@@ -69,34 +69,47 @@ def _colwise(L, a, offsets, dtype="bf16", row_index=None):
     L.moe_group_quant_mxfp8(x, q, s, axis=1, group_offsets=dev_i32(offsets), block_start=bs,
                             row_index=None if row_index is None else dev_i32(row_index))
     torch.cuda.synchronize()
-    return q.cpu().numpy(), s.cpu().numpy(), bs.cpu().numpy()
+    return q.cpu().numpy().reshape(-1), s.cpu().numpy().reshape(-1), bs.cpu().numpy()
 
 
-def _check_colwise(a, offsets, q, s, bs):
+def _group_blocks(qf, sf, bs, cols, g):
+    """Group g's transposed block of the group-major layout: codes [cols, 32 n_g] starting at
+    byte 32*cols*block_start[g], scales [cols, n_g] at cols*block_start[g]."""
+    b0, b1 = int(bs[g]), int(bs[g + 1])
+    return (qf[32 * cols * b0:32 * cols * b1].reshape(cols, 32 * (b1 - b0)),
+            sf[cols * b0:cols * b1].reshape(cols, b1 - b0))
+
+
+def _check_colwise(a, offsets, qf, sf, bs, cols=None, col_subset=None):
+    """a: the input columns checked ([rows, len(col_subset)] when a subset is given)."""
     off = np.asarray(offsets, np.int64)
     nb = 4 * (-(-np.diff(off) // 128))
     np.testing.assert_array_equal(bs, np.concatenate([[0], np.cumsum(nb)]))
+    cols = a.shape[1] if cols is None else cols
+    sel = np.arange(cols) if col_subset is None else np.asarray(col_subset)
     codes, scales, _ = O.mx_quantize_colwise_grouped(a, off)
     for g in range(len(off) - 1):
         lo, hi = int(off[g]), int(off[g + 1])
         m = hi - lo
+        qg, sg = _group_blocks(qf, sf, bs, cols, g)
+        qg, sg = qg[sel], sg[sel]
         for i in range(int(nb[g])):
-            j = int(bs[g]) + i
-            blk = q[:, 32 * j:32 * j + 32]
+            blk = qg[:, 32 * i:32 * i + 32]
             if 32 * i >= m:      # alignment block past the group's rows
-                assert np.all(s[:, j] == 0) and np.all(blk == 0), f"group {g} block {i} must be all zero"
+                assert np.all(sg[:, i] == 0) and np.all(blk == 0), f"group {g} block {i} must be all zero"
                 continue
             n = min(32, m - 32 * i)
-            np.testing.assert_array_equal(s[:, j], scales[g][i], err_msg=f"group {g} block {i}")
+            np.testing.assert_array_equal(sg[:, i], scales[g][i], err_msg=f"group {g} block {i}")
             np.testing.assert_array_equal(blk[:, :n], codes[lo + 32 * i:lo + 32 * i + n].T)
             assert np.all(blk[:, n:] == 0), "padding rows of a partial block must be zero codes"
 
 
-@pytest.mark.parametrize("sizes,cols", [([0, 1, 33, 0, 100, 64, 31], 96), ([5], 64), ([300, 0, 0], 320)])
-def test_quant_colwise_grouped_bit_exact(L, sizes, cols):
+@pytest.mark.parametrize("sizes,cols,dtype", [([0, 1, 33, 0, 100, 64, 31], 96, "bf16"), ([5], 64, "bf16"),
+                                              ([300, 0, 0], 320, "bf16"), ([0, 1, 33, 0, 200, 64, 31], 200, "f32")])
+def test_quant_colwise_grouped_bit_exact(L, sizes, cols, dtype):
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    a = _nasty(int(off[-1]), cols, cols + len(sizes))
-    q, s, bs = _colwise(L, a, off)
+    a = _nasty(int(off[-1]), cols, cols + len(sizes), dtype)
+    q, s, bs = _colwise(L, a, off, dtype)
     _check_colwise(a, off, q, s, bs)
 
 
@@ -144,5 +157,40 @@ def test_quant_dsv3_shapes_sampled(L):
     np.testing.assert_array_equal(q[rs_t].cpu().numpy(), wq)
     c_s = np.unique(np.concatenate([[0, cols - 1], rng.integers(0, cols, 6)]))
     full_cols = mi.randn_np(w.seed, mi.D_OUT, 9, rows, cols, 1.0, "bf16", col_index=c_s).astype(np.float64)
-    cs_t = torch.from_numpy(c_s).cuda()
-    _check_colwise(full_cols, off, qc[cs_t].cpu().numpy(), sc[cs_t].cpu().numpy(), bs.cpu().numpy())
+    _check_colwise(full_cols, off, qc.cpu().numpy().reshape(-1), sc.cpu().numpy().reshape(-1), bs.cpu().numpy(),
+                   cols=cols, col_subset=c_s)
+
+
+def _rounding_sweep():
+    """Blocks of 32 whose maximum is 1.0 (scale byte 119: values are multiplied by 2^8 before
+    rounding), the other 31 elements sweeping every E4M3 rounding case: the subnormal range
+    in half-quantum steps (ties between subnormal codes included), and in every normal
+    binade the midpoints between adjacent codes and the bf16 values just either side of
+    them, in both signs. All values are exact in bf16."""
+    vals = [k * 2.0 ** -18 for k in range(0, 17)]                       # scaled k * 2^-10: subnormals
+    for e in range(-6, 8):
+        for m in range(8):
+            for d in (-1, 0, 1):
+                vals.append((1.0 + (2 * m + 1) / 16.0 + d / 128.0) * 2.0 ** (e - 8))
+    vals = [v for v in vals if v <= 1.0]
+    vals = np.array(vals + [-v for v in vals])
+    n_rows = -(-len(vals) // 31)
+    n_rows += (-n_rows) % 8                                              # columns of the transpose: 16-byte rows
+    a = np.zeros((n_rows, 32))
+    a[:, 0] = 1.0
+    flat = a[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    a[:, 1:] = flat.reshape(n_rows, 31)
+    return a
+
+
+def test_quant_rounding_sweep_bit_exact(L):
+    a = _rounding_sweep()
+    q, s = _rowwise(L, a)
+    wq, ws, _ = O.mx_quantize_rowwise(a)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(q, wq)
+    at = np.ascontiguousarray(a.T)                                       # the same blocks, column-wise
+    off = np.array([0, 32], np.int32)
+    qc, sc, bs = _colwise(L, at, off)
+    _check_colwise(at, off, qc, sc, bs)
