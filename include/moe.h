@@ -178,8 +178,10 @@ typedef struct moe_gemm_args {
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047. A, B, C, aux 16-byte
  * aligned; A and B rows (lda, ldb, b_group_stride) 16-byte multiples; ldc, ld_aux multiples
- * of 8; MXFP8 scale pointers and their strides 4-byte multiples. The args struct is read on
- * the host during the call only. */
+ * of 8; MXFP8 scale pointers and their strides 4-byte multiples. A (A_rows x lda) and one
+ * group's B (N or 2N rows x ldb) must each span less than 4 GiB (MOE_ENOTSUP otherwise: the
+ * loads use 32-bit offsets from the tile's base). The args struct is read on the host during
+ * the call only. */
 moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size_t workspace_bytes,
                               void* stream);
 
