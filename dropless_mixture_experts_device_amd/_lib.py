@@ -53,6 +53,9 @@ _lib.moe_combine.restype = _i32
 _lib.moe_group_quant_mxfp8.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _i32, _vp, _i64, _vp, _i64,
                                        _vp, _vp, _sz, _vp]
 _lib.moe_group_quant_mxfp8.restype = _i32
+_lib.moe_group_quant_mxfp8_dual.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _vp, _i64,
+                                            _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
+_lib.moe_group_quant_mxfp8_dual.restype = _i32
 
 _lib.moe_combine_backward.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]
 _lib.moe_combine_backward.restype = _i32
@@ -60,7 +63,7 @@ _lib.moe_swiglu_backward.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp
 _lib.moe_swiglu_backward.restype = _i32
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
-            "moe_group_quant_mxfp8", "moe_combine_backward", "moe_swiglu_backward")
+            "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward")
 
 
 class MoeError(RuntimeError):
@@ -227,3 +230,17 @@ def moe_group_quant_mxfp8(x, q, scales, axis: int = 0, group_offsets=None, block
     _check("moe_group_quant_mxfp8", _lib.moe_group_quant_mxfp8(
         _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(row_index), in_rows, _ptr(group_offsets), G, axis,
         _ptr(q), q.stride(0), _ptr(scales), scales.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
+
+
+def moe_group_quant_mxfp8_dual(x, q_row, s_row, q_col, s_col, group_offsets, block_start=None, workspace=None,
+                               stream=None, row_index=None, rows=None):
+    """Both MXFP8 copies from one read of x: the row-wise copy into q_row / s_row (as axis 0 of
+    moe_group_quant_mxfp8) and the group-aware column-wise copy into q_col / s_col (as axis 1)."""
+    in_rows, cols = x.shape
+    if rows is None:
+        rows = in_rows if row_index is None else row_index.numel()
+    ws, wsb = _ws(workspace)
+    _check("moe_group_quant_mxfp8_dual", _lib.moe_group_quant_mxfp8_dual(
+        _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(row_index), in_rows, _ptr(group_offsets),
+        group_offsets.numel() - 1, _ptr(q_row), q_row.stride(0), _ptr(s_row), s_row.stride(0), _ptr(q_col),
+        q_col.stride(0), _ptr(s_col), s_col.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))

@@ -54,8 +54,29 @@ __device__ __forceinline__ void store8(char* p, const float (&v)[8]) {
     }
 }
 
-// One workgroup per token; each thread owns 8 consecutive columns at a time.
 template <int ESIZE>
+__device__ __forceinline__ void cvt8(const u32x4& a, const u32x4& b, float (&v)[8]) {
+    if (ESIZE == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(a[i] << 16);
+            v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    }
+}
+
+// One workgroup per token; each thread owns 8 consecutive columns at a time. KK > 0 is the
+// number of routed rows per token known at compile time: then the KK row loads (and the
+// shared expert's) are all issued before the first one is used, so a lane keeps KK+1 loads
+// in flight instead of one. The fp32 sum runs in the same order either way (slot 0 .. k-1,
+// then the shared row), so every KK gives the same bits.
+template <int ESIZE, int KK>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __restrict__ y,
                                                                const float* __restrict__ topk_w,
                                                                const int32_t* __restrict__ row_of,
@@ -72,6 +93,40 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __res
     __syncthreads();
     const int ngroups = d / 8;
     const int64_t rowbytes = (int64_t)d * ESIZE;
+    if constexpr (KK > 0) {
+        for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
+            const int64_t col = (int64_t)c * 8 * ESIZE;
+            u32x4 ra[KK], rb[KK], sa = {}, sb = {};
+#pragma unroll
+            for (int j = 0; j < KK; ++j) {
+                const char* src = y + rows[j] * rowbytes + col;
+                ra[j] = *reinterpret_cast<const u32x4*>(src);
+                if (ESIZE == 4) rb[j] = *reinterpret_cast<const u32x4*>(src + 16);
+            }
+            if (y_shared != nullptr) {
+                const char* src = y_shared + t * rowbytes + col;
+                sa = *reinterpret_cast<const u32x4*>(src);
+                if (ESIZE == 4) sb = *reinterpret_cast<const u32x4*>(src + 16);
+            }
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KK; ++j) {
+                float v[8];
+                cvt8<ESIZE>(ra[j], rb[j], v);
+                const float w = wts[j];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+            }
+            if (y_shared != nullptr) {
+                float v[8];
+                cvt8<ESIZE>(sa, sb, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += v[i];
+            }
+            store8<ESIZE>(out + t * rowbytes + col, acc);
+        }
+        return;
+    }
     for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
@@ -173,6 +228,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_bwd_kernel(const char* _
     }
 }
 
+template <int ESIZE>
+void launch_combine(int k, const char* y, const float* topk_w, const int32_t* row_of, const char* y_shared,
+                    int64_t T, int64_t d, char* out, hipStream_t s) {
+    const dim3 grid((unsigned)T), block(kCombThreads);
+    switch (k) {
+        case 1: hipLaunchKernelGGL((combine_kernel<ESIZE, 1>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+        case 2: hipLaunchKernelGGL((combine_kernel<ESIZE, 2>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+        case 4: hipLaunchKernelGGL((combine_kernel<ESIZE, 4>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+        case 6: hipLaunchKernelGGL((combine_kernel<ESIZE, 6>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+        case 8: hipLaunchKernelGGL((combine_kernel<ESIZE, 8>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+        default: hipLaunchKernelGGL((combine_kernel<ESIZE, 0>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -210,12 +279,8 @@ extern "C" moe_status_t moe_combine(const void* y, int32_t dtype, const float* t
     if (!y || !row_of || !out) return MOE_EINVAL;
     if (!moe_aligned16(y) || !moe_aligned16(out) || (y_shared && !moe_aligned16(y_shared))) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    if (dtype == MOE_BF16)
-        hipLaunchKernelGGL(moe::combine_kernel<2>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
-                           (const char*)y, topk_w, row_of, (const char*)y_shared, (int)T, (int)d, k, (char*)out);
-    else
-        hipLaunchKernelGGL(moe::combine_kernel<4>, dim3((unsigned)T), dim3(moe::kCombThreads), 0, s,
-                           (const char*)y, topk_w, row_of, (const char*)y_shared, (int)T, (int)d, k, (char*)out);
+    if (dtype == MOE_BF16) moe::launch_combine<2>(k, (const char*)y, topk_w, row_of, (const char*)y_shared, T, d, (char*)out, s);
+    else moe::launch_combine<4>(k, (const char*)y, topk_w, row_of, (const char*)y_shared, T, d, (char*)out, s);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }

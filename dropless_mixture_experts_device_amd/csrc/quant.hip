@@ -147,18 +147,24 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
 // group starts on a multiple of 4 blocks) by kColTile columns. The rows are loaded with
 // coalesced 16-byte loads into LDS (read through row_index when given); then two threads own
 // each column, two blocks each: their maxima, scale bytes and codes, written as contiguous
-// 64-byte code segments and 2-byte scale pairs of the group's transposed block. A 32 KiB tile
+// 64-byte code segments and 2-byte scale pairs of the group's transposed block. A 34 KiB tile
 // keeps several workgroups resident per CU, so one's loads overlap another's arithmetic.
+// With q_row given, the same tile also yields the row-wise copy (blocks of 32 along each of
+// its valid rows, at the logical row index): both layouts from one read of the input. LDS
+// rows are padded by 16 bytes so that the row-wise pass's 16-byte reads of 16 rows at one
+// column offset land on distinct banks.
 constexpr int kColTile = 128;        // columns per workgroup (bf16; 64 for fp32)
 template <int ESIZE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, const int32_t* __restrict__ row_index,
                                                          int64_t in_rows, const int32_t* __restrict__ offsets, int G,
                                                          const int32_t* __restrict__ block_start,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                         uint8_t* __restrict__ q_row, int64_t ld_q_row,
+                                                         uint8_t* __restrict__ s_row, int64_t ld_s_row) {
     constexpr int TC = ESIZE == 2 ? kColTile : kColTile / 2;    // columns of this tile
-    constexpr int PITCH = TC * ESIZE;                            // LDS bytes per row (256)
-    __shared__ __attribute__((aligned(16))) char tile[kGroupAlign * kBlock * PITCH];   // 32 KiB
+    constexpr int PITCH = TC * ESIZE + 16;                       // LDS bytes per row (256 + pad)
+    __shared__ __attribute__((aligned(16))) char tile[kGroupAlign * kBlock * PITCH];   // 34 KiB
     const int j = blockIdx.y * kGroupAlign;                      // first block of the chunk
     const int c0 = blockIdx.x * TC;
     const int t = threadIdx.x;
@@ -189,6 +195,50 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
         *reinterpret_cast<u32x4*>(tile + i * PITCH + pc * 16) = v;
     }
     __syncthreads();
+    if (q_row != nullptr) {
+        // row-wise copy: unit u = (tile row u / RBK, row block u % RBK); consecutive threads
+        // write consecutive 32-byte code segments of one row
+        constexpr int RBK = TC / kBlock;                         // row blocks per tile row
+        constexpr int P16 = kBlock * ESIZE / 16;                 // 16-byte LDS reads per block
+        for (int u = t; u < kGroupAlign * kBlock * RBK; u += 256) {
+            const int i = u / RBK, b = u % RBK;
+            if (i >= n || b * kBlock >= ncols) continue;
+            const char* src = tile + i * PITCH + b * kBlock * ESIZE;
+            float v[kBlock];
+#pragma unroll
+            for (int c = 0; c < P16; ++c) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
+                if (ESIZE == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[c * 8 + 2 * e] = __uint_as_float(w[e] << 16);
+                        v[c * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[c * 4 + e] = __uint_as_float(w[e]);
+                }
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < kBlock; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            const uint32_t byte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(byte);
+            u32x4 out[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* e = v + h * 16 + w * 4;
+                    out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+                }
+            const int64_t r = r0 + i;                            // logical row
+            uint8_t* dst = q_row + r * ld_q_row + c0 + b * kBlock;
+            *reinterpret_cast<u32x4*>(dst) = out[0];
+            *reinterpret_cast<u32x4*>(dst + 16) = out[1];
+            s_row[r * ld_s_row + c0 / kBlock + b] = (uint8_t)byte;
+        }
+    }
     constexpr int TPC = 256 / TC;                                // threads per column (2 bf16, 4 fp32)
     constexpr int BPT = kGroupAlign / TPC;                       // blocks per thread (2 bf16, 1 fp32)
     const int col = t % TC, part = t / TC;
@@ -230,6 +280,42 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
 
 size_t moe_quant_workspace_bytes(int32_t G) { return ((size_t)(G < 1 ? 1 : G) + 1) * 4 + 255 & ~size_t(255); }
 
+// Shared host path of the column-wise mode (and of the dual mode when q_row is given).
+static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                  const int32_t* row_index, int64_t in_rows, const int32_t* group_offsets, int32_t G,
+                                  uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
+                                  uint8_t* q_row, int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                  int32_t* block_start, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    const int esize = dtype == MOE_BF16 ? 2 : 4;
+    if (G < 1 || !group_offsets || rows > INT32_MAX / 2) return MOE_EINVAL;
+    // blocks over all groups, upper bound: sum_g 4 ceil(m_g / 128) <= 4 (ceil(rows / 128) + G)
+    const int64_t nblk_cap = moe::kGroupAlign * (moe::cdiv<int64_t>(rows, moe::kGroupAlign * moe::kBlock) + G);
+    if (!workspace && !block_start) return MOE_EWORKSPACE;
+    if (!block_start && workspace_bytes < moe_quant_workspace_bytes(G)) return MOE_EWORKSPACE;
+    // group-major output: the caller passes the capacity in blocks as ld_scales (and 32 times
+    // it as ld_q): q holds 32 * cols * nblk bytes, scales cols * nblk bytes
+    if (!q || !scales || ld_scales < nblk_cap || ld_q != 32 * ld_scales) return MOE_EINVAL;
+    if (rows > 0 && !in) return MOE_EINVAL;
+    if (!moe_aligned16(q)) return MOE_EINVAL;
+    // 16-byte row loads and 4-byte scale words
+    if ((reinterpret_cast<uintptr_t>(in) & 15) || (ld_in * esize) % 16 || (cols * esize) % 16) return MOE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(scales) & 3) return MOE_EINVAL;
+    int32_t* bs = block_start ? block_start : (int32_t*)workspace;
+    hipLaunchKernelGGL(moe::quant_block_prefix_kernel, dim3(1), dim3(1024), 0, s, group_offsets, G, rows, bs);
+    MOE_CHECK_LAUNCH();
+    if (rows == 0) return MOE_OK;
+    const int tc = esize == 2 ? moe::kColTile : moe::kColTile / 2;
+    const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, tc), (unsigned)(nblk_cap / moe::kGroupAlign));
+    if (esize == 2)
+        hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
+                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row);
+    else
+        hipLaunchKernelGGL(moe::quant_cols_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
+                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
 extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, int64_t cols,
                                               int64_t ld_in, const int32_t* row_index, int64_t in_rows,
                                               const int32_t* group_offsets, int32_t G, int32_t axis,
@@ -260,31 +346,24 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
         return MOE_OK;
     }
     // axis 1: group-aware blocks of rows, transposed output
-    if (G < 1 || !group_offsets || rows > INT32_MAX / 2) return MOE_EINVAL;
-    // blocks over all groups, upper bound: sum_g 4 ceil(m_g / 128) <= 4 (ceil(rows / 128) + G)
-    const int64_t nblk_cap = moe::kGroupAlign * (moe::cdiv<int64_t>(rows, moe::kGroupAlign * moe::kBlock) + G);
-    if (!workspace && !block_start) return MOE_EWORKSPACE;
-    if (!block_start && workspace_bytes < moe_quant_workspace_bytes(G)) return MOE_EWORKSPACE;
-    // group-major output: the caller passes the capacity in blocks as ld_scales (and 32 times
-    // it as ld_q): q holds 32 * cols * nblk bytes, scales cols * nblk bytes
-    if (!q || !scales || ld_scales < nblk_cap || ld_q != 32 * ld_scales) return MOE_EINVAL;
-    if (rows > 0 && !in) return MOE_EINVAL;
-    if (!moe_aligned16(q)) return MOE_EINVAL;
-    // 16-byte row loads and 4-byte scale words
-    if ((reinterpret_cast<uintptr_t>(in) & 15) || (ld_in * esize) % 16 || (cols * esize) % 16) return MOE_EINVAL;
-    if (reinterpret_cast<uintptr_t>(scales) & 3) return MOE_EINVAL;
-    int32_t* bs = block_start ? block_start : (int32_t*)workspace;
-    hipLaunchKernelGGL(moe::quant_block_prefix_kernel, dim3(1), dim3(1024), 0, s, group_offsets, G, rows, bs);
-    MOE_CHECK_LAUNCH();
-    if (rows == 0) return MOE_OK;
-    const int tc = esize == 2 ? moe::kColTile : moe::kColTile / 2;
-    const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, tc), (unsigned)(nblk_cap / moe::kGroupAlign));
-    if (esize == 2)
-        hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, scales);
-    else
-        hipLaunchKernelGGL(moe::quant_cols_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, scales);
-    MOE_CHECK_LAUNCH();
-    return MOE_OK;
+    return quant_colwise(in, dtype, rows, cols, ld_in, row_index, in_rows, group_offsets, G, q, ld_q, scales,
+                         ld_scales, nullptr, 0, nullptr, 0, block_start, workspace, workspace_bytes, s);
+}
+
+extern "C" moe_status_t moe_group_quant_mxfp8_dual(const void* in, int32_t dtype, int64_t rows, int64_t cols,
+                                                   int64_t ld_in, const int32_t* row_index, int64_t in_rows,
+                                                   const int32_t* group_offsets, int32_t G, uint8_t* q_row,
+                                                   int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                                   uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col,
+                                                   int64_t ld_s_col, int32_t* block_start, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+    if (rows < 0 || cols <= 0 || cols > INT32_MAX / 2 || ld_in < cols || cols % moe::kBlock != 0) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (!row_index) in_rows = rows;
+    else if (in_rows <= 0 && rows > 0) return MOE_EINVAL;
+    if (!q_row || !s_row || ld_q_row < cols || ld_s_row < cols / moe::kBlock) return MOE_EINVAL;
+    if (!moe_aligned16(q_row) || ld_q_row % 16 != 0) return MOE_EINVAL;
+    return quant_colwise(in, dtype, rows, cols, ld_in, row_index, in_rows, group_offsets, G, q_col, ld_q_col, s_col,
+                         ld_s_col, q_row, ld_q_row, s_row, ld_s_row, block_start, workspace, workspace_bytes,
+                         (hipStream_t)stream);
 }

@@ -135,17 +135,15 @@ class MxWeights:
         self.bs = torch.empty((G + 1,), dtype=torch.int32, device=dev)
 
     def quantise(self, w_gu, w_down):
+        """Both copies of each weight stack from one read of it (2f and d are multiples of 128,
+        so group g's transposed blocks start at g*2f/32 and g*d/32)."""
         s = self.shape
         G, d, f = s.groups, s.d, s.f
-        L.moe_group_quant_mxfp8(w_gu.view(G * 2 * f, d), self.q_gu.view(G * 2 * f, d),
-                                self.s_gu.view(G * 2 * f, d // 32), axis=0)
-        L.moe_group_quant_mxfp8(w_down.view(G * d, f), self.q_dn.view(G * d, f), self.s_dn.view(G * d, f // 32),
-                                axis=0)
-        # 2f and d are multiples of 128, so group g's transposed blocks start at g*2f/32 (g*d/32)
-        L.moe_group_quant_mxfp8(w_gu.view(G * 2 * f, d), self.q_guT, self.s_guT, axis=1, group_offsets=self.off_gu,
-                                block_start=self.bs)
-        L.moe_group_quant_mxfp8(w_down.view(G * d, f), self.q_dnT, self.s_dnT, axis=1, group_offsets=self.off_dn,
-                                block_start=self.bs)
+        L.moe_group_quant_mxfp8_dual(w_gu.view(G * 2 * f, d), self.q_gu.view(G * 2 * f, d),
+                                     self.s_gu.view(G * 2 * f, d // 32), self.q_guT, self.s_guT, self.off_gu,
+                                     block_start=self.bs)
+        L.moe_group_quant_mxfp8_dual(w_down.view(G * d, f), self.q_dn.view(G * d, f), self.s_dn.view(G * d, f // 32),
+                                     self.q_dnT, self.s_dnT, self.off_dn, block_start=self.bs)
 
     # The column-wise quantiser writes each group's transposed block contiguously (group-major);
     # with 2f and d multiples of 128 there is no padding, so the copies are plain [G, ., .] arrays.
@@ -201,7 +199,8 @@ def _nomark(name):
 def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False, mark=None):
     """MXFP8 forward: route and permute as in bf16, x quantised row-wise once per token (the
     GEMM gathers codes and scale rows through src_token), GEMM 1 + SwiGLU saving G and U,
-    H quantised row-wise, GEMM 2, combine. mw must hold this step's quantised weights.
+    H quantised row-wise (and, in the same pass, column-wise for the backward's wgrad 2),
+    GEMM 2, combine. mw must hold this step's quantised weights.
     routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment.
     mark(name), if given, is called after each stage (e.g. to record a timing event)."""
     mark = mark or _nomark
@@ -215,7 +214,7 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
     L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, aux=b.GU,
                        workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu)
     mark("gemm1_swiglu")
-    L.moe_group_quant_mxfp8(b.H, b.q_h, b.s_h, axis=0)
+    L.moe_group_quant_mxfp8_dual(b.H, b.q_h, b.s_h, b.qc_h, b.sc_h, b.offsets, block_start=b.bs)
     mark("quant_h")
     L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
                        b_scale=mw.s_dn)
@@ -238,31 +237,27 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None)
                            dy_shared=b.dY[tk:] if s.shared else None, dw=b.dw)
     mark("combine_bwd")
     # dgrad 2 and wgrad 2
-    L.moe_group_quant_mxfp8(b.dY, b.q_dy, b.s_dy, axis=0)
+    L.moe_group_quant_mxfp8_dual(b.dY, b.q_dy, b.s_dy, b.qc_dy, b.sc_dy, b.offsets, block_start=b.bs)
     mark("quant_dy")
     q_dnT, s_dnT = mw.dn_T()
     L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
                        b_scale=s_dnT)
     mark("dgrad2")
-    L.moe_group_quant_mxfp8(b.dY, b.qc_dy, b.sc_dy, axis=1, group_offsets=b.offsets, block_start=b.bs)
-    L.moe_group_quant_mxfp8(b.H, b.qc_h, b.sc_h, axis=1, group_offsets=b.offsets, block_start=b.bs)
-    mark("quant_cols_dy_h")
     L.moe_grouped_gemm(b.qc_dy, b.qc_h, b.dW_down, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dy, b_scale=b.sc_h, ragged_k=True)
     mark("wgrad2")
     # SwiGLU backward, dgrad 1 and wgrad 1
     L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
     mark("swiglu_bwd")
-    L.moe_group_quant_mxfp8(b.dGU, b.q_dgu, b.s_dgu, axis=0)
+    L.moe_group_quant_mxfp8_dual(b.dGU, b.q_dgu, b.s_dgu, b.qc_dgu, b.sc_dgu, b.offsets, block_start=b.bs)
     mark("quant_dgu")
     q_guT, s_guT = mw.gu_T()
     L.moe_grouped_gemm(b.q_dgu, q_guT, b.dXp, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_dgu,
                        b_scale=s_guT)
     mark("dgrad1")
-    L.moe_group_quant_mxfp8(b.dGU, b.qc_dgu, b.sc_dgu, axis=1, group_offsets=b.offsets, block_start=b.bs)
     L.moe_group_quant_mxfp8(x, b.qc_x, b.sc_x, axis=1, group_offsets=b.offsets, block_start=b.bs,
                             row_index=b.src_token)
-    mark("quant_cols_dgu_x")
+    mark("quant_cols_x")
     L.moe_grouped_gemm(b.qc_dgu, b.qc_x, b.dW_gu, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dgu, b_scale=b.sc_x, ragged_k=True)
     mark("wgrad1")

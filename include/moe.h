@@ -275,6 +275,29 @@ moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, 
                                    uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                    int32_t* block_start, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_group_quant_mxfp8_dual -- both MXFP8 copies of one operand from a single read of it:
+ * the row-wise copy (axis 0 above) and the group-aware column-wise copy (axis 1 above).
+ * [Blog] "Optimisations dropless MoE needs": an expert GEMM operand of the MXFP8 training step
+ * is contracted along its rows in one product and along its columns (each group's tokens) in
+ * another, so both quantisations are needed; [Reading] contribution 3: group quantisation.
+ *
+ *   Arguments as in moe_group_quant_mxfp8 with axis 1 (in, dtype, rows, cols, ld_in,
+ *   row_index, in_rows, group_offsets, G, block_start, workspace): q_col / ld_q_col /
+ *   s_col / ld_s_col take the column-wise output with that mode's layout and capacity rules;
+ *   q_row [rows, ld_q_row >= cols] and s_row [rows, ld_s_row >= cols/32] take the row-wise
+ *   output of logical row r (read through row_index like the column-wise copy). cols % 32 == 0;
+ *   q_row 16-byte aligned with ld_q_row % 16 == 0.
+ *   Every code and scale byte equals what the two single-axis calls write. Rows outside
+ *   every group (offsets[G] < rows) get neither copy.
+ */
+moe_status_t moe_group_quant_mxfp8_dual(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                        const int32_t* row_index, int64_t in_rows, const int32_t* group_offsets,
+                                        int32_t G, uint8_t* q_row, int64_t ld_q_row, uint8_t* s_row,
+                                        int64_t ld_s_row, uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col,
+                                        int64_t ld_s_col, int32_t* block_start, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -137,3 +137,18 @@ def test_host_argument_errors_backward_and_quant(lib):
              None) == L.MOE_EINVAL
     assert q(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, 1, fake, 32 * cap, fake, cap, None, None, 0,
              None) == L.MOE_EWORKSPACE
+    # dual quantiser: cols % 32, row-wise leading dimensions and pointers, column-wise capacity,
+    # workspace; checks run before anything is enqueued
+    qd = L._lib.moe_group_quant_mxfp8_dual
+    assert qd(fake, L.MOE_BF16, 64, 48, 48, None, 0, fake, 3, fake, 48, fake, 2, fake, 32 * cap, fake, cap, fake,
+              None, 0, None) == L.MOE_EINVAL
+    assert qd(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, fake, 32, fake, 2, fake, 32 * cap, fake, cap, fake,
+              None, 0, None) == L.MOE_EINVAL
+    assert qd(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, None, 64, fake, 2, fake, 32 * cap, fake, cap, fake,
+              None, 0, None) == L.MOE_EINVAL
+    assert qd(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, fake, 64, fake, 2, fake, 32 * cap - 32, fake, cap,
+              fake, None, 0, None) == L.MOE_EINVAL
+    assert qd(fake, L.MOE_BF16, 64, 64, 64, None, 0, fake, 3, fake, 64, fake, 2, fake, 32 * cap, fake, cap, None,
+              None, 0, None) == L.MOE_EWORKSPACE
+    assert qd(fake, L.MOE_E4M3, 64, 64, 64, None, 0, fake, 3, fake, 64, fake, 2, fake, 32 * cap, fake, cap, fake,
+              None, 0, None) == L.MOE_ENOTSUP

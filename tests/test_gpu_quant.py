@@ -194,3 +194,101 @@ def test_quant_rounding_sweep_bit_exact(L):
     off = np.array([0, 32], np.int32)
     qc, sc, bs = _colwise(L, at, off)
     _check_colwise(at, off, qc, sc, bs)
+
+
+def _dual(L, a, offsets, dtype="bf16", row_index=None):
+    """Both copies from moe_group_quant_mxfp8_dual, sentinel-filled so unwritten bytes show."""
+    G = len(offsets) - 1
+    rows = a.shape[0] if row_index is None else len(row_index)
+    cols = a.shape[1]
+    nblk = L.quant_col_blocks(rows, G)
+    x = dev(a, dtype)
+    qr = torch.full((rows, cols), 0xAB, dtype=torch.uint8, device="cuda")
+    sr = torch.full((rows, cols // 32), 0xAB, dtype=torch.uint8, device="cuda")
+    qc = torch.full((cols, 32 * nblk), 0xAB, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cols, nblk), 0xAB, dtype=torch.uint8, device="cuda")
+    bs = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8_dual(x, qr, sr, qc, sc, dev_i32(offsets), block_start=bs,
+                                 row_index=None if row_index is None else dev_i32(row_index))
+    torch.cuda.synchronize()
+    return (qr.cpu().numpy(), sr.cpu().numpy(), qc.cpu().numpy().reshape(-1), sc.cpu().numpy().reshape(-1),
+            bs.cpu().numpy())
+
+
+@pytest.mark.parametrize("sizes,cols,dtype", [([0, 1, 33, 0, 100, 64, 31], 96, "bf16"), ([5], 64, "bf16"),
+                                              ([300, 0, 0], 320, "bf16"), ([0, 1, 33, 0, 200, 64, 31], 224, "f32"),
+                                              ([128, 256, 128], 160, "bf16")])
+def test_quant_dual_bit_exact(L, sizes, cols, dtype):
+    """Both copies of the one-pass quantiser against the oracle: row-wise codes and scales of
+    every row, and the group-major column-wise layout (alignment blocks all zero)."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    a = _nasty(int(off[-1]), cols, 3 * cols + len(sizes), dtype)
+    qr, sr, qc, sc, bs = _dual(L, a, off, dtype)
+    wq, ws, _ = O.mx_quantize_rowwise(a)
+    np.testing.assert_array_equal(sr, ws)
+    np.testing.assert_array_equal(qr, wq)
+    _check_colwise(a, off, qc, sc, bs)
+
+
+def test_quant_dual_gather_matches_single_calls(L):
+    """Through a row gather (repeated rows, an empty group): the dual call writes exactly the
+    bytes of the two single-axis calls."""
+    a = _nasty(90, 192, 8)
+    ri = np.random.Generator(np.random.PCG64(9)).integers(0, 90, 333).astype(np.int32)
+    off = np.array([0, 70, 70, 171, 333], np.int32)
+    qr, sr, qc, sc, bs = _dual(L, a, off, row_index=ri)
+    x = dev(a, "bf16")
+    q1 = torch.full((333, 192), 0xAB, dtype=torch.uint8, device="cuda")
+    s1 = torch.full((333, 6), 0xAB, dtype=torch.uint8, device="cuda")
+    L.moe_group_quant_mxfp8(x, q1, s1, axis=0, row_index=dev_i32(ri))
+    q2, s2, bs2 = _colwise(L, a, off, row_index=ri)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(qr, q1.cpu().numpy())
+    np.testing.assert_array_equal(sr, s1.cpu().numpy())
+    np.testing.assert_array_equal(qc, q2)
+    np.testing.assert_array_equal(sc, s2)
+    np.testing.assert_array_equal(bs, bs2)
+
+
+def test_quant_dual_expert_weight_stack(L):
+    """The layer's use on a stack of expert weights (8 groups of 2f = 4096 rows, d = 7168, the
+    DeepSeek-V3 gate/up shape for 8 experts): both copies equal the single-axis calls byte for
+    byte, and sampled rows / columns equal the oracle."""
+    G, R, C = 8, 4096, 7168
+    w = torch.empty((G * R, C), dtype=torch.bfloat16, device="cuda")
+    mi.randn_torch(11, mi.X, 0, G * R, C, 0.02, "bf16", "cuda", out=w)
+    off = torch.arange(G + 1, dtype=torch.int32, device="cuda") * R
+    nblk = L.quant_col_blocks(G * R, G)
+    qr = torch.empty((G * R, C), dtype=torch.uint8, device="cuda")
+    sr = torch.empty((G * R, C // 32), dtype=torch.uint8, device="cuda")
+    qc = torch.empty((C, 32 * nblk), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((C, nblk), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8_dual(w, qr, sr, qc, sc, off, block_start=bs)
+    q1, s1 = torch.empty_like(qr), torch.empty_like(sr)
+    L.moe_group_quant_mxfp8(w, q1, s1, axis=0)
+    assert torch.equal(qr, q1) and torch.equal(sr, s1)
+    del q1, s1
+    q2, s2 = torch.empty_like(qc), torch.empty_like(sc)
+    L.moe_group_quant_mxfp8(w, q2, s2, axis=1, group_offsets=off, block_start=torch.empty_like(bs))
+    used = G * R // 32                                  # blocks written; the capacity holds 4 G more
+    assert torch.equal(qc.view(-1)[:32 * C * used], q2.view(-1)[:32 * C * used])
+    assert torch.equal(sc.view(-1)[:C * used], s2.view(-1)[:C * used])
+    assert bs.cpu().tolist() == [g * used // G for g in range(G + 1)]
+    del q2, s2
+    g = np.random.Generator(np.random.PCG64(12))
+    rws = np.unique(np.concatenate([[0, G * R - 1], g.integers(0, G * R, 40)]))
+    a_rows = mi.randn_np(11, mi.X, 0, rws, C, 0.02, "bf16")
+    wq, ws, _ = O.mx_quantize_rowwise(a_rows)
+    idx = torch.from_numpy(rws).cuda()
+    np.testing.assert_array_equal(qr[idx].cpu().numpy(), wq)
+    np.testing.assert_array_equal(sr[idx].cpu().numpy(), ws)
+    cs = np.unique(np.concatenate([[0, C - 1], g.integers(0, C, 6)]))
+    grp = 5
+    blk = mi.randn_np(11, mi.X, 0, np.arange(grp * R, (grp + 1) * R), C, 0.02, "bf16", col_index=cs)
+    codes, scales, _ = O.mx_quantize_colwise_grouped(blk, np.array([0, R]))
+    qg = qc.view(-1)[32 * C * grp * (R // 32):32 * C * (grp + 1) * (R // 32)].view(C, R)
+    sg = sc.view(-1)[C * grp * (R // 32):C * (grp + 1) * (R // 32)].view(C, R // 32)
+    cs_t = torch.from_numpy(cs).cuda()
+    np.testing.assert_array_equal(qg[cs_t].cpu().numpy(), codes.T)
+    np.testing.assert_array_equal(sg[cs_t].cpu().numpy(), scales[0].T)
