@@ -198,15 +198,17 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     }
     __syncthreads();
     if (q_row != nullptr) {
-        // row-wise copy: unit u = (tile row u / RBK, row block u % RBK); consecutive threads
-        // write consecutive 32-byte code segments of one row
-        constexpr int RBK = TC / kBlock;                         // row blocks per tile row
-        constexpr int P16 = kBlock * ESIZE / 16;                 // 16-byte LDS reads per block
-        for (int u = t; u < kGroupAlign * kBlock * RBK; u += 256) {
-            const int i = u / RBK, b = u % RBK;
-            if (i >= n || b * kBlock >= ncols) continue;
-            const char* src = tile + i * PITCH + b * kBlock * ESIZE;
-            float v[kBlock];
+        // row-wise copy: unit u = (tile row u / HB, half block u % HB); the two lanes of a block
+        // combine their maxima with one shuffle, and 8 consecutive lanes write 128 contiguous
+        // bytes of one row (bf16; 4 lanes and 64 bytes for fp32)
+        constexpr int HB = TC / 16;                              // half blocks per tile row
+        constexpr int P16 = 16 * ESIZE / 16;                     // 16-byte LDS reads per half block
+        static_assert((kGroupAlign * kBlock * HB) % 256 == 0, "whole waves per pass");
+        for (int u = t; u < kGroupAlign * kBlock * HB; u += 256) {
+            const int i = u / HB, hb = u % HB;
+            const bool live = i < n && hb * 16 < ncols;          // same for both lanes of a block
+            const char* src = tile + i * PITCH + hb * 16 * ESIZE;
+            float v[16];
 #pragma unroll
             for (int c = 0; c < P16; ++c) {
                 const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
@@ -223,22 +225,19 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
             }
             float amax = 0.f;
 #pragma unroll
-            for (int e = 0; e < kBlock; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));      // the block's other half
             const uint32_t byte = mx_scale_byte(amax);
             const float inv = mx_inv_scale(byte);
-            u32x4 out[2];
+            u32x4 out;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float* e = v + h * 16 + w * 4;
-                    out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
-                }
-            const int64_t r = r0 + i;                            // logical row
-            uint8_t* dst = q_row + r * ld_q_row + c0 + b * kBlock;
-            *reinterpret_cast<u32x4*>(dst) = out[0];
-            *reinterpret_cast<u32x4*>(dst + 16) = out[1];
-            s_row[r * ld_s_row + c0 / kBlock + b] = (uint8_t)byte;
+            for (int w = 0; w < 4; ++w) out[w] = pack4_e4m3(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                                             v[4 * w + 3] * inv);
+            if (live) {
+                const int64_t r = r0 + i;                        // logical row
+                *reinterpret_cast<u32x4*>(q_row + r * ld_q_row + c0 + hb * 16) = out;
+                if ((hb & 1) == 0) s_row[r * ld_s_row + c0 / kBlock + hb / 2] = (uint8_t)byte;
+            }
         }
     }
     constexpr int TPC = 256 / TC;                                // threads per column (2 bf16, 4 fp32)
