@@ -91,6 +91,9 @@ constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 constexpr int kSuper = 4;         // column tiles per supertile
+#ifndef MOE_GEMM_RK_STREAM
+#define MOE_GEMM_RK_STREAM 1      // ragged-K bf16-output tiles as one stream of K slices (gemm_rk_stream)
+#endif
 
 // 16-byte chunk c of LDS row r lives at slot c ^ swz(r). Measured on gfx950 with 128-byte
 // rows: this XOR keeps ds_read_b128 of 16x16 and 32x32 MFMA fragments (16 or 32 rows at one
@@ -803,6 +806,218 @@ __device__ __forceinline__ void tile_coords(int L, int MT, int NT, int& mt, int&
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Ragged-K (weight-gradient) tiles as one stream of K slices. A group averages a few K slices,
+// so a tile that fills the ring from empty and then drains it through LDS spends most of
+// its time waiting for memory. Here the load waves walk this workgroup's (tile, slice)
+// sequence without stopping at tile boundaries (tiles of empty groups have no slice), ring
+// slot = running slice count mod NST, one barrier per slice for both roles; the MFMA waves
+// write each finished tile straight from registers through a wave-private 1 KiB LDS
+// transpose (8 rows x 64 columns of bf16 at a time, one 128-byte line per 8 lanes), which
+// lies outside the ring, so the next tile's first slices load during that epilogue. Both
+// roles derive every tile's slice count the same way, so their barrier counts match.
+// bf16 output only (the caller keeps fp32 outputs on the per-tile path).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, int slot) {
+    constexpr int BM = 128, NST = Stage<BM>::kCount, SB = Stage<BM>::kBytes;
+    constexpr int MS = 32, WM = 2, WN = kWaves / WM, WTM = BM / WM, WTN = kBN / WN;
+    constexpr int MI = WTM / MS, NI = WTN / MS;
+    using MF = Mfma<MS, true>;
+    using FragT = typename Frag<MS, true>::t;
+    constexpr int NKS = MF::KS;
+    constexpr int ROWS_PER_INSTR = 1024 / kRowBytes, CH = kRowBytes / 16;
+    constexpr int A_INSTR = BM / ROWS_PER_INSTR;
+    constexpr int A_PER_WAVE = A_INSTR / kLWaves, B_PER_WAVE = kBN / ROWS_PER_INSTR / kLWaves;
+    constexpr int AS_INSTR = BM / 64, BS_INSTR = kBN / 64;
+    constexpr int SC_PER_WAVE = cdiv(AS_INSTR + BS_INSTR, kLWaves);
+    constexpr int LOADS_MIN = A_PER_WAVE + B_PER_WAVE;
+    static_assert(kPWaves > 0 && A_INSTR % kLWaves == 0 && MI >= 1 && NI >= 1, "load-wave layout");
+    static_assert(kPipeBytes + kWaves * 1024 <= kLdsBytes, "epilogue staging fits past the ring");
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const bool producer = wave >= kWaves;
+    const int per_group = p.MT * p.NT, total = p.G * per_group;
+    const int kb_max = p.K / 32;
+    // tile -> group, row/column tile and the group's whole 128-element K slices (as gemm_tile)
+    auto tile_info = [&](int tile, int& g, int& mt, int& nt, int& kb0, int& nbe) {
+        g = tile / per_group;
+        tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
+        kb0 = min(max(p.offsets[g], 0), kb_max) & ~3;
+        nbe = (max(min(p.offsets[g + 1], kb_max), kb0) - kb0) & ~3;
+    };
+    lds_barrier();
+    if (producer) {
+#if MOE_BUF_DMA
+        const int lw = wave - kWaves;
+        int tile = slot, kt = 0, nk = 0, issued = 0;
+        // placeholders until next_tile() finds a tile (no load is issued before it does)
+        __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0, 0x00020000);
+        __amdgpu_buffer_rsrc_t rsrc_b = rsrc_a;
+        uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
+        const uint8_t* s_src[SC_PER_WAVE] = {};
+        int s_lds[SC_PER_WAVE] = {};
+        // from `tile` on, the next tile of this workgroup with a slice; sets its sources
+        auto next_tile = [&]() -> bool {
+            for (; tile < total; tile += gridDim.x) {
+                int g, mt, nt, kb0, nbe;
+                tile_info(tile, g, mt, nt, kb0, nbe);
+                nk = nbe / 4;
+                if (nk == 0) continue;
+                const int r0 = mt * BM, n0 = nt * kBN;
+                const int64_t ld = (int64_t)32 * nbe;
+                rsrc_a = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)32 * p.M * kb0), (short)0,
+                                                           (int)0xFFFFFFFF, 0x00020000);
+                rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)32 * p.N * kb0), (short)0,
+                                                           (int)0xFFFFFFFF, 0x00020000);
+#pragma unroll
+                for (int i = 0; i < A_PER_WAVE; ++i) {
+                    const int row = (lw + kLWaves * i) * ROWS_PER_INSTR + lane / CH;
+                    const int chunk = (lane % CH) ^ swz(row);
+                    a_voff[i] = (uint32_t)(min(r0 + row, p.M - 1) * ld + chunk * 16);
+                }
+#pragma unroll
+                for (int i = 0; i < B_PER_WAVE; ++i) {
+                    const int rho = (lw * B_PER_WAVE + i) * ROWS_PER_INSTR + lane / CH;
+                    const int chunk = (lane % CH) ^ swz(rho);
+                    b_voff[i] = (uint32_t)(min(n0 + rho, p.N - 1) * ld + chunk * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < SC_PER_WAVE; ++u) {
+                    const int q = lw + kLWaves * u;
+                    if (q < AS_INSTR) {
+                        s_src[u] = p.a_scale + (int64_t)p.M * kb0 + (int64_t)min(r0 + q * 64 + lane, p.M - 1) * nbe;
+                        s_lds[u] = Stage<BM>::kScaleA + q * 256;
+                    } else if (q < AS_INSTR + BS_INSTR) {
+                        const int rho = (q - AS_INSTR) * 64 + lane;
+                        s_src[u] = p.b_scale + (int64_t)p.N * kb0 + (int64_t)min(n0 + rho, p.N - 1) * nbe;
+                        s_lds[u] = Stage<BM>::kScaleB + (q - AS_INSTR) * 256;
+                    }
+                }
+                kt = 0;
+                return true;
+            }
+            return false;
+        };
+        bool have = next_tile();
+        // issue the next slice of the stream into ring slot issued % NST
+        auto issue_next = [&]() {
+            if (!have) return;
+            char* st = lds + (issued % NST) * SB;
+            const uint32_t koff = (uint32_t)(kt * kRowBytes);
+#pragma unroll
+            for (int i = 0; i < A_PER_WAVE; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + (lw + kLWaves * i) * 1024), 16, a_voff[i],
+                                                         koff, 0, 0);
+#pragma unroll
+            for (int i = 0; i < B_PER_WAVE; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b,
+                                                         MOE_LDS(st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024),
+                                                         16, b_voff[i], koff, 0, 0);
+#pragma unroll
+            for (int u = 0; u < SC_PER_WAVE; ++u)
+                if (lw + kLWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4, st + s_lds[u]);
+            ++issued;
+            if (++kt >= nk) {
+                tile += gridDim.x;
+                have = next_tile();
+            }
+        };
+#pragma unroll
+        for (int s0 = 0; s0 < NST - 1; ++s0) issue_next();
+        for (int q = 0; q < issued; ++q) {
+            static_assert(NST == 3, "one later slice in flight at each wait");
+            if (q + 1 < issued) wait_vm_lgkm0<LOADS_MIN>();
+            else wait_vm_lgkm0<0>();
+            lds_barrier();
+            issue_next();   // slice q + NST - 1 into the slot compute(q - 1) has left
+        }
+#endif
+        return;
+    }
+    // ---- MFMA waves ----
+    const int wm = wave / WN, wn = wave % WN;
+    int a_off[NKS][2], b_off[NKS][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int chunk = MF::frag_chunk(lane, ks);
+        const int ra = wm * WTM + MF::frag_row(lane), rb = wn * WTN + MF::frag_row(lane);
+        a_off[ks][0] = ra * kRowBytes + ((chunk ^ swz(ra)) << 4);
+        a_off[ks][1] = ra * kRowBytes + (((chunk + MF::kChunk2) ^ swz(ra)) << 4);
+        b_off[ks][0] = BM * kRowBytes + rb * kRowBytes + ((chunk ^ swz(rb)) << 4);
+        b_off[ks][1] = BM * kRowBytes + rb * kRowBytes + (((chunk + MF::kChunk2) ^ swz(rb)) << 4);
+    }
+    constexpr int FSTEP = MS * kRowBytes;
+    char* stg = lds + kPipeBytes + wave * 1024;   // this wave's transpose buffer
+    int q = 0;
+    for (int tile = slot; tile < total; tile += gridDim.x) {
+        int g, mt, nt, kb0, nbe;
+        tile_info(tile, g, mt, nt, kb0, nbe);
+        const int nk = nbe / 4;
+        typename MF::acc_t acc[MI][NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, true>();
+        for (int kt = 0; kt < nk; ++kt, ++q) {
+            wait_vm_lgkm0<63>();   // this wave's LDS reads of the previous slice are done
+            lds_barrier();
+            const char* st = lds + (q % NST) * SB;
+            int sa_w[MI], sb_w[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                sa_w[i] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4);
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                sb_w[j] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
+            FragT af[2][MI], bfr[2][NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, true>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, true>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int cur = ks & 1, nxt = cur ^ 1;
+                if (ks + 1 < NKS) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        af[nxt][i] = load_frag<MS, true>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        bfr[nxt][j] = load_frag<MS, true>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const int sh = 8 * MF::frag_block(lane, ks);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        acc[i][j] = mfma<MS, true>(af[cur][i], bfr[cur][j], acc[i][j], (sa_w[i] >> sh) & 0xFF,
+                                                   (sb_w[j] >> sh) & 0xFF);
+            }
+        }
+        // epilogue: 8 output rows x 64 columns at a time through the wave's LDS buffer
+        char* Cg = p.C + (int64_t)g * p.c_stride * 2;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < MS / 8; ++q4) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        *reinterpret_cast<uint16_t*>(stg + ((lane / 32) * 4 + rr) * 128 + (j * MS + lane % 32) * 2) =
+                            f32_to_bf16(acc[i][j][4 * q4 + rr]);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (lane / 8) * 128 + (lane % 8) * 16);
+                const int row = mt * BM + wm * WTM + i * MS + 8 * q4 + lane / 8;
+                const int col = nt * kBN + wn * WTN + (lane % 8) * 8;
+                if (row < p.M && col < p.N) *reinterpret_cast<u32x4*>(Cg + ((int64_t)row * p.ldc + col) * 2) = v;
+                asm volatile("" ::: "memory");
+            }
+    }
+}
+
 template <bool SWIGLU, bool MX, bool RK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -812,6 +1027,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     const int per_xcd = gridDim.x / nxcd;
     const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
     if constexpr (RK) {
+        if constexpr (MOE_GEMM_RK_STREAM && MOE_BUF_DMA && kPWaves > 0 && kWaves == 8) {
+            if (!p.c_f32) {
+                gemm_rk_stream(p, lds, slot);
+                return;
+            }
+        }
         const int per_group = p.MT * p.NT;
         const int total = p.G * per_group;
         for (int tile = slot; tile < total; tile += gridDim.x) {
