@@ -91,11 +91,13 @@ def test_mx_gemm_quantised_random_within_tolerance(L, epi):
     assert_close(host(C), want, "bf16", f"mx {epi}")
 
 
-def test_mx_gemm_ragged_k_on_grid_bit_exact(L):
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])   # bf16 output takes the K-slice streaming path
+def test_mx_gemm_ragged_k_on_grid_bit_exact(L, cdt):
     """Weight-gradient form: C[g] = A_g @ B_g^T over each group's own blocks (multiples of 4
     blocks), the operands in the column-wise quantiser's group-major layout (group g's
     [M, 32 n_g] block at 32*M*offsets[g]), with an empty range whose C[g] must come back as
-    zeros, and M, N that leave partial tiles."""
+    zeros, and M, N that leave partial tiles. On-grid operands make every fp32 sum exact, so
+    the fp32 output is the exact product and the bf16 output its one nearest-even rounding."""
     blocks = np.array([0, 4, 4, 12, 16, 28], np.int32)          # group K ranges in 32-element blocks
     G, M, N, K = len(blocks) - 1, 192, 320, 32 * int(blocks[-1])
     parts = [(_grid_operand((M, 32 * int(blocks[g + 1] - blocks[g])), 11 + g),
@@ -105,14 +107,15 @@ def test_mx_gemm_ragged_k_on_grid_bit_exact(L):
     As = flat([p[0][1] for p in parts], M, K // 32)
     B = flat([p[1][0] for p in parts], N, K)
     Bs = flat([p[1][1] for p in parts], N, K // 32)
-    C = torch.full((G, M, N), float("nan"), dtype=torch.float32, device="cuda")
+    C = torch.full((G, M, N), float("nan"), dtype=torch.float32 if cdt == "f32" else torch.bfloat16, device="cuda")
     L.moe_grouped_gemm(_u8(A), _u8(B), C, dev_i32(blocks), L.MOE_EPI_NONE, workspace=_ws(L, G),
                        a_scale=_u8(As), b_scale=_u8(Bs), ragged_k=True)
     torch.cuda.synchronize()
     got = host(C)
+    rnd = (lambda v: v) if cdt == "f32" else O.round_bf16
     for g in range(G):
         (Ag, Ags), (Bg, Bgs) = parts[g]
-        np.testing.assert_array_equal(got[g], _dequant(Ag, Ags) @ _dequant(Bg, Bgs).T, err_msg=f"group {g}")
+        np.testing.assert_array_equal(got[g], rnd(_dequant(Ag, Ags) @ _dequant(Bg, Bgs).T), err_msg=f"group {g}")
 
 
 def test_mx_wgrad_quantised_within_tolerance(L):
