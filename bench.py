@@ -400,7 +400,8 @@ def main():
     perm_bytes = w.T * w.k * 4 * 4 + (0 if fused else (w.T * w.d * 2 + rows * w.d * 2))
     comb_bytes = w.T * w.k * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2 + (w.T * w.d * 2 if w.shared_f else 0)
     res = {
-        "metric": "MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped bf16",
+        "metric": ("MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped bf16" if w.name == "dsv3"
+                   else f"MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, {w.name} bf16"),
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

