@@ -145,8 +145,9 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
 
 // Column-wise tile: one workgroup quantises a 4-block chunk (128 rows of one group: every
 // group starts on a multiple of 4 blocks) by kColTile columns. The rows are loaded with
-// coalesced 16-byte loads into LDS (read through row_index when given); then two threads own
-// each column, two blocks each: their maxima, scale bytes and codes. The codes are staged back
+// coalesced 16-byte loads into LDS (read through row_index when given); then each thread takes
+// one block of two adjacent columns (one 4-byte LDS read per row; fp32: one block of one
+// column): their maxima, scale bytes and codes. The codes are staged back
 // in LDS transposed, so that the stores write each column's 128 bytes of the group's
 // transposed block as one full line (8 lanes x 16 bytes) and its 4 scale bytes as one dword
 // (16-byte pieces of 64 different lines per store instruction measured ~30% slower). A 34 KiB tile
@@ -240,33 +241,46 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
             }
         }
     }
-    constexpr int TPC = 256 / TC;                                // threads per column (2 bf16, 4 fp32)
-    constexpr int BPT = kGroupAlign / TPC;                       // blocks per thread (2 bf16, 1 fp32)
-    const int col = t % TC, part = t / TC;
-    // codes and scale bytes of this thread's blocks, kept in registers until the tile is free
-    u32x4 codes[BPT][2];
-    uint32_t sbytes = 0;
-#pragma unroll
-    for (int bb = 0; bb < BPT; ++bb) {
-        const int b = BPT * part + bb;
-        float v[kBlock];
-        float amax = 0.f;
+    // (column, block) units of this thread: bf16 threads read two adjacent columns with one
+    // 4-byte LDS read per row and quantise one block of each; fp32 threads one block of one column
+    constexpr int NU = kGroupAlign * TC / 256;                   // 2 bf16, 1 fp32
+    int ucol[NU], ublk[NU];
+    float v[NU][kBlock];
+    if constexpr (ESIZE == 2) {
+        const int cp = t % (TC / 2), b = t / (TC / 2);
 #pragma unroll
         for (int i = 0; i < kBlock; ++i) {
-            const char* e = tile + (b * kBlock + i) * PITCH + col * ESIZE;
-            v[i] = ESIZE == 2 ? __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(e) << 16)
-                              : *reinterpret_cast<const float*>(e);
-            amax = fmaxf(amax, fabsf(v[i]));
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (b * kBlock + i) * PITCH + cp * 4);
+            v[0][i] = __uint_as_float(w << 16);
+            v[NU - 1][i] = __uint_as_float(w & 0xFFFF0000u);
         }
+        ucol[0] = 2 * cp;
+        ucol[NU - 1] = 2 * cp + 1;
+        ublk[0] = ublk[NU - 1] = b;
+    } else {
+        const int col = t % TC, b = t / TC;
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) v[0][i] = *reinterpret_cast<const float*>(tile + (b * kBlock + i) * PITCH + col * 4);
+        ucol[0] = col;
+        ublk[0] = b;
+    }
+    // codes and scale bytes of the units, kept in registers until the tile is free
+    u32x4 codes[NU][2];
+    uint32_t sbytes[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
         const uint32_t byte = mx_scale_byte(amax);
         const float inv = mx_inv_scale(byte);
-        sbytes |= byte << (8 * bb);
+        sbytes[u] = byte;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float* e = v + h * 16 + w * 4;
-                codes[bb][h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+                const float* e = v[u] + h * 16 + w * 4;
+                codes[u][h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
             }
     }
     // Stage the chunk's transposed codes in LDS (column c's 4 blocks = 128 contiguous bytes,
@@ -278,14 +292,12 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     static_assert(TC * SP + TC * 4 <= kGroupAlign * kBlock * PITCH, "staging fits in the tile");
     __syncthreads();                                             // every thread is done reading the tile
 #pragma unroll
-    for (int bb = 0; bb < BPT; ++bb) {
-        char* d = stage + col * SP + (BPT * part + bb) * kBlock;
-        *reinterpret_cast<u32x4*>(d) = codes[bb][0];
-        *reinterpret_cast<u32x4*>(d + 16) = codes[bb][1];
+    for (int u = 0; u < NU; ++u) {
+        char* d = stage + ucol[u] * SP + ublk[u] * kBlock;
+        *reinterpret_cast<u32x4*>(d) = codes[u][0];
+        *reinterpret_cast<u32x4*>(d + 16) = codes[u][1];
+        reinterpret_cast<uint8_t*>(sstage)[ucol[u] * kGroupAlign + ublk[u]] = (uint8_t)sbytes[u];
     }
-#pragma unroll
-    for (int bb = 0; bb < BPT; ++bb)
-        reinterpret_cast<uint8_t*>(sstage)[col * kGroupAlign + BPT * part + bb] = (uint8_t)(sbytes >> (8 * bb));
     __syncthreads();
     const int64_t gbase = (int64_t)cols * block_start[g];      // the group's transposed block
     constexpr int PIECES_OUT = TC * kGroupAlign * kBlock / 16;   // 16-byte pieces of the chunk
