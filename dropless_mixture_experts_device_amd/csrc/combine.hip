@@ -8,12 +8,15 @@
 // position and accumulates the experts' results. Written as a gather-reduce per token
 // rather than a scatter-add: every output element is produced by exactly one lane, so the
 // result is deterministic and needs no atomics or zero-initialised output.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kCombThreads = 256;
+constexpr int kCombMaxThreads = 512;   // forward combine: block sized to the row (see comb_threads)
 
 template <int ESIZE>
 __device__ __forceinline__ void load8(const char* p, float (&v)[8]) {
@@ -77,7 +80,7 @@ __device__ __forceinline__ void cvt8(const u32x4& a, const u32x4& b, float (&v)[
 // in flight instead of one. The fp32 sum runs in the same order either way (slot 0 .. k-1,
 // then the shared row), so every KK gives the same bits.
 template <int ESIZE, int KK>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __restrict__ y,
+__global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(const char* __restrict__ y,
                                                                const float* __restrict__ topk_w,
                                                                const int32_t* __restrict__ row_of,
                                                                const char* __restrict__ y_shared, int T, int d,
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __res
     const int ngroups = d / 8;
     const int64_t rowbytes = (int64_t)d * ESIZE;
     if constexpr (KK > 0) {
-        for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
+        for (int c = threadIdx.x; c < ngroups; c += blockDim.x) {
             const int64_t col = (int64_t)c * 8 * ESIZE;
             u32x4 ra[KK], rb[KK], sa = {}, sb = {};
 #pragma unroll
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const char* __res
         }
         return;
     }
-    for (int c = threadIdx.x; c < ngroups; c += kCombThreads) {
+    for (int c = threadIdx.x; c < ngroups; c += blockDim.x) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
             float v[8];
@@ -228,10 +231,19 @@ __global__ __launch_bounds__(kCombThreads) void combine_bwd_kernel(const char* _
     }
 }
 
+// Threads per token: whole waves, as few passes over the row's 8-column groups as 512
+// threads allow, split evenly (d = 7168: 896 groups -> 448 threads x 2 passes, where 256
+// threads would leave half of them idle in the last pass).
+inline int comb_threads(int64_t d) {
+    const int64_t groups = d / 8;
+    const int64_t passes = cdiv<int64_t>(groups, kCombMaxThreads);
+    return (int)std::min<int64_t>(kCombMaxThreads, std::max<int64_t>(kWave, kWave * cdiv<int64_t>(cdiv<int64_t>(groups, passes), kWave)));
+}
+
 template <int ESIZE>
 void launch_combine(int k, const char* y, const float* topk_w, const int32_t* row_of, const char* y_shared,
                     int64_t T, int64_t d, char* out, hipStream_t s) {
-    const dim3 grid((unsigned)T), block(kCombThreads);
+    const dim3 grid((unsigned)T), block((unsigned)comb_threads(d));
     switch (k) {
         case 1: hipLaunchKernelGGL((combine_kernel<ESIZE, 1>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
         case 2: hipLaunchKernelGGL((combine_kernel<ESIZE, 2>), grid, block, 0, s, y, topk_w, row_of, y_shared, (int)T, (int)d, k, out); break;
