@@ -15,7 +15,16 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1   // expert rows are read once: non-temporal loads (measured 230 -> 203 us at DeepSeek-V3 size)
+#endif
+
 constexpr int kCombThreads = 256;
+
+__device__ __forceinline__ u32x4 ld_row16(const char* p) {
+    if constexpr (MOE_COMBINE_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
 constexpr int kCombMaxThreads = 512;   // forward combine: block sized to the row (see comb_threads)
 
 template <int ESIZE>
@@ -103,13 +112,13 @@ __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(const char* __
 #pragma unroll
             for (int j = 0; j < KK; ++j) {
                 const char* src = y + rows[j] * rowbytes + col;
-                ra[j] = *reinterpret_cast<const u32x4*>(src);
-                if (ESIZE == 4) rb[j] = *reinterpret_cast<const u32x4*>(src + 16);
+                ra[j] = ld_row16(src);
+                if (ESIZE == 4) rb[j] = ld_row16(src + 16);
             }
             if (y_shared != nullptr) {
                 const char* src = y_shared + t * rowbytes + col;
-                sa = *reinterpret_cast<const u32x4*>(src);
-                if (ESIZE == 4) sb = *reinterpret_cast<const u32x4*>(src + 16);
+                sa = ld_row16(src);
+                if (ESIZE == 4) sb = ld_row16(src + 16);
             }
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll

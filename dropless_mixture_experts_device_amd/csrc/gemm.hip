@@ -195,12 +195,14 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
                                                              int32_t* __restrict__ order) {
     __shared__ unsigned long long key[2048];
     __shared__ int tiles_of[2048];
+    __shared__ int sorted[2048];
     __shared__ unsigned long long wsum[16];
     __shared__ unsigned long long carry_s;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     // tiles per group, and each group's exclusive prefix of tiles within its class: one scan of
     // (small-class tiles << 32 | large-class tiles)
     unsigned long long pre[2];
+    int rows_of[2] = {0, 0};   // this thread's groups' row counts (offsets are read once)
     if (tid == 0) carry_s = 0;
     __syncthreads();
     for (int h = 0; h < 2; ++h) {
@@ -209,6 +211,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
         if (g < G) {
             int b, e;
             group_rows(offsets, g, M, b, e);
+            rows_of[h] = e - b;
             t = row_tiles(e - b, allow256 != 0).count() * NT;
             small = (e - b) <= 128;
         }
@@ -235,9 +238,8 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
         const int g = h * 1024 + tid;
         unsigned long long k = ~0ull;   // padding and empty groups sort last
         if (g < G && tiles_of[g] > 0) {
-            int b, e;
-            group_rows(offsets, g, M, b, e);
-            const bool small = (e - b) <= 128;
+            const int m = rows_of[h];
+            const bool small = m <= 128;
             const unsigned long long p = small ? (pre[h] >> 32) : (pre[h] & 0xFFFFFFFFull);
             const unsigned long long total = small ? tot_small : tot_large;
             // midpoint fraction of the class's tiles in 2^-24 units
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
             const bool first = small ? (tot_small >= tot_large) : (tot_large > tot_small);
             // groups cut into 256-row tiles (the longest tiles) go first, so the short tiles
             // of the other groups fill the end of the run instead of a long tile ending it
-            const unsigned long long late = (allow256 != 0 && (e - b) >= 256) ? 0ull : 1ull;
+            const unsigned long long late = (allow256 != 0 && m >= 256) ? 0ull : 1ull;
             k = (late << 60) | (frac << 32) | ((unsigned long long)(first ? 0 : 1) << 16) | (unsigned long long)g;
         } else if (g < G) {
             k = (0xFFFFFFFull << 32) | (2ull << 60) | (unsigned long long)g;   // empty group: last, by id
@@ -253,25 +255,20 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
         key[g] = k;
     }
     __syncthreads();
-    // bitonic sort, ascending, of the first n keys (n = the power of two >= G; the rest are
-    // padding that already sorts last)
-    int n = 2;
-    while (n < G) n <<= 1;
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (tid < n / 2) {
-                const int i = 2 * tid - (tid & (stride - 1));   // lower index of the pair
-                const int j = i + stride;
-                const bool up = (i & size) == 0;
-                const unsigned long long a = key[i], c = key[j];
-                if ((a > c) == up) {
-                    key[i] = c;
-                    key[j] = a;
-                }
-            }
-            __syncthreads();
+    // ascending order by rank: the G keys are distinct (the group id is in the low bits), so a
+    // key's position is the number of smaller keys; every thread counts them for its own keys
+    // with broadcast LDS reads
+    for (int h = 0; h < 2; ++h) {
+        const int g = h * 1024 + tid;
+        if (g < G) {
+            const unsigned long long kg = key[g];
+            int r = 0;
+#pragma unroll 8
+            for (int q = 0; q < G; ++q) r += key[q] < kg ? 1 : 0;
+            sorted[r] = g;
         }
     }
+    __syncthreads();
     // order and the tile prefix in schedule order
     if (tid == 0) carry_s = 0;
     __syncthreads();
@@ -279,7 +276,7 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
         const int p = h * 1024 + tid;
         int t = 0, g = 0;
         if (p < G) {
-            g = (int)(key[p] & 0xFFFF);
+            g = sorted[p];
             t = tiles_of[g];
             order[p] = g;
         }

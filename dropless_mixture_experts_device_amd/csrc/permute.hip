@@ -44,23 +44,39 @@ __host__ __device__ inline PermWs perm_ws(void* ws, int64_t T, int E) {
     return w;
 }
 
-__global__ __launch_bounds__(kPermThreads) void perm_mask_kernel(const int32_t* __restrict__ topk_idx, int T,
+// One workgroup of kMaskThreads per 1024-token tile. Each thread first loads all of its
+// (token, slot) pairs' expert ids (independent loads in flight together), then ORs the
+// token bits into the LDS masks.
+constexpr int kMaskThreads = 1024;
+constexpr int kMaskPer = 16;   // pairs per thread per pass (k <= 16: one pass per tile)
+
+__global__ __launch_bounds__(kMaskThreads) void perm_mask_kernel(const int32_t* __restrict__ topk_idx, int T,
                                                                  int E, int k, PermWs ws) {
     extern __shared__ unsigned long long smask[];   // [kSubPerTile][E]
     const int tile = blockIdx.x;
-    for (int i = threadIdx.x; i < kSubPerTile * E; i += kPermThreads) smask[i] = 0ull;
+    for (int i = threadIdx.x; i < kSubPerTile * E; i += kMaskThreads) smask[i] = 0ull;
     __syncthreads();
     const int t_begin = tile * kTile;
     const int npairs = min(kTile, T - t_begin) * k;
-    for (int p = threadIdx.x; p < npairs; p += kPermThreads) {
-        const int tl = p / k;
-        const int e = topk_idx[(int64_t)(t_begin + tl) * k + (p % k)];
-        if ((unsigned)e < (unsigned)E) atomicOr(&smask[(tl / kSub) * E + e], 1ull << (tl % kSub));
+    const int32_t* src = topk_idx + (int64_t)t_begin * k;
+    for (int p0 = 0; p0 < npairs; p0 += kMaskThreads * kMaskPer) {
+        int ev[kMaskPer];
+#pragma unroll
+        for (int u = 0; u < kMaskPer; ++u) {
+            const int p = p0 + u * kMaskThreads + threadIdx.x;
+            ev[u] = p < npairs ? src[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kMaskPer; ++u) {
+            const int p = p0 + u * kMaskThreads + threadIdx.x;
+            const int tl = p / k;
+            if ((unsigned)ev[u] < (unsigned)E) atomicOr(&smask[(tl / kSub) * E + ev[u]], 1ull << (tl % kSub));
+        }
     }
     __syncthreads();
     const int nsub_here = cdiv(min(kTile, T - t_begin), kSub);
     const int64_t sub0 = (int64_t)tile * kSubPerTile;
-    for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    for (int e = threadIdx.x; e < E; e += kMaskThreads) {
         int run = 0;
         for (int s = 0; s < nsub_here; ++s) {
             const unsigned long long m = smask[s * E + e];
@@ -80,10 +96,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int k, in
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int t = 0; t < ntile; ++t) {
-            const int c = ws.base[(int64_t)t * E + e];
-            ws.base[(int64_t)t * E + e] = run;
-            run += c;
+        // 8 tiles' counts are loaded together before any is overwritten, so their latencies overlap
+        constexpr int U = 8;
+        for (int t0 = 0; t0 < ntile; t0 += U) {
+            int c[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) c[u] = t0 + u < ntile ? ws.base[(int64_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (t0 + u < ntile) ws.base[(int64_t)(t0 + u) * E + e] = run;
+                run += c[u];
+            }
         }
     }
     // exclusive scan of run over e (E <= 1024) with wave prefix sums
@@ -188,7 +211,7 @@ extern "C" moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t*
     moe::PermWs ws = moe::perm_ws(workspace, T, E);
     if (T > 0) {
         const int ntile = moe::cdiv(Ti, moe::kTile);
-        hipLaunchKernelGGL(moe::perm_mask_kernel, dim3(ntile), dim3(moe::kPermThreads),
+        hipLaunchKernelGGL(moe::perm_mask_kernel, dim3(ntile), dim3(moe::kMaskThreads),
                            moe::kSubPerTile * E * sizeof(unsigned long long), s, topk_idx, Ti, E, k, ws);
         MOE_CHECK_LAUNCH();
     }

@@ -17,34 +17,36 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One DPP step of a 64-bit max: lanes outside `row_mask` keep their own value.
+// Wave-wide max of a 32-bit value, returned to every lane. DPP lane moves stay in the VALU
+// (no LDS round trip): pairs, quads, then rotations inside each 16-lane row give every lane
+// its row's max; two row broadcasts fold the rows so lane 63 holds the wave max. Lanes
+// outside a step's row mask keep their own value.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
     return o > v ? o : v;
 }
 
-// Wave-wide max of a 64-bit value, returned to every lane. DPP lane moves stay in the VALU
-// (no LDS round trip): pairs, quads, then rotations inside each 16-lane row give every lane
-// its row's max; two row broadcasts fold rows so lane 63 holds the wave max.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = dpp_max_step<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
     v = dpp_max_step<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
     v = dpp_max_step<0x124, 0xF>(v);   // row_ror:4
     v = dpp_max_step<0x128, 0xF>(v);   // row_ror:8
     v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
     v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Top-k over keys held in LDS ([kRouteBT][pitch] floats, bias already added). Each wave
-// handles tokens wave, wave+4, ... of the tile. Selection order: larger key first, equal
-// keys -> lower expert id (the packed low word is ~e, so the larger packed value wins).
+__device__ __forceinline__ float key_of_ordered(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Top-k over keys held in LDS ([BT][pitch] floats, bias already added). Each wave handles
+// tokens wave, wave+4, ... of the tile; lane l holds experts l, 64+l, ... as order-preserving
+// 32-bit codes (0 = absent or already taken; every finite key codes above 0). One round per
+// selection: the wave max of the codes, then the lowest expert id holding it (ballots in
+// expert order), which is removed. Selection order: larger key first, equal keys -> lower
+// expert id. Lane j keeps the j-th selection and writes it with its weight.
 template <int NQ, int BT = kRouteBT>
 __device__ void topk_tile(const float* keys, int pitch, int t0, int T, int E, int k, int score,
                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
@@ -53,39 +55,44 @@ __device__ void topk_tile(const float* keys, int pitch, int t0, int T, int E, in
     for (int tl = wave; tl < BT; tl += kRouteThreads / kWave) {
         const int t = t0 + tl;
         if (t >= T) break;
-        uint64_t cand[NQ];
+        uint32_t cand[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int e = q * kWave + lane;
-            cand[q] = (e < E) ? (((uint64_t)ordered_bits(keys[tl * pitch + e]) << 32) | (uint32_t)(~e)) : 0ull;
+            cand[q] = (e < E) ? ordered_bits(keys[tl * pitch + e]) : 0u;
         }
-        float sel_key[16];
-        int sel_e[16];
+        uint32_t my_code = 0u, code0 = 0u;
+        int my_e = 0;
         for (int j = 0; j < k; ++j) {
-            uint64_t best = 0;
-            int bq = 0;
+            uint32_t m = cand[0];
+#pragma unroll
+            for (int q = 1; q < NQ; ++q) m = cand[q] > m ? cand[q] : m;
+            m = wave_max_u32(m);
+            int win = -1;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const unsigned long long b = __ballot(cand[q] == m);
+                if (win < 0 && b != 0ull) win = q * kWave + __builtin_ctzll(b);
+            }
+            win = min(max(win, 0), E - 1);   // in range even for non-finite keys (unsupported)
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                if (cand[q] > best) { best = cand[q]; bq = q; }
-            const uint64_t win = wave_max_u64(best);
-            const int e = (int)(~(uint32_t)win);
-            if (best == win) cand[bq] = 0ull;   // only the owner of e holds this packed value
-            sel_e[j] = e;
-            const uint32_t u = (uint32_t)(win >> 32);
-            sel_key[j] = __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-        }
-        // weights: every lane computes the same normaliser in the same order
-        float z[16];
-        float sum = 0.f;
-        for (int j = 0; j < k; ++j) {
-            z[j] = (score == MOE_SOFTMAX) ? expf(sel_key[j] - sel_key[0]) : 1.0f / (1.0f + expf(-sel_key[j]));
-            sum += z[j];
-        }
-        for (int j = 0; j < k; ++j) {
+                if (q * kWave + lane == win) cand[q] = 0u;
             if (lane == j) {
-                topk_idx[(int64_t)t * k + j] = sel_e[j];
-                topk_w[(int64_t)t * k + j] = z[j] / sum;
+                my_code = m;
+                my_e = win;
             }
+            if (j == 0) code0 = m;
+        }
+        // weights: lane j < k forms its term; the normaliser adds the terms in the order j = 0 .. k-1
+        const float key0 = key_of_ordered(code0), kj = key_of_ordered(my_code);
+        float z = 0.f;
+        if (lane < k) z = (score == MOE_SOFTMAX) ? expf(kj - key0) : 1.0f / (1.0f + expf(-kj));
+        float sum = 0.f;
+        for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+        if (lane < k) {
+            topk_idx[(int64_t)t * k + lane] = my_e;
+            topk_w[(int64_t)t * k + lane] = z / sum;
         }
     }
 }
