@@ -91,6 +91,13 @@ constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 constexpr int kSuper = 4;         // column tiles per supertile
+// Ragged-K (weight-gradient) tiles write a 128 x 256 bf16 block each over a short K range, so
+// output stores weigh more than operand reuse: with 16 or more column tiles they take wider
+// supertiles (16 columns; measured on the DeepSeek-V3-shaped step: 6.59 -> 5.86 ms for the
+// 28-column dW_gate/up, where 8 / 32 columns gave 5.95 / 6.15 ms and 2 gave 6.71 ms); narrower
+// outputs keep kSuper (4 beat 2 and 8 on the 8-column dW_down).
+constexpr int kSuperRK = 16;
+constexpr int kSuperRKMinNT = 16;
 #ifndef MOE_GEMM_RK_STREAM
 #define MOE_GEMM_RK_STREAM 1      // ragged-K bf16-output tiles as one stream of K slices (gemm_rk_stream)
 #endif
@@ -788,20 +795,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     }
 }
 
-// Ordering of the tiles of one group: supertiles of kSuper column tiles x all MT row tiles,
+// Ordering of the tiles of one group: supertiles of SUP column tiles x all MT row tiles,
 // row-major inside a supertile, so consecutive tiles share B panels and A panels.
+template <int SUP = kSuper>
 __device__ __forceinline__ void tile_coords(int L, int MT, int NT, int& mt, int& nt) {
-    const int full = NT / kSuper;
-    if (L < full * MT * kSuper) {
-        const int s = L / (MT * kSuper), rem = L % (MT * kSuper);
-        mt = rem / kSuper;
-        nt = s * kSuper + rem % kSuper;
+    const int full = NT / SUP;
+    if (L < full * MT * SUP) {
+        const int s = L / (MT * SUP), rem = L % (MT * SUP);
+        mt = rem / SUP;
+        nt = s * SUP + rem % SUP;
     } else {
-        const int rem = L - full * MT * kSuper, w = NT - full * kSuper;
+        const int rem = L - full * MT * SUP, w = NT - full * SUP;
         mt = rem / w;
-        nt = full * kSuper + rem % w;
+        nt = full * SUP + rem % w;
     }
 }
+
 
 
 // ---------------------------------------------------------------------------------------
@@ -839,7 +848,8 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
     // tile -> group, row/column tile and the group's whole 128-element K slices (as gemm_tile)
     auto tile_info = [&](int tile, int& g, int& mt, int& nt, int& kb0, int& nbe) {
         g = tile / per_group;
-        tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
+        if (p.NT >= kSuperRKMinNT) tile_coords<kSuperRK>(tile - g * per_group, p.MT, p.NT, mt, nt);
+        else tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
         kb0 = min(max(p.offsets[g], 0), kb_max) & ~3;
         nbe = (max(min(p.offsets[g + 1], kb_max), kb0) - kb0) & ~3;
     };
@@ -1035,7 +1045,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
         for (int tile = slot; tile < total; tile += gridDim.x) {
             const int g = tile / per_group;
             int mt, nt;
-            tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
+            if (p.NT >= kSuperRKMinNT) tile_coords<kSuperRK>(tile - g * per_group, p.MT, p.NT, mt, nt);
+            else tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
             gemm_tile<128, false, true, true>(p, lds, g, mt * 128, nt);
         }
         return;
