@@ -421,6 +421,27 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    # The step fuses the gather into GEMM 1, so its permute moves only indices. The permutation
+    # with the gather materialised (x read once, written to its k rows and the shared row) is
+    # timed here on its own, outside the step, to report the dispatch's HBM rate.
+    gbuf = layer.LayerBuffers(s, dev, fused_gather=False)
+    gbuf.topk_idx.copy_(buf.topk_idx)    # the step's routing
+    for _ in range(2):
+        layer.permute(x, s, gbuf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        layer.permute(x, s, gbuf)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pg_ms = e0.elapsed_time(e1) / reps
+    pg_bytes = w.T * w.d * 2 + rows * w.d * 2 + w.T * w.k * 4 * 4
+    same = bool(torch.equal(gbuf.src_token, buf.src_token) and torch.equal(gbuf.offsets, buf.offsets))
+    res["permute_materialised"] = {"ms": round(pg_ms, 4), "gbs": round(pg_bytes / (pg_ms * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(pg_bytes / (pg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "bytes": pg_bytes, "indices_match_step": same}
+    del gbuf
     if args.calibrate_copy:
         src = torch.zeros((COPY_CAL_BYTES // 2,), dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)

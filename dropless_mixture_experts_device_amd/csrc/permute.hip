@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_place_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave;
-                if (c < nchunk) dst[c] = v[u];
+                if (c < nchunk) __builtin_nontemporal_store(v[u], dst + c);   // x_perm is not read here again
             }
         }
     }
