@@ -16,7 +16,7 @@ namespace {
 template <int ESIZE>
 __device__ __forceinline__ void ld8(const char* p, float (&v)[8]) {
     if (ESIZE == 2) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));   // read once
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = __uint_as_float(q[i] << 16);
@@ -39,7 +39,7 @@ __device__ __forceinline__ void st8(char* p, const float (&v)[8]) {
         u32x4 q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-        *reinterpret_cast<u32x4*>(p) = q;
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));                      // written once
     } else {
         u32x4 a, b;
 #pragma unroll
