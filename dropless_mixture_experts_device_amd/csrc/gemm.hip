@@ -98,6 +98,10 @@ constexpr int kSuper = 4;         // column tiles per supertile
 // outputs keep kSuper (4 beat 2 and 8 on the 8-column dW_down).
 constexpr int kSuperRK = 16;
 constexpr int kSuperRKMinNT = 16;
+#ifndef MOE_GEMM_C_NT
+#define MOE_GEMM_C_NT 1           // ragged-row C stores non-temporal: 0 never, 1 without SwiGLU (outputs
+                                  // the next kernel streams once; GEMM 2 at DeepSeek-V3 size -1.3%), 2 always
+#endif
 #ifndef MOE_GEMM_RK_STREAM
 #define MOE_GEMM_RK_STREAM 1      // ragged-K bf16-output tiles as one stream of K slices (gemm_rk_stream)
 #endif
@@ -790,7 +794,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         const int col = n0 + ch * cols_per_chunk;
         if (row < rows_valid && col < p.N) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + ch * 16);
-            *reinterpret_cast<u32x4*>(Cg + ((int64_t)(r0 + row) * p.ldc + col) * esize) = v;
+            u32x4* cp = reinterpret_cast<u32x4*>(Cg + ((int64_t)(r0 + row) * p.ldc + col) * esize);
+            if (MOE_GEMM_C_NT == 2 || (MOE_GEMM_C_NT == 1 && !SWIGLU)) __builtin_nontemporal_store(v, cp);
+            else *cp = v;
         }
     }
 }
