@@ -188,6 +188,11 @@ struct GemmParams {
     int allow256;                // ragged rows: 256-row tiles allowed (not for fp32 C)
     int64_t c_stride;            // ragged K: elements between groups' C
     int MT;                      // ragged K: row tiles per group
+    // uniform groups (internal, 0 = off): group g owns C rows [g R, (g+1) R), its A rows are
+    // A + (r - g R) * lda + g * a_group_stride (the K slices of one matrix), and no offsets,
+    // row index or schedule are read
+    int uniform_rows;
+    int64_t a_group_stride;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -498,6 +503,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         bs_base = p.b_scale + (int64_t)p.N * kb0;
         bs_ld = nbe;
         Cg = p.C + (int64_t)g * p.c_stride * (p.c_f32 ? 4 : 2);
+    } else if (p.uniform_rows > 0) {
+        row_begin = min(g * p.uniform_rows, p.M);
+        row_end = min(row_begin + p.uniform_rows, p.M);
+        a_base = p.A + (int64_t)g * p.a_group_stride * EB;
     } else {
         group_rows(p.offsets, g, p.M, row_begin, row_end);
     }
@@ -506,7 +515,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 
     auto a_row_of = [&](int row) -> int64_t {             // A row feeding tile row `row`
         const int r = min(r0 + row, row_end - 1);
-        int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
+        int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)(p.uniform_rows > 0 ? r - row_begin : r);
         return ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
     };
     auto b_row_of = [&](int rho) -> int {                 // B row feeding LDS B-row `rho`
@@ -1057,23 +1066,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
         }
         return;
     }
+    // uniform groups: every group has the same rows, so the tile -> group map is fixed;
+    // otherwise the schedule's tile prefix (position -> first tile) and order (position -> group)
+    const bool uniform = p.uniform_rows > 0;
+    const RowTiles rt_u = row_tiles(uniform ? p.uniform_rows : 0, false);
+    const int per_group_u = rt_u.count() * p.NT;
     int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
-    for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
-    __syncthreads();
-    const int total = ts[p.G];
+    int total;
+    if (uniform) {
+        total = p.G * per_group_u;
+    } else {
+        for (int g = threadIdx.x; g <= p.G; g += kThreads) ts[g] = p.tile_start[g];
+        __syncthreads();
+        total = ts[p.G];
+    }
     for (int tile = slot; tile < total; tile += gridDim.x) {
-        // schedule position = last q with ts[q] <= tile; its group from the order table
-        int lo = 0, hi = p.G - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (ts[mid] <= tile) lo = mid;
-            else hi = mid - 1;
+        int g, L;
+        RowTiles rt;
+        if (uniform) {
+            g = tile / per_group_u;
+            L = tile - g * per_group_u;
+            rt = rt_u;
+        } else {
+            // schedule position = last q with ts[q] <= tile; its group from the order table
+            int lo = 0, hi = p.G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (ts[mid] <= tile) lo = mid;
+                else hi = mid - 1;
+            }
+            g = min(max(p.order[lo], 0), p.G - 1);
+            L = tile - ts[lo];
+            int gb, ge;
+            group_rows(p.offsets, g, p.M, gb, ge);
+            rt = row_tiles(ge - gb, p.allow256 != 0);
         }
-        const int g = min(max(p.order[lo], 0), p.G - 1);
-        const int L = tile - ts[lo];
-        int gb, ge;
-        group_rows(p.offsets, g, p.M, gb, ge);
-        const RowTiles rt = row_tiles(ge - gb, p.allow256 != 0);
         int mt, nt, r_off, bm;
         tile_coords(L, rt.count(), p.NT, mt, nt);
         row_tile(rt, mt, r_off, bm);
@@ -1277,4 +1304,38 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
     if (swiglu) return mx ? moe::launch<true, true>(p, grid, s) : moe::launch<true, false>(p, grid, s);
     return mx ? moe::launch<false, true>(p, grid, s) : moe::launch<false, false>(p, grid, s);
+}
+
+// Internal entry (route.hip): a bf16 K-split projection as one launch over KS uniform groups,
+// C[s T + t, n] = sum over k in slice s of x[t, k] w[n, k], fp32 out (the slices' partial sums).
+// Group s reads columns [s K, (s+1) K) of x and of w in place (K = d / KS): no row index,
+// offsets or schedule kernel are needed. Arguments as moe_grouped_gemm's checks require.
+moe_status_t moe_gemm_ksplit_f32(const void* x, const void* w, int64_t T, int64_t d, int32_t N, int32_t KS, float* C,
+                                 hipStream_t s) {
+    if (!x || !w || !C || T <= 0 || d <= 0 || N <= 0 || KS < 1) return MOE_EINVAL;
+    if (N % 8 != 0 || d % (64 * (int64_t)KS) != 0 || T * KS > INT32_MAX / 2 || N > (1 << 24)) return MOE_EINVAL;
+    if (!moe_aligned16(x) || !moe_aligned16(w) || !moe_aligned16(C)) return MOE_EINVAL;
+    const int64_t lim = (int64_t)1 << 32;   // buffer DMA: 32-bit lane offsets from each group's base
+    if (T * d * 2 >= lim || (int64_t)N * d * 2 >= lim) return MOE_ENOTSUP;
+    moe::GemmParams p{};
+    p.G = KS;
+    p.M = (int)(T * KS);
+    p.N = N;
+    p.K = (int)(d / KS);
+    p.NT = (int)moe::cdiv<int64_t>(N, moe::kBN);
+    p.A = (const char*)x;
+    p.lda = d;
+    p.A_rows = T;
+    p.B = (const char*)w;
+    p.ldb = d;
+    p.b_stride = d / KS;
+    p.C = (char*)C;
+    p.ldc = N;
+    p.c_f32 = 1;
+    p.uniform_rows = (int)T;
+    p.a_group_stride = d / KS;
+    const int64_t row_tiles = T <= 128 ? 1 : T / 128 + (T % 128 ? 1 : 0);
+    const int64_t tiles = row_tiles * p.NT * KS;
+    const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), tiles);
+    return moe::launch<false, false>(p, grid, s);
 }

@@ -68,5 +68,7 @@ __host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
 
 size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E);
 size_t moe_gemm_workspace_bytes(int32_t G);
+moe_status_t moe_gemm_ksplit_f32(const void* x, const void* w, int64_t T, int64_t d, int32_t N, int32_t KS, float* C,
+                                 hipStream_t s);
 
 static inline bool moe_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

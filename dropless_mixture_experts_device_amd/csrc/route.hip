@@ -209,46 +209,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
 
 // ---- split-K router for large layers -------------------------------------------------------
 // The projection x[T,d] . w_router[E,d]^T is a skinny GEMM (E <= 256 columns): with one
-// 128-token tile per workgroup it fills only T/128 CUs. It is therefore run on the tuned
-// grouped-GEMM kernel as KS groups, group s multiplying the s-th K slice: x is viewed as
-// [KS*T, d/KS] (row t*KS+s is x[t, s*d/KS : (s+1)*d/KS]) through a gather index, and group
-// s's B is w_router[:, s*d/KS : ...] (leading dimension d). The fp32 partial logits are
-// then summed in the fixed order s = 0..KS-1, the bias added, and the top-k taken.
+// 128-token tile per workgroup it fills only T/128 CUs. It therefore runs on the grouped-GEMM
+// kernel as KS uniform groups, group s multiplying the s-th K slice of x and of w_router in
+// place (every group has the same T rows, so no index, offsets or schedule are built). The
+// fp32 partial logits are then summed in the fixed order s = 0..KS-1, the bias added, and the
+// top-k taken.
 constexpr int kRouteKS = 4;
 
 __host__ __device__ inline size_t ralign(size_t v) { return (v + 255) & ~size_t(255); }
 
-struct RouteWs {
-    float* partial;     // [KS*T, E]
-    int32_t* a_rows;    // [KS*T]
-    int32_t* offsets;   // [KS+1]
-    char* gemm_ws;
-};
-
-inline RouteWs route_ws(void* ws, int64_t T, int E) {
-    char* p = (char*)ws;
-    RouteWs r;
-    r.partial = (float*)p;
-    p += ralign((size_t)kRouteKS * T * E * 4);
-    r.a_rows = (int32_t*)p;
-    p += ralign((size_t)kRouteKS * T * 4);
-    r.offsets = (int32_t*)p;
-    p += ralign((kRouteKS + 1) * 4);
-    r.gemm_ws = p;
-    return r;
-}
-
 inline bool route_uses_split(int64_t T, int64_t d, int E) {
     return T >= 256 && E % 8 == 0 && d % (64 * kRouteKS) == 0;
-}
-
-__global__ void route_split_init_kernel(int T, int32_t* __restrict__ a_rows, int32_t* __restrict__ offsets) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < kRouteKS * T) {
-        const int s = i / T, t = i % T;
-        a_rows[i] = t * kRouteKS + s;
-    }
-    if (i <= kRouteKS) offsets[i] = i * T;
 }
 
 constexpr int kTopkBT = 8;   // tokens per workgroup of the split-K top-k pass (2 per wave)
@@ -315,8 +286,7 @@ void launch_route_bf16(dim3 g, hipStream_t s, const void* x, const void* w, cons
 
 size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E) {
     if (T <= 0 || E <= 0 || !moe::route_uses_split(T, d, E)) return 0;
-    return moe::ralign((size_t)moe::kRouteKS * T * E * 4) + moe::ralign((size_t)moe::kRouteKS * T * 4) +
-           moe::ralign((moe::kRouteKS + 1) * 4) + moe_gemm_workspace_bytes(moe::kRouteKS);
+    return moe::ralign((size_t)moe::kRouteKS * T * E * 4);   // partial logits [KS*T, E] fp32
 }
 
 extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
@@ -337,42 +307,19 @@ extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t d
     dim3 grid((unsigned)moe::cdiv<int64_t>(T, moe::kRouteBT));
     const int Ti = (int)T, di = (int)d;
     if (split) {
-        moe::RouteWs ws = moe::route_ws(workspace, T, E);
-        const int n = moe::kRouteKS * Ti;
-        hipLaunchKernelGGL(moe::route_split_init_kernel, dim3(moe::cdiv(n + 1, 256)), dim3(256), 0, s, Ti, ws.a_rows,
-                           ws.offsets);
-        MOE_CHECK_LAUNCH();
-        moe_gemm_args_t g{};   // zero-initialised: no MXFP8 scales
-        g.G = moe::kRouteKS;
-        g.offsets = ws.offsets;
-        g.M = (int64_t)moe::kRouteKS * T;
-        g.N = E;
-        g.K = d / moe::kRouteKS;
-        g.A = x;
-        g.a_dtype = MOE_BF16;
-        g.lda = d / moe::kRouteKS;
-        g.A_rows = (int64_t)moe::kRouteKS * T;
-        g.a_rows = ws.a_rows;
-        g.B = w_router;
-        g.b_dtype = MOE_BF16;
-        g.ldb = d;
-        g.b_group_stride = d / moe::kRouteKS;
-        g.C = ws.partial;
-        g.c_dtype = MOE_F32;
-        g.ldc = E;
-        g.epilogue = MOE_EPI_NONE;
-        const moe_status_t st = moe_grouped_gemm(&g, ws.gemm_ws, moe_gemm_workspace_bytes(moe::kRouteKS), stream);
+        float* partial = (float*)workspace;
+        const moe_status_t st = moe_gemm_ksplit_f32(x, w_router, T, d, E, moe::kRouteKS, partial, s);
         if (st != MOE_OK) return st;
         const int nq = moe::cdiv(E, 64);
         const dim3 tgrid((unsigned)moe::cdiv<int64_t>(T, moe::kTopkBT));
         if (nq <= 1)
-            hipLaunchKernelGGL((moe::route_topk_kernel<1>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+            hipLaunchKernelGGL((moe::route_topk_kernel<1>), tgrid, dim3(moe::kRouteThreads), 0, s, partial, bias, Ti, E,
                                k, score, topk_idx, topk_w, keys_out);
         else if (nq <= 2)
-            hipLaunchKernelGGL((moe::route_topk_kernel<2>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+            hipLaunchKernelGGL((moe::route_topk_kernel<2>), tgrid, dim3(moe::kRouteThreads), 0, s, partial, bias, Ti, E,
                                k, score, topk_idx, topk_w, keys_out);
         else
-            hipLaunchKernelGGL((moe::route_topk_kernel<4>), tgrid, dim3(moe::kRouteThreads), 0, s, ws.partial, bias, Ti, E,
+            hipLaunchKernelGGL((moe::route_topk_kernel<4>), tgrid, dim3(moe::kRouteThreads), 0, s, partial, bias, Ti, E,
                                k, score, topk_idx, topk_w, keys_out);
         MOE_CHECK_LAUNCH();
         return MOE_OK;
