@@ -1,5 +1,8 @@
 // moe_route: router projection (bf16 MFMA, fp32 accumulate), expert bias, top-k selection
-// and normalised routing weights, fused in one kernel per 32-token tile.
+// and normalised routing weights. Small layers: one fused kernel per 32-token tile. Large
+// layers (the skinny projection would fill too few CUs): the projection as K-split partial
+// sums on the grouped-GEMM kernel, then one pass that sums them in a fixed order, adds the
+// bias and selects (two launches).
 //
 // [Blog] opening section: a learnable router picks each token's top-K experts;
 // [Blog] "Optimisation 2": a single fused router kernel assigns the experts.
