@@ -157,6 +157,10 @@ __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t*
 // rows are padded by 16 bytes so that the row-wise pass's 16-byte reads of 16 rows at one
 // column offset land on distinct banks.
 constexpr int kColTile = 128;        // columns per workgroup (bf16; 64 for fp32)
+#ifndef MOE_QUANT_NT
+#define MOE_QUANT_NT 1                // E4M3 code stores of the column-wise / dual pass non-temporal
+                                      // (DeepSeek-V3 weight stacks 9.85 -> 9.62 ms)
+#endif
 template <int ESIZE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, const int32_t* __restrict__ row_index,
@@ -236,7 +240,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
                                                              v[4 * w + 3] * inv);
             if (live) {
                 const int64_t r = r0 + i;                        // logical row
-                *reinterpret_cast<u32x4*>(q_row + r * ld_q_row + c0 + hb * 16) = out;
+                u32x4* dst = reinterpret_cast<u32x4*>(q_row + r * ld_q_row + c0 + hb * 16);
+                if (MOE_QUANT_NT) __builtin_nontemporal_store(out, dst);
+                else *dst = out;
                 if ((hb & 1) == 0) s_row[r * ld_s_row + c0 / kBlock + hb / 2] = (uint8_t)byte;
             }
         }
@@ -305,8 +311,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
         const int cc = pcs / (kGroupAlign * kBlock / 16), ch = pcs % (kGroupAlign * kBlock / 16);
         if (cc >= ncols) continue;
         const int64_t c = c0 + cc;
-        *reinterpret_cast<u32x4*>(q + (gbase + c * nbg + jb) * kBlock + ch * 16) =
-            *reinterpret_cast<const u32x4*>(stage + cc * SP + ch * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + cc * SP + ch * 16);
+        u32x4* dst = reinterpret_cast<u32x4*>(q + (gbase + c * nbg + jb) * kBlock + ch * 16);
+        if (MOE_QUANT_NT) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
     }
     if (t < ncols) *reinterpret_cast<uint32_t*>(sc + gbase + (int64_t)(c0 + t) * nbg + jb) = sstage[t];
 }
