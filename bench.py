@@ -60,11 +60,12 @@ def gemm_source_digest():
     return h.hexdigest()
 
 
-def pmc_traffic(workload):
-    """HBM bytes per launch of the gate/up GEMM kernel from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE passes, each scaled by the same counter's reading for a copy
-    of known size). None when no summary exists or the GEMM sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"gemm1_swiglu_{workload}_pmc.md")
+def pmc_traffic(workload, kernel="gemm1_swiglu"):
+    """HBM bytes per launch of one GEMM kernel (the bf16 gate/up GEMM, or an MXFP8 step's
+    dominant GEMM) from the committed counter summary (FETCH_SIZE and WRITE_SIZE passes, each
+    scaled by the same counter's reading for a copy of known size). None when no summary
+    exists or the GEMM sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -79,6 +80,18 @@ def pmc_traffic(workload):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def calibrate_copy(dev):
+    """A plain 1 GiB copy (torch.neg into a second buffer), three times, so a counter pass of
+    the same command sees the HBM bytes of a copy of known size."""
+    import torch
+    src = torch.zeros((COPY_CAL_BYTES // 2,), dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def useful_flops(w, counts):
@@ -280,7 +293,7 @@ def main_mx(args, w):
     else:
         roof = {"bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(fl / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": None, "kernel": f"moe_grouped_gemm MXFP8 {dom}", "algorithmic_bytes": int(by),
+    roof.update({"traffic": pmc_traffic(w.name, dom), "kernel": f"moe_grouped_gemm MXFP8 {dom}", "algorithmic_bytes": int(by),
                  "algorithmic_flops": fl, "ms": round(pm[dom], 4)})
     step_ms = float(per.sum(1).mean())
     no_wq = step_ms - pm["weight_quant"]
@@ -307,6 +320,8 @@ def main_mx(args, w):
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_mx(w, w_gu, w_down)
     print(json.dumps(res), flush=True)
@@ -443,12 +458,7 @@ def main():
                                    "bytes": pg_bytes, "indices_match_step": same}
     del gbuf
     if args.calibrate_copy:
-        src = torch.zeros((COPY_CAL_BYTES // 2,), dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_copy(dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, w_gu, w_down)
     print(json.dumps(res), flush=True)
