@@ -77,6 +77,9 @@ size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t 
  *   Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, d, E, k, 0) bytes, 256-byte aligned (it
  *   is non-zero for large bf16 layers, whose projection runs as a K-split grouped GEMM with
  *   fp32 partial logits summed in a fixed order; workspace may be NULL when it is zero).
+ *   Errors: MOE_EINVAL for bad sizes or pointers, MOE_EWORKSPACE for a missing or short
+ *   workspace, MOE_ENOTSUP for an unsupported dtype or (K-split path) x or w_router of 4 GiB
+ *   or more, MOE_EHIP for a failed launch.
  */
 moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const float* bias,
                        int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
