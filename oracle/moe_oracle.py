@@ -126,6 +126,44 @@ def route(x, w_router, bias, k: int, score: str):
     return idx, topk_weights(keys, idx, score), keys
 
 
+def topk_weights_backward(keys, topk_idx, d_topk_w, score: str) -> np.ndarray:
+    """Gradient with respect to the keys [T, E] of a loss whose gradient with respect to the
+    normalised routing weights is d_topk_w [T, k]. The selection is piecewise constant in the
+    keys, so only the selected experts receive gradient ([Blog] opening section: the router
+    picks the top-K experts; READING: the router's own backward is the derivative of the
+    weight formula of topk_weights with the selection held fixed).
+
+    softmax: w = softmax over the selected keys, so d kappa_j = w_j (g_j - sum_i w_i g_i).
+    sigmoid: w_j = s_j / S with S = sum_i s_i, so dL/ds_j = (g_j - sum_i w_i g_i) / S and
+             d kappa_j = dL/ds_j * s_j (1 - s_j).
+    """
+    keys = np.asarray(keys, F64)
+    idx = np.asarray(topk_idx, np.int64)
+    g = np.asarray(d_topk_w, F64)
+    kk = np.take_along_axis(keys, idx, axis=1)
+    if score == "softmax":
+        z = np.exp(kk - kk[:, :1])
+        w = z / z.sum(axis=1, keepdims=True)
+        dk = w * (g - (w * g).sum(axis=1, keepdims=True))
+    elif score == "sigmoid":
+        sg = 1.0 / (1.0 + np.exp(-kk))
+        S = sg.sum(axis=1, keepdims=True)
+        w = sg / S
+        dk = (g - (w * g).sum(axis=1, keepdims=True)) / S * sg * (1.0 - sg)
+    else:
+        raise ValueError(score)
+    out = np.zeros_like(keys)
+    np.put_along_axis(out, idx, dk, axis=1)
+    return out
+
+
+def router_backward(x, w_router, d_keys):
+    """The keys are x W_r^T + b, so with G = d_keys [T, E]: dW_r = G^T x [E, d],
+    dx = G W_r [T, d] (the router's share of the input gradient), d_bias = column sums [E]."""
+    G = np.asarray(d_keys, F64)
+    return G.T @ np.asarray(x, F64), G @ np.asarray(w_router, F64), G.sum(axis=0)
+
+
 # --------------------------------------------------------------------------------------
 # dispatch: counts, offsets, permutation, gather
 #   ([Blog] "Optimisation 2": dispatch reorders tokens locally so each expert's tokens

@@ -456,3 +456,74 @@ def test_mx_backward_on_grid_inputs_matches_plain_where_operands_are_on_grid():
     np.testing.assert_array_equal(a["G"], b["G"])
     np.testing.assert_array_equal(a["U"], b["U"])
     np.testing.assert_array_equal(a["dH"], b["dH"])
+
+
+# ----------------------------------------------------------------------------- router backward
+
+def _router_loss(x, wr, b, g, idx, score):
+    """sum_tj g[t,j] w[t,j] with the pure fp64 keys x W_r^T + b and a fixed selection."""
+    keys = x @ wr.T + b
+    return float((g * O.topk_weights(keys, idx, score)).sum())
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_router_backward_matches_finite_differences(score):
+    gen = np.random.Generator(np.random.PCG64(31))
+    T, d, E, k = 5, 6, 7, 3
+    x = gen.standard_normal((T, d))
+    wr = gen.standard_normal((E, d)) * 0.5
+    b = gen.standard_normal(E) * 0.3
+    g = gen.standard_normal((T, k))
+    keys = x @ wr.T + b
+    idx = O.select_topk(keys, k)
+    srt = -np.sort(-keys, axis=1)
+    assert (srt[:, k - 1] - srt[:, k]).min() > 1e-3          # the selection cannot move under eps
+    dkeys = O.topk_weights_backward(keys, idx, g, score)
+    dW, dx, db = O.router_backward(x, wr, dkeys)
+    eps = 1e-6
+    for arr, grad in ((x, dx), (wr, dW), (b, db)):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            a0 = arr[i]
+            arr[i] = a0 + eps
+            lp = _router_loss(x, wr, b, g, idx, score)
+            arr[i] = a0 - eps
+            lm = _router_loss(x, wr, b, g, idx, score)
+            arr[i] = a0
+            num[i] = (lp - lm) / (2 * eps)
+        assert np.abs(num - grad).max() <= 1e-7 * max(1.0, np.abs(num).max())
+    # unselected experts get no gradient
+    mask = np.zeros_like(keys, dtype=bool)
+    np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+    assert np.all(dkeys[~mask] == 0.0)
+
+
+def test_router_backward_softmax_k_equals_E_is_softmax_jacobian():
+    # with every expert selected the weights are a plain softmax: d kappa = (diag(w) - w w^T) g
+    gen = np.random.Generator(np.random.PCG64(32))
+    T, E = 4, 6
+    keys = gen.standard_normal((T, E))
+    g = gen.standard_normal((T, E))
+    idx = O.select_topk(keys, E)
+    dk = O.topk_weights_backward(keys, idx, g, "softmax")
+    for t in range(T):
+        w = scipy.special.softmax(keys[t])
+        J = np.diag(w) - np.outer(w, w)
+        g_e = np.zeros(E)
+        g_e[idx[t]] = g[t]                                  # weights are stored in selection order
+        np.testing.assert_allclose(dk[t], J @ g_e, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_router_backward_invariants(score):
+    gen = np.random.Generator(np.random.PCG64(33))
+    T, E, k = 50, 16, 4
+    keys = gen.standard_normal((T, E))
+    idx = O.select_topk(keys, k)
+    # a gradient equal on every selected weight changes nothing: the weights sum to one
+    c = gen.standard_normal((T, 1)) * np.ones((1, k))
+    assert np.abs(O.topk_weights_backward(keys, idx, c, score)).max() < 1e-15
+    if score == "softmax":
+        # a common shift of the selected keys leaves a softmax unchanged
+        g = gen.standard_normal((T, k))
+        assert np.abs(O.topk_weights_backward(keys, idx, g, score).sum(axis=1)).max() < 1e-14
