@@ -20,7 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT = 0, 1, 2, 3
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT, MOE_OP_ROUTE_BWD = 0, 1, 2, 3, 4
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -61,9 +61,13 @@ _lib.moe_combine_backward.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32
 _lib.moe_combine_backward.restype = _i32
 _lib.moe_swiglu_backward.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i64, _vp]
 _lib.moe_swiglu_backward.restype = _i32
+_lib.moe_route_backward.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
+                                    _vp, _vp, _vp, _sz, _vp]
+_lib.moe_route_backward.restype = _i32
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
-            "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward")
+            "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward",
+            "moe_route_backward")
 
 
 class MoeError(RuntimeError):
@@ -202,6 +206,22 @@ def moe_combine_backward(d_out, topk_w, row_of, dy, y=None, dy_shared=None, dw=N
     _check("moe_combine_backward", _lib.moe_combine_backward(
         _ptr(d_out), _dtype(d_out), _ptr(topk_w), _ptr(row_of), _ptr(y), T, d, k, _ptr(dy), _ptr(dy_shared),
         _ptr(dw), _stream(stream)))
+
+
+def moe_route_backward(x, w_router, keys, topk_idx, d_topk_w, score: int, row_of, offsets=None, src_token=None,
+                       d_keys_sel=None, d_x=None, d_w_router=None, d_bias=None, workspace=None, stream=None):
+    """Router backward: d_topk_w [T,k] fp32 -> d_keys_sel [T,k] fp32, d_x [T,d] (dtype of x),
+    d_w_router [E,d] fp32, d_bias [E] fp32 (each optional). keys [T,E] fp32 and topk_idx come from
+    moe_route, offsets / row_of / src_token from moe_permute. `workspace`: a uint8 device tensor of
+    moe_workspace_bytes(MOE_OP_ROUTE_BWD, T, 0, 0, k) bytes."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    k = topk_idx.shape[1]
+    ws, wsb = _ws(workspace)
+    _check("moe_route_backward", _lib.moe_route_backward(
+        _ptr(x), _ptr(w_router), _dtype(x), _ptr(keys), _ptr(topk_idx), _ptr(d_topk_w), _ptr(offsets), _ptr(row_of),
+        _ptr(src_token), T, d, E, k, score, _ptr(d_keys_sel), _ptr(d_x), _ptr(d_w_router), _ptr(d_bias), ws, wsb,
+        _stream(stream)))
 
 
 def moe_swiglu_backward(dh, gu, dgu, stream=None):

@@ -48,7 +48,13 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
 typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue_t;
-typedef enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2, MOE_OP_QUANT = 3 } moe_op_t;
+typedef enum {
+    MOE_OP_ROUTE = 0,
+    MOE_OP_PERMUTE = 1,
+    MOE_OP_GROUPED_GEMM = 2,
+    MOE_OP_QUANT = 3,
+    MOE_OP_ROUTE_BWD = 4
+} moe_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_str(int32_t status);
@@ -85,6 +91,42 @@ moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const
                        int64_t T, int64_t d, int32_t E, int32_t k, int32_t score,
                        int32_t* topk_idx, float* topk_w, float* keys_out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_backward -- the router's backward: from the gradient of the loss with respect to
+ * the normalised top-k weights to the gradients of the keys, the router weights, the expert
+ * bias and the router's share of the input gradient.
+ * [Blog] opening section: the router is learnable and trained with the layer. The top-k
+ * selection is piecewise constant in the keys, so only the k selected keys of a token get
+ * gradient (g = d_topk_w[t,:], w = topk_w as moe_route forms it, S = sum_j s_j):
+ *   score == MOE_SOFTMAX: dkey_j = w_j * (g_j - sum_i w_i g_i)
+ *   score == MOE_SIGMOID: dkey_j = (g_j - sum_i w_i g_i) / S * s_j * (1 - s_j)
+ * and with key = x w_router^T + bias (dkey zero for unselected experts):
+ *   d_keys_sel[t,j]  = dkey_j of expert topk_idx[t,j]                      [T, k] fp32
+ *   d_x[t,:]         = sum_j dkey_j * w_router[topk_idx[t,j],:]  fp32 sum in slot order,
+ *                      rounded once to dtype                                [T, d]
+ *   d_w_router[e,:]  = sum over tokens t that picked e of dkey * x[t,:]     [E, d] fp32
+ *                      (rows of expert e in ascending token order)
+ *   d_bias[e]        = sum of the same dkey (fixed-order tree)              [E] fp32
+ * Each of the four outputs may be NULL (not computed). The call overwrites the outputs it
+ * computes: d_x holds only the router's share and is not accumulated into.
+ *
+ *   x [T, d], w_router [E, d]: dtype MOE_BF16 or MOE_F32, 16-byte aligned, d % 8 == 0;
+ *   keys [T, E] fp32: moe_route's keys_out; topk_idx [T, k]: moe_route's selection;
+ *   d_topk_w [T, k] fp32; offsets [E+1 or more], row_of [T, k], src_token [T*k or more]:
+ *   moe_permute's outputs for this topk_idx (needed when d_w_router or d_bias is wanted;
+ *   row_of always). 1 <= k <= min(E, 16), 1 <= E <= 256.
+ *   Workspace: moe_workspace_bytes(MOE_OP_ROUTE_BWD, T, d, E, k, 0) bytes, 256-byte aligned.
+ *   Deterministic: no atomics. Errors: MOE_EINVAL for bad sizes or pointers (d_w_router
+ *   must be 16-byte aligned), MOE_ENOTSUP for another dtype, MOE_EWORKSPACE for a missing or
+ *   short workspace, MOE_EHIP for a failed launch.
+ */
+moe_status_t moe_route_backward(const void* x, const void* w_router, int32_t dtype, const float* keys,
+                                const int32_t* topk_idx, const float* d_topk_w, const int32_t* offsets,
+                                const int32_t* row_of, const int32_t* src_token, int64_t T, int64_t d,
+                                int32_t E, int32_t k, int32_t score, float* d_keys_sel, void* d_x,
+                                float* d_w_router, float* d_bias, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * moe_permute -- dispatch on one GPU: per-expert histogram, group offsets, permutation and

@@ -33,6 +33,7 @@ _M3 = 0x297A2D39
 
 # tensor ids of the key derivation
 X, W_ROUTER, W_GATE, W_UP, W_DOWN, SHARED, D_OUT = 0, 1, 3, 4, 5, 6, 7
+D_TOPK_W = 8   # the gradient reaching the routing weights, for the router backward alone
 
 
 def _mix(x):
