@@ -562,11 +562,16 @@ def expert_backward(X, w_gu_e, w_down_e, dY, rnd=None, mx=False):
     return dict(dX=dX, dW_gu=dWgu, dW_down=dWd, dH=dH, dG=dG, dU=dU, H=H, G=G, U=U)
 
 
-def layer_backward(fwd, d_out, w_gu, w_down, E, shared=False, rnd=None, mx=False):
+def layer_backward(fwd, d_out, w_gu, w_down, E, shared=False, rnd=None, mx=False, router=None):
     """Backward of the expert, permute and combine steps of `layer_forward`'s result.
 
     Returns dict(dx [T,d], dY [T*k,d] (routed rows), dw [T,k], dW_gu {g: [2f,d]},
     dW_down {g: [d,f]}, dX_perm [rows,d]). An empty group's weight gradients are zeros.
+
+    router = (x, w_router, score) adds the router's backward ([Blog] opening section: the
+    router is trained with the layer, so the loss reaches the keys through the routing
+    weights): d_keys [T,E], dW_router [E,d], d_bias [E], and the layer input's gradient
+    becomes the expert path's (as stored) plus the router's share, rounded once.
     """
     r = _rounder(rnd)
     T, k = fwd["row_of"].shape
@@ -587,4 +592,10 @@ def layer_backward(fwd, d_out, w_gu, w_down, E, shared=False, rnd=None, mx=False
         dXp[lo:hi] = res["dX"]
         dWgu[g], dWd[g] = res["dW_gu"], res["dW_down"]
     dx = permute_backward(dXp[:T * k], fwd["row_of"], dXp[T * k:] if shared else None, rnd)
-    return dict(dx=dx, dY=dY, dw=dw, dW_gu=dWgu, dW_down=dWd, dX_perm=dXp)
+    out = dict(dx=dx, dY=dY, dw=dw, dW_gu=dWgu, dW_down=dWd, dX_perm=dXp)
+    if router is not None:
+        x, w_router, score = router
+        d_keys = topk_weights_backward(fwd["keys"], fwd["topk_idx"], dw, score)
+        dWr, dx_r, db = router_backward(x, w_router, d_keys)
+        out.update(dx=r(dx + dx_r), d_keys=d_keys, dW_router=dWr, d_bias=db)
+    return out

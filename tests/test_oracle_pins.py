@@ -427,6 +427,42 @@ def test_backward_matches_finite_differences():
         assert bwd["dW_down"][e][i, n % 3] == pytest.approx(num, rel=1e-6, abs=1e-9)
 
 
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_layer_backward_with_router_matches_finite_differences(score):
+    """The whole layer, routing included: the loss's gradients with respect to the input, the
+    router weights and the expert bias, by central differences with the routing recomputed
+    at every point (the keys' top-k margin is far above the step, so the selection holds).
+    The keys are stored in fp32, so x, the router weights, the bias and the step are dyadic
+    with few bits: every perturbed key is then exact and the differences carry no rounding."""
+    x, wr, b, Wgu, Wd = _tiny_layer(16, T=6, d=5, f=3, E=4)
+    x, wr, b = np.round(x * 8) / 8, np.round(wr * 16) / 16, np.round(b * 64) / 64
+    E, k = 4, 2
+    dO = np.random.Generator(np.random.PCG64(5)).standard_normal(x.shape)
+    gu, dn = (lambda e: Wgu[e]), (lambda e: Wd[e])
+
+    def loss(xx, wr_, b_):
+        return np.sum(O.layer_forward(xx, wr_, b_, k, score, gu, dn, E, shared=True)["out"] * dO)
+
+    fwd = O.layer_forward(x, wr, b, k, score, gu, dn, E, shared=True)
+    h = 2.0 ** -12
+    srt = -np.sort(-fwd["keys"].astype(np.float64), axis=1)
+    assert np.min(srt[:, k - 1] - srt[:, k]) > 2 * h * max(np.abs(x).max(), np.abs(wr).max(), 1.0)
+    bwd = O.layer_backward(fwd, dO, gu, dn, E, shared=True, router=(x, wr, score))
+
+    def num(a, pos, f):
+        ap, am = a.copy(), a.copy()
+        ap[pos] += h
+        am[pos] -= h
+        return (f(ap) - f(am)) / (2 * h)
+
+    for pos in [(0, 0), (3, 4), (5, 2)]:
+        assert bwd["dx"][pos] == pytest.approx(num(x, pos, lambda a: loss(a, wr, b)), rel=1e-6, abs=1e-9)
+    for pos in [(0, 1), (2, 3), (3, 0)]:
+        assert bwd["dW_router"][pos] == pytest.approx(num(wr, pos, lambda a: loss(x, a, b)), rel=1e-6, abs=1e-9)
+    for e in range(E):
+        assert bwd["d_bias"][e] == pytest.approx(num(b, (e,), lambda a: loss(x, wr, a)), rel=1e-6, abs=1e-9)
+
+
 def test_backward_empty_group_has_zero_weight_grad():
     x, wr, b, Wgu, Wd = _tiny_layer(15, d=64, f=32, E=4)
     idx = np.array([[0, 1]] * x.shape[0], np.int32)   # experts 2 and 3 empty
