@@ -264,7 +264,7 @@ def main_mx(args, w):
         if mark:
             mark("weight_quant")
         layer.forward_mx(x, wr, bias, mw, s, b, mark=mark)
-        layer.backward_mx(x, d_out, mw, s, b, mark=mark)
+        layer.backward_mx(x, d_out, mw, s, b, mark=mark, w_router=wr)
 
     for _ in range(args.warmup):
         step()

@@ -9,8 +9,9 @@
 //   softmax: w = softmax over the selected keys,  dk_j = w_j (g_j - sum_i w_i g_i)
 //   sigmoid: w_j = s_j / S, s_j = sigmoid(k_j),    dk_j = (g_j - sum_i w_i g_i) / S * s_j (1 - s_j)
 // and with the keys = x W_r^T + b:
-//   dW_r[e] = sum over tokens t that selected e of dk[t,e] x[t]   (fp32, one expert group at a
-//             time, rows in the permutation's ascending token order)
+//   dW_r[e] = sum over tokens t that selected e of dk[t,e] x[t]   (fp32; the expert's rows in
+//             the permutation's ascending token order, in chunks of 256 rows whose partial
+//             sums are then added in chunk order)
 //   d_bias[e] = sum of the same dk[t,e]                             (fp32, fixed-order tree)
 //   dx[t]   = sum_j dk[t,j] W_r[S_tj]                                (fp32 sum in slot order,
 //             one rounding to the input dtype)
@@ -21,6 +22,7 @@ namespace {
 
 constexpr int kRbThreads = 256;
 constexpr int kRbCols = kRbThreads * 8;   // columns of dW_r per workgroup (8 per thread)
+constexpr int kRbChunk = 256;             // permuted rows per weight-gradient partial sum
 
 __host__ __device__ inline size_t rb_align(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -105,7 +107,7 @@ template <int ESIZE>
 __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __restrict__ w_router,
                                                                   const int32_t* __restrict__ topk_idx,
                                                                   const float* __restrict__ dk_sel, int d, int E,
-                                                                  int k, char* __restrict__ dx) {
+                                                                  int k, int accumulate, char* __restrict__ dx) {
     const int t = blockIdx.x;
     __shared__ int rows[16];
     __shared__ float coef[16];
@@ -125,6 +127,12 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __
             for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
         }
         char* o = dx + t * rowbytes + (int64_t)c * 8 * ESIZE;
+        if (accumulate) {   // the incoming gradient joins the fp32 sum; still one rounding
+            float v[8];
+            ld8f<ESIZE>(o, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
         if (ESIZE == 2) {
             u32x4 q;
 #pragma unroll
@@ -144,50 +152,112 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __
     }
 }
 
-// dW_r[e, cols] over expert e's group of permuted rows (ascending token order, four rows'
-// loads issued together), and d_bias[e] from the workgroups of the first column block.
+// Each expert's group of permuted rows is cut into chunks of kRbChunk rows, so a hot
+// expert's rows spread over many workgroups. chunk_off[e] = number of chunks of experts < e.
+__global__ __launch_bounds__(kRbThreads) void route_bwd_chunks_kernel(const int32_t* __restrict__ offsets, int E,
+                                                                      int TK, int32_t* __restrict__ chunk_off) {
+    __shared__ int c[kRbThreads];
+    const int e = threadIdx.x;
+    int n = 0;
+    if (e < E) {
+        const int rb = min(max(offsets[e], 0), TK);
+        const int re = min(max(offsets[e + 1], rb), TK);
+        n = cdiv(re - rb, kRbChunk);
+    }
+    c[e] = n;
+    __syncthreads();
+    for (int h = 1; h < kRbThreads; h <<= 1) {   // inclusive scan
+        const int v = e >= h ? c[e - h] : 0;
+        __syncthreads();
+        c[e] += v;
+        __syncthreads();
+    }
+    if (e == 0) chunk_off[0] = 0;
+    if (e < E) chunk_off[e + 1] = c[e];
+}
+
+// partial[chunk, cols] = sum over the chunk's rows (ascending) of dk[r] * x[src_token[r], cols];
+// four rows' loads are issued together. Workgroups past the last chunk exit at once.
 template <int ESIZE>
-__global__ __launch_bounds__(kRbThreads) void route_bwd_dw_kernel(const char* __restrict__ x,
-                                                                  const int32_t* __restrict__ offsets,
-                                                                  const int32_t* __restrict__ src_token,
-                                                                  const float* __restrict__ dk_perm, int T, int d,
-                                                                  int TK, float* __restrict__ dw,
-                                                                  float* __restrict__ dbias) {
-    const int e = blockIdx.x;
-    const int col = blockIdx.y * kRbCols + threadIdx.x * 8;
+__global__ __launch_bounds__(kRbThreads) void route_bwd_dw_partial_kernel(const char* __restrict__ x,
+                                                                          const int32_t* __restrict__ offsets,
+                                                                          const int32_t* __restrict__ chunk_off,
+                                                                          const int32_t* __restrict__ src_token,
+                                                                          const float* __restrict__ dk_perm, int T,
+                                                                          int d, int E, int TK,
+                                                                          float* __restrict__ partial) {
+    const int ch = blockIdx.x;
+    if (ch >= chunk_off[E]) return;
+    int lo = 0, hi = E - 1;   // the expert whose chunks hold ch: largest e with chunk_off[e] <= ch
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= ch) lo = mid;
+        else hi = mid - 1;
+    }
+    const int e = lo;
     const int rb = min(max(offsets[e], 0), TK);
     const int re = min(max(offsets[e + 1], rb), TK);
+    const int r_begin = min(rb + (ch - chunk_off[e]) * kRbChunk, re);
+    const int r_end = min(r_begin + kRbChunk, re);
+    const int col = blockIdx.y * kRbCols + threadIdx.x * 8;
+    if (col >= d) return;
     const int64_t rowbytes = (int64_t)d * ESIZE;
-    if (dw != nullptr && col < d) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        constexpr int U = 4;
-        for (int r0 = rb; r0 < re; r0 += U) {
-            float v[U][8], c[U];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 4;
+    for (int r0 = r_begin; r0 < r_end; r0 += U) {
+        float v[U][8], c[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = r0 + u;
-                c[u] = 0.f;
-                if (r < re) {
-                    const int tok = min(max(src_token[r], 0), T - 1);
-                    c[u] = dk_perm[r];
-                    ld8f<ESIZE>(x + tok * rowbytes + (int64_t)col * ESIZE, v[u]);
-                }
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u;
+            c[u] = 0.f;
+            if (r < r_end) {
+                const int tok = min(max(src_token[r], 0), T - 1);
+                c[u] = dk_perm[r];
+                ld8f<ESIZE>(x + tok * rowbytes + (int64_t)col * ESIZE, v[u]);
             }
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (r0 + u < re)
+        for (int u = 0; u < U; ++u)
+            if (r0 + u < r_end)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(c[u], v[u][i], acc[i]);
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(c[u], v[u][i], acc[i]);
+    }
+    float* o = partial + (int64_t)ch * d + col;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// dW_r[e, cols] = expert e's chunk partials summed in chunk order (zero for an empty group);
+// d_bias[e] from the workgroups of the first column block (fixed-order tree over the rows).
+__global__ __launch_bounds__(kRbThreads) void route_bwd_dw_reduce_kernel(const float* __restrict__ partial,
+                                                                         const int32_t* __restrict__ offsets,
+                                                                         const int32_t* __restrict__ chunk_off,
+                                                                         const float* __restrict__ dk_perm, int d,
+                                                                         int TK, int max_chunks,
+                                                                         float* __restrict__ dw,
+                                                                         float* __restrict__ dbias) {
+    const int e = blockIdx.x;
+    const int col = blockIdx.y * kRbCols + threadIdx.x * 8;
+    if (dw != nullptr && col < d) {
+        const int c0 = min(chunk_off[e], max_chunks);
+        const int c1 = min(max(chunk_off[e + 1], c0), max_chunks);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        for (int c = c0; c < c1; ++c) {
+            const float* p = partial + (int64_t)c * d + col;
+            a += *reinterpret_cast<const f32x4*>(p);
+            b += *reinterpret_cast<const f32x4*>(p + 4);
         }
         float* o = dw + (int64_t)e * d + col;
-        *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        *reinterpret_cast<f32x4*>(o) = a;
+        *reinterpret_cast<f32x4*>(o + 4) = b;
     }
     if (dbias != nullptr && blockIdx.y == 0) {
+        const int rb = min(max(offsets[e], 0), TK);
+        const int re = min(max(offsets[e + 1], rb), TK);
         __shared__ float part[kRbThreads];
-        float s = 0.f;
-        for (int r = rb + (int)threadIdx.x; r < re; r += kRbThreads) s += dk_perm[r];
-        part[threadIdx.x] = s;
+        float sum = 0.f;
+        for (int r = rb + (int)threadIdx.x; r < re; r += kRbThreads) sum += dk_perm[r];
+        part[threadIdx.x] = sum;
         __syncthreads();
         for (int h = kRbThreads / 2; h > 0; h >>= 1) {
             if ((int)threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
@@ -200,19 +270,27 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dw_kernel(const char* __
 }  // namespace
 }  // namespace moe
 
-size_t moe_route_backward_workspace_bytes(int64_t T, int32_t k) {
-    if (T <= 0 || k <= 0) return 256;
-    return 2 * moe::rb_align((size_t)T * k * 4);   // dk per slot [T, k], dk per permuted row [T*k]
+namespace {
+int64_t rb_max_chunks(int64_t T, int32_t k, int32_t E) { return moe::cdiv<int64_t>(T * k, moe::kRbChunk) + E; }
+}  // namespace
+
+// dk per slot [T, k], dk per permuted row [T*k], chunk offsets [E+1], and the weight
+// gradient's chunk partials [cdiv(T*k, kRbChunk) + E, d] fp32.
+size_t moe_route_backward_workspace_bytes(int64_t T, int64_t d, int32_t E, int32_t k) {
+    if (T < 0 || d <= 0 || E < 1 || k < 1) return 256;
+    return 2 * moe::rb_align((size_t)T * k * 4) + moe::rb_align((size_t)(E + 1) * 4) +
+           moe::rb_align((size_t)rb_max_chunks(T, k, E) * d * 4);
 }
 
 extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, int32_t dtype, const float* keys,
                                            const int32_t* topk_idx, const float* d_topk_w, const int32_t* offsets,
                                            const int32_t* row_of, const int32_t* src_token, int64_t T, int64_t d,
                                            int32_t E, int32_t k, int32_t score, float* d_keys_sel, void* d_x,
-                                           float* d_w_router, float* d_bias, void* workspace,
+                                           int32_t accumulate_dx, float* d_w_router, float* d_bias, void* workspace,
                                            size_t workspace_bytes, void* stream) {
     if (T < 0 || d <= 0 || d % 8 != 0 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return MOE_EINVAL;
-    if (T > INT32_MAX / 16 || d > INT32_MAX / 16 || T * (int64_t)d > ((int64_t)1 << 40)) return MOE_EINVAL;
+    if (T * (int64_t)k > ((int64_t)1 << 30) || d > INT32_MAX / 16 || T * (int64_t)d > ((int64_t)1 << 40))
+        return MOE_EINVAL;
     if (score != MOE_SOFTMAX && score != MOE_SIGMOID) return MOE_EINVAL;
     if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
     const bool want_w = d_w_router != nullptr || d_bias != nullptr;
@@ -225,7 +303,7 @@ extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, 
         if (want_w && (!x || !src_token || !moe_aligned16(x))) return MOE_EINVAL;
     }
     if (d_w_router && !moe_aligned16(d_w_router)) return MOE_EINVAL;
-    if (!workspace || workspace_bytes < moe_route_backward_workspace_bytes(T, k)) return MOE_EWORKSPACE;
+    if (!workspace || workspace_bytes < moe_route_backward_workspace_bytes(T, d, E, k)) return MOE_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     const int Ti = (int)T, di = (int)d, TK = (int)(T * k);
@@ -241,21 +319,36 @@ extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, 
         if (d_x != nullptr) {
             if (esize == 2)
                 hipLaunchKernelGGL(moe::route_bwd_dx_kernel<2>, dim3((unsigned)Ti), dim3(moe::kRbThreads), 0, s,
-                                   (const char*)w_router, topk_idx, dk_sel, di, E, k, (char*)d_x);
+                                   (const char*)w_router, topk_idx, dk_sel, di, E, k, accumulate_dx != 0 ? 1 : 0,
+                                   (char*)d_x);
             else
                 hipLaunchKernelGGL(moe::route_bwd_dx_kernel<4>, dim3((unsigned)Ti), dim3(moe::kRbThreads), 0, s,
-                                   (const char*)w_router, topk_idx, dk_sel, di, E, k, (char*)d_x);
+                                   (const char*)w_router, topk_idx, dk_sel, di, E, k, accumulate_dx != 0 ? 1 : 0,
+                                   (char*)d_x);
             MOE_CHECK_LAUNCH();
         }
     }
     if (want_w) {
-        const dim3 grid((unsigned)E, (unsigned)moe::cdiv(di, moe::kRbCols));
-        if (esize == 2)
-            hipLaunchKernelGGL(moe::route_bwd_dw_kernel<2>, grid, dim3(moe::kRbThreads), 0, s, (const char*)x, offsets,
-                               src_token, dk_perm, Ti, di, TK, d_w_router, d_bias);
-        else
-            hipLaunchKernelGGL(moe::route_bwd_dw_kernel<4>, grid, dim3(moe::kRbThreads), 0, s, (const char*)x, offsets,
-                               src_token, dk_perm, Ti, di, TK, d_w_router, d_bias);
+        const int max_chunks = (int)rb_max_chunks(T, k, E);
+        const int col_blocks = moe::cdiv(di, moe::kRbCols);
+        int32_t* chunk_off = (int32_t*)((char*)dk_perm + moe::rb_align((size_t)T * k * 4));
+        float* partial = (float*)((char*)chunk_off + moe::rb_align((size_t)(E + 1) * 4));
+        hipLaunchKernelGGL(moe::route_bwd_chunks_kernel, dim3(1), dim3(moe::kRbThreads), 0, s, offsets, E, TK,
+                           chunk_off);
+        MOE_CHECK_LAUNCH();
+        if (d_w_router != nullptr) {
+            const dim3 grid((unsigned)max_chunks, (unsigned)col_blocks);
+            if (esize == 2)
+                hipLaunchKernelGGL(moe::route_bwd_dw_partial_kernel<2>, grid, dim3(moe::kRbThreads), 0, s,
+                                   (const char*)x, offsets, chunk_off, src_token, dk_perm, Ti, di, E, TK, partial);
+            else
+                hipLaunchKernelGGL(moe::route_bwd_dw_partial_kernel<4>, grid, dim3(moe::kRbThreads), 0, s,
+                                   (const char*)x, offsets, chunk_off, src_token, dk_perm, Ti, di, E, TK, partial);
+            MOE_CHECK_LAUNCH();
+        }
+        hipLaunchKernelGGL(moe::route_bwd_dw_reduce_kernel, dim3((unsigned)E, (unsigned)col_blocks),
+                           dim3(moe::kRbThreads), 0, s, partial, offsets, chunk_off, dk_perm, di, TK, max_chunks,
+                           d_w_router, d_bias);
         MOE_CHECK_LAUNCH();
     }
     return MOE_OK;

@@ -188,6 +188,12 @@ class MxBuffers(LayerBuffers):
         self.bs = torch.empty((G + 1,), dtype=torch.int32, device=dev)
         self.dW_gu = torch.empty((G, 2 * f, d), **bf)
         self.dW_down = torch.empty((G, d, f), **bf)
+        # the router's backward: keys saved by the forward, fp32 gradients of its parameters
+        self.keys = torch.empty((s.T, s.E), dtype=torch.float32, device=dev)
+        self.dW_router = torch.empty((s.E, d), dtype=torch.float32, device=dev)
+        self.d_bias = torch.empty((s.E,), dtype=torch.float32, device=dev)
+        rbb = L.moe_workspace_bytes(L.MOE_OP_ROUTE_BWD, s.T, d, s.E, s.k, 0)
+        self.ws_route_bwd = torch.empty((rbb,), dtype=torch.uint8, device=dev)
         gb = L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, G)
         self.ws_gemm3 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
 
@@ -202,10 +208,11 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
     H quantised row-wise (and, in the same pass, column-wise for the backward's wgrad 2),
     GEMM 2, combine. mw must hold this step's quantised weights.
     routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment.
+    Otherwise the router's keys are kept in b.keys for its backward.
     mark(name), if given, is called after each stage (e.g. to record a timing event)."""
     mark = mark or _nomark
     if not routed:
-        route(x, w_router, bias, s, b)
+        route(x, w_router, bias, s, b, keys_out=b.keys)
     mark("route")
     permute(x, s, b)
     mark("permute")
@@ -224,13 +231,16 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
     return b.out
 
 
-def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None):
-    """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down.
+def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None, w_router=None):
+    """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down and,
+    when w_router is given (a forward that ran the router), b.dW_router and b.d_bias.
 
     combine^T -> dY; dgrad 2 (dH = dY W_down, contracted over d) and wgrad 2 (dW_down[g] =
     dY_g^T H_g over the group's tokens); SwiGLU backward from the saved G, U; dgrad 1
-    (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx.
-    The router's own backward is not part of this step."""
+    (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx;
+    then the router's backward: the routing weights' gradient dw through the top-k
+    normalisation to the keys, from there to W_router and the bias, and the router's share
+    of the input gradient added into dx."""
     mark = mark or _nomark
     tk = s.T * s.k
     L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
@@ -264,3 +274,8 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None)
     # permute^T: each token's rows summed back (plus the shared expert's row)
     L.moe_combine(b.dXp[:tk], None, b.row_of, b.dXp[tk:] if s.shared else None, b.dx)
     mark("unpermute")
+    if w_router is not None:
+        L.moe_route_backward(x, w_router, b.keys, b.topk_idx, b.dw, s.score, b.row_of, offsets=b.offsets,
+                             src_token=b.src_token, d_x=b.dx, accumulate_dx=True, d_w_router=b.dW_router,
+                             d_bias=b.d_bias, workspace=b.ws_route_bwd)
+        mark("route_bwd")

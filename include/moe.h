@@ -105,11 +105,15 @@ moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const
  *   d_keys_sel[t,j]  = dkey_j of expert topk_idx[t,j]                      [T, k] fp32
  *   d_x[t,:]         = sum_j dkey_j * w_router[topk_idx[t,j],:]  fp32 sum in slot order,
  *                      rounded once to dtype                                [T, d]
+ *                      (accumulate_dx != 0: d_x[t,:] + that sum, the incoming value
+ *                      read into the fp32 sum and the total rounded once, so the expert
+ *                      path's input gradient and the router's join in one buffer)
  *   d_w_router[e,:]  = sum over tokens t that picked e of dkey * x[t,:]     [E, d] fp32
- *                      (rows of expert e in ascending token order)
+ *                      (rows of expert e in ascending token order, summed in
+ *                      chunks of 256 rows whose partials are added in chunk order)
  *   d_bias[e]        = sum of the same dkey (fixed-order tree)              [E] fp32
  * Each of the four outputs may be NULL (not computed). The call overwrites the outputs it
- * computes: d_x holds only the router's share and is not accumulated into.
+ * computes (d_x as stated above).
  *
  *   x [T, d], w_router [E, d]: dtype MOE_BF16 or MOE_F32, 16-byte aligned, d % 8 == 0;
  *   keys [T, E] fp32: moe_route's keys_out; topk_idx [T, k]: moe_route's selection;
@@ -125,8 +129,8 @@ moe_status_t moe_route_backward(const void* x, const void* w_router, int32_t dty
                                 const int32_t* topk_idx, const float* d_topk_w, const int32_t* offsets,
                                 const int32_t* row_of, const int32_t* src_token, int64_t T, int64_t d,
                                 int32_t E, int32_t k, int32_t score, float* d_keys_sel, void* d_x,
-                                float* d_w_router, float* d_bias, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                int32_t accumulate_dx, float* d_w_router, float* d_bias, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * moe_permute -- dispatch on one GPU: per-expert histogram, group offsets, permutation and

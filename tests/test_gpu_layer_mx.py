@@ -1,5 +1,5 @@
-"""The MXFP8 training step (forward + backward of the experts, the permutation and the
-combine) on the GPU vs the MX-mirroring oracle, on the GPU's own routing so the expert path
+"""The MXFP8 training step (forward + backward of the router, the experts, the permutation
+and the combine) on the GPU vs the MX-mirroring oracle, on the GPU's own routing so the expert path
 is compared on identical groups (routing parity is covered by the route tests). dY is one
 rounding of an exact product and must match bit for bit. Every other stage is checked
 against the oracle's functions applied to the GPU's own inputs of that stage (bf16
@@ -35,12 +35,12 @@ def _step(L, layer, w, topk=None):
         b.topk_w.copy_(torch.from_numpy(topk[1]).cuda())
     layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, routed=topk is not None)
     d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
-    layer.backward_mx(dw.x, d_out, mw, s, b)
+    layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router if topk is None else None)
     torch.cuda.synchronize()
     return b
 
 
-def _oracle(w, b):
+def _oracle(w, b, routed_here=True):
     idx = b.topk_idx.cpu().numpy()
     wt = b.topk_w.cpu().numpy().astype(np.float64)
     gu = lambda e: mi.w_gate_up_np(w, e)
@@ -48,11 +48,16 @@ def _oracle(w, b):
     fwd = O.layer_forward(mi.x_np(w), mi.w_router_np(w), mi.expert_bias(w), w.k, w.score, gu, dn, w.E,
                           shared=bool(w.shared_f), rnd=O.round_bf16, topk=(idx, wt), mx=True)
     d_out = mi.randn_np(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16").astype(np.float64)
-    bwd = O.layer_backward(fwd, d_out, gu, dn, w.E, shared=bool(w.shared_f), rnd=O.round_bf16, mx=True)
+    if routed_here:
+        # the forward's keys (the GPU's selection is the oracle's, checked by the route tests)
+        fwd["keys"] = O.router_keys(mi.x_np(w), mi.w_router_np(w), mi.expert_bias(w))
+    router = (mi.x_np(w), mi.w_router_np(w), w.score) if routed_here else None
+    bwd = O.layer_backward(fwd, d_out, gu, dn, w.E, shared=bool(w.shared_f), rnd=O.round_bf16, mx=True,
+                           router=router)
     return fwd, bwd
 
 
-def _stage_refs(w, b, x, d_out):
+def _stage_refs(w, b, x, d_out, router):
     """Each stage of the step recomputed by the oracle's functions from the GPU's own inputs
     to that stage, so a mismatch points at one kernel."""
     f64 = lambda t: host(t)
@@ -87,10 +92,15 @@ def _stage_refs(w, b, x, d_out):
     ref["out"] = O.combine(Y[:tk], wt, ro, Y[tk:] if shared else None, O.round_bf16)
     ref["dY"], ref["dw"] = O.combine_backward(d_out, Y[:tk], wt, ro, O.round_bf16)
     ref["dx"] = O.permute_backward(dXp[:tk], ro, dXp[tk:] if shared else None, O.round_bf16)
+    if router:
+        # the router's backward from the GPU's keys, selection and routing-weight gradient
+        dk = O.topk_weights_backward(host(b.keys), b.topk_idx.cpu().numpy(), host(b.dw), w.score)
+        ref["dW_router"], dx_r, ref["d_bias"] = O.router_backward(x, mi.w_router_np(w), dk)
+        ref["dx"] = O.round_bf16(ref["dx"] + dx_r)
     return ref
 
 
-def _compare(w, b, fwd, bwd):
+def _compare(w, b, fwd, bwd, router=True):
     tk = w.T * w.k
     np.testing.assert_array_equal(b.offsets.cpu().numpy(), fwd["offsets"])
     np.testing.assert_array_equal(b.row_of.cpu().numpy(), fwd["row_of"])
@@ -100,7 +110,7 @@ def _compare(w, b, fwd, bwd):
     x = mi.x_np(w).astype(np.float64)
     d_out = mi.randn_np(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16").astype(np.float64)
     # stage by stage, each kernel on the GPU's own inputs
-    st = _stage_refs(w, b, x, d_out)
+    st = _stage_refs(w, b, x, d_out, router)
     got = {"H": host(b.H), "GU": host(b.GU), "Y": host(b.Y), "out": host(b.out), "dH": host(b.dH),
            "dGU": host(b.dGU), "dX_perm": host(b.dXp), "dx": host(b.dx)}
     dWgu, dWd = host(b.dW_gu), host(b.dW_down)
@@ -115,11 +125,17 @@ def _compare(w, b, fwd, bwd):
             continue
         worst = max(worst, assert_close(dWgu[g], st["dW_gu"][g], "bf16", f"dW_gu[{g}] (stage)")[0])
         worst = max(worst, assert_close(dWd[g], st["dW_down"][g], "bf16", f"dW_down[{g}] (stage)")[0])
+    if router:
+        assert_close(host(b.dW_router), st["dW_router"], "f32", "dW_router (stage)")
+        assert_close(host(b.d_bias), st["d_bias"], "f32", "d_bias (stage)")
     # end to end against the independent MX oracle
     e2e = {"H": (got["H"], fwd["H"]), "Y": (got["Y"], fwd["Y"]), "out": (got["out"], fwd["out"]),
            "dw": (host(b.dw), bwd["dw"]), "dX_perm": (got["dX_perm"], bwd["dX_perm"]), "dx": (got["dx"], bwd["dx"]),
            "dW_gu": (dWgu[live], np.stack([bwd["dW_gu"][g] for g in live])),
            "dW_down": (dWd[live], np.stack([bwd["dW_down"][g] for g in live]))}
+    if router:
+        e2e["dW_router"] = (host(b.dW_router), bwd["dW_router"])
+        e2e["d_bias"] = (host(b.d_bias), bwd["d_bias"])
     msg = []
     for n, (a, r) in e2e.items():
         mx, mean = assert_close(a, r, "mx_e2e", f"{n} (end to end)")
@@ -144,16 +160,17 @@ def test_mx_step_forced_routing_with_empty_group(LY):
     wt = g.random((w.T, w.k)).astype(np.float32)
     wt /= wt.sum(1, keepdims=True)
     b = _step(L, layer, w, topk=(idx, wt))
-    fwd, bwd = _oracle(w, b)
+    fwd, bwd = _oracle(w, b, routed_here=False)
     assert np.diff(fwd["offsets"])[5] == 0
-    _compare(w, b, fwd, bwd)
+    _compare(w, b, fwd, bwd, router=False)
 
 
 def test_mx_step_dsv3_sampled(LY):
     """The full DeepSeek-V3-shaped MXFP8 step (T=8192, d=7168, f=2048, 256 experts + shared,
     k=8) in the configuration the benchmark times, checked stage by stage on sampled rows of
     a large, a small and the shared group, whole weight gradients of the smallest group and
-    sampled gradient rows of the largest, and sampled tokens of out, dw and dx."""
+    sampled gradient rows of the largest, sampled tokens of out, dw and dx, and the whole
+    router-weight and bias gradients."""
     L, layer = LY
     w = mi.WORKLOADS["dsv3_mxfp8"]
     b = _step(L, layer, w)
@@ -204,5 +221,12 @@ def test_mx_step_dsv3_sampled(LY):
     want_dy, want_dw = O.combine_backward(d_out, Y_r, wt, local, O.round_bf16)
     np.testing.assert_array_equal(pick(b.dY, need), want_dy[local.reshape(-1)])
     assert_close(pick(b.dw, toks), want_dw, "f32", "dw")
-    assert_close(pick(b.dx, toks), O.permute_backward(dXp_r, local, pick(b.dXp, tk + toks), O.round_bf16), "bf16",
-                 "dx")
+    # the router's backward from the GPU's keys and dw: its share of dx on the sampled tokens,
+    # and the whole router-weight and bias gradients
+    dk = O.topk_weights_backward(host(b.keys), b.topk_idx.cpu().numpy(), host(b.dw), w.score)
+    wr = mi.w_router_np(w).astype(np.float64)
+    dx_exp = O.permute_backward(dXp_r, local, pick(b.dXp, tk + toks), O.round_bf16)
+    assert_close(pick(b.dx, toks), O.round_bf16(dx_exp + dk[toks] @ wr), "bf16", "dx")
+    dWr, _, db = O.router_backward(mi.x_np(w), wr, dk)
+    assert_close(host(b.dW_router), dWr, "f32", "dW_router")
+    assert_close(host(b.d_bias), db, "f32", "d_bias")

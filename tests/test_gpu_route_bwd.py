@@ -72,13 +72,33 @@ def _check(got, x, w, keys, idx, g, score, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("score", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("T,d,E,k", [(1000, 256, 16, 4), (777, 320, 24, 6), (64, 2056, 8, 2), (5, 128, 16, 16),
-                                     (33, 64, 128, 1), (20, 7168, 256, 8), (300, 4104, 64, 8)])
+                                     (33, 64, 128, 1), (20, 7168, 256, 8), (300, 4104, 64, 8),
+                                     (3000, 264, 4, 2)])
 def test_route_backward(L, dtype, score, T, d, E, k):
     # d = 2056 and 4104 end in a partial column block of the weight gradient; E = 128 and 256
-    # with few tokens leave most experts without rows; k = E = 16 selects every expert
+    # with few tokens leave most experts without rows; k = E = 16 selects every expert;
+    # T = 3000 over 4 experts gives groups of many 256-row chunks with a ragged last chunk
     x, w, keys, idx, g = _problem(T, d, E, k, score, dtype, seed=T + d + E + k, bias_skew=1.0)
     got = _run(L, x, w, keys, idx, g, E, score, dtype)
     _check(got, x, w, keys, idx, g, score, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_route_backward_accumulates_into_dx(L, dtype):
+    """accumulate_dx: the router's share is added to the incoming input gradient, one rounding."""
+    T, d, E, k = 300, 1032, 32, 4
+    x, w, keys, idx, g = _problem(T, d, E, k, "sigmoid", dtype, seed=9, bias_skew=0.5)
+    offsets, row_of, src = O.permutation(idx, E)
+    prior = mi.randn_np(9, mi.D_OUT, 0, T, d, 0.02, dtype)
+    dx = dev(prior, dtype)
+    nb = L.moe_workspace_bytes(L.MOE_OP_ROUTE_BWD, T, d, E, k, 0)
+    L.moe_route_backward(dev(x, dtype), dev(w, dtype), dev(keys), dev_i32(idx), dev(g), L.MOE_SIGMOID, dev_i32(row_of), offsets=dev_i32(offsets),
+                         src_token=dev_i32(src), d_x=dx, accumulate_dx=True,
+                         workspace=torch.empty((nb,), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    _, dx_r, _ = O.router_backward(x, w, O.topk_weights_backward(keys, idx, g, "sigmoid"))
+    rnd = O.round_bf16 if dtype == "bf16" else O.round_f32
+    assert_close(host(dx), rnd(prior + dx_r), dtype, "d_x accumulated")
 
 
 def test_route_backward_outputs_independent(L):
