@@ -189,18 +189,41 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     const int nbg = block_start[g + 1] - block_start[g];        // the group's blocks (row stride / 32)
     const int r0 = gb + jb * kBlock;
     const int n = max(0, min(kGroupAlign * kBlock, ge - r0));   // valid rows of the chunk
-    // load: 128 rows x PITCH bytes in 16-byte pieces (rows past n read as zero)
-    constexpr int PIECES = PITCH / 16;
+    // load: 128 rows x 256 bytes in 16-byte pieces (rows past n and columns past the matrix
+    // read as zero; the 16 pad bytes of each LDS row are never read). A thread's 8 loads are
+    // all issued before the first LDS write, so 8 are in flight per lane instead of one.
+    constexpr int PR = TC * ESIZE / 16;                          // 16-byte pieces per tile row
+    constexpr int RS = 256 / PR;                                 // rows per pass of the workgroup
+    constexpr int NL = kGroupAlign * kBlock / RS;                // rows (pieces) per thread
+    static_assert(NL * RS == kGroupAlign * kBlock, "whole rows per thread");
     const int ncols = min(TC, cols - c0);
-    for (int idx = t; idx < kGroupAlign * kBlock * PIECES; idx += 256) {
-        const int i = idx / PIECES, pc = idx % PIECES;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i < n && pc * 16 < ncols * ESIZE) {
-            const int64_t r = in_row(row_index, in_rows, r0 + i);
-            v = *reinterpret_cast<const u32x4*>(in + (r * ld_in + c0) * ESIZE + pc * 16);
-        }
-        *reinterpret_cast<u32x4*>(tile + i * PITCH + pc * 16) = v;
+    const int pc = t % PR, i0 = t / PR;                          // this thread's piece column and first row
+    const bool col_ok = pc * 16 < ncols * ESIZE;
+    // every load reads a valid address (row and piece clamped into the matrix) and is issued
+    // unconditionally, so all NL are in flight together; pieces outside the chunk become zero
+    const int pc_safe = min(pc, ncols * ESIZE / 16 - 1);
+    int64_t roff[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) roff[u] = min<int64_t>(r0 + i0 + u * RS, rows - 1);
+    if (row_index != nullptr) {   // gathered rows: all index loads first, then the clamps
+        int32_t ix[NL];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) ix[u] = row_index[roff[u]];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) roff[u] = min<int64_t>(max(ix[u], 0), in_rows - 1);
     }
+    u32x4 lv[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u)
+        lv[u] = *reinterpret_cast<const u32x4*>(in + (roff[u] * ld_in + c0) * ESIZE + pc_safe * 16);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const bool ok = col_ok && i0 + u * RS < n;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lv[u][w] = ok ? lv[u][w] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) *reinterpret_cast<u32x4*>(tile + (i0 + u * RS) * PITCH + pc * 16) = lv[u];
     __syncthreads();
     if (q_row != nullptr) {
         // row-wise copy: unit u = (tile row u / HB, half block u % HB); the two lanes of a block
