@@ -202,21 +202,32 @@ __global__ __launch_bounds__(kCombThreads) void combine_bwd_kernel(const char* _
         float g[8];
         load8<ESIZE>(d_out + t * rowbytes + c * 8 * ESIZE, g);
         if (dy_shared != nullptr) store8<ESIZE>(dy_shared + t * rowbytes + c * 8 * ESIZE, g);
-        for (int j = 0; j < k; ++j) {
-            float o[8];
-            const float w = wts[j];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = ESIZE == 2 ? mul_round_odd(w, g[i]) : w * g[i];
-            store8<ESIZE>(dy + rows[j] * rowbytes + c * 8 * ESIZE, o);
+        // the slots in batches of 8: the batch's expert rows of y are all loaded (slot index
+        // clamped, so every load is valid and issued together) before any is used
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float v[8][8];
             if (dw != nullptr) {
-                float v[8];
-                load8<ESIZE>(y + rows[j] * rowbytes + c * 8 * ESIZE, v);
-                float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(g[i], v[i], acc);
+                for (int u = 0; u < 8; ++u)
+                    load8<ESIZE>(y + rows[min(j0 + u, k - 1)] * rowbytes + c * 8 * ESIZE, v[u]);
+            }
 #pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (q == j) part[q] += acc;
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                if (j >= k) break;
+                float o[8];
+                const float w = wts[j];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = ESIZE == 2 ? mul_round_odd(w, g[i]) : w * g[i];
+                store8<ESIZE>(dy + rows[j] * rowbytes + c * 8 * ESIZE, o);
+                if (dw != nullptr) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = fmaf(g[i], v[u][i], acc);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        if (q == j) part[q] += acc;
+                }
             }
         }
     }

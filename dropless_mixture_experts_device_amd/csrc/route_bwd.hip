@@ -119,12 +119,17 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __
     const int64_t rowbytes = (int64_t)d * ESIZE;
     for (int c = threadIdx.x; c < d / 8; c += kRbThreads) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            float v[8];
-            ld8f<ESIZE>(w_router + rows[j] * rowbytes + (int64_t)c * 8 * ESIZE, v);
-            const float w = coef[j];
+        for (int j0 = 0; j0 < k; j0 += 8) {   // batches of 8 slots, every row load issued first
+            float v[8][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+            for (int u = 0; u < 8; ++u)
+                ld8f<ESIZE>(w_router + rows[min(j0 + u, k - 1)] * rowbytes + (int64_t)c * 8 * ESIZE, v[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {   // slots past k repeat a finite row with weight zero
+                const float w = j0 + u < k ? coef[min(j0 + u, 15)] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
+            }
         }
         char* o = dx + t * rowbytes + (int64_t)c * 8 * ESIZE;
         if (accumulate) {   // the incoming gradient joins the fp32 sum; still one rounding
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_chunks_kernel(const int3
 }
 
 // partial[chunk, cols] = sum over the chunk's rows (ascending) of dk[r] * x[src_token[r], cols];
-// four rows' loads are issued together. Workgroups past the last chunk exit at once.
+// rows are taken four at a time. Workgroups past the last chunk exit at once.
 template <int ESIZE>
 __global__ __launch_bounds__(kRbThreads) void route_bwd_dw_partial_kernel(const char* __restrict__ x,
                                                                           const int32_t* __restrict__ offsets,
@@ -203,6 +208,8 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dw_partial_kernel(const 
     if (col >= d) return;
     const int64_t rowbytes = (int64_t)d * ESIZE;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // four rows per step; loads guarded by the row bound (a batched form with clamped rows
+    // and eight loads in flight measured slower here: 134 -> 157 us at the DeepSeek-V3 shape)
     constexpr int U = 4;
     for (int r0 = r_begin; r0 < r_end; r0 += U) {
         float v[U][8], c[U];
