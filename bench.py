@@ -330,7 +330,7 @@ def main_mx(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the layer runs on one GPU only (no collectives); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
