@@ -64,10 +64,13 @@ _lib.moe_swiglu_backward.restype = _i32
 _lib.moe_route_backward.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
                                     _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_route_backward.restype = _i32
+_lib.moe_swiglu_backward_quant_mxfp8_dual.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _vp, _i64,
+                                                      _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
+_lib.moe_swiglu_backward_quant_mxfp8_dual.restype = _i32
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
             "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward",
-            "moe_route_backward")
+            "moe_route_backward", "moe_swiglu_backward_quant_mxfp8_dual")
 
 
 class MoeError(RuntimeError):
@@ -225,6 +228,19 @@ def moe_route_backward(x, w_router, keys, topk_idx, d_topk_w, score: int, row_of
         _ptr(src_token), T, d, E, k, score, _ptr(d_keys_sel), _ptr(d_x), int(accumulate_dx), _ptr(d_w_router),
         _ptr(d_bias), ws, wsb,
         _stream(stream)))
+
+
+def moe_swiglu_backward_quant_mxfp8_dual(dh, gu, q_row, s_row, q_col, s_col, group_offsets, block_start=None,
+                                         workspace=None, stream=None):
+    """The SwiGLU backward of (dh [rows, f], gu [rows, 2f]) quantised straight into both MXFP8
+    copies (as moe_swiglu_backward followed by moe_group_quant_mxfp8_dual, without the bf16
+    gate/up gradient in memory)."""
+    rows, f = dh.shape
+    ws, wsb = _ws(workspace)
+    _check("moe_swiglu_backward_quant_mxfp8_dual", _lib.moe_swiglu_backward_quant_mxfp8_dual(
+        _ptr(dh), dh.stride(0), _ptr(gu), gu.stride(0), _dtype(dh), rows, f, _ptr(group_offsets),
+        group_offsets.numel() - 1, _ptr(q_row), q_row.stride(0), _ptr(s_row), s_row.stride(0), _ptr(q_col),
+        q_col.stride(0), _ptr(s_col), s_col.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
 
 
 def moe_swiglu_backward(dh, gu, dgu, stream=None):

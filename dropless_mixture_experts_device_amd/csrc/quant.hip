@@ -7,6 +7,7 @@
 // largest exponent), stored as an E8M0 byte (+127, clamped to 0..254); each element is
 // rounded to nearest-even E4M3 after division by 2^exponent, saturating at +-448.
 #include "moe_internal.h"
+#include "swiglu_math.h"
 
 namespace moe {
 namespace {
@@ -161,14 +162,22 @@ constexpr int kColTile = 128;        // columns per workgroup (bf16; 64 for fp32
 #define MOE_QUANT_NT 1                // E4M3 code stores of the column-wise / dual pass non-temporal
                                       // (DeepSeek-V3 weight stacks 9.85 -> 9.62 ms)
 #endif
-template <int ESIZE>
+// SWB: the input is not read as such but formed while loading: the SwiGLU backward's
+// dgu = [dg | du] (cols = 2f) from dh [rows, f] (`in`, ld_in) and the saved gate/up
+// pre-activations gu [rows, 2f] (ld_gu), each value rounded to bf16 as moe_swiglu_backward
+// stores it, so the codes equal those of quantising that kernel's output (f % 128 == 0: a
+// tile lies in one half).
+template <int ESIZE, bool SWB = false>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, const int32_t* __restrict__ row_index,
                                                          int64_t in_rows, const int32_t* __restrict__ offsets, int G,
                                                          const int32_t* __restrict__ block_start,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
                                                          uint8_t* __restrict__ q_row, int64_t ld_q_row,
-                                                         uint8_t* __restrict__ s_row, int64_t ld_s_row) {
+                                                         uint8_t* __restrict__ s_row, int64_t ld_s_row,
+                                                         const char* __restrict__ gu = nullptr, int64_t ld_gu = 0,
+                                                         int f = 0) {
+    static_assert(!SWB || ESIZE == 2, "the fused SwiGLU-backward mode reads bf16");
     constexpr int TC = ESIZE == 2 ? kColTile : kColTile / 2;    // columns of this tile
     constexpr int PITCH = TC * ESIZE + 16;                       // LDS bytes per row (256 + pad)
     __shared__ __attribute__((aligned(16))) char tile[kGroupAlign * kBlock * PITCH];   // 34 KiB
@@ -213,133 +222,186 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
         for (int u = 0; u < NL; ++u) roff[u] = min<int64_t>(max(ix[u], 0), in_rows - 1);
     }
     u32x4 lv[NL];
+    u32x4 lv_up[SWB ? NL : 1];
+    if constexpr (SWB) {
+        // this workgroup owns columns [c0, c0 + TC) of dh and g: both the gate tile (dgu columns
+        // c0..) and the up tile (columns f + c0..) come from one read of dh, g and u, in two
+        // batches of NL/2 pieces; each value is rounded to bf16 as moe_swiglu_backward stores it
+        constexpr int NB = NL / 2;
 #pragma unroll
-    for (int u = 0; u < NL; ++u)
-        lv[u] = *reinterpret_cast<const u32x4*>(in + (roff[u] * ld_in + c0) * ESIZE + pc_safe * 16);
+        for (int hb = 0; hb < 2; ++hb) {
+            u32x4 hv[NB], gv[NB], uv[NB];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-        const bool ok = col_ok && i0 + u * RS < n;
+            for (int u = 0; u < NB; ++u) {
+                const int64_t r = roff[hb * NB + u];
+                hv[u] = *reinterpret_cast<const u32x4*>(in + (r * ld_in + c0) * 2 + pc_safe * 16);
+                gv[u] = *reinterpret_cast<const u32x4*>(gu + (r * ld_gu + c0) * 2 + pc_safe * 16);
+                uv[u] = *reinterpret_cast<const u32x4*>(gu + (r * ld_gu + f + c0) * 2 + pc_safe * 16);
+            }
 #pragma unroll
-        for (int w = 0; w < 4; ++w) lv[u][w] = ok ? lv[u][w] : 0u;
-    }
+            for (int u = 0; u < NB; ++u) {
+                u32x4 og, ou;
 #pragma unroll
-    for (int u = 0; u < NL; ++u) *reinterpret_cast<u32x4*>(tile + (i0 + u * RS) * PITCH + pc * 16) = lv[u];
-    __syncthreads();
-    if (q_row != nullptr) {
-        // row-wise copy: unit u = (tile row u / HB, half block u % HB); the two lanes of a block
-        // combine their maxima with one shuffle, and 8 consecutive lanes write 128 contiguous
-        // bytes of one row (bf16; 4 lanes and 64 bytes for fp32)
-        constexpr int HB = TC / 16;                              // half blocks per tile row
-        constexpr int P16 = 16 * ESIZE / 16;                     // 16-byte LDS reads per half block
-        static_assert((kGroupAlign * kBlock * HB) % 256 == 0, "whole waves per pass");
-        for (int u = t; u < kGroupAlign * kBlock * HB; u += 256) {
-            const int i = u / HB, hb = u % HB;
-            const bool live = i < n && hb * 16 < ncols;          // same for both lanes of a block
-            const char* src = tile + i * PITCH + hb * 16 * ESIZE;
-            float v[16];
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t pg = 0u, pu = 0u;
 #pragma unroll
-            for (int c = 0; c < P16; ++c) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
-                if (ESIZE == 2) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[c * 8 + 2 * e] = __uint_as_float(w[e] << 16);
-                        v[c * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                    for (int e = 0; e < 2; ++e) {
+                        const int sh = 16 * e;
+                        const float hh = __uint_as_float(((hv[u][w] >> sh) & 0xFFFFu) << 16);
+                        const float gg = __uint_as_float(((gv[u][w] >> sh) & 0xFFFFu) << 16);
+                        const float uu = __uint_as_float(((uv[u][w] >> sh) & 0xFFFFu) << 16);
+                        float dg, du;
+                        swiglu_grad(hh, gg, uu, dg, du);
+                        pg |= (uint32_t)f32_to_bf16(dg) << sh;
+                        pu |= (uint32_t)f32_to_bf16(du) << sh;
                     }
-                } else {
+                    og[w] = pg;
+                    ou[w] = pu;
+                }
+                lv[hb * NB + u] = og;
+                lv_up[hb * NB + u] = ou;
+            }
+        }
+    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[c * 4 + e] = __uint_as_float(w[e]);
+        for (int u = 0; u < NL; ++u)
+            lv[u] = *reinterpret_cast<const u32x4*>(in + (roff[u] * ld_in + c0) * ESIZE + pc_safe * 16);
+    }
+    // one pass per output tile: the tile's values go to LDS, then both copies are written
+    // (the fused SwiGLU-backward mode makes a second pass for the up half's tile)
+#pragma unroll 1
+    for (int half = 0; half < (SWB ? 2 : 1); ++half) {
+        const int c0o = c0 + half * f;                           // first output column of the tile
+        if (half == 1) {
+            __syncthreads();                                     // the first pass's stores have read LDS
+#pragma unroll
+            for (int u = 0; u < NL; ++u) lv[u] = lv_up[SWB ? u : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const bool ok = col_ok && i0 + u * RS < n;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) lv[u][w] = ok ? lv[u][w] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) *reinterpret_cast<u32x4*>(tile + (i0 + u * RS) * PITCH + pc * 16) = lv[u];
+        __syncthreads();
+        if (q_row != nullptr) {
+            // row-wise copy: unit u = (tile row u / HB, half block u % HB); the two lanes of a block
+            // combine their maxima with one shuffle, and 8 consecutive lanes write 128 contiguous
+            // bytes of one row (bf16; 4 lanes and 64 bytes for fp32)
+            constexpr int HB = TC / 16;                              // half blocks per tile row
+            constexpr int P16 = 16 * ESIZE / 16;                     // 16-byte LDS reads per half block
+            static_assert((kGroupAlign * kBlock * HB) % 256 == 0, "whole waves per pass");
+            for (int u = t; u < kGroupAlign * kBlock * HB; u += 256) {
+                const int i = u / HB, hb = u % HB;
+                const bool live = i < n && hb * 16 < ncols;          // same for both lanes of a block
+                const char* src = tile + i * PITCH + hb * 16 * ESIZE;
+                float v[16];
+#pragma unroll
+                for (int c = 0; c < P16; ++c) {
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
+                    if (ESIZE == 2) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[c * 8 + 2 * e] = __uint_as_float(w[e] << 16);
+                            v[c * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[c * 4 + e] = __uint_as_float(w[e]);
+                    }
+                }
+                float amax = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));      // the block's other half
+                const uint32_t byte = mx_scale_byte(amax);
+                const float inv = mx_inv_scale(byte);
+                u32x4 out;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) out[w] = pack4_e4m3(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                                                 v[4 * w + 3] * inv);
+                if (live) {
+                    const int64_t r = r0 + i;                        // logical row
+                    u32x4* dst = reinterpret_cast<u32x4*>(q_row + r * ld_q_row + c0o + hb * 16);
+                    if (MOE_QUANT_NT) __builtin_nontemporal_store(out, dst);
+                    else *dst = out;
+                    if ((hb & 1) == 0) s_row[r * ld_s_row + c0o / kBlock + hb / 2] = (uint8_t)byte;
                 }
             }
+        }
+        // (column, block) units of this thread: bf16 threads read two adjacent columns with one
+        // 4-byte LDS read per row and quantise one block of each; fp32 threads one block of one column
+        constexpr int NU = kGroupAlign * TC / 256;                   // 2 bf16, 1 fp32
+        int ucol[NU], ublk[NU];
+        float v[NU][kBlock];
+        if constexpr (ESIZE == 2) {
+            const int cp = t % (TC / 2), b = t / (TC / 2);
+#pragma unroll
+            for (int i = 0; i < kBlock; ++i) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (b * kBlock + i) * PITCH + cp * 4);
+                v[0][i] = __uint_as_float(w << 16);
+                v[NU - 1][i] = __uint_as_float(w & 0xFFFF0000u);
+            }
+            ucol[0] = 2 * cp;
+            ucol[NU - 1] = 2 * cp + 1;
+            ublk[0] = ublk[NU - 1] = b;
+        } else {
+            const int col = t % TC, b = t / TC;
+#pragma unroll
+            for (int i = 0; i < kBlock; ++i) v[0][i] = *reinterpret_cast<const float*>(tile + (b * kBlock + i) * PITCH + col * 4);
+            ucol[0] = col;
+            ublk[0] = b;
+        }
+        // codes and scale bytes of the units, kept in registers until the tile is free
+        u32x4 codes[NU][2];
+        uint32_t sbytes[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
             float amax = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));      // the block's other half
+            for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
             const uint32_t byte = mx_scale_byte(amax);
             const float inv = mx_inv_scale(byte);
-            u32x4 out;
+            sbytes[u] = byte;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = pack4_e4m3(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
-                                                             v[4 * w + 3] * inv);
-            if (live) {
-                const int64_t r = r0 + i;                        // logical row
-                u32x4* dst = reinterpret_cast<u32x4*>(q_row + r * ld_q_row + c0 + hb * 16);
-                if (MOE_QUANT_NT) __builtin_nontemporal_store(out, dst);
-                else *dst = out;
-                if ((hb & 1) == 0) s_row[r * ld_s_row + c0 / kBlock + hb / 2] = (uint8_t)byte;
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* e = v[u] + h * 16 + w * 4;
+                    codes[u][h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+                }
         }
-    }
-    // (column, block) units of this thread: bf16 threads read two adjacent columns with one
-    // 4-byte LDS read per row and quantise one block of each; fp32 threads one block of one column
-    constexpr int NU = kGroupAlign * TC / 256;                   // 2 bf16, 1 fp32
-    int ucol[NU], ublk[NU];
-    float v[NU][kBlock];
-    if constexpr (ESIZE == 2) {
-        const int cp = t % (TC / 2), b = t / (TC / 2);
+        // Stage the chunk's transposed codes in LDS (column c's 4 blocks = 128 contiguous bytes,
+        // rows padded to 144 bytes) and its scale bytes (4 per column, one dword), then write
+        // them out so that 8 consecutive lanes cover one column's full 128-byte line.
+        constexpr int SP = kGroupAlign * kBlock + 16;               // staged bytes per column
+        char* stage = tile;                                          // TC * SP <= the tile's size
+        uint32_t* sstage = reinterpret_cast<uint32_t*>(tile + TC * SP);
+        static_assert(TC * SP + TC * 4 <= kGroupAlign * kBlock * PITCH, "staging fits in the tile");
+        __syncthreads();                                             // every thread is done reading the tile
 #pragma unroll
-        for (int i = 0; i < kBlock; ++i) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (b * kBlock + i) * PITCH + cp * 4);
-            v[0][i] = __uint_as_float(w << 16);
-            v[NU - 1][i] = __uint_as_float(w & 0xFFFF0000u);
+        for (int u = 0; u < NU; ++u) {
+            char* d = stage + ucol[u] * SP + ublk[u] * kBlock;
+            *reinterpret_cast<u32x4*>(d) = codes[u][0];
+            *reinterpret_cast<u32x4*>(d + 16) = codes[u][1];
+            reinterpret_cast<uint8_t*>(sstage)[ucol[u] * kGroupAlign + ublk[u]] = (uint8_t)sbytes[u];
         }
-        ucol[0] = 2 * cp;
-        ucol[NU - 1] = 2 * cp + 1;
-        ublk[0] = ublk[NU - 1] = b;
-    } else {
-        const int col = t % TC, b = t / TC;
-#pragma unroll
-        for (int i = 0; i < kBlock; ++i) v[0][i] = *reinterpret_cast<const float*>(tile + (b * kBlock + i) * PITCH + col * 4);
-        ucol[0] = col;
-        ublk[0] = b;
+        __syncthreads();
+        const int64_t gbase = (int64_t)cols * block_start[g];      // the group's transposed block
+        constexpr int PIECES_OUT = TC * kGroupAlign * kBlock / 16;   // 16-byte pieces of the chunk
+        for (int pcs = t; pcs < PIECES_OUT; pcs += 256) {
+            const int cc = pcs / (kGroupAlign * kBlock / 16), ch = pcs % (kGroupAlign * kBlock / 16);
+            if (cc >= ncols) continue;
+            const int64_t c = c0o + cc;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + cc * SP + ch * 16);
+            u32x4* dst = reinterpret_cast<u32x4*>(q + (gbase + c * nbg + jb) * kBlock + ch * 16);
+            if (MOE_QUANT_NT) __builtin_nontemporal_store(v, dst);
+            else *dst = v;
+        }
+        if (t < ncols) *reinterpret_cast<uint32_t*>(sc + gbase + (int64_t)(c0o + t) * nbg + jb) = sstage[t];
     }
-    // codes and scale bytes of the units, kept in registers until the tile is free
-    u32x4 codes[NU][2];
-    uint32_t sbytes[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
-        const uint32_t byte = mx_scale_byte(amax);
-        const float inv = mx_inv_scale(byte);
-        sbytes[u] = byte;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float* e = v[u] + h * 16 + w * 4;
-                codes[u][h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
-            }
-    }
-    // Stage the chunk's transposed codes in LDS (column c's 4 blocks = 128 contiguous bytes,
-    // rows padded to 144 bytes) and its scale bytes (4 per column, one dword), then write
-    // them out so that 8 consecutive lanes cover one column's full 128-byte line.
-    constexpr int SP = kGroupAlign * kBlock + 16;               // staged bytes per column
-    char* stage = tile;                                          // TC * SP <= the tile's size
-    uint32_t* sstage = reinterpret_cast<uint32_t*>(tile + TC * SP);
-    static_assert(TC * SP + TC * 4 <= kGroupAlign * kBlock * PITCH, "staging fits in the tile");
-    __syncthreads();                                             // every thread is done reading the tile
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        char* d = stage + ucol[u] * SP + ublk[u] * kBlock;
-        *reinterpret_cast<u32x4*>(d) = codes[u][0];
-        *reinterpret_cast<u32x4*>(d + 16) = codes[u][1];
-        reinterpret_cast<uint8_t*>(sstage)[ucol[u] * kGroupAlign + ublk[u]] = (uint8_t)sbytes[u];
-    }
-    __syncthreads();
-    const int64_t gbase = (int64_t)cols * block_start[g];      // the group's transposed block
-    constexpr int PIECES_OUT = TC * kGroupAlign * kBlock / 16;   // 16-byte pieces of the chunk
-    for (int pcs = t; pcs < PIECES_OUT; pcs += 256) {
-        const int cc = pcs / (kGroupAlign * kBlock / 16), ch = pcs % (kGroupAlign * kBlock / 16);
-        if (cc >= ncols) continue;
-        const int64_t c = c0 + cc;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + cc * SP + ch * 16);
-        u32x4* dst = reinterpret_cast<u32x4*>(q + (gbase + c * nbg + jb) * kBlock + ch * 16);
-        if (MOE_QUANT_NT) __builtin_nontemporal_store(v, dst);
-        else *dst = v;
-    }
-    if (t < ncols) *reinterpret_cast<uint32_t*>(sc + gbase + (int64_t)(c0 + t) * nbg + jb) = sstage[t];
 }
 
 }  // namespace
@@ -352,7 +414,8 @@ static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, i
                                   const int32_t* row_index, int64_t in_rows, const int32_t* group_offsets, int32_t G,
                                   uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                   uint8_t* q_row, int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
-                                  int32_t* block_start, void* workspace, size_t workspace_bytes, hipStream_t s) {
+                                  int32_t* block_start, void* workspace, size_t workspace_bytes, hipStream_t s,
+                                  const void* gu = nullptr, int64_t ld_gu = 0, int64_t f = 0) {
     const int esize = dtype == MOE_BF16 ? 2 : 4;
     if (G < 1 || !group_offsets || rows > INT32_MAX / 2) return MOE_EINVAL;
     // blocks over all groups, upper bound: sum_g 4 ceil(m_g / 128) <= 4 (ceil(rows / 128) + G)
@@ -372,8 +435,13 @@ static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, i
     MOE_CHECK_LAUNCH();
     if (rows == 0) return MOE_OK;
     const int tc = esize == 2 ? moe::kColTile : moe::kColTile / 2;
-    const dim3 grid((unsigned)moe::cdiv<int64_t>(cols, tc), (unsigned)(nblk_cap / moe::kGroupAlign));
-    if (esize == 2)
+    // the fused SwiGLU-backward mode: one workgroup per TC columns of dh writes two tiles
+    const dim3 grid((unsigned)moe::cdiv<int64_t>(gu != nullptr ? f : cols, tc), (unsigned)(nblk_cap / moe::kGroupAlign));
+    if (gu != nullptr)
+        hipLaunchKernelGGL((moe::quant_cols_kernel<2, true>), grid, dim3(256), 0, s, (const char*)in, rows, (int)cols,
+                           ld_in, row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row,
+                           ld_s_row, (const char*)gu, ld_gu, (int)f);
+    else if (esize == 2)
         hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
                            row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row);
     else
@@ -433,4 +501,23 @@ extern "C" moe_status_t moe_group_quant_mxfp8_dual(const void* in, int32_t dtype
     return quant_colwise(in, dtype, rows, cols, ld_in, row_index, in_rows, group_offsets, G, q_col, ld_q_col, s_col,
                          ld_s_col, q_row, ld_q_row, s_row, ld_s_row, block_start, workspace, workspace_bytes,
                          (hipStream_t)stream);
+}
+
+extern "C" moe_status_t moe_swiglu_backward_quant_mxfp8_dual(const void* dh, int64_t ld_dh, const void* gu,
+                                                             int64_t ld_gu, int32_t dtype, int64_t rows, int64_t f,
+                                                             const int32_t* group_offsets, int32_t G, uint8_t* q_row,
+                                                             int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                                             uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col,
+                                                             int64_t ld_s_col, int32_t* block_start, void* workspace,
+                                                             size_t workspace_bytes, void* stream) {
+    if (rows < 0 || f <= 0 || f % (moe::kColTile) != 0 || f > INT32_MAX / 4) return MOE_EINVAL;
+    if (ld_dh < f || ld_gu < 2 * f || ld_dh % 8 != 0 || ld_gu % 8 != 0) return MOE_EINVAL;
+    if (dtype != MOE_BF16) return MOE_ENOTSUP;
+    if (rows > 0 && (!gu || !moe_aligned16(gu))) return MOE_EINVAL;
+    const int64_t cols = 2 * f;
+    if (!q_row || !s_row || ld_q_row < cols || ld_s_row < cols / moe::kBlock) return MOE_EINVAL;
+    if (!moe_aligned16(q_row) || ld_q_row % 16 != 0) return MOE_EINVAL;
+    return quant_colwise(dh, dtype, rows, cols, ld_dh, nullptr, rows, group_offsets, G, q_col, ld_q_col, s_col,
+                         ld_s_col, q_row, ld_q_row, s_row, ld_s_row, block_start, workspace, workspace_bytes,
+                         (hipStream_t)stream, gu, ld_gu, f);
 }

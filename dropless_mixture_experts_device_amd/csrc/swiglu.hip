@@ -9,6 +9,7 @@
 // Elementwise and bandwidth-bound: each thread handles 8 consecutive columns (16-byte
 // loads of dh, g and u, 16-byte stores of dg and du), math in fp32, one rounding per output.
 #include "moe_internal.h"
+#include "swiglu_math.h"
 
 namespace moe {
 namespace {
@@ -67,11 +68,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const char* __restrict_
     ld8<ESIZE>(gu + (r * ld_gu + c) * ESIZE, g);
     ld8<ESIZE>(gu + (r * ld_gu + f + c) * ESIZE, u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float sg = 1.f / (1.f + expf(-g[i]));
-        du[i] = h[i] * (g[i] * sg);
-        dg[i] = h[i] * u[i] * (sg * (1.f + g[i] * (1.f - sg)));
-    }
+    for (int i = 0; i < 8; ++i) swiglu_grad(h[i], g[i], u[i], dg[i], du[i]);
     st8<ESIZE>(dgu + (r * ld_dgu + c) * ESIZE, dg);
     st8<ESIZE>(dgu + (r * ld_dgu + f + c) * ESIZE, du);
 }

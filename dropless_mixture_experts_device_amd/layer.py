@@ -231,7 +231,8 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
     return b.out
 
 
-def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None, w_router=None):
+def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None, w_router=None,
+                fuse_swiglu_quant: bool = True):
     """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down and,
     when w_router is given (a forward that ran the router), b.dW_router and b.d_bias.
 
@@ -240,7 +241,9 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
     (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx;
     then the router's backward: the routing weights' gradient dw through the top-k
     normalisation to the keys, from there to W_router and the bias, and the router's share
-    of the input gradient added into dx."""
+    of the input gradient added into dx. With fuse_swiglu_quant (the default) the SwiGLU
+    backward is formed inside the quantiser that writes both MXFP8 copies of dGU, so b.dGU is
+    not written; otherwise it is written by its own kernel and then quantised."""
     mark = mark or _nomark
     tk = s.T * s.k
     L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
@@ -257,10 +260,15 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
                        a_scale=b.sc_dy, b_scale=b.sc_h, ragged_k=True)
     mark("wgrad2")
     # SwiGLU backward, dgrad 1 and wgrad 1
-    L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
-    mark("swiglu_bwd")
-    L.moe_group_quant_mxfp8_dual(b.dGU, b.q_dgu, b.s_dgu, b.qc_dgu, b.sc_dgu, b.offsets, block_start=b.bs)
-    mark("quant_dgu")
+    if fuse_swiglu_quant:
+        L.moe_swiglu_backward_quant_mxfp8_dual(b.dH, b.GU, b.q_dgu, b.s_dgu, b.qc_dgu, b.sc_dgu, b.offsets,
+                                               block_start=b.bs)
+        mark("swiglu_bwd_quant_dgu")
+    else:
+        L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
+        mark("swiglu_bwd")
+        L.moe_group_quant_mxfp8_dual(b.dGU, b.q_dgu, b.s_dgu, b.qc_dgu, b.sc_dgu, b.offsets, block_start=b.bs)
+        mark("quant_dgu")
     q_guT, s_guT = mw.gu_T()
     L.moe_grouped_gemm(b.q_dgu, q_guT, b.dXp, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_dgu,
                        b_scale=s_guT)

@@ -347,6 +347,29 @@ moe_status_t moe_group_quant_mxfp8_dual(const void* in, int32_t dtype, int64_t r
                                         int64_t ld_s_col, int32_t* block_start, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/*
+ * moe_swiglu_backward_quant_mxfp8_dual -- the SwiGLU backward and both MXFP8 copies of its
+ * output in one pass, so the bf16 gate/up gradient never goes to memory.
+ * [Blog] "Optimisations dropless MoE needs": the expert GEMMs' operands are MXFP8 with
+ * group-aware quantisation, and the dgrad 1 / wgrad 1 GEMMs read only those copies of the
+ * gate/up gradient; [Blog] Figure 3 paragraph: the experts are SwiGLU MLPs.
+ *
+ *   The output equals moe_swiglu_backward(dh, ld_dh, gu, ld_gu, dtype, rows, f, dgu, 2f)
+ *   followed by moe_group_quant_mxfp8_dual(dgu, dtype, rows, 2f, 2f, NULL, rows,
+ *   group_offsets, G, q_row, ..., s_col, ...) byte for byte: each dgu value is formed in
+ *   fp32 as that kernel does, rounded to dtype, then quantised.
+ *   dh [rows, f] (ld_dh), gu [rows, 2f] (ld_gu) as moe_swiglu_backward; dtype MOE_BF16 only
+ *   (MOE_ENOTSUP otherwise); f % 128 == 0; q_row/s_row/q_col/s_col, block_start, workspace and
+ *   their capacity rules as moe_group_quant_mxfp8_dual with cols = 2f. Errors as those two.
+ */
+moe_status_t moe_swiglu_backward_quant_mxfp8_dual(const void* dh, int64_t ld_dh, const void* gu, int64_t ld_gu,
+                                                  int32_t dtype, int64_t rows, int64_t f,
+                                                  const int32_t* group_offsets, int32_t G, uint8_t* q_row,
+                                                  int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                                  uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col, int64_t ld_s_col,
+                                                  int32_t* block_start, void* workspace, size_t workspace_bytes,
+                                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

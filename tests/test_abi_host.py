@@ -138,6 +138,16 @@ def test_host_argument_errors_backward_and_quant(lib):
         assert rb(*args) == want, (i, v)
     assert rb(None, None, L.MOE_BF16, None, None, None, None, None, None, 0, 64, 8, 2, L.MOE_SOFTMAX,
               None, None, 0, None, None, fake, 256, None) == L.MOE_OK
+    # fused SwiGLU backward + MXFP8: f % 128, bf16 only, leading dimensions, outputs
+    fq = L._lib.moe_swiglu_backward_quant_mxfp8_dual
+    okf = [fake, 256, fake, 512, L.MOE_BF16, 64, 256, fake, 2, fake, 512, fake, 16, fake, 32 * 16, fake, 16, fake,
+           None, 0, None]
+    for i, v, want in ((6, 192, L.MOE_EINVAL), (4, L.MOE_F32, L.MOE_ENOTSUP), (1, 128, L.MOE_EINVAL),
+                       (3, 256, L.MOE_EINVAL), (9, None, L.MOE_EINVAL), (10, 256, L.MOE_EINVAL),
+                       (2, None, L.MOE_EINVAL), (14, 32 * 15, L.MOE_EINVAL)):
+        args = list(okf)
+        args[i] = v
+        assert fq(*args) == want, (i, v)
     # SwiGLU backward: f % 8, leading dimensions
     assert L._lib.moe_swiglu_backward(fake, 64, fake, 128, L.MOE_BF16, 16, 60, fake, 128, None) == L.MOE_EINVAL
     assert L._lib.moe_swiglu_backward(fake, 64, fake, 96, L.MOE_BF16, 16, 64, fake, 128, None) == L.MOE_EINVAL

@@ -12,7 +12,7 @@ import torch
 
 import moe_inputs as mi
 from oracle import moe_oracle as O
-from tests.gpu_util import DeviceWorkload, assert_close, host
+from tests.gpu_util import DeviceWorkload, assert_close, bits, host
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def LY():
     return _lib, layer
 
 
-def _step(L, layer, w, topk=None):
+def _step(L, layer, w, topk=None, fused=True):
     dw = DeviceWorkload(w)
     s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
                          score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
@@ -35,7 +35,12 @@ def _step(L, layer, w, topk=None):
         b.topk_w.copy_(torch.from_numpy(topk[1]).cuda())
     layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, routed=topk is not None)
     d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
-    layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router if topk is None else None)
+    layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router if topk is None else None,
+                      fuse_swiglu_quant=fused)
+    if fused:
+        # the stage checks read dGU: the standalone SwiGLU backward writes the exact values the
+        # fused quantiser formed (equal bytes, checked in the quantiser tests)
+        L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
     torch.cuda.synchronize()
     return b
 
@@ -149,6 +154,17 @@ def test_mx_step_small(LY):
     b = _step(L, layer, w)
     fwd, bwd = _oracle(w, b)
     _compare(w, b, fwd, bwd)
+    # the two-kernel SwiGLU backward + quantisation gives the same step, byte for byte
+    u = _step(L, layer, w, fused=False)
+    for n in ("q_dgu", "s_dgu", "dGU", "dXp", "dW_gu", "dW_down", "dx", "dW_router", "d_bias"):
+        np.testing.assert_array_equal(bits(getattr(b, n)), bits(getattr(u, n)), err_msg=n)
+    # column-wise copies: the group-major blocks written (capacity past block_start[G] is unused)
+    nb = int(b.bs[-1].item())
+    assert nb == int(u.bs[-1].item())
+    cols = 2 * w.f
+    for n, per in (("qc_dgu", 32 * cols), ("sc_dgu", cols)):
+        np.testing.assert_array_equal(getattr(b, n).reshape(-1)[:per * nb].cpu().numpy(),
+                                      getattr(u, n).reshape(-1)[:per * nb].cpu().numpy(), err_msg=n)
 
 
 def test_mx_step_forced_routing_with_empty_group(LY):

@@ -292,3 +292,50 @@ def test_quant_dual_expert_weight_stack(L):
     cs_t = torch.from_numpy(cs).cuda()
     np.testing.assert_array_equal(qg[cs_t].cpu().numpy(), codes.T)
     np.testing.assert_array_equal(sg[cs_t].cpu().numpy(), scales[0].T)
+
+
+@pytest.mark.parametrize("sizes,f", [([0, 1, 33, 0, 500, 64, 402], 256), ([700, 0, 2048, 129, 5, 1300], 2048)])
+def test_swiglu_backward_quant_fused(L, sizes, f):
+    """moe_swiglu_backward_quant_mxfp8_dual writes exactly the bytes of moe_swiglu_backward
+    followed by moe_group_quant_mxfp8_dual; those bytes are the oracle's quantisation of that
+    gradient (row-wise and group-aware column-wise), and their decoded values agree with the
+    oracle's own SwiGLU backward to the MXFP8 tolerance."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows, G = int(off[-1]), len(sizes)
+    dh = mi.randn_np(f, mi.D_OUT, 0, rows, f, 1.0, "bf16")
+    gu = mi.randn_np(f, mi.D_OUT, 1, rows, 2 * f, 2.0, "bf16")
+    dh_d, gu_d = dev(dh, "bf16"), dev(gu, "bf16")
+    nblk = L.quant_col_blocks(rows, G)
+
+    def bufs():
+        return (torch.full((rows, 2 * f), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((rows, 2 * f // 32), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((2 * f, 32 * nblk), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((2 * f, nblk), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((G + 1,), -1, dtype=torch.int32, device="cuda"))
+
+    fused, two = bufs(), bufs()
+    L.moe_swiglu_backward_quant_mxfp8_dual(dh_d, gu_d, *fused[:4], dev_i32(off), block_start=fused[4])
+    dgu = torch.empty((rows, 2 * f), dtype=torch.bfloat16, device="cuda")
+    L.moe_swiglu_backward(dh_d, gu_d, dgu)
+    L.moe_group_quant_mxfp8_dual(dgu, *two[:4], dev_i32(off), block_start=two[4])
+    torch.cuda.synchronize()
+    fb, tb = [t.cpu().numpy() for t in fused], [t.cpu().numpy() for t in two]
+    for a, b, n in zip(fb, tb, ("q_row", "s_row", "q_col", "s_col", "block_start")):
+        np.testing.assert_array_equal(a, b, err_msg=n)
+    # the oracle's quantisation of that gradient, bit for bit
+    g_gpu = dgu.float().cpu().numpy().astype(np.float64)
+    wq, ws, _ = O.mx_quantize_rowwise(g_gpu)
+    np.testing.assert_array_equal(fb[0], wq)
+    np.testing.assert_array_equal(fb[1], ws)
+    _check_colwise(g_gpu, off, fb[2].reshape(-1), fb[3].reshape(-1), fb[4])
+    # decoded row-wise values against the oracle's own SwiGLU backward, quantised the same way
+    G_, U_ = gu[:, :f].astype(np.float64), gu[:, f:].astype(np.float64)
+    dh64 = dh.astype(np.float64)
+    ref = np.concatenate([O.round_bf16(dh64 * U_ * O.silu_grad(G_)), O.round_bf16(dh64 * O.silu(G_))], 1)
+    # (the GPU forms dgu in fp32, the oracle in fp64: where the two bf16 roundings differ by an
+    # ulp the E4M3 code can move one step, at most 2**-3 of that element; the mean stays tiny)
+    dec = O.e4m3_decode(fb[0]) * np.ldexp(1.0, fb[1].astype(np.int64) - 127).repeat(32, axis=1)
+    from tests.gpu_util import rel_err
+    mx, mean = rel_err(dec, O.mx_q_rows(ref))
+    assert mx <= 0.125 and mean <= 1e-5, f"decoded dgu: max rel {mx:.3e} mean rel {mean:.3e}"
