@@ -246,3 +246,56 @@ def test_mx_step_dsv3_sampled(LY):
     dWr, _, db = O.router_backward(mi.x_np(w), wr, dk)
     assert_close(host(b.dW_router), dWr, "f32", "dW_router")
     assert_close(host(b.d_bias), db, "f32", "d_bias")
+
+
+def test_mx_step_graph_replay_with_new_inputs(LY):
+    """The whole MXFP8 training step (weight quantisation, forward, backward with the router
+    backward and the fused SwiGLU-backward quantiser) captured once in a HIP graph and
+    replayed on new inputs whose routing and group sizes differ: every replay, with eager
+    work and synchronisations between replays, equals the eager step bit for bit."""
+    L, layer = LY
+    w = mi.WORKLOADS["small_mxfp8"]
+    dw = DeviceWorkload(w)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.MxWeights(s, "cuda")
+    b = layer.MxBuffers(s, "cuda")
+    x_static = dw.x.clone()
+    d_static = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
+    inputs = [(dw.x.clone(), d_static.clone())]
+    for seed in (301, 302):
+        xi, di = torch.empty_like(dw.x), torch.empty_like(d_static)
+        mi.randn_torch(seed, mi.X, 0, w.T, w.d, 1.0, w.dtype, "cuda", out=xi)
+        mi.randn_torch(seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda", out=di)
+        inputs.append((xi, di))
+    names = ("out", "dx", "dW_gu", "dW_down", "dW_router", "d_bias", "offsets")
+
+    def step(x, d_out):
+        mw.quantise(dw.w_gu, dw.w_down)
+        layer.forward_mx(x, dw.w_router, dw.bias, mw, s, b)
+        layer.backward_mx(x, d_out, mw, s, b, w_router=dw.w_router)
+
+    eager = []
+    for xi, di in inputs:
+        step(xi, di)
+        torch.cuda.synchronize()
+        eager.append({n: bits(getattr(b, n)).copy() for n in names})
+    assert not np.array_equal(eager[0]["offsets"], eager[1]["offsets"])   # the routings really differ
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step(x_static, d_static)                       # warm-up off the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            step(x_static, d_static)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for (xi, di), want in zip(inputs, eager):
+            x_static.copy_(xi)
+            d_static.copy_(di)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for n in names:
+                np.testing.assert_array_equal(bits(getattr(b, n)), want[n], err_msg=f"{n}, replay {rep}")
