@@ -327,12 +327,22 @@ def main_mx(args, w):
     print(json.dumps(res), flush=True)
 
 
+# Workloads that were benchmarked together in one GPU run that ended in a GPU memory fault;
+# which of them faulted, and why, is not known, so none of them is run until the cause is.
+HELD_WORKLOADS = ("dsv3_ep8", "mixtral", "qwen3")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "the layer runs on one GPU only (no collectives); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload in HELD_WORKLOADS:
+        print(json.dumps({"error": f"workload {args.workload} is held: the first GPU run that included it "
+                                   "ended in a GPU memory fault whose cause is not yet found",
+                          "workload": args.workload}))
+        sys.exit(3)
     import torch
     import moe_inputs as mi
     from dropless_mixture_experts_device_amd import _lib as L

@@ -1,5 +1,6 @@
 """Host-side arithmetic of bench.py (no GPU): useful FLOPs, algorithmic GEMM bytes, the MXFP8
 step's per-GEMM work table, and the reading of the committed counter summary."""
+import json
 import os
 
 import numpy as np
@@ -72,3 +73,12 @@ def test_gpus_above_one_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().out
+
+
+@pytest.mark.parametrize("name", ["dsv3_ep8", "mixtral", "qwen3"])
+def test_held_workloads_refused(monkeypatch, capsys, name):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--workload", name])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 3
+    assert "held" in json.loads(capsys.readouterr().out.strip())["error"]
