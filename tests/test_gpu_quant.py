@@ -294,7 +294,8 @@ def test_quant_dual_expert_weight_stack(L):
     np.testing.assert_array_equal(sg[cs_t].cpu().numpy(), scales[0].T)
 
 
-@pytest.mark.parametrize("sizes,f", [([0, 1, 33, 0, 500, 64, 402], 256), ([700, 0, 2048, 129, 5, 1300], 2048)])
+@pytest.mark.parametrize("sizes,f", [([0, 1, 33, 0, 500, 64, 402], 256), ([700, 0, 2048, 129, 5, 1300], 2048),
+                                     ([3, 0, 130, 1], 128)])
 def test_swiglu_backward_quant_fused(L, sizes, f):
     """moe_swiglu_backward_quant_mxfp8_dual writes exactly the bytes of moe_swiglu_backward
     followed by moe_group_quant_mxfp8_dual; those bytes are the oracle's quantisation of that
