@@ -61,7 +61,8 @@ const char* moe_status_str(int32_t status);
 
 /* Device bytes of workspace an entry point needs (0 if none). Arguments that do not apply
  * to `op` are ignored: ROUTE uses (T, d, E); PERMUTE uses (T, E); GROUPED_GEMM and QUANT use
- * G (the group count). The result depends only on sizes, never on data. */
+ * G (the group count); ROUTE_BWD uses (T, d, E, k). The result depends only on sizes, never
+ * on data. An unknown op returns 0. */
 size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G);
 
 /*
