@@ -20,7 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT, MOE_OP_ROUTE_BWD = 0, 1, 2, 3, 4
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_BWD_QUANT = 0, 1, 2, 3, 4, 5
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -67,10 +67,13 @@ _lib.moe_route_backward.restype = _i32
 _lib.moe_swiglu_backward_quant_mxfp8_dual.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _vp, _i64,
                                                       _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
 _lib.moe_swiglu_backward_quant_mxfp8_dual.restype = _i32
+_lib.moe_combine_backward_quant_mxfp8_dual.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _i32,
+                                                       _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
+_lib.moe_combine_backward_quant_mxfp8_dual.restype = _i32
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
             "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward",
-            "moe_route_backward", "moe_swiglu_backward_quant_mxfp8_dual")
+            "moe_route_backward", "moe_swiglu_backward_quant_mxfp8_dual", "moe_combine_backward_quant_mxfp8_dual")
 
 
 class MoeError(RuntimeError):
@@ -241,6 +244,20 @@ def moe_swiglu_backward_quant_mxfp8_dual(dh, gu, q_row, s_row, q_col, s_col, gro
         _ptr(dh), dh.stride(0), _ptr(gu), gu.stride(0), _dtype(dh), rows, f, _ptr(group_offsets),
         group_offsets.numel() - 1, _ptr(q_row), q_row.stride(0), _ptr(s_row), s_row.stride(0), _ptr(q_col),
         q_col.stride(0), _ptr(s_col), s_col.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
+
+
+def moe_combine_backward_quant_mxfp8_dual(d_out, topk_w, row_of, src_token, shared: bool, q_row, s_row, q_col, s_col,
+                                          group_offsets, block_start=None, workspace=None, stream=None):
+    """The combine's transpose (dY rows = topk_w * d_out in expert order, plus d_out as the
+    shared rows) quantised straight into both MXFP8 copies, without dY in memory. `workspace`:
+    moe_workspace_bytes(MOE_OP_COMBINE_BWD_QUANT, T, 0, 0, k, G) bytes."""
+    T, k = row_of.shape
+    d = d_out.shape[1]
+    ws, wsb = _ws(workspace)
+    _check("moe_combine_backward_quant_mxfp8_dual", _lib.moe_combine_backward_quant_mxfp8_dual(
+        _ptr(d_out), _dtype(d_out), _ptr(topk_w), _ptr(row_of), _ptr(src_token), T, d, k, int(bool(shared)),
+        _ptr(group_offsets), group_offsets.numel() - 1, _ptr(q_row), q_row.stride(0), _ptr(s_row), s_row.stride(0),
+        _ptr(q_col), q_col.stride(0), _ptr(s_col), s_col.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
 
 
 def moe_swiglu_backward(dh, gu, dgu, stream=None):

@@ -11,6 +11,7 @@
 #include <algorithm>
 
 #include "moe_internal.h"
+#include "round_math.h"
 
 namespace moe {
 namespace {
@@ -158,19 +159,6 @@ __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(const char* __
     }
 }
 
-// x * w rounded once to the storage type: the product of an fp32 weight and a bf16/fp32
-// value is exact in double; round-to-odd to fp32 keeps enough bits that the final
-// nearest-even rounding to bf16 equals a single rounding of the exact product.
-__device__ __forceinline__ float mul_round_odd(float w, float x) {
-    const double p = (double)w * (double)x;
-    float f = (float)p;
-    if ((double)f != p) {
-        uint32_t u = __float_as_uint(f);
-        if (fabs((double)f) > fabs(p)) u -= 1;   // truncate toward zero ...
-        f = __uint_as_float(u | 1u);             // ... and mark inexact in the last bit
-    }
-    return f;
-}
 
 // Transpose of the combine, one workgroup per token:
 //   dy[row_of[t,j]] = w[t,j] * d_out[t]       (every routed row is written exactly once)
@@ -219,7 +207,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_bwd_kernel(const char* _
                 const float w = wts[j];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = ESIZE == 2 ? mul_round_odd(w, g[i]) : w * g[i];
-                store8<ESIZE>(dy + rows[j] * rowbytes + c * 8 * ESIZE, o);
+                if (dy != nullptr) store8<ESIZE>(dy + rows[j] * rowbytes + c * 8 * ESIZE, o);
                 if (dw != nullptr) {
                     float acc = 0.f;
 #pragma unroll
@@ -284,8 +272,8 @@ extern "C" moe_status_t moe_combine_backward(const void* d_out, int32_t dtype, c
     if (T * (int64_t)k > INT32_MAX || d > INT32_MAX / 16) return MOE_EINVAL;
     if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
-    if (!d_out || !topk_w || !row_of || !dy || (dw && !y)) return MOE_EINVAL;
-    if (!moe_aligned16(d_out) || !moe_aligned16(dy) || (dy_shared && !moe_aligned16(dy_shared)) ||
+    if (!d_out || !topk_w || !row_of || (dw && !y)) return MOE_EINVAL;
+    if (!moe_aligned16(d_out) || (dy && !moe_aligned16(dy)) || (dy_shared && !moe_aligned16(dy_shared)) ||
         (dw && !moe_aligned16(y)))
         return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;

@@ -8,6 +8,7 @@
 // rounded to nearest-even E4M3 after division by 2^exponent, saturating at +-448.
 #include "moe_internal.h"
 #include "swiglu_math.h"
+#include "round_math.h"
 
 namespace moe {
 namespace {
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
                                                          uint8_t* __restrict__ q_row, int64_t ld_q_row,
                                                          uint8_t* __restrict__ s_row, int64_t ld_s_row,
                                                          const char* __restrict__ gu = nullptr, int64_t ld_gu = 0,
-                                                         int f = 0) {
+                                                         int f = 0, const float* __restrict__ row_scale = nullptr) {
     static_assert(!SWB || ESIZE == 2, "the fused SwiGLU-backward mode reads bf16");
     constexpr int TC = ESIZE == 2 ? kColTile : kColTile / 2;    // columns of this tile
     constexpr int PITCH = TC * ESIZE + 16;                       // LDS bytes per row (256 + pad)
@@ -214,6 +215,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     int64_t roff[NL];
 #pragma unroll
     for (int u = 0; u < NL; ++u) roff[u] = min<int64_t>(r0 + i0 + u * RS, rows - 1);
+    // scaled-gather mode: logical row r's values are row_scale[r] * in[row r], one rounding
+    float rsc[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) rsc[u] = row_scale != nullptr ? row_scale[roff[u]] : 1.0f;
     if (row_index != nullptr) {   // gathered rows: all index loads first, then the clamps
         int32_t ix[NL];
 #pragma unroll
@@ -266,6 +271,20 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
 #pragma unroll
         for (int u = 0; u < NL; ++u)
             lv[u] = *reinterpret_cast<const u32x4*>(in + (roff[u] * ld_in + c0) * ESIZE + pc_safe * 16);
+        if (row_scale != nullptr) {
+#pragma unroll
+            for (int u = 0; u < NL; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if (ESIZE == 2) {
+                        const float lo = mul_round_odd(rsc[u], __uint_as_float(lv[u][w] << 16));
+                        const float hi = mul_round_odd(rsc[u], __uint_as_float(lv[u][w] & 0xFFFF0000u));
+                        lv[u][w] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                    } else {
+                        lv[u][w] = __float_as_uint(rsc[u] * __uint_as_float(lv[u][w]));
+                    }
+                }
+        }
     }
     // one pass per output tile: the tile's values go to LDS, then both copies are written
     // (the fused SwiGLU-backward mode makes a second pass for the up half's tile)
@@ -404,18 +423,27 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const char* __restrict_
     }
 }
 
+// Weight of each permuted row for the combine's transpose: the routed row of (t, j) carries
+// topk_w[t, j]; the shared expert's rows (T*k + t) carry 1.
+__global__ __launch_bounds__(256) void row_weights_kernel(const float* __restrict__ topk_w,
+                                                          const int32_t* __restrict__ row_of, int T, int k,
+                                                          int shared, float* __restrict__ w_perm) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int TK = T * k;
+    if (i < TK) w_perm[min(max(row_of[i], 0), TK - 1)] = topk_w[i];
+    else if (shared && i < TK + T) w_perm[i] = 1.0f;
+}
+
 }  // namespace
 }  // namespace moe
 
 size_t moe_quant_workspace_bytes(int32_t G) { return ((size_t)(G < 1 ? 1 : G) + 1) * 4 + 255 & ~size_t(255); }
 
-// Shared host path of the column-wise mode (and of the dual mode when q_row is given).
-static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
-                                  const int32_t* row_index, int64_t in_rows, const int32_t* group_offsets, int32_t G,
-                                  uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
-                                  uint8_t* q_row, int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
-                                  int32_t* block_start, void* workspace, size_t workspace_bytes, hipStream_t s,
-                                  const void* gu = nullptr, int64_t ld_gu = 0, int64_t f = 0) {
+// Argument checks of the column-wise path, done before anything is enqueued.
+static moe_status_t quant_colwise_check(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                        const int32_t* group_offsets, int32_t G, const uint8_t* q, int64_t ld_q,
+                                        const uint8_t* scales, int64_t ld_scales, const int32_t* block_start,
+                                        const void* workspace, size_t workspace_bytes) {
     const int esize = dtype == MOE_BF16 ? 2 : 4;
     if (G < 1 || !group_offsets || rows > INT32_MAX / 2) return MOE_EINVAL;
     // blocks over all groups, upper bound: sum_g 4 ceil(m_g / 128) <= 4 (ceil(rows / 128) + G)
@@ -430,6 +458,22 @@ static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, i
     // 16-byte row loads and 4-byte scale words
     if ((reinterpret_cast<uintptr_t>(in) & 15) || (ld_in * esize) % 16 || (cols * esize) % 16) return MOE_EINVAL;
     if (reinterpret_cast<uintptr_t>(scales) & 3) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+// Shared host path of the column-wise mode (and of the dual mode when q_row is given).
+static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                  const int32_t* row_index, int64_t in_rows, const int32_t* group_offsets, int32_t G,
+                                  uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
+                                  uint8_t* q_row, int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                  int32_t* block_start, void* workspace, size_t workspace_bytes, hipStream_t s,
+                                  const void* gu = nullptr, int64_t ld_gu = 0, int64_t f = 0,
+                                  const float* row_scale = nullptr) {
+    const int esize = dtype == MOE_BF16 ? 2 : 4;
+    const moe_status_t chk = quant_colwise_check(in, dtype, rows, cols, ld_in, group_offsets, G, q, ld_q, scales,
+                                                 ld_scales, block_start, workspace, workspace_bytes);
+    if (chk != MOE_OK) return chk;
+    const int64_t nblk_cap = moe::kGroupAlign * (moe::cdiv<int64_t>(rows, moe::kGroupAlign * moe::kBlock) + G);
     int32_t* bs = block_start ? block_start : (int32_t*)workspace;
     hipLaunchKernelGGL(moe::quant_block_prefix_kernel, dim3(1), dim3(1024), 0, s, group_offsets, G, rows, bs);
     MOE_CHECK_LAUNCH();
@@ -443,10 +487,12 @@ static moe_status_t quant_colwise(const void* in, int32_t dtype, int64_t rows, i
                            ld_s_row, (const char*)gu, ld_gu, (int)f);
     else if (esize == 2)
         hipLaunchKernelGGL(moe::quant_cols_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row);
+                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row,
+                           nullptr, 0, 0, row_scale);
     else
         hipLaunchKernelGGL(moe::quant_cols_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
-                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row);
+                           row_index, in_rows, group_offsets, G, bs, q, scales, q_row, ld_q_row, s_row, ld_s_row,
+                           nullptr, 0, 0, row_scale);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
@@ -520,4 +566,41 @@ extern "C" moe_status_t moe_swiglu_backward_quant_mxfp8_dual(const void* dh, int
     return quant_colwise(dh, dtype, rows, cols, ld_dh, nullptr, rows, group_offsets, G, q_col, ld_q_col, s_col,
                          ld_s_col, q_row, ld_q_row, s_row, ld_s_row, block_start, workspace, workspace_bytes,
                          (hipStream_t)stream, gu, ld_gu, f);
+}
+
+size_t moe_combine_bwd_quant_workspace_bytes(int64_t T, int32_t k, int32_t G) {
+    const int64_t rows = T > 0 ? T * (k > 0 ? k : 1) + T : 0;    // room for the shared rows
+    return (((size_t)rows * 4 + 255) & ~size_t(255)) + moe_quant_workspace_bytes(G);
+}
+
+extern "C" moe_status_t moe_combine_backward_quant_mxfp8_dual(
+    const void* d_out, int32_t dtype, const float* topk_w, const int32_t* row_of, const int32_t* src_token, int64_t T,
+    int64_t d, int32_t k, int32_t shared_group, const int32_t* group_offsets, int32_t G, uint8_t* q_row,
+    int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row, uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col,
+    int64_t ld_s_col, int32_t* block_start, void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || d <= 0 || d % moe::kBlock != 0 || d > INT32_MAX / 2 || k < 1 || k > 16) return MOE_EINVAL;
+    if (T * (int64_t)(k + 1) > INT32_MAX / 4) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (!workspace || workspace_bytes < moe_combine_bwd_quant_workspace_bytes(T, k, G)) return MOE_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_EINVAL;
+    if (T > 0 && (!d_out || !topk_w || !row_of || !src_token)) return MOE_EINVAL;
+    if (!q_row || !s_row || ld_q_row < d || ld_s_row < d / moe::kBlock) return MOE_EINVAL;
+    if (!moe_aligned16(q_row) || ld_q_row % 16 != 0) return MOE_EINVAL;
+    const int64_t rows = T * k + (shared_group ? T : 0);
+    const size_t wbytes = ((size_t)(T > 0 ? T * k + T : 0) * 4 + 255) & ~size_t(255);
+    // every argument of the quantiser is checked before the row-weight kernel is enqueued
+    const moe_status_t chk = quant_colwise_check(d_out, dtype, rows, d, d, group_offsets, G, q_col, ld_q_col, s_col,
+                                                 ld_s_col, block_start, (char*)workspace + wbytes,
+                                                 workspace_bytes - wbytes);
+    if (chk != MOE_OK) return chk;
+    float* w_perm = (float*)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    if (rows > 0) {
+        hipLaunchKernelGGL(moe::row_weights_kernel, dim3((unsigned)moe::cdiv<int64_t>(rows, 256)), dim3(256), 0, s,
+                           topk_w, row_of, (int)T, k, shared_group ? 1 : 0, w_perm);
+        MOE_CHECK_LAUNCH();
+    }
+    return quant_colwise(d_out, dtype, rows, d, d, src_token, T > 0 ? T : 1, group_offsets, G, q_col, ld_q_col, s_col,
+                         ld_s_col, q_row, ld_q_row, s_row, ld_s_row, block_start, (char*)workspace + wbytes,
+                         workspace_bytes - wbytes, s, nullptr, 0, 0, w_perm);
 }

@@ -194,6 +194,8 @@ class MxBuffers(LayerBuffers):
         self.d_bias = torch.empty((s.E,), dtype=torch.float32, device=dev)
         rbb = L.moe_workspace_bytes(L.MOE_OP_ROUTE_BWD, s.T, d, s.E, s.k, 0)
         self.ws_route_bwd = torch.empty((rbb,), dtype=torch.uint8, device=dev)
+        cqb = L.moe_workspace_bytes(L.MOE_OP_COMBINE_BWD_QUANT, s.T, 0, 0, s.k, G)
+        self.ws_combine_quant = torch.empty((cqb,), dtype=torch.uint8, device=dev)
         gb = L.moe_workspace_bytes(L.MOE_OP_GROUPED_GEMM, 0, 0, 0, 0, G)
         self.ws_gemm3 = torch.empty((max(gb, 256),), dtype=torch.uint8, device=dev)
 
@@ -232,7 +234,7 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
 
 
 def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None, w_router=None,
-                fuse_swiglu_quant: bool = True):
+                fuse_swiglu_quant: bool = True, fuse_combine_quant: bool = True):
     """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down and,
     when w_router is given (a forward that ran the router), b.dW_router and b.d_bias.
 
@@ -243,15 +245,25 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
     normalisation to the keys, from there to W_router and the bias, and the router's share
     of the input gradient added into dx. With fuse_swiglu_quant (the default) the SwiGLU
     backward is formed inside the quantiser that writes both MXFP8 copies of dGU, so b.dGU is
-    not written; otherwise it is written by its own kernel and then quantised."""
+    not written; otherwise it is written by its own kernel and then quantised. Likewise with
+    fuse_combine_quant (the default) dY is formed inside the quantiser from d_out and the
+    routing weights, so b.dY is not written and the combine's transpose only computes dw."""
     mark = mark or _nomark
     tk = s.T * s.k
-    L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
-                           dy_shared=b.dY[tk:] if s.shared else None, dw=b.dw)
-    mark("combine_bwd")
+    if fuse_combine_quant:
+        L.moe_combine_backward(d_out, b.topk_w, b.row_of, None, y=b.Y[:tk], dw=b.dw)
+        mark("combine_bwd")
+        L.moe_combine_backward_quant_mxfp8_dual(d_out, b.topk_w, b.row_of, b.src_token, s.shared, b.q_dy, b.s_dy,
+                                                b.qc_dy, b.sc_dy, b.offsets, block_start=b.bs,
+                                                workspace=b.ws_combine_quant)
+        mark("quant_dy")
+    else:
+        L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], y=b.Y[:tk],
+                               dy_shared=b.dY[tk:] if s.shared else None, dw=b.dw)
+        mark("combine_bwd")
+        L.moe_group_quant_mxfp8_dual(b.dY, b.q_dy, b.s_dy, b.qc_dy, b.sc_dy, b.offsets, block_start=b.bs)
+        mark("quant_dy")
     # dgrad 2 and wgrad 2
-    L.moe_group_quant_mxfp8_dual(b.dY, b.q_dy, b.s_dy, b.qc_dy, b.sc_dy, b.offsets, block_start=b.bs)
-    mark("quant_dy")
     q_dnT, s_dnT = mw.dn_T()
     L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
                        b_scale=s_dnT)

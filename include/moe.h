@@ -53,7 +53,8 @@ typedef enum {
     MOE_OP_PERMUTE = 1,
     MOE_OP_GROUPED_GEMM = 2,
     MOE_OP_QUANT = 3,
-    MOE_OP_ROUTE_BWD = 4
+    MOE_OP_ROUTE_BWD = 4,
+    MOE_OP_COMBINE_BWD_QUANT = 5
 } moe_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -61,7 +62,8 @@ const char* moe_status_str(int32_t status);
 
 /* Device bytes of workspace an entry point needs (0 if none). Arguments that do not apply
  * to `op` are ignored: ROUTE uses (T, d, E); PERMUTE uses (T, E); GROUPED_GEMM and QUANT use
- * G (the group count); ROUTE_BWD uses (T, d, E, k). The result depends only on sizes, never
+ * G (the group count); ROUTE_BWD uses (T, d, E, k); COMBINE_BWD_QUANT uses (T, k, G). The
+ * result depends only on sizes, never
  * on data. An unknown op returns 0. */
 size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int32_t G);
 
@@ -259,7 +261,8 @@ moe_status_t moe_combine(const void* y, int32_t dtype, const float* topk_w, cons
  *   dy_shared[t,:]    = d_out[t,:]                         (if dy_shared != NULL)
  *   dw[t,j]           = sum_c d_out[t,c] * y[row_of[t,j],c] (if dw != NULL; fp32, fixed order)
  *   d_out [T, d], y [T*k, d] (the forward's expert outputs; read only when dw != NULL),
- *   dy [T*k, d] (every row written once, since row_of is a permutation), dy_shared [T, d],
+ *   dy [T*k, d] (every row written once, since row_of is a permutation; may be NULL when
+ *   only dw or dy_shared are wanted), dy_shared [T, d],
  *   topk_w and dw [T, k] fp32; dtype MOE_BF16 or MOE_F32; d % 8 == 0; 16-byte aligned.
  */
 moe_status_t moe_combine_backward(const void* d_out, int32_t dtype, const float* topk_w, const int32_t* row_of,
@@ -370,6 +373,33 @@ moe_status_t moe_swiglu_backward_quant_mxfp8_dual(const void* dh, int64_t ld_dh,
                                                   uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col, int64_t ld_s_col,
                                                   int32_t* block_start, void* workspace, size_t workspace_bytes,
                                                   void* stream);
+
+/*
+ * moe_combine_backward_quant_mxfp8_dual -- the combine's transpose quantised straight into
+ * both MXFP8 copies, so the bf16 dY never goes to memory ([Blog] "Optimisation 2": the combine
+ * weights each expert row by its routing weight; [Blog] "Optimisations dropless MoE needs":
+ * the expert GEMMs, whose data- and weight-gradient products read dY, run in MXFP8 with
+ * group-aware quantisation).
+ *
+ *   The output equals moe_combine_backward(d_out, dtype, topk_w, row_of, ..., dy = dY,
+ *   dy_shared = the shared rows of dY) followed by moe_group_quant_mxfp8_dual(dY, dtype,
+ *   rows, d, d, NULL, rows, group_offsets, G, q_row, ..., s_col, ...) byte for byte, with
+ *   rows = T*k (+ T when shared_group != 0, those rows being d_out itself): each dY row is
+ *   topk_w[t,j] * d_out[t] rounded once to dtype, read through src_token.
+ *   d_out [T, d] (leading dimension d); topk_w, row_of [T, k]; src_token [rows] as
+ *   moe_permute writes them; d % 32 == 0; q_row/s_row/q_col/s_col/block_start and their
+ *   capacity rules as moe_group_quant_mxfp8_dual with cols = d.
+ *   Workspace: moe_workspace_bytes(MOE_OP_COMBINE_BWD_QUANT, T, 0, 0, k, G) bytes, 256-byte
+ *   aligned (each permuted row's weight, then the quantiser's). Errors as those two calls.
+ */
+moe_status_t moe_combine_backward_quant_mxfp8_dual(const void* d_out, int32_t dtype, const float* topk_w,
+                                                   const int32_t* row_of, const int32_t* src_token, int64_t T,
+                                                   int64_t d, int32_t k, int32_t shared_group,
+                                                   const int32_t* group_offsets, int32_t G, uint8_t* q_row,
+                                                   int64_t ld_q_row, uint8_t* s_row, int64_t ld_s_row,
+                                                   uint8_t* q_col, int64_t ld_q_col, uint8_t* s_col, int64_t ld_s_col,
+                                                   int32_t* block_start, void* workspace, size_t workspace_bytes,
+                                                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -148,6 +148,21 @@ def test_host_argument_errors_backward_and_quant(lib):
         args = list(okf)
         args[i] = v
         assert fq(*args) == want, (i, v)
+    # combine backward may skip dy (only dw wanted) ...
+    assert L._lib.moe_combine_backward(None, L.MOE_BF16, None, None, None, 0, 64, 2, None, None, None, None) == L.MOE_OK
+    # ... and its fused MXFP8 form: d % 32, k range, dtype, workspace, outputs
+    cq = L._lib.moe_combine_backward_quant_mxfp8_dual
+    wsb = L.moe_workspace_bytes(L.MOE_OP_COMBINE_BWD_QUANT, 16, 0, 0, 2, 5)
+    okc = [fake, L.MOE_BF16, fake, fake, fake, 16, 64, 2, 1, fake, 5, fake, 64, fake, 2, fake, 32 * 64, fake, 64, fake,
+           fake, wsb, None]
+    for i, v, want in ((6, 48, L.MOE_EINVAL), (7, 17, L.MOE_EINVAL), (1, L.MOE_E4M3, L.MOE_ENOTSUP),
+                       (20, None, L.MOE_EWORKSPACE), (21, wsb - 1, L.MOE_EWORKSPACE), (20, fake.value + 16, L.MOE_EINVAL),
+                       (4, None, L.MOE_EINVAL), (11, None, L.MOE_EINVAL), (12, 32, L.MOE_EINVAL),
+                       (16, 32 * 63, L.MOE_EINVAL), (15, None, L.MOE_EINVAL), (9, None, L.MOE_EINVAL),
+                       (18, 8, L.MOE_EINVAL)):
+        args = list(okc)
+        args[i] = v
+        assert cq(*args) == want, (i, v)
     # SwiGLU backward: f % 8, leading dimensions
     assert L._lib.moe_swiglu_backward(fake, 64, fake, 128, L.MOE_BF16, 16, 60, fake, 128, None) == L.MOE_EINVAL
     assert L._lib.moe_swiglu_backward(fake, 64, fake, 96, L.MOE_BF16, 16, 64, fake, 128, None) == L.MOE_EINVAL

@@ -36,10 +36,12 @@ def _step(L, layer, w, topk=None, fused=True):
     layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, routed=topk is not None)
     d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
     layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router if topk is None else None,
-                      fuse_swiglu_quant=fused)
+                      fuse_swiglu_quant=fused, fuse_combine_quant=fused)
     if fused:
-        # the stage checks read dGU: the standalone SwiGLU backward writes the exact values the
-        # fused quantiser formed (equal bytes, checked in the quantiser tests)
+        # the stage checks read dY and dGU: the standalone kernels write the exact values the
+        # fused quantisers formed (equal bytes, checked in the quantiser tests)
+        tk = w.T * w.k
+        L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], dy_shared=b.dY[tk:] if s.shared else None)
         L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
     torch.cuda.synchronize()
     return b
@@ -156,13 +158,14 @@ def test_mx_step_small(LY):
     _compare(w, b, fwd, bwd)
     # the two-kernel SwiGLU backward + quantisation gives the same step, byte for byte
     u = _step(L, layer, w, fused=False)
-    for n in ("q_dgu", "s_dgu", "dGU", "dXp", "dW_gu", "dW_down", "dx", "dW_router", "d_bias"):
+    for n in ("q_dy", "s_dy", "dY", "q_dgu", "s_dgu", "dGU", "dH", "dXp", "dW_gu", "dW_down", "dx", "dw", "dW_router",
+              "d_bias"):
         np.testing.assert_array_equal(bits(getattr(b, n)), bits(getattr(u, n)), err_msg=n)
     # column-wise copies: the group-major blocks written (capacity past block_start[G] is unused)
     nb = int(b.bs[-1].item())
     assert nb == int(u.bs[-1].item())
     cols = 2 * w.f
-    for n, per in (("qc_dgu", 32 * cols), ("sc_dgu", cols)):
+    for n, per in (("qc_dgu", 32 * cols), ("sc_dgu", cols), ("qc_dy", 32 * w.d), ("sc_dy", w.d)):
         np.testing.assert_array_equal(getattr(b, n).reshape(-1)[:per * nb].cpu().numpy(),
                                       getattr(u, n).reshape(-1)[:per * nb].cpu().numpy(), err_msg=n)
 

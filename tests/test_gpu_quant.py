@@ -340,3 +340,50 @@ def test_swiglu_backward_quant_fused(L, sizes, f):
     from tests.gpu_util import rel_err
     mx, mean = rel_err(dec, O.mx_q_rows(ref))
     assert mx <= 0.125 and mean <= 1e-5, f"decoded dgu: max rel {mx:.3e} mean rel {mean:.3e}"
+
+
+@pytest.mark.parametrize("T,d,E,k,shared,dtype", [(300, 256, 8, 2, True, "bf16"), (777, 320, 24, 6, False, "bf16"),
+                                                  (129, 96, 5, 3, True, "f32"), (1, 64, 4, 4, True, "bf16")])
+def test_combine_backward_quant_fused(L, T, d, E, k, shared, dtype):
+    """moe_combine_backward_quant_mxfp8_dual writes exactly the bytes of moe_combine_backward
+    (dY) followed by moe_group_quant_mxfp8_dual(dY), and those are the oracle's quantisation
+    of the oracle's own dY (one rounding of each exact product, so bit-exact on both sides)."""
+    g = np.random.Generator(np.random.PCG64(T + d + k))
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    wt = g.random((T, k)).astype(np.float32) + np.float32(0.05)
+    wt /= wt.sum(1, keepdims=True)
+    off, row_of, src = O.permutation(idx, E, shared_rows=T if shared else 0)
+    rows, G, tk = int(off[-1]), len(off) - 1, T * k
+    d_out = mi.randn_np(d, mi.D_OUT, 0, T, d, 1.0, dtype)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d_out_d, wt_d, ro_d, src_d, off_d = dev(d_out, dtype), torch.from_numpy(wt).cuda(), dev_i32(row_of), dev_i32(src), \
+        dev_i32(off)
+    nblk = L.quant_col_blocks(rows, G)
+
+    def bufs():
+        return (torch.full((rows, d), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((rows, d // 32), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((d, 32 * nblk), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((d, nblk), 0xAB, dtype=torch.uint8, device="cuda"),
+                torch.full((G + 1,), -1, dtype=torch.int32, device="cuda"))
+
+    fused, two = bufs(), bufs()
+    ws = torch.empty((L.moe_workspace_bytes(L.MOE_OP_COMBINE_BWD_QUANT, T, 0, 0, k, G),), dtype=torch.uint8,
+                     device="cuda")
+    L.moe_combine_backward_quant_mxfp8_dual(d_out_d, wt_d, ro_d, src_d, shared, *fused[:4], off_d, block_start=fused[4],
+                                            workspace=ws)
+    dY = torch.full((rows, d), float("nan"), dtype=dt, device="cuda")
+    L.moe_combine_backward(d_out_d, wt_d, ro_d, dY[:tk], dy_shared=dY[tk:] if shared else None)
+    L.moe_group_quant_mxfp8_dual(dY, *two[:4], off_d, block_start=two[4])
+    torch.cuda.synchronize()
+    fb, tb = [t.cpu().numpy() for t in fused], [t.cpu().numpy() for t in two]
+    for a, b, n in zip(fb, tb, ("q_row", "s_row", "q_col", "s_col", "block_start")):
+        np.testing.assert_array_equal(a, b, err_msg=n)
+    rnd = O.round_bf16 if dtype == "bf16" else O.round_f32
+    dY_ref, _ = O.combine_backward(d_out, np.zeros((tk, d)), wt, row_of, rnd)
+    if shared:
+        dY_ref = np.concatenate([dY_ref, rnd(d_out.astype(np.float64))], axis=0)
+    wq, wsc, _ = O.mx_quantize_rowwise(dY_ref)
+    np.testing.assert_array_equal(fb[0], wq)
+    np.testing.assert_array_equal(fb[1], wsc)
+    _check_colwise(dY_ref, off, fb[2].reshape(-1), fb[3].reshape(-1), fb[4])
