@@ -62,7 +62,7 @@ _lib.moe_combine_backward.restype = _i32
 _lib.moe_swiglu_backward.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i64, _vp]
 _lib.moe_swiglu_backward.restype = _i32
 _lib.moe_route_backward.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
-                                    _i32, _vp, _vp, _vp, _sz, _vp]
+                                    _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_route_backward.restype = _i32
 _lib.moe_swiglu_backward_quant_mxfp8_dual.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _vp, _i64,
                                                       _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
@@ -216,9 +216,11 @@ def moe_combine_backward(d_out, topk_w, row_of, dy, y=None, dy_shared=None, dw=N
 
 def moe_route_backward(x, w_router, keys, topk_idx, d_topk_w, score: int, row_of, offsets=None, src_token=None,
                        d_keys_sel=None, d_x=None, d_w_router=None, d_bias=None, workspace=None, stream=None,
-                       accumulate_dx: bool = False):
+                       accumulate_dx: bool = False, d_x_perm=None, d_x_perm_shared=None):
     """Router backward: d_topk_w [T,k] fp32 -> d_keys_sel [T,k] fp32, d_x [T,d] (dtype of x; with
-    accumulate_dx the router's share is added to what d_x holds), d_w_router [E,d] fp32,
+    accumulate_dx the router's share is added to what d_x holds; with d_x_perm it is added to the
+    permutation's transpose of d_x_perm (+ d_x_perm_shared), formed in the same kernel and
+    rounded as moe_combine would store it), d_w_router [E,d] fp32,
     d_bias [E] fp32 (each optional). keys [T,E] fp32 and topk_idx come from
     moe_route, offsets / row_of / src_token from moe_permute. `workspace`: a uint8 device tensor of
     moe_workspace_bytes(MOE_OP_ROUTE_BWD, T, d, E, k) bytes."""
@@ -228,8 +230,8 @@ def moe_route_backward(x, w_router, keys, topk_idx, d_topk_w, score: int, row_of
     ws, wsb = _ws(workspace)
     _check("moe_route_backward", _lib.moe_route_backward(
         _ptr(x), _ptr(w_router), _dtype(x), _ptr(keys), _ptr(topk_idx), _ptr(d_topk_w), _ptr(offsets), _ptr(row_of),
-        _ptr(src_token), T, d, E, k, score, _ptr(d_keys_sel), _ptr(d_x), int(accumulate_dx), _ptr(d_w_router),
-        _ptr(d_bias), ws, wsb,
+        _ptr(src_token), T, d, E, k, score, _ptr(d_keys_sel), _ptr(d_x), int(accumulate_dx), _ptr(d_x_perm),
+        _ptr(d_x_perm_shared), _ptr(d_w_router), _ptr(d_bias), ws, wsb,
         _stream(stream)))
 
 

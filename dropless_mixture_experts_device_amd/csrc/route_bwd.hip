@@ -107,13 +107,18 @@ template <int ESIZE>
 __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __restrict__ w_router,
                                                                   const int32_t* __restrict__ topk_idx,
                                                                   const float* __restrict__ dk_sel, int d, int E,
-                                                                  int k, int accumulate, char* __restrict__ dx) {
+                                                                  int k, int accumulate, char* __restrict__ dx,
+                                                                  const char* __restrict__ dxp,
+                                                                  const char* __restrict__ dxp_shared,
+                                                                  const int32_t* __restrict__ row_of, int TK) {
     const int t = blockIdx.x;
     __shared__ int rows[16];
+    __shared__ int prow[16];
     __shared__ float coef[16];
     if (threadIdx.x < k) {
         rows[threadIdx.x] = min(max(topk_idx[(int64_t)t * k + threadIdx.x], 0), E - 1);
         coef[threadIdx.x] = dk_sel[(int64_t)t * k + threadIdx.x];
+        if (dxp != nullptr) prow[threadIdx.x] = min(max(row_of[(int64_t)t * k + threadIdx.x], 0), TK - 1);
     }
     __syncthreads();
     const int64_t rowbytes = (int64_t)d * ESIZE;
@@ -132,7 +137,31 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_dx_kernel(const char* __
             }
         }
         char* o = dx + t * rowbytes + (int64_t)c * 8 * ESIZE;
-        if (accumulate) {   // the incoming gradient joins the fp32 sum; still one rounding
+        if (dxp != nullptr) {
+            // the incoming gradient formed here as the permutation's transpose: the token's
+            // permuted rows summed in fp32 in slot order, then its shared row, rounded once to
+            // the storage type (exactly what moe_combine without weights stores)
+            float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                float v[8][8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    ld8f<ESIZE>(dxp + prow[min(j0 + u, k - 1)] * rowbytes + (int64_t)c * 8 * ESIZE, v[u]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sum[i] = j0 + u < k ? fmaf(1.f, v[u][i], sum[i]) : sum[i];
+            }
+            if (dxp_shared != nullptr) {
+                float v[8];
+                ld8f<ESIZE>(dxp_shared + t * rowbytes + (int64_t)c * 8 * ESIZE, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sum[i] += v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += ESIZE == 2 ? bf16_to_f32(f32_to_bf16(sum[i])) : sum[i];
+        } else if (accumulate) {   // the incoming gradient joins the fp32 sum; still one rounding
             float v[8];
             ld8f<ESIZE>(o, v);
 #pragma unroll
@@ -293,7 +322,8 @@ extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, 
                                            const int32_t* topk_idx, const float* d_topk_w, const int32_t* offsets,
                                            const int32_t* row_of, const int32_t* src_token, int64_t T, int64_t d,
                                            int32_t E, int32_t k, int32_t score, float* d_keys_sel, void* d_x,
-                                           int32_t accumulate_dx, float* d_w_router, float* d_bias, void* workspace,
+                                           int32_t accumulate_dx, const void* d_x_perm, const void* d_x_perm_shared,
+                                           float* d_w_router, float* d_bias, void* workspace,
                                            size_t workspace_bytes, void* stream) {
     if (T < 0 || d <= 0 || d % 8 != 0 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return MOE_EINVAL;
     if (T * (int64_t)k > ((int64_t)1 << 30) || d > INT32_MAX / 16 || T * (int64_t)d > ((int64_t)1 << 40))
@@ -307,6 +337,8 @@ extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, 
     } else {
         if (!keys || !topk_idx || !d_topk_w || !row_of) return MOE_EINVAL;
         if (d_x && (!w_router || !moe_aligned16(w_router) || !moe_aligned16(d_x))) return MOE_EINVAL;
+        if (d_x_perm && (!d_x || !moe_aligned16(d_x_perm))) return MOE_EINVAL;
+        if (d_x_perm_shared && (!d_x_perm || !moe_aligned16(d_x_perm_shared))) return MOE_EINVAL;
         if (want_w && (!x || !src_token || !moe_aligned16(x))) return MOE_EINVAL;
     }
     if (d_w_router && !moe_aligned16(d_w_router)) return MOE_EINVAL;
@@ -327,11 +359,11 @@ extern "C" moe_status_t moe_route_backward(const void* x, const void* w_router, 
             if (esize == 2)
                 hipLaunchKernelGGL(moe::route_bwd_dx_kernel<2>, dim3((unsigned)Ti), dim3(moe::kRbThreads), 0, s,
                                    (const char*)w_router, topk_idx, dk_sel, di, E, k, accumulate_dx != 0 ? 1 : 0,
-                                   (char*)d_x);
+                                   (char*)d_x, (const char*)d_x_perm, (const char*)d_x_perm_shared, row_of, TK);
             else
                 hipLaunchKernelGGL(moe::route_bwd_dx_kernel<4>, dim3((unsigned)Ti), dim3(moe::kRbThreads), 0, s,
                                    (const char*)w_router, topk_idx, dk_sel, di, E, k, accumulate_dx != 0 ? 1 : 0,
-                                   (char*)d_x);
+                                   (char*)d_x, (const char*)d_x_perm, (const char*)d_x_perm_shared, row_of, TK);
             MOE_CHECK_LAUNCH();
         }
     }

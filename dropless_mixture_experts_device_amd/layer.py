@@ -243,7 +243,7 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
     (dX_perm = dGU W_gu, over 2f) and wgrad 1 (dW_gu[g] = dGU_g^T X_g); permute^T -> dx;
     then the router's backward: the routing weights' gradient dw through the top-k
     normalisation to the keys, from there to W_router and the bias, and the router's share
-    of the input gradient added into dx. With fuse_swiglu_quant (the default) the SwiGLU
+    of the input gradient added into dx (its dx pass forms permute^T itself). With fuse_swiglu_quant (the default) the SwiGLU
     backward is formed inside the quantiser that writes both MXFP8 copies of dGU, so b.dGU is
     not written; otherwise it is written by its own kernel and then quantised. Likewise with
     fuse_combine_quant (the default) dY is formed inside the quantiser from d_out and the
@@ -291,11 +291,15 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
     L.moe_grouped_gemm(b.qc_dgu, b.qc_x, b.dW_gu, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dgu, b_scale=b.sc_x, ragged_k=True)
     mark("wgrad1")
-    # permute^T: each token's rows summed back (plus the shared expert's row)
-    L.moe_combine(b.dXp[:tk], None, b.row_of, b.dXp[tk:] if s.shared else None, b.dx)
-    mark("unpermute")
-    if w_router is not None:
+    if w_router is None:
+        # permute^T: each token's rows summed back (plus the shared expert's row)
+        L.moe_combine(b.dXp[:tk], None, b.row_of, b.dXp[tk:] if s.shared else None, b.dx)
+        mark("unpermute")
+    else:
+        # the router's backward; its dx pass forms permute^T itself (the same sum and rounding
+        # as moe_combine without weights) and adds the router's share
         L.moe_route_backward(x, w_router, b.keys, b.topk_idx, b.dw, s.score, b.row_of, offsets=b.offsets,
-                             src_token=b.src_token, d_x=b.dx, accumulate_dx=True, d_w_router=b.dW_router,
+                             src_token=b.src_token, d_x=b.dx, d_x_perm=b.dXp[:tk],
+                             d_x_perm_shared=b.dXp[tk:] if s.shared else None, d_w_router=b.dW_router,
                              d_bias=b.d_bias, workspace=b.ws_route_bwd)
-        mark("route_bwd")
+        mark("unpermute_route_bwd")

@@ -110,7 +110,13 @@ moe_status_t moe_route(const void* x, const void* w_router, int32_t dtype, const
  *                      rounded once to dtype                                [T, d]
  *                      (accumulate_dx != 0: d_x[t,:] + that sum, the incoming value
  *                      read into the fp32 sum and the total rounded once, so the expert
- *                      path's input gradient and the router's join in one buffer)
+ *                      path's input gradient and the router's join in one buffer;
+ *                      d_x_perm != NULL: the incoming value is not read from d_x but formed
+ *                      as the permutation's transpose of d_x_perm [T*k, d] (rows in expert
+ *                      order, through row_of) plus d_x_perm_shared [T, d] if not NULL,
+ *                      rounded once to dtype exactly as moe_combine(d_x_perm, NULL, row_of,
+ *                      d_x_perm_shared) stores it, then the router's share is added as
+ *                      above; accumulate_dx is then ignored)
  *   d_w_router[e,:]  = sum over tokens t that picked e of dkey * x[t,:]     [E, d] fp32
  *                      (rows of expert e in ascending token order, summed in
  *                      chunks of 256 rows whose partials are added in chunk order)
@@ -132,8 +138,9 @@ moe_status_t moe_route_backward(const void* x, const void* w_router, int32_t dty
                                 const int32_t* topk_idx, const float* d_topk_w, const int32_t* offsets,
                                 const int32_t* row_of, const int32_t* src_token, int64_t T, int64_t d,
                                 int32_t E, int32_t k, int32_t score, float* d_keys_sel, void* d_x,
-                                int32_t accumulate_dx, float* d_w_router, float* d_bias, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                int32_t accumulate_dx, const void* d_x_perm, const void* d_x_perm_shared,
+                                float* d_w_router, float* d_bias, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * moe_permute -- dispatch on one GPU: per-expert histogram, group offsets, permutation and

@@ -127,17 +127,18 @@ def test_host_argument_errors_backward_and_quant(lib):
     wsb = L.moe_workspace_bytes(L.MOE_OP_ROUTE_BWD, 16, 64, 8, 2)
     assert wsb >= 2 * 16 * 2 * 4
     ok = (fake, fake, L.MOE_BF16, fake, fake, fake, fake, fake, fake, 16, 64, 8, 2, L.MOE_SIGMOID,
-          fake, fake, 1, fake, fake, fake, wsb, None)
+          fake, fake, 1, None, None, fake, fake, fake, wsb, None)
     for i, v, want in ((10, 60, L.MOE_EINVAL), (12, 17, L.MOE_EINVAL), (12, 0, L.MOE_EINVAL), (11, 300, L.MOE_EINVAL),
                        (11, 1, L.MOE_EINVAL),
                        (13, 2, L.MOE_EINVAL), (2, L.MOE_E4M3, L.MOE_ENOTSUP), (6, None, L.MOE_EINVAL),
                        (8, None, L.MOE_EINVAL), (7, None, L.MOE_EINVAL), (3, None, L.MOE_EINVAL),
-                       (19, None, L.MOE_EWORKSPACE), (20, wsb - 1, L.MOE_EWORKSPACE), (19, fake.value + 16, L.MOE_EINVAL)):
+                       (21, None, L.MOE_EWORKSPACE), (22, wsb - 1, L.MOE_EWORKSPACE), (21, fake.value + 16, L.MOE_EINVAL),
+                       (18, fake, L.MOE_EINVAL), (17, fake.value + 8, L.MOE_EINVAL)):
         args = list(ok)
         args[i] = v
         assert rb(*args) == want, (i, v)
     assert rb(None, None, L.MOE_BF16, None, None, None, None, None, None, 0, 64, 8, 2, L.MOE_SOFTMAX,
-              None, None, 0, None, None, fake, 256, None) == L.MOE_OK
+              None, None, 0, None, None, None, None, fake, 256, None) == L.MOE_OK
     # fused SwiGLU backward + MXFP8: f % 128, bf16 only, leading dimensions, outputs
     fq = L._lib.moe_swiglu_backward_quant_mxfp8_dual
     okf = [fake, 256, fake, 512, L.MOE_BF16, 64, 256, fake, 2, fake, 512, fake, 16, fake, 32 * 16, fake, 16, fake,

@@ -101,6 +101,37 @@ def test_route_backward_accumulates_into_dx(L, dtype):
     assert_close(host(dx), rnd(prior + dx_r), dtype, "d_x accumulated")
 
 
+@pytest.mark.parametrize("dtype,shared", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_route_backward_forms_unpermute(L, dtype, shared):
+    """d_x_perm: the dx pass forms the permutation's transpose itself; the bytes equal
+    moe_combine without weights followed by the accumulate mode."""
+    T, d, E, k = 300, 1032, 32, 6
+    x, w, keys, idx, g = _problem(T, d, E, k, "softmax", dtype, seed=13)
+    offsets, row_of, src = O.permutation(idx, E, shared_rows=T if shared else 0)
+    rows = T * k + (T if shared else 0)
+    dxp = dev(mi.randn_np(13, mi.D_OUT, 2, rows, d, 0.05, dtype), dtype)
+    nb = L.moe_workspace_bytes(L.MOE_OP_ROUTE_BWD, T, d, E, k, 0)
+    common = dict(offsets=dev_i32(offsets), src_token=dev_i32(src),
+                  workspace=torch.empty((nb,), dtype=torch.uint8, device="cuda"))
+    args = (dev(x, dtype), dev(w, dtype), dev(keys), dev_i32(idx), dev(g), L.MOE_SOFTMAX, dev_i32(row_of))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    fused = torch.full((T, d), float("nan"), dtype=dt, device="cuda")
+    L.moe_route_backward(*args, d_x=fused, d_x_perm=dxp[:T * k], d_x_perm_shared=dxp[T * k:] if shared else None,
+                         **common)
+    two = torch.full((T, d), float("nan"), dtype=dt, device="cuda")
+    L.moe_combine(dxp[:T * k], None, dev_i32(row_of), dxp[T * k:] if shared else None, two)
+    L.moe_route_backward(*args, d_x=two, accumulate_dx=True, **common)
+    torch.cuda.synchronize()
+    from tests.gpu_util import bits
+    np.testing.assert_array_equal(bits(fused), bits(two))
+    # and against the oracle: the transpose of the permutation (as stored) plus the router's share
+    rnd = O.round_bf16 if dtype == "bf16" else O.round_f32
+    dxp_h = host(dxp)
+    prior = O.permute_backward(dxp_h[:T * k], row_of, dxp_h[T * k:] if shared else None, rnd)
+    _, dx_r, _ = O.router_backward(x, w, O.topk_weights_backward(keys, idx, g, "softmax"))
+    assert_close(host(fused), rnd(prior + dx_r), dtype, "d_x with the permutation's transpose")
+
+
 def test_route_backward_outputs_independent(L):
     """Each output may be requested alone; requesting fewer changes none of the others."""
     x, w, keys, idx, g = _problem(500, 512, 32, 4, "sigmoid", "bf16", seed=5)
