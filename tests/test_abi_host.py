@@ -194,3 +194,19 @@ def test_host_argument_errors_backward_and_quant(lib):
               None, 0, None) == L.MOE_EWORKSPACE
     assert qd(fake, L.MOE_E4M3, 64, 64, 64, None, 0, fake, 3, fake, 64, fake, 2, fake, 32 * cap, fake, cap, fake,
               None, 0, None) == L.MOE_ENOTSUP
+
+
+def test_binding_constants_match_header_enums():
+    """Every enumerator of include/moe.h has the same value in the Python binding, and every
+    workspace op id is answered (an unknown one returns 0)."""
+    from dropless_mixture_experts_device_amd import _lib as L
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    found = dict((n, int(v)) for n, v in re.findall(r"\b(MOE_[A-Z0-9_]+)\s*=\s*(\d+)", src))
+    assert {"MOE_OK", "MOE_BF16", "MOE_SIGMOID", "MOE_OP_ROUTE_BWD", "MOE_OP_COMBINE_BWD_QUANT"} <= set(found)
+    for name, value in found.items():
+        assert getattr(L, name) == value, name
+    ops = [v for n, v in found.items() if n.startswith("MOE_OP_")]
+    assert sorted(ops) == list(range(len(ops)))
+    assert L.moe_workspace_bytes(max(ops) + 1, 1024, 512, 64, 8, 65) == 0
+    assert L.moe_workspace_bytes(found["MOE_OP_ROUTE_BWD"], 1024, 512, 64, 8, 0) > 0
+    assert L.moe_workspace_bytes(found["MOE_OP_COMBINE_BWD_QUANT"], 1024, 0, 0, 8, 65) > 1024 * 9 * 4
