@@ -199,8 +199,12 @@ def cpu_baseline_mx(w, w_gu_dev, w_down_dev):
     x = mi.x_np(w)
     spent = 0.0
     t0 = time.perf_counter()
-    idx, wt, _ = O.route(x, mi.w_router_np(w), mi.expert_bias(w), w.k, w.score)
+    wr = mi.w_router_np(w)
+    idx, wt, keys = O.route(x, wr, mi.expert_bias(w), w.k, w.score)
     off, row_of, src = O.permutation(idx, w.E, w.T if w.shared_f else 0)
+    # the router's backward for every token (the step runs it; its FLOPs are not counted)
+    g_w = mi.randn_np(w.seed, mi.D_TOPK_W, 0, w.T, w.k, 1.0, "f32")
+    O.router_backward(x, wr, O.topk_weights_backward(keys, idx, g_w, w.score))
     spent += time.perf_counter() - t0
     groups = ([w.E] if w.shared_f else []) + [e for r in range(16) for e in range(int(f"{r:04b}"[::-1], 2), w.E, 16)]
     flops, done = 0.0, 0
@@ -220,7 +224,8 @@ def cpu_baseline_mx(w, w_gu_dev, w_down_dev):
         flops += 18.0 * (hi - lo) * w.d * (gu.shape[0] // 2)
     return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
             "seconds": round(spent, 2),
-            "sample": f"fp64 numpy MX oracle: routing and permutation of all {w.T} tokens, then the MXFP8 forward "
+            "sample": f"fp64 numpy MX oracle: routing, permutation and the router's backward of all {w.T} tokens, "
+                      f"then the MXFP8 forward "
                       f"and backward of {done} of {len(groups)} expert groups (shared first, then ids "
                       f"0,16,32,...,8,24,...) on their real rows, stopped at {CPU_BUDGET_S:.0f} s; value = useful "
                       f"FLOPs (18 m d f per group) of the finished groups / oracle time"}
