@@ -94,6 +94,81 @@ def calibrate_copy(dev):
     del src, dst
 
 
+FLUSH_BYTES = 1 << 30   # written between timed steps: twice the 256 MB MALL plus every XCD's L2
+
+
+class CacheFlush:
+    """A 1 GiB device buffer read and written once (x += 1) before each timed step, outside the
+    timing events, so no step starts with its inputs or weights left in L2 or the MALL by the
+    step before it."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros((FLUSH_BYTES // 4,), dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+def spread(v):
+    """Median, 10th and 90th percentile of per-step times (ms)."""
+    a = np.asarray(v, np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS numpy is built against."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{cfg.get('name')} {cfg.get('version')}"
+    except Exception:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except Exception:
+        ncpu = os.cpu_count()
+    return {"cpu_model": model, "blas": blas, "cpus_available": ncpu}
+
+
+def time_graph(step, steps, flush):
+    """The step captured once in a HIP graph, then `steps` replays, each after a cache flush,
+    timed with events around the replay on the launching stream. Returns per-replay ms."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        flush()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    out = [e0.elapsed_time(e1) for e0, e1 in ev]
+    del g
+    return out
+
+
 def useful_flops(w, counts):
     routed = 6.0 * w.T * w.k * w.d * w.f
     shared = 6.0 * w.T * w.d * w.shared_f
@@ -102,11 +177,11 @@ def useful_flops(w, counts):
 
 def gemm1_bytes(w, counts, fused):
     """Algorithmic HBM bytes of grouped GEMM 1 (gate/up + SwiGLU): the gate/up weights of
-    every non-empty group once, the A rows once (x itself when the gather is fused, else
+    every non-empty routed group and of the shared expert once, the A rows once (x itself when the gather is fused, else
     x_perm), H written once, plus the index metadata."""
     nonempty = int(np.count_nonzero(counts))
     rows = w.T * w.k + (w.T if w.shared_f else 0)
-    wbytes = nonempty * 2 * w.f * w.d * 2
+    wbytes = nonempty * 2 * w.f * w.d * 2 + (2 * w.shared_f * w.d * 2 if w.shared_f else 0)
     abytes = (w.T * w.d * 2) if fused else rows * w.d * 2
     hbytes = rows * w.f * 2
     return wbytes + abytes + hbytes + rows * 4
@@ -164,7 +239,7 @@ def cpu_baseline(w, w_gu_dev, w_down_dev):
             f"(shared first, then ids in the order 0,16,32,...,8,24,...) on their real rows, stopped at "
             f"{CPU_BUDGET_S:.0f} s; no combine")
     return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
-            "seconds": round(spent, 2),
+            "seconds": round(spent, 2), "host": host_info(),
             "sample": f"fp64 numpy oracle on {what}; value = useful FLOPs of the finished groups / oracle time"}
 
 
@@ -223,7 +298,7 @@ def cpu_baseline_mx(w, w_gu_dev, w_down_dev):
         spent += time.perf_counter() - t0
         flops += 18.0 * (hi - lo) * w.d * (gu.shape[0] // 2)
     return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
-            "seconds": round(spent, 2),
+            "seconds": round(spent, 2), "host": host_info(),
             "sample": f"fp64 numpy MX oracle: routing, permutation and the router's backward of all {w.T} tokens, "
                       f"then the MXFP8 forward "
                       f"and backward of {done} of {len(groups)} expert groups (shared first, then ids "
@@ -271,18 +346,24 @@ def main_mx(args, w):
         layer.forward_mx(x, wr, bias, mw, s, b, mark=mark)
         layer.backward_mx(x, d_out, mw, s, b, mark=mark, w_router=wr)
 
+    flush = CacheFlush(dev)
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     recs = [[] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(recs[i])
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     names = [n for n, _ in recs[0][1:]]
     per = np.array([[r[j][1].elapsed_time(r[j + 1][1]) for j in range(len(r) - 1)] for r in recs])
-    pm = dict(zip(names, per.mean(0)))
+    pm = dict(zip(names, np.median(per, axis=0)))
+    step_all = np.array([r[0][1].elapsed_time(r[-1][1]) for r in recs])
+    ms = float(np.median(step_all))
+    graph_ms = time_graph(step, args.steps, flush)
     counts = np.diff(b.offsets.cpu().numpy())[:w.E]
     rows = s.rows
     flops = 18.0 * rows * w.d * w.f
@@ -300,8 +381,7 @@ def main_mx(args, w):
                 "frac": round(fl / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
     roof.update({"traffic": pmc_traffic(w.name, dom), "kernel": f"moe_grouped_gemm MXFP8 {dom}", "algorithmic_bytes": int(by),
                  "algorithmic_flops": fl, "ms": round(pm[dom], 4)})
-    step_ms = float(per.sum(1).mean())
-    no_wq = step_ms - pm["weight_quant"]
+    no_wq = ms - pm["weight_quant"]
     gemm_ms = sum(pm[k] for k in work)
     res = {
         "metric": "MoE layer fwd+bwd TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped MXFP8 training step",
@@ -315,11 +395,16 @@ def main_mx(args, w):
                    "shared_f": w.shared_f, "groups_nonempty": int(np.count_nonzero(counts)),
                    "group_max": int(counts.max()), "group_min": int(counts.min()),
                    "groups_empty": int((counts == 0).sum())},
+        "timing": ("median over the timed steps of HIP events on the launching stream; every timed step "
+                   f"starts after a {FLUSH_BYTES >> 20} MiB read+write of a scratch buffer outside the events"),
+        "step_ms": spread(step_all),
+        "wall_ms_per_step_incl_flush": round(wall_ms, 4),
+        "graph_ms_per_step": spread(graph_ms),
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "ms_without_weight_quant": round(no_wq, 4),
         "value_without_weight_quant": round(flops / (no_wq * 1e-3) / 1e12, 2),
         "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
-        "stage_ms": {k: round(v, 4) for k, v in pm.items()},
+        "stage_ms": {k: spread(per[:, j]) for j, k in enumerate(names)},
         "gemm_tflops_by_stage": {k: round(work[k][1] / (pm[k] * 1e-3) / 1e12, 1) for k in work},
         "gemm_gbs_by_stage": {k: round(work[k][0] / (pm[k] * 1e-3) / 1e9, 1) for k in work},
         "roofline": roof,
@@ -376,7 +461,9 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    flush = CacheFlush(dev)
+    STAGES = ("route", "permute", "gemm1_swiglu", "gemm2", "combine")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
 
     def step(evs=None):
         if evs: evs[0].record(stream)
@@ -396,16 +483,30 @@ def main():
         if evs: evs[5].record(stream)
 
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
+    # timed: each step starts with cold caches (the flush runs before the step's first event)
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    parts = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(5)] for i in range(args.steps)])
-    pm = parts.mean(0)    # route, permute, gemm1, gemm2, combine (ms)
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    parts = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(STAGES))] for i in range(args.steps)])
+    step_ms = np.array([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)])
+    pm = np.median(parts, axis=0)   # per-stage medians (ms)
+    ms = float(np.median(step_ms))
+    # the same steps back to back with no flush (caches warm from the step before), for reference
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+    graph_ms = time_graph(step, args.steps, flush)
 
     counts = np.diff(buf.offsets.cpu().numpy())[:w.E]
     flops = useful_flops(w, counts)
@@ -425,10 +526,12 @@ def main():
     roof["traffic"] = pmc_traffic(w.name) if fused else None
     roof.update({"kernel": "moe_grouped_gemm gate/up+SwiGLU (schedule + main kernel)",
                  "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops, "ms": round(g1_ms, 4),
-                 "tflops": round(g1_tflops, 1), "gbs": round(g1_gbs, 1)})
+                 "tflops": round(g1_tflops, 1), "gbs": round(g1_gbs, 1),
+                 "mfma_frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4)})
     route_bytes = w.T * w.d * 2 + w.E * w.d * 2 + w.T * w.k * 8
-    perm_bytes = w.T * w.k * 4 * 4 + (0 if fused else (w.T * w.d * 2 + rows * w.d * 2))
+    perm_bytes = w.T * w.k * 12 + (0 if fused else (w.T * w.d * 2 + rows * w.d * 2))
     comb_bytes = w.T * w.k * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2 + (w.T * w.d * 2 if w.shared_f else 0)
+    gemm_ms = pm[2] + pm[3]
     res = {
         "metric": ("MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped bf16" if w.name == "dsv3"
                    else f"MoE layer grouped-GEMM TFLOPS (useful FLOPs) + tokens/s, {w.name} bf16"),
@@ -441,34 +544,49 @@ def main():
                    "shared_f": w.shared_f, "gather": "fused into GEMM 1" if fused else "materialised x_perm",
                    "groups_nonempty": int(np.count_nonzero(counts)), "group_max": int(counts.max()),
                    "group_min": int(counts.min()), "groups_empty": int((counts == 0).sum())},
+        "timing": ("median over the timed steps of HIP events on the launching stream; every timed step "
+                   f"starts after a {FLUSH_BYTES >> 20} MiB read+write of a scratch buffer outside the events"),
+        "step_ms": spread(step_ms),
+        "wall_ms_per_step_incl_flush": round(wall_ms, 4),
+        "graph_ms_per_step": spread(graph_ms),
+        "warm_ms_per_step": round(warm_ms, 4),
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
-        "gemm_tflops": round(flops / ((pm[2] + pm[3]) * 1e-3) / 1e12, 2),
-        "stage_ms": {"route": round(pm[0], 4), "permute": round(pm[1], 4), "gemm1_swiglu": round(pm[2], 4),
-                     "gemm2": round(pm[3], 4), "combine": round(pm[4], 4)},
+        "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "gemm_mfma_frac": round(flops / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "stage_ms": {n: spread(parts[:, j]) for j, n in enumerate(STAGES)},
         "stage_gbs": {"route": round(route_bytes / (pm[0] * 1e-3) / 1e9, 1),
                       "permute": round(perm_bytes / (pm[1] * 1e-3) / 1e9, 1),
                       "combine": round(comb_bytes / (pm[4] * 1e-3) / 1e9, 1)},
+        "stage_hbm_frac": {"route": round(route_bytes / (pm[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "combine": round(comb_bytes / (pm[4] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
         "cpu_baseline": None,
     }
-    # The step fuses the gather into GEMM 1, so its permute moves only indices. The permutation
-    # with the gather materialised (x read once, written to its k rows and the shared row) is
-    # timed here on its own, outside the step, to report the dispatch's HBM rate.
-    gbuf = layer.LayerBuffers(s, dev, fused_gather=False)
+    # The step fuses the gather into GEMM 1, so its permute moves only indices. The dispatch
+    # with the gather written out (histogram, offsets, permutation and x_perm [T*k, d]: x read
+    # once, each token row written to its k rows) is timed here on its own, outside the step,
+    # on the step's routing and with a flush before each repetition, so the dispatch's HBM
+    # rate is measured on real data movement. The shared expert reads x directly, so no
+    # shared rows are copied here.
+    gs = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=False, score=s.score)
+    gbuf = layer.LayerBuffers(gs, dev, fused_gather=False)
     gbuf.topk_idx.copy_(buf.topk_idx)    # the step's routing
     for _ in range(2):
-        layer.permute(x, s, gbuf)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    e0.record(stream)
-    for _ in range(reps):
-        layer.permute(x, s, gbuf)
-    e1.record(stream)
+        layer.permute(x, gs, gbuf)
+    reps = max(5, min(args.steps, 20))
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in pev:
+        flush()
+        e0.record(stream)
+        layer.permute(x, gs, gbuf)
+        e1.record(stream)
     torch.cuda.synchronize()
-    pg_ms = e0.elapsed_time(e1) / reps
-    pg_bytes = w.T * w.d * 2 + rows * w.d * 2 + w.T * w.k * 4 * 4
-    same = bool(torch.equal(gbuf.src_token, buf.src_token) and torch.equal(gbuf.offsets, buf.offsets))
-    res["permute_materialised"] = {"ms": round(pg_ms, 4), "gbs": round(pg_bytes / (pg_ms * 1e-3) / 1e9, 1),
+    pg = [e0.elapsed_time(e1) for e0, e1 in pev]
+    pg_ms = float(np.median(pg))
+    pg_bytes = w.T * w.d * 2 + w.T * w.k * w.d * 2 + w.T * w.k * 12
+    tk = w.T * w.k
+    same = bool(torch.equal(gbuf.src_token, buf.src_token[:tk]) and torch.equal(gbuf.offsets, buf.offsets[:w.E + 1]))
+    res["permute_materialised"] = {"ms": spread(pg), "gbs": round(pg_bytes / (pg_ms * 1e-3) / 1e9, 1),
                                    "hbm_frac": round(pg_bytes / (pg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                    "bytes": pg_bytes, "indices_match_step": same}
     del gbuf

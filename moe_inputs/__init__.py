@@ -193,6 +193,10 @@ WORKLOADS = {
     # the MXFP8 training step at a reduced shape (d, f multiples of 128 as its GEMMs need)
     "small_mxfp8": Workload("small_mxfp8", 600, 384, 256, 12, 3, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 256,
                             seed=13, mxfp8=True, backward=True),
+    # the MXFP8 step with contraction lengths of 1024 or more in every forward and data-gradient
+    # GEMM, still small enough for the oracle to finish in seconds
+    "mid_mxfp8": Workload("mid_mxfp8", 1024, 1024, 1024, 8, 2, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 1024,
+                          seed=21, mxfp8=True, backward=True),
 }
 
 

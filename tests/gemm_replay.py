@@ -1,0 +1,285 @@
+"""Host-side replay of the grouped GEMM's integer index math (no floating point).
+
+A line-by-line model, in numpy, of what moe_grouped_gemm's kernels compute from the group
+offsets: the schedule kernel's tile prefix and group order, the persistent workgroups' walk
+over the tile list (XCD-aware slots, binary search of the prefix, row-tile and column-tile
+decomposition), and for every tile the byte ranges its load waves' DMA instructions read (A
+rows through the gather index, B rows of the group, MXFP8 scale dwords, over every K slice),
+the LDS bytes they fill, and the output elements the epilogue writes. It asserts that every
+access stays inside its buffer and that every output element of every group is written by
+exactly one tile, so a launch shape can be cleared on the CPU before it runs on a GPU.
+
+Constants and formulas follow the kernel source (csrc/gemm.hip); a change there must be
+mirrored here.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+WAVE = 64
+L_WAVES = 4            # load-issuing waves
+BN = 256               # B rows per tile
+ROW_BYTES = 128        # one LDS row per stage
+ROWS_PER_INSTR = 1024 // ROW_BYTES
+MAX_GROUPS = 2047
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def stage_bytes(bm):
+    scale_rows_a = cdiv(bm, 64) * 64
+    data = (bm + BN) * ROW_BYTES
+    return dict(data=data, scale_a=data, scale_b=data + scale_rows_a * 4,
+                bytes=data + (scale_rows_a + BN) * 4, count=2 if bm == 256 else 3)
+
+
+PIPE_BYTES = max(3 * stage_bytes(128)["bytes"], 2 * stage_bytes(256)["bytes"])
+LDS_BYTES = PIPE_BYTES + (MAX_GROUPS + 1) * 4
+
+
+def bm_of_rows(m):
+    return 16 if m <= 16 else 32 if m <= 32 else 64 if m <= 64 else 128
+
+
+def row_tiles(m, allow256=False):
+    """(n256, n128, last) as the kernel's row_tiles."""
+    if m <= 128:
+        return (0, 0, bm_of_rows(m) if m > 0 else 0)
+    rest, n256 = m, 0
+    if allow256 and m >= 256:
+        n256 = m // 256
+        rest -= 256 * n256
+    n128 = rest // 128
+    rest -= 128 * n128
+    return (n256, n128, bm_of_rows(rest) if rest > 0 else 0)
+
+
+def rt_count(rt):
+    return rt[0] + rt[1] + (1 if rt[2] > 0 else 0)
+
+
+def row_tile(rt, mt):
+    n256, n128, last = rt
+    if mt < n256:
+        return 256 * mt, 256
+    if mt < n256 + n128:
+        return 256 * n256 + 128 * (mt - n256), 128
+    return 256 * n256 + 128 * n128, last
+
+
+def tile_coords(L, MT, NT, sup=4):
+    full = NT // sup
+    if L < full * MT * sup:
+        s, rem = divmod(L, MT * sup)
+        return rem // sup, s * sup + rem % sup
+    rem = L - full * MT * sup
+    w = NT - full * sup
+    return rem // w, full * sup + rem % w
+
+
+def group_rows(offsets, g, M):
+    b = min(max(int(offsets[g]), 0), M)
+    e = min(max(int(offsets[g + 1]), b), M)
+    return b, e
+
+
+def schedule(offsets, G, M, NT, allow256=False):
+    """tile_start [G+1] and order [G] as gemm_schedule_kernel writes them."""
+    tiles = np.zeros(G, np.int64)
+    small = np.zeros(G, bool)
+    rows = np.zeros(G, np.int64)
+    for g in range(G):
+        b, e = group_rows(offsets, g, M)
+        rows[g] = e - b
+        tiles[g] = rt_count(row_tiles(e - b, allow256)) * NT
+        small[g] = (e - b) <= 128
+    tot_small = int(tiles[small].sum())
+    tot_large = int(tiles[~small].sum())
+    pre_small = np.cumsum(np.where(small, tiles, 0)) - np.where(small, tiles, 0)
+    pre_large = np.cumsum(np.where(~small, tiles, 0)) - np.where(~small, tiles, 0)
+    keys = []
+    for g in range(G):
+        if tiles[g] > 0:
+            p = int(pre_small[g] if small[g] else pre_large[g])
+            total = tot_small if small[g] else tot_large
+            frac = ((2 * p + int(tiles[g])) << 23) // total
+            first = (tot_small >= tot_large) if small[g] else (tot_large > tot_small)
+            late = 0 if (allow256 and rows[g] >= 256) else 1
+            k = (late << 60) | (frac << 32) | ((0 if first else 1) << 16) | g
+        else:
+            k = (0xFFFFFFF << 32) | (2 << 60) | g
+        assert k < (1 << 64)
+        keys.append(k)
+    assert len(set(keys)) == G, "schedule keys must be distinct"
+    order = np.array(sorted(range(G), key=lambda g: keys[g]), np.int64)
+    ts = np.zeros(G + 1, np.int64)
+    ts[1:] = np.cumsum(tiles[order])
+    return ts, order
+
+
+@dataclasses.dataclass
+class Launch:
+    """One ragged-row grouped GEMM launch as the host entry point sets it up."""
+    offsets: np.ndarray     # [G+1]
+    M: int                  # rows of C
+    N: int                  # output columns
+    K: int
+    A_rows: int
+    lda: int
+    a_rows: np.ndarray | None
+    b_groups: int           # groups the B buffer holds (B tensor's first dimension)
+    ldb: int
+    b_stride: int           # elements between groups' B
+    b_bytes: int            # bytes of the B allocation reachable from its base
+    ldc: int
+    c_esize: int
+    swiglu: bool
+    mx: bool = False
+    lda_scale: int = 0
+    ldb_scale: int = 0
+    b_scale_stride: int = 0
+    b_scale_bytes: int = 0
+    aux_ld: int = 0
+    num_cus: int = 256
+
+
+def check_launch(la: Launch):
+    """Replay the whole launch; raise AssertionError at the first access outside a buffer or
+    at any output element not written exactly once. Returns a summary dict."""
+    G = len(la.offsets) - 1
+    eb = 1 if la.mx else 2
+    assert 1 <= G <= MAX_GROUPS
+    bn_out = BN // 2 if la.swiglu else BN
+    NT = cdiv(la.N, bn_out)
+    assert la.K % (ROW_BYTES // eb) == 0
+    nk = la.K // (ROW_BYTES // eb)
+    a_bytes = la.A_rows * la.lda * eb
+    # the host's 4 GiB rule for 32-bit lane offsets
+    b_span = (2 if la.swiglu else 1) * la.N * la.ldb * eb
+    assert a_bytes + la.K * eb < 1 << 32 and b_span + la.K * eb < 1 << 32
+    ts, order = schedule(la.offsets, G, la.M, NT)
+    total = int(ts[G])
+    bound = (la.M // 16 + G) * NT
+    grid = min(la.num_cus, max(bound, 1))
+    nxcd = 8 if grid % 8 == 0 else 1
+    per_xcd = grid // nxcd
+    written = np.zeros((la.M, la.N), np.int32)
+    lane = np.arange(WAVE)
+    seen_tiles = 0
+    for bid in range(grid):
+        slot = (bid % nxcd) * per_xcd + bid // nxcd
+        for tile in range(slot, total, grid):
+            seen_tiles += 1
+            lo, hi = 0, G - 1
+            while lo < hi:
+                mid = (lo + hi + 1) >> 1
+                if ts[mid] <= tile:
+                    lo = mid
+                else:
+                    hi = mid - 1
+            g = min(max(int(order[lo]), 0), G - 1)
+            L = tile - int(ts[lo])
+            rb, re = group_rows(la.offsets, g, la.M)
+            rt = row_tiles(re - rb)
+            mt, nt = tile_coords(L, rt_count(rt), NT)
+            assert 0 <= mt < rt_count(rt) and 0 <= nt < NT, (tile, g, mt, nt)
+            r_off, bm = row_tile(rt, mt)
+            assert bm in (16, 32, 64, 128)
+            _check_tile(la, g, rb, re, r_off, bm, nt, nk, eb, written)
+    assert seen_tiles == total
+    # every row of every group: columns [0, N) written exactly once; other rows untouched
+    live = np.zeros(la.M, bool)
+    for g in range(G):
+        b, e = group_rows(la.offsets, g, la.M)
+        live[b:e] = True
+    assert np.all(written[live] == 1), "an output element of a group was not written exactly once"
+    assert np.all(written[~live] == 0), "a row outside every group was written"
+    return dict(grid=grid, tiles=total, nk=nk, NT=NT)
+
+
+def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
+    lane = np.arange(WAVE)
+    WM = 1 if bm == 16 else 2
+    WN = 8 // WM
+    WTN = BN // WN
+    bn_out = BN // 2 if la.swiglu else BN
+    r0 = row_begin + r_off
+    n0 = nt * bn_out
+    st = stage_bytes(bm)
+    a_instr = bm // ROWS_PER_INSTR
+    a_per_wave = cdiv(a_instr, L_WAVES)
+    b_per_wave = BN // ROWS_PER_INSTR // L_WAVES
+    k_extent = (nk - 1) * ROW_BYTES + 16        # bytes a lane reads past its offset over the K loop
+    assert st["count"] * st["bytes"] <= PIPE_BYTES
+
+    def a_row_of(row):
+        r = np.minimum(r0 + row, row_end - 1)
+        ar = la.a_rows[r].astype(np.int64) if la.a_rows is not None else r.astype(np.int64)
+        return np.clip(ar, 0, la.A_rows - 1)
+
+    def b_row_of(rho):
+        if la.swiglu:
+            wnb, within = rho // WTN, rho % WTN
+            half, idx = within // (WTN // 2), within % (WTN // 2)
+            return half * la.N + np.minimum(n0 + wnb * (WTN // 2) + idx, la.N - 1)
+        return np.minimum(n0 + rho, la.N - 1)
+
+    b_base = g * la.b_stride * eb
+    for lw in range(L_WAVES):
+        for i in range(a_per_wave):
+            instr = lw + L_WAVES * i
+            if not (a_instr % L_WAVES == 0 or instr < a_instr):
+                continue
+            row = instr * ROWS_PER_INSTR + lane // 8
+            chunk = (lane % 8) ^ ((row >> 1) & 7)
+            voff = a_row_of(row) * la.lda * eb + chunk * 16
+            assert voff.min() >= 0 and voff.max() + k_extent <= la.A_rows * la.lda * eb, ("A", g, r0, bm)
+            assert voff.max() + k_extent - 16 < 1 << 32
+            lds = instr * 1024 + lane * 16
+            assert lds.max() + 16 <= bm * ROW_BYTES, ("A LDS", bm)
+        for i in range(b_per_wave):
+            instr = lw * b_per_wave + i
+            rho = instr * ROWS_PER_INSTR + lane // 8
+            chunk = (lane % 8) ^ ((rho >> 1) & 7)
+            voff = b_row_of(rho) * la.ldb * eb + chunk * 16
+            assert voff.min() >= 0 and voff.max() + k_extent - 16 < 1 << 32
+            assert b_base + voff.max() + k_extent <= la.b_bytes, ("B", g, nt)
+            lds = bm * ROW_BYTES + instr * 1024 + lane * 16
+            assert lds.max() + 16 <= st["data"], ("B LDS", bm)
+        if la.mx:
+            as_instr, bs_instr = cdiv(bm, 64), BN // 64
+            sc_per_wave = cdiv(as_instr + bs_instr, L_WAVES)
+            for u in range(sc_per_wave):
+                q = lw + L_WAVES * u
+                if q < as_instr:
+                    off = a_row_of(q * 64 + lane) * la.lda_scale
+                    assert off.max() + (nk - 1) * 4 + 4 <= la.A_rows * la.lda_scale, ("A scale", g)
+                    lds = st["scale_a"] + q * 256 + lane * 4
+                    assert lds.max() + 4 <= st["scale_b"]
+                elif q < as_instr + bs_instr:
+                    rho = (q - as_instr) * 64 + lane
+                    off = g * la.b_scale_stride + b_row_of(rho) * la.ldb_scale
+                    assert off.max() + (nk - 1) * 4 + 4 <= la.b_scale_bytes, ("B scale", g)
+                    lds = st["scale_b"] + (q - as_instr) * 256 + lane * 4
+                    assert lds.max() + 4 <= st["bytes"]
+    # epilogue: LDS staging of the output tile, then 16-byte stores of valid rows and columns
+    pitch = bn_out * la.c_esize + 16
+    assert bm * pitch <= PIPE_BYTES, ("epilogue LDS", bm)
+    rows_valid = min(bm, row_end - r0)
+    assert rows_valid >= 1
+    cols_per_chunk = 16 // la.c_esize
+    cols = n0 + np.arange(0, bn_out, cols_per_chunk)
+    cols = cols[cols < la.N]
+    for row in range(rows_valid):
+        r = r0 + row
+        assert r < la.M
+        last = (r * la.ldc + cols.max()) * la.c_esize + 16
+        assert last <= la.M * la.ldc * la.c_esize, ("C", g, r)
+        for c in cols:
+            written[r, c:min(c + cols_per_chunk, la.N)] += 1
+    if la.swiglu and la.aux_ld:
+        assert (r0 + rows_valid - 1) * la.aux_ld + la.N + min(n0 + bn_out, la.N) <= la.M * la.aux_ld

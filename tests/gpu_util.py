@@ -17,28 +17,51 @@ F32_MAX_REL, F32_MEAN_REL = 1e-4, 1e-5
 # MXFP8 pipelines against the MX-mirroring oracle: an intermediate that lands on the other
 # side of an E4M3 rounding boundary moves one element by up to one E4M3 step (1/16 relative)
 MX_MAX_REL, MX_MEAN_REL = 6e-2, 6e-3
-# A whole MXFP8 step against the fully independent oracle: every bf16 intermediate the GPU
-# rounds one ulp differently can flip the E4M3 code of a block maximum by a whole step (up to
-# 1/8 relative), which moves single outputs by ~2/sqrt(K) of the output rms; the mean stays
-# at the bf16 level. Stage-wise checks (each stage on the GPU's own inputs) use the bf16 gate.
-MX_E2E_MAX_REL, MX_E2E_MEAN_REL = 0.25, 2e-3
+# A whole MXFP8 step against the fully independent oracle: the MXFP8 bound 6e-2 holds for
+# 99.99% of the elements of every output, the mean at the bf16 level. The worst single elements
+# can go further: a bf16 intermediate (H, dGU) one ulp away from the oracle's can flip the E4M3
+# code or the block scale of a large element of these heavy-tailed tensors, which moves the
+# outputs it feeds by up to ~0.15-0.3 of their rms (a CPU test shows a one-ulp nudge of one
+# element of the oracle's own H moving Y by more than 6e-2). The max gate bounds that effect.
+# Stage-wise checks (each stage on the GPU's own inputs) use the bf16 gate.
+MX_E2E_QUANTILE, MX_E2E_QUANTILE_REL, MX_E2E_MEAN_REL, MX_E2E_MAX_REL = 0.9999, 6e-2, 2e-3, 0.5
 
 
-def rel_err(y, r):
+def rel_errs(y, r):
+    """e_i = |y_i - r_i| / max(|r_i|, rms(r)) for every element."""
     y = np.asarray(y, F64)
     r = np.asarray(r, F64)
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     den = np.maximum(np.abs(r), rms if rms > 0 else 1.0)
-    e = np.abs(y - r) / den
+    return (np.abs(y - r) / den).ravel()
+
+
+def rel_err(y, r):
+    e = rel_errs(y, r)
     return float(e.max()) if e.size else 0.0, float(e.mean()) if e.size else 0.0
 
 
 def assert_close(y, r, dtype: str, what: str = ""):
+    if dtype == "mx_e2e":
+        return assert_close_mx_e2e(y, r, what)[:2]
     mx, mean = rel_err(y, r)
-    lim = {"bf16": (BF16_MAX_REL, BF16_MEAN_REL), "mx": (MX_MAX_REL, MX_MEAN_REL),
-           "mx_e2e": (MX_E2E_MAX_REL, MX_E2E_MEAN_REL)}.get(dtype, (F32_MAX_REL, F32_MEAN_REL))
+    lim = {"bf16": (BF16_MAX_REL, BF16_MEAN_REL), "mx": (MX_MAX_REL, MX_MEAN_REL)}.get(
+        dtype, (F32_MAX_REL, F32_MEAN_REL))
     assert mx <= lim[0] and mean <= lim[1], f"{what}: max rel {mx:.3e} mean rel {mean:.3e} (limits {lim})"
     return mx, mean
+
+
+def assert_close_mx_e2e(y, r, what: str = ""):
+    """Whole MXFP8 step vs the independent oracle: the 99.99th percentile of e within 6e-2, the
+    mean within 2e-3, every element within 0.5. Returns (max, mean, quantile)."""
+    e = rel_errs(y, r)
+    if e.size == 0:
+        return 0.0, 0.0, 0.0
+    mx, mean, q = float(e.max()), float(e.mean()), float(np.quantile(e, MX_E2E_QUANTILE))
+    assert q <= MX_E2E_QUANTILE_REL and mean <= MX_E2E_MEAN_REL and mx <= MX_E2E_MAX_REL, (
+        f"{what}: q{MX_E2E_QUANTILE} rel {q:.3e} mean rel {mean:.3e} max rel {mx:.3e} (limits "
+        f"{MX_E2E_QUANTILE_REL}, {MX_E2E_MEAN_REL}, {MX_E2E_MAX_REL})")
+    return mx, mean, q
 
 
 def dev(a, dtype: str = "f32"):

@@ -30,7 +30,7 @@ def test_gemm1_bytes_counts_each_operand_once():
     rows = w.T * w.k + w.T
     fused = bench.gemm1_bytes(w, counts, True)
     mat = bench.gemm1_bytes(w, counts, False)
-    wbytes = (w.E - 10) * 2 * w.f * w.d * 2
+    wbytes = (w.E - 10) * 2 * w.f * w.d * 2 + 2 * w.shared_f * w.d * 2   # + the shared expert's gate/up
     assert fused == wbytes + w.T * w.d * 2 + rows * w.f * 2 + rows * 4
     assert mat - fused == rows * w.d * 2 - w.T * w.d * 2   # x_perm instead of x
 
@@ -82,3 +82,11 @@ def test_held_workloads_refused(monkeypatch, capsys, name):
         bench.main()
     assert e.value.code == 3
     assert "held" in json.loads(capsys.readouterr().out.strip())["error"]
+
+
+def test_spread_and_host_info():
+    sp = bench.spread([1.0, 2.0, 3.0, 4.0, 5.0])
+    assert sp["median"] == 3.0 and sp["p10"] == pytest.approx(1.4) and sp["p90"] == pytest.approx(4.6)
+    info = bench.host_info()
+    assert set(info) == {"cpu_model", "blas", "cpus_available"}
+    assert info["cpus_available"] >= 1
