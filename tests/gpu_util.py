@@ -51,13 +51,21 @@ def assert_close(y, r, dtype: str, what: str = ""):
     return mx, mean
 
 
+MX_E2E_MIN_FOR_STATS = 1024   # fewer elements (e.g. the E bias gradients): every element within 6e-2
+
+
 def assert_close_mx_e2e(y, r, what: str = ""):
     """Whole MXFP8 step vs the independent oracle: the 99.99th percentile of e within 6e-2, the
-    mean within 2e-3, every element within 0.5. Returns (max, mean, quantile)."""
+    mean within 2e-3, every element within 0.5. A tensor of fewer than 1024 elements (a mean
+    and a high quantile of a handful of values say nothing) holds 6e-2 on every element.
+    Returns (max, mean, quantile)."""
     e = rel_errs(y, r)
     if e.size == 0:
         return 0.0, 0.0, 0.0
     mx, mean, q = float(e.max()), float(e.mean()), float(np.quantile(e, MX_E2E_QUANTILE))
+    if e.size < MX_E2E_MIN_FOR_STATS:
+        assert mx <= MX_E2E_QUANTILE_REL, f"{what}: max rel {mx:.3e} (limit {MX_E2E_QUANTILE_REL}, {e.size} elements)"
+        return mx, mean, q
     assert q <= MX_E2E_QUANTILE_REL and mean <= MX_E2E_MEAN_REL and mx <= MX_E2E_MAX_REL, (
         f"{what}: q{MX_E2E_QUANTILE} rel {q:.3e} mean rel {mean:.3e} max rel {mx:.3e} (limits "
         f"{MX_E2E_QUANTILE_REL}, {MX_E2E_MEAN_REL}, {MX_E2E_MAX_REL})")
