@@ -139,6 +139,8 @@ class Launch:
     c_esize: int
     swiglu: bool
     mx: bool = False
+    uniform_rows: int = 0   # the router's K-split mode: group g owns C rows [g R, (g+1) R), no schedule
+    a_group_stride: int = 0
     lda_scale: int = 0
     ldb_scale: int = 0
     b_scale_stride: int = 0
@@ -161,40 +163,57 @@ def check_launch(la: Launch):
     # the host's 4 GiB rule for 32-bit lane offsets
     b_span = (2 if la.swiglu else 1) * la.N * la.ldb * eb
     assert a_bytes + la.K * eb < 1 << 32 and b_span + la.K * eb < 1 << 32
-    ts, order = schedule(la.offsets, G, la.M, NT)
-    total = int(ts[G])
-    bound = (la.M // 16 + G) * NT
-    grid = min(la.num_cus, max(bound, 1))
+    uniform = la.uniform_rows > 0
+    if uniform:
+        rt_u = row_tiles(la.uniform_rows)
+        per_group_u = rt_count(rt_u) * NT
+        total = G * per_group_u
+        tiles = total
+        grid = min(la.num_cus, tiles)
+    else:
+        ts, order = schedule(la.offsets, G, la.M, NT)
+        total = int(ts[G])
+        bound = (la.M // 16 + G) * NT
+        grid = min(la.num_cus, max(bound, 1))
     nxcd = 8 if grid % 8 == 0 else 1
     per_xcd = grid // nxcd
-    written = np.zeros((la.M, la.N), np.int32)
-    lane = np.arange(WAVE)
+    written = np.zeros((la.M, NT), np.int32)     # tiles covering each (row, column tile)
     seen_tiles = 0
     for bid in range(grid):
         slot = (bid % nxcd) * per_xcd + bid // nxcd
         for tile in range(slot, total, grid):
             seen_tiles += 1
-            lo, hi = 0, G - 1
-            while lo < hi:
-                mid = (lo + hi + 1) >> 1
-                if ts[mid] <= tile:
-                    lo = mid
-                else:
-                    hi = mid - 1
-            g = min(max(int(order[lo]), 0), G - 1)
-            L = tile - int(ts[lo])
-            rb, re = group_rows(la.offsets, g, la.M)
-            rt = row_tiles(re - rb)
+            if uniform:
+                g, L = divmod(tile, per_group_u)
+                rb = min(g * la.uniform_rows, la.M)
+                re = min(rb + la.uniform_rows, la.M)
+                rt = rt_u
+            else:
+                lo, hi = 0, G - 1
+                while lo < hi:
+                    mid = (lo + hi + 1) >> 1
+                    if ts[mid] <= tile:
+                        lo = mid
+                    else:
+                        hi = mid - 1
+                g = min(max(int(order[lo]), 0), G - 1)
+                L = tile - int(ts[lo])
+                rb, re = group_rows(la.offsets, g, la.M)
+                rt = row_tiles(re - rb)
             mt, nt = tile_coords(L, rt_count(rt), NT)
             assert 0 <= mt < rt_count(rt) and 0 <= nt < NT, (tile, g, mt, nt)
             r_off, bm = row_tile(rt, mt)
             assert bm in (16, 32, 64, 128)
             _check_tile(la, g, rb, re, r_off, bm, nt, nk, eb, written)
     assert seen_tiles == total
-    # every row of every group: columns [0, N) written exactly once; other rows untouched
+    # every row of every group: each column tile written exactly once; other rows untouched
     live = np.zeros(la.M, bool)
     for g in range(G):
-        b, e = group_rows(la.offsets, g, la.M)
+        if uniform:
+            b = min(g * la.uniform_rows, la.M)
+            e = min(b + la.uniform_rows, la.M)
+        else:
+            b, e = group_rows(la.offsets, g, la.M)
         live[b:e] = True
     assert np.all(written[live] == 1), "an output element of a group was not written exactly once"
     assert np.all(written[~live] == 0), "a row outside every group was written"
@@ -216,9 +235,14 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
     k_extent = (nk - 1) * ROW_BYTES + 16        # bytes a lane reads past its offset over the K loop
     assert st["count"] * st["bytes"] <= PIPE_BYTES
 
+    a_base = g * la.a_group_stride * eb if la.uniform_rows else 0
+
     def a_row_of(row):
         r = np.minimum(r0 + row, row_end - 1)
-        ar = la.a_rows[r].astype(np.int64) if la.a_rows is not None else r.astype(np.int64)
+        if la.a_rows is not None:
+            ar = la.a_rows[r].astype(np.int64)
+        else:
+            ar = (r - row_begin if la.uniform_rows else r).astype(np.int64)
         return np.clip(ar, 0, la.A_rows - 1)
 
     def b_row_of(rho):
@@ -237,7 +261,7 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
             row = instr * ROWS_PER_INSTR + lane // 8
             chunk = (lane % 8) ^ ((row >> 1) & 7)
             voff = a_row_of(row) * la.lda * eb + chunk * 16
-            assert voff.min() >= 0 and voff.max() + k_extent <= la.A_rows * la.lda * eb, ("A", g, r0, bm)
+            assert voff.min() >= 0 and a_base + voff.max() + k_extent <= la.A_rows * la.lda * eb, ("A", g, r0, bm)
             assert voff.max() + k_extent - 16 < 1 << 32
             lds = instr * 1024 + lane * 16
             assert lds.max() + 16 <= bm * ROW_BYTES, ("A LDS", bm)
@@ -274,12 +298,11 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
     cols_per_chunk = 16 // la.c_esize
     cols = n0 + np.arange(0, bn_out, cols_per_chunk)
     cols = cols[cols < la.N]
-    for row in range(rows_valid):
-        r = r0 + row
-        assert r < la.M
-        last = (r * la.ldc + cols.max()) * la.c_esize + 16
-        assert last <= la.M * la.ldc * la.c_esize, ("C", g, r)
-        for c in cols:
-            written[r, c:min(c + cols_per_chunk, la.N)] += 1
+    assert r0 + rows_valid <= la.M
+    last = ((r0 + rows_valid - 1) * la.ldc + cols.max()) * la.c_esize + 16
+    assert last <= la.M * la.ldc * la.c_esize, ("C", g, r0)
+    # the chunks' columns are exactly this column tile's part of [0, N)
+    assert cols[0] == n0 and cols.max() + cols_per_chunk >= min(n0 + bn_out, la.N)
+    written[r0:r0 + rows_valid, nt] += 1
     if la.swiglu and la.aux_ld:
         assert (r0 + rows_valid - 1) * la.aux_ld + la.N + min(n0 + bn_out, la.N) <= la.M * la.aux_ld
