@@ -106,6 +106,9 @@ constexpr int kSuperRKMinNT = 16;
 #define MOE_GEMM_RK_C_NT 1        // weight-gradient (ragged-K) outputs stored non-temporally (never re-read
                                   // here; DeepSeek-V3 dW_gate/up 5.87 -> 5.52 ms, dW_down 2.84 -> 2.71 ms)
 #endif
+#ifndef MOE_GEMM_MX_FRAG_DB
+#define MOE_GEMM_MX_FRAG_DB 1     // MXFP8 operand fragments double-buffered in registers like bf16 ones
+#endif
 #ifndef MOE_GEMM_RK_STREAM
 #define MOE_GEMM_RK_STREAM 1      // ragged-K bf16-output tiles as one stream of K slices (gemm_rk_stream)
 #endif
@@ -341,6 +344,7 @@ struct Mfma<16, false> {
     static constexpr int kChunk2 = 0;                               // one 16-byte chunk
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 16; }
+    static constexpr __device__ __host__ int frag_block(int, int) { return 0; }   // no scales
     static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
 };
@@ -352,6 +356,7 @@ struct Mfma<32, false> {
     static constexpr int kChunk2 = 0;
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 2 + lane / 32; }
+    static constexpr __device__ __host__ int frag_block(int, int) { return 0; }   // no scales
     static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
 };
@@ -369,7 +374,7 @@ struct Mfma<16, true> {
     static constexpr int NACC = 4;
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
     static constexpr int kChunk2 = 4;
-    static __device__ __forceinline__ int frag_block(int lane, int ks) { return ks * 4 + lane / 16; }
+    static constexpr __device__ __host__ int frag_block(int lane, int ks) { return ks * 4 + lane / 16; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 8 + lane / 16; }
     static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
@@ -381,7 +386,7 @@ struct Mfma<32, true> {
     static constexpr int NACC = 16;
     static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
     static constexpr int kChunk2 = 2;
-    static __device__ __forceinline__ int frag_block(int lane, int ks) { return ks * 2 + lane / 32; }
+    static constexpr __device__ __host__ int frag_block(int lane, int ks) { return ks * 2 + lane / 32; }
     static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 32; }
     static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
@@ -408,7 +413,8 @@ __device__ __forceinline__ typename Frag<MS, MX>::t load_frag(const char* st, in
     }
 }
 
-template <int MS, bool MX>
+// SEL: MXFP8 only, which byte of the scale registers sa / sb the instruction applies (op_sel)
+template <int MS, bool MX, int SEL = 0>
 __device__ __forceinline__ typename Mfma<MS, MX>::acc_t mfma(typename Frag<MS, MX>::t a, typename Frag<MS, MX>::t b,
                                                              typename Mfma<MS, MX>::acc_t c, int sa, int sb) {
     if constexpr (!MX) {
@@ -417,9 +423,9 @@ __device__ __forceinline__ typename Mfma<MS, MX>::acc_t mfma(typename Frag<MS, M
         if constexpr (MS == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
         else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     } else {
-        // format 0 = E4M3 for both operands; scale bytes in bits [7:0] (opsel 0)
-        if constexpr (MS == 32) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
-        else return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+        // format 0 = E4M3 for both operands; the scale byte SEL of each scale register
+        if constexpr (MS == 32) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
+        else return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
     }
 }
 
@@ -472,7 +478,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     if constexpr (BM == 256) {
         if (p.c_f32) return;   // never scheduled: 256-row tiles are only chosen for 2-byte outputs
     }
-    const int tid = threadIdx.x, lane = tid % kWave;
+    // MXFP8: the lane index is made opaque per tile so its per-lane offsets are recomputed in
+    // each tile (a few ALU operations) rather than hoisted out of the persistent tile loop and
+    // kept live across it, which costs registers the MXFP8 tiles do not have (it spilled)
+    int tid = threadIdx.x;
+    if constexpr (MX) asm volatile("" : "+v"(tid));
+    const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     const bool producer = kPWaves > 0 && wave >= kWaves;
@@ -648,70 +659,79 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         b_off[ks][1] = BM * kRowBytes + rb * kRowBytes + (((chunk + MF::kChunk2) ^ swz(rb)) << 4);
     }
     constexpr int FSTEP = MS * kRowBytes;   // bytes between consecutive fragments' rows
-    // Fragments are double-buffered in registers: the LDS reads of k-step ks+1 are issued
-    // before the MFMAs of k-step ks, so LDS latency overlaps matrix work.
     // compute(kt, kn): multiply stage kt; when kn >= 0 also issue this wave's loads of stage kn,
     // a share after the first MFMA of every k-step, so the DMA instructions queue while the
     // matrix core works instead of all waves issuing them back to back after the barrier.
     auto compute = [&](int kt, int kn) {
         const char* st = lds + (kt % NST) * SB;
-        int sa_w[MI], sb_w[NI];   // MXFP8: this lane's rows' 4 scale bytes of the stage
+        // MXFP8: this lane's rows' 4 scale bytes of the stage, shifted so that byte SEL of the
+        // register is the block of k-step ks for this lane (the instruction's op_sel picks it)
+        int sa_w[MI], sb_w[NI];
         if constexpr (MX) {
+            const uint32_t sh0 = 8 * MF::frag_block(lane, 0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                sa_w[i] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4);
+                sa_w[i] = (int)(*reinterpret_cast<const uint32_t*>(
+                                    st + Stage<BM>::kScaleA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4) >> sh0);
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                sb_w[j] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
+                sb_w[j] = (int)(*reinterpret_cast<const uint32_t*>(
+                                    st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4) >> sh0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) sa_w[i] = 0;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) sb_w[j] = 0;
         }
-        FragT af[2][MI], bfr[2][NI];
+        // Fragments are double-buffered in registers (the LDS reads of k-step ks+1 go out before
+        // the MFMAs of k-step ks); MOE_GEMM_MX_FRAG_DB=0 loads the MXFP8 fragments (twice the
+        // size of bf16 ones) one k-step at a time instead
+        constexpr bool DB = !MX || MOE_GEMM_MX_FRAG_DB;
+        FragT af[DB ? 2 : 1][MI], bfr[DB ? 2 : 1][NI];
 #pragma unroll
         for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
 #pragma unroll
         for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
+        static_for<0>(
+            [&](auto ks_tag) {
+                constexpr int ks = decltype(ks_tag)::value;
+                constexpr int cur = DB ? (ks & 1) : 0, nxt = DB ? (cur ^ 1) : 0;
+                constexpr int SEL = MX ? MF::frag_block(0, ks) - MF::frag_block(0, 0) : 0;
+                if constexpr (!DB && ks > 0) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int cur = ks & 1, nxt = cur ^ 1;
-            if (ks + 1 < NKS) {
+                    for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[ks][0], a_off[ks][1]);
+#pragma unroll
+                    for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[ks][0], b_off[ks][1]);
+                }
+                if constexpr (DB && ks + 1 < NKS) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        af[nxt][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        bfr[nxt][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
+                acc[0][0] = mfma<MS, MX, SEL>(af[cur][0], bfr[cur][0], acc[0][0], sa_w[0], sb_w[0]);
+                if (kn >= 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    static_for<0>(
+                        [&](auto l) {
+                            // k-step ks issues loads [ks*NLOADS/NKS, (ks+1)*NLOADS/NKS)
+                            constexpr int lo = decltype(l)::value;
+                            if constexpr (lo * NKS >= ks * NLOADS && lo * NKS < (ks + 1) * NLOADS) issue_one(kn, l);
+                        },
+                        std::make_integer_sequence<int, NLOADS>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                }
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
-                    af[nxt][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    bfr[nxt][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
-            int sa[MI], sb[NI];
-            if constexpr (MX) {
-                const int sh = 8 * MF::frag_block(lane, ks);
-#pragma unroll
-                for (int i = 0; i < MI; ++i) sa[i] = (sa_w[i] >> sh) & 0xFF;
-#pragma unroll
-                for (int j = 0; j < NI; ++j) sb[j] = (sb_w[j] >> sh) & 0xFF;
-            } else {
-#pragma unroll
-                for (int i = 0; i < MI; ++i) sa[i] = 0;
-#pragma unroll
-                for (int j = 0; j < NI; ++j) sb[j] = 0;
-            }
-            acc[0][0] = mfma<MS, MX>(af[cur][0], bfr[cur][0], acc[0][0], sa[0], sb[0]);
-            if (kn >= 0) {
-                __builtin_amdgcn_sched_barrier(0);
-                static_for<0>(
-                    [&](auto l) {
-                        // k-step ks issues loads [ks*NLOADS/NKS, (ks+1)*NLOADS/NKS)
-                        constexpr int lo = decltype(l)::value;
-                        if (lo * NKS >= ks * NLOADS && lo * NKS < (ks + 1) * NLOADS) issue_one(kn, l);
-                    },
-                    std::make_integer_sequence<int, NLOADS>{});
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    if (i != 0 || j != 0) acc[i][j] = mfma<MS, MX>(af[cur][i], bfr[cur][j], acc[i][j], sa[i], sb[j]);
-        }
+                    for (int j = 0; j < NI; ++j)
+                        if (i != 0 || j != 0)
+                            acc[i][j] = mfma<MS, MX, SEL>(af[cur][i], bfr[cur][j], acc[i][j], sa_w[i], sb_w[j]);
+            },
+            std::make_integer_sequence<int, NKS>{});
     };
 
     // Ring of NST LDS stages: stages kt+1 .. kt+NST-2 may still be streaming in when stage kt
