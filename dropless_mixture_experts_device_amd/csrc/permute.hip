@@ -22,6 +22,9 @@ constexpr int kSub = 64;                 // tokens per mask word
 constexpr int kSubPerTile = 16;
 constexpr int kTile = kSub * kSubPerTile; // 1024 tokens per histogram tile
 constexpr int kPermThreads = 256;
+#ifndef MOE_PERMUTE_UNROLL
+#define MOE_PERMUTE_UNROLL 4
+#endif
 
 struct PermWs {
     uint64_t* mask;      // [nsub][E]
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_place_kernel(
     const int nrows = k + (shared_group ? 1 : 0);
     const int nchunk = d * ESIZE / 16;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * d * ESIZE);
-    constexpr int U = 4;
+    constexpr int U = MOE_PERMUTE_UNROLL;   // 16-byte chunks per lane in flight before the stores
     for (int c0 = lane; c0 < nchunk; c0 += kWave * U) {
         u32x4 v[U];
 #pragma unroll

@@ -225,7 +225,36 @@ inline bool route_uses_split(int64_t T, int64_t d, int E) {
     return T >= 256 && E % 8 == 0 && d % (64 * kRouteKS) == 0;
 }
 
-constexpr int kTopkBT = 8;   // tokens per workgroup of the split-K top-k pass (2 per wave)
+// The split-K pass's selection: 16 lanes per token, 4 tokens per wave, 16 tokens per
+// workgroup. Lane r of a token's group owns the experts 64q + 4r + i (i < 4, q < NQ): each of
+// its loads is one 16-byte chunk of a partial-logit row, so the 16 lanes read 256 contiguous
+// bytes. The KS partials of a chunk are loaded before any is summed, then summed in the
+// order s = 0..KS-1 and the bias added, exactly as the keys are defined. Each selection round
+// takes the 16-lane maximum of the order-preserving codes, then the 16-lane minimum of the
+// expert ids holding it (equal keys -> lower expert id), and the owner removes it; lane j of
+// the group keeps selection j. Row-wide (16-lane) reductions use DPP moves inside the row.
+constexpr int kTopkTok = 16;   // tokens per workgroup of the split-K selection pass
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_min_step(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    return o < v ? o : v;
+}
+
+// every lane gets the maximum (minimum) of its 16-lane row: quad swaps, then rotations by 4, 8
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    v = dpp_max_step<0xB1, 0xF>(v);
+    v = dpp_max_step<0x4E, 0xF>(v);
+    v = dpp_max_step<0x124, 0xF>(v);
+    return dpp_max_step<0x128, 0xF>(v);
+}
+
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
+    v = dpp_min_step<0xB1>(v);
+    v = dpp_min_step<0x4E>(v);
+    v = dpp_min_step<0x124>(v);
+    return dpp_min_step<0x128>(v);
+}
 
 template <int NQ>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ partial,
@@ -233,47 +262,71 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
                                                                    int k, int score, int32_t* __restrict__ topk_idx,
                                                                    float* __restrict__ topk_w,
                                                                    float* __restrict__ keys_out) {
-    constexpr int PITCH = NQ * kWave + 4;
-    __shared__ float keys[kTopkBT * PITCH];
-    const int t0 = blockIdx.x * kTopkBT;
-    // 4 consecutive experts per lane-load (E % 8 == 0 here); every partial of a chunk is
-    // loaded before any is summed so the loads overlap, then summed in the order q = 0..KS-1
-    const int e4 = E / 4;
-    constexpr int PER = cdiv(kTopkBT * NQ * kWave / 4, kRouteThreads);   // chunks per thread (upper bound)
-    f32x4 v[PER][kRouteKS];
+    constexpr int P = 4 * NQ;   // candidates per lane
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int r = lane % 16, grp = lane / 16;
+    const int t = blockIdx.x * kTopkTok + wave * 4 + grp;
+    const int tc = min(t, T - 1);   // rows past T load the last token's row and write nothing
+    f32x4 v[NQ][kRouteKS];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int c = threadIdx.x + u * kRouteThreads;
-        const int tl = c / e4, e = (c % e4) * 4;
-        const int t = min(t0 + tl, T - 1);
-        if (tl < kTopkBT) {
+    for (int q = 0; q < NQ; ++q) {
+        const int e0 = 64 * q + 4 * r;
+        if (e0 < E) {
 #pragma unroll
-            for (int q = 0; q < kRouteKS; ++q)
-                v[u][q] = *reinterpret_cast<const f32x4*>(partial + ((int64_t)q * T + t) * E + e);
+            for (int s = 0; s < kRouteKS; ++s)
+                v[q][s] = *reinterpret_cast<const f32x4*>(partial + ((int64_t)s * T + tc) * E + e0);
         }
     }
+    uint32_t code[P];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int c = threadIdx.x + u * kRouteThreads;
-        const int tl = c / e4, e = (c % e4) * 4;
-        if (tl < kTopkBT) {
+    for (int q = 0; q < NQ; ++q) {
+        const int e0 = 64 * q + 4 * r;
+        f32x4 key = {0.f, 0.f, 0.f, 0.f};
+        if (e0 < E) {   // E % 4 == 0 on this path, so a chunk is wholly in or out
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s = 0.f;
+                float sum = 0.f;
 #pragma unroll
-                for (int q = 0; q < kRouteKS; ++q) s += v[u][q][i];
-                keys[tl * PITCH + e + i] = s + (bias != nullptr ? bias[e + i] : 0.f);
+                for (int s = 0; s < kRouteKS; ++s) sum += v[q][s][i];
+                key[i] = sum + (bias != nullptr ? bias[e0 + i] : 0.f);
             }
+            if (keys_out != nullptr && t < T) *reinterpret_cast<f32x4*>(keys_out + (int64_t)t * E + e0) = key;
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) code[4 * q + i] = e0 < E ? ordered_bits(key[i]) : 0u;
     }
-    __syncthreads();
-    if (keys_out != nullptr) {
-        for (int idx = threadIdx.x; idx < kTopkBT * E; idx += kRouteThreads) {
-            const int tl = idx / E, e = idx % E;
-            if (t0 + tl < T) keys_out[(int64_t)(t0 + tl) * E + e] = keys[tl * PITCH + e];
+    uint32_t my_code = 0u, code0 = 0u;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        uint32_t m = code[0];
+#pragma unroll
+        for (int c = 1; c < P; ++c) m = code[c] > m ? code[c] : m;
+        m = row_max_u32(m);
+        uint32_t el = 0xFFFFFFFFu;   // this lane's lowest expert id holding the maximum
+#pragma unroll
+        for (int c = P - 1; c >= 0; --c)
+            if (m != 0u && code[c] == m) el = (uint32_t)(64 * (c / 4) + 4 * r + c % 4);
+        const uint32_t ew = row_min_u32(el);
+        const int win = min(max((int)ew, 0), E - 1);   // in range even for non-finite keys (unsupported)
+#pragma unroll
+        for (int c = 0; c < P; ++c)
+            if (64 * (c / 4) + 4 * r + c % 4 == win) code[c] = 0u;
+        if (r == j) {
+            my_code = m;
+            my_e = win;
         }
+        if (j == 0) code0 = m;
     }
-    topk_tile<NQ, kTopkBT>(keys, PITCH, t0, T, E, k, score, topk_idx, topk_w);
+    // weights: lane j < k of the group forms its term; the normaliser adds the terms in the order j = 0 .. k-1
+    const float key0 = key_of_ordered(code0), kj = key_of_ordered(my_code);
+    float z = 0.f;
+    if (r < k) z = (score == MOE_SOFTMAX) ? expf(kj - key0) : 1.0f / (1.0f + expf(-kj));
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __shfl(z, grp * 16 + j, kWave);
+    if (t < T && r < k) {
+        topk_idx[(int64_t)t * k + r] = my_e;
+        topk_w[(int64_t)t * k + r] = z / sum;
+    }
 }
 
 template <int NTW>
@@ -314,7 +367,7 @@ extern "C" moe_status_t moe_route(const void* x, const void* w_router, int32_t d
         const moe_status_t st = moe_gemm_ksplit_f32(x, w_router, T, d, E, moe::kRouteKS, partial, s);
         if (st != MOE_OK) return st;
         const int nq = moe::cdiv(E, 64);
-        const dim3 tgrid((unsigned)moe::cdiv<int64_t>(T, moe::kTopkBT));
+        const dim3 tgrid((unsigned)moe::cdiv<int64_t>(T, moe::kTopkTok));
         if (nq <= 1)
             hipLaunchKernelGGL((moe::route_topk_kernel<1>), tgrid, dim3(moe::kRouteThreads), 0, s, partial, bias, Ti, E,
                                k, score, topk_idx, topk_w, keys_out);
