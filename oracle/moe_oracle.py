@@ -493,6 +493,91 @@ def mx_q_rows(a):
 
 
 # --------------------------------------------------------------------------------------
+# MXFP4  ([Blog] "JAX plus Transformer Engine MoE training performance": a 4-bit block-scaled
+#   format is the planned next precision; [Reading] contribution 3: FP8/FP4 recipes.
+#   [OCP-MX] defines MXFP4 as E2M1 elements sharing one E8M0 scale per block of 32.)
+# --------------------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+
+
+def e2m1_round(v) -> np.ndarray:
+    """Round float64 values to the nearest OCP E2M1 value (ties to even), saturating.
+
+    E2M1 ([OCP-MX] FP4 E2M1): exponent bias 1, 1 mantissa bit, normals 1, 1.5, 2, 3, 4, 6
+    (exponent 0..2), subnormal 0.5, largest finite 6, no infinities or NaN. The spacing is
+    2**(floor(log2|v|) - 1) for |v| >= 1 and 0.5 below; magnitudes above 6 saturate to 6
+    (READING: the MX conversion clamps to the largest normal, as for E4M3).
+    """
+    v = np.asarray(v, F64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                      # a = m 2**e, m in [0.5, 1): floor(log2 a) = e - 1
+    q = np.maximum(e - 2, -1)
+    r = np.ldexp(np.rint(np.ldexp(a, -q)), q)
+    r = np.minimum(r, E2M1_MAX)
+    return np.copysign(r, v)
+
+
+def e2m1_encode(r) -> np.ndarray:
+    """4-bit code of values already on the E2M1 grid: sign in bit 3, exponent field in bits
+    2..1, mantissa in bit 0 (the sign bit kept, also for zero)."""
+    r = np.asarray(r, F64)
+    a = np.abs(r)
+    sign = np.signbit(r).astype(np.int64) << 3
+    _, e = np.frexp(a)
+    normal = a >= 1.0
+    ef = np.where(normal, e, 0)             # a in [2**(e-1), 2**e): exponent field (e - 1) + 1
+    mant = np.where(normal, np.ldexp(a, 1 - e) * 2.0 - 2.0, a * 2.0)
+    return (sign | (ef.astype(np.int64) << 1) | np.rint(mant).astype(np.int64)).astype(np.uint8)
+
+
+def e2m1_decode(code) -> np.ndarray:
+    c = np.asarray(code, np.int64)
+    s = np.where(c & 0x8, -1.0, 1.0)
+    ef = (c >> 1) & 0x3
+    m = c & 1
+    mag = np.where(ef == 0, 0.5 * m, np.ldexp(1.0 + m / 2.0, ef - 1))
+    return s * mag
+
+
+def mx4_scale_byte(amax) -> np.ndarray:
+    """E8M0 shared-scale byte of an MXFP4 block: [OCP-MX] section 6.3 with emax_elem = 2 for
+    E2M1 (largest normal 6 = 1.5 * 2**2); an all-zero block gets byte 0."""
+    amax = np.asarray(amax, F64)
+    _, e = np.frexp(amax)
+    b = np.clip(e - 1 - 2 + 127, 0, 254)
+    return np.where(amax > 0, b, 0).astype(np.uint8)
+
+
+def mx4_quantize_blocks(blocks):
+    """Quantise blocks [..., n<=32] to MXFP4 (padding elements, if any, must be zero).
+
+    Returns (4-bit codes uint8 [..., n], scale bytes uint8 [...], dequantised float64 [..., n]).
+    """
+    blocks = np.asarray(blocks, F64)
+    amax = np.max(np.abs(blocks), axis=-1)
+    sb = mx4_scale_byte(amax)
+    X = np.ldexp(1.0, sb.astype(np.int64) - 127)
+    r = e2m1_round(blocks / X[..., None])
+    return e2m1_encode(r), sb, r * X[..., None]
+
+
+def mx4_quantize_rowwise(a):
+    """MXFP4 blocks of 32 consecutive elements along each row (cols % 32 == 0): codes [rows,
+    cols] (one 4-bit code per element), scales [rows, cols/32], dequantised [rows, cols]."""
+    a = np.asarray(a, F64)
+    R, C = a.shape
+    assert C % MX_BLOCK == 0
+    codes, sb, dq = mx4_quantize_blocks(a.reshape(R, C // MX_BLOCK, MX_BLOCK))
+    return codes.reshape(R, C), sb, dq.reshape(R, C)
+
+
+def mx4_q_rows(a):
+    """Dequantised value of a after row-wise MXFP4 quantisation."""
+    return mx4_quantize_rowwise(a)[2]
+
+
+# --------------------------------------------------------------------------------------
 # backward (the expert/permute/combine part; the router's own backward is not included)
 # --------------------------------------------------------------------------------------
 

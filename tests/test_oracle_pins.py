@@ -563,3 +563,67 @@ def test_router_backward_invariants(score):
         # a common shift of the selected keys leaves a softmax unchanged
         g = gen.standard_normal((T, k))
         assert np.abs(O.topk_weights_backward(keys, idx, g, score).sum(axis=1)).max() < 1e-14
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def _golden_mx4():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "mx_e2m1_cases.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        amax, sb, el, scaled, code = line.split()
+        rows.append((eval(amax), int(sb), eval(el), float(scaled), int(code, 16)))
+    return rows
+
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def test_mx4_golden_cases():
+    rows = _golden_mx4()
+    assert len(rows) >= 20
+    for amax, sb, el, scaled, code in rows:
+        block = np.zeros(32)
+        block[0] = amax
+        block[7] = el
+        codes, sbs, dq = O.mx4_quantize_blocks(block[None])
+        assert int(sbs[0]) == sb, (amax, sbs)
+        X = 2.0 ** (sb - 127)
+        assert el / X == pytest.approx(scaled, rel=1e-15)
+        assert int(codes[0, 7]) == code, (amax, el, hex(int(codes[0, 7])))
+        assert O.e2m1_decode(codes[0, 7]) * X == dq[0, 7]
+
+
+def test_e2m1_every_code_round_trips_and_decodes_to_the_table():
+    codes = np.arange(16, dtype=np.uint8)
+    vals = O.e2m1_decode(codes)
+    np.testing.assert_array_equal(np.abs(vals[:8]), E2M1_GRID)
+    np.testing.assert_array_equal(vals[8:], -E2M1_GRID)
+    np.testing.assert_array_equal(O.e2m1_encode(O.e2m1_round(vals)), codes)
+
+
+def test_e2m1_round_is_nearest_with_ties_to_even_mantissa():
+    """Brute force over the 8 magnitudes: the nearest one wins; at an exact midpoint the one
+    with mantissa bit 0 (codes 0, 2, 4, 6); above 6 saturates."""
+    g = np.random.Generator(np.random.PCG64(41))
+    mids = (E2M1_GRID[:-1] + E2M1_GRID[1:]) / 2
+    v = np.concatenate([g.uniform(-8, 8, 20000), mids, -mids, [6.0, 6.5, 100.0, 0.0]])
+    got = O.e2m1_round(v)
+    a = np.abs(v)
+    dist = np.abs(a[:, None] - E2M1_GRID[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = np.where(dist == best, np.arange(8)[None, :], 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=1)
+    pick = np.where(even < 99, even, cand.min(axis=1))
+    np.testing.assert_array_equal(np.abs(got), E2M1_GRID[pick])
+    np.testing.assert_array_equal(np.signbit(got[a > 0.25]), np.signbit(v[a > 0.25]))
+
+
+def test_mx4_values_on_grid_are_fixed_points():
+    g = np.random.Generator(np.random.PCG64(42))
+    vals = E2M1_GRID[g.integers(0, 8, (5, 64))] * np.where(g.random((5, 64)) < 0.5, -1, 1)
+    vals[:, ::32] = 6.0                                  # every block holds its maximum
+    a = vals * 2.0 ** -7
+    np.testing.assert_array_equal(O.mx4_q_rows(a), a)
