@@ -17,7 +17,7 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
-MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_E2M1 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_BWD_QUANT = 0, 1, 2, 3, 4, 5
@@ -53,6 +53,8 @@ _lib.moe_combine.restype = _i32
 _lib.moe_group_quant_mxfp8.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _i32, _vp, _i64, _vp, _i64,
                                        _vp, _vp, _sz, _vp]
 _lib.moe_group_quant_mxfp8.restype = _i32
+_lib.moe_group_quant_mxfp4.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+_lib.moe_group_quant_mxfp4.restype = _i32
 _lib.moe_group_quant_mxfp8_dual.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _vp, _i64,
                                             _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
 _lib.moe_group_quant_mxfp8_dual.restype = _i32
@@ -72,7 +74,7 @@ _lib.moe_combine_backward_quant_mxfp8_dual.argtypes = [_vp, _i32, _vp, _vp, _vp,
 _lib.moe_combine_backward_quant_mxfp8_dual.restype = _i32
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine",
-            "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_combine_backward", "moe_swiglu_backward",
+            "moe_group_quant_mxfp8", "moe_group_quant_mxfp8_dual", "moe_group_quant_mxfp4", "moe_combine_backward", "moe_swiglu_backward",
             "moe_route_backward", "moe_swiglu_backward_quant_mxfp8_dual", "moe_combine_backward_quant_mxfp8_dual")
 
 
@@ -145,14 +147,15 @@ def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_to
 
 
 def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None, aux=None, workspace=None,
-                     stream=None, a_scale=None, b_scale=None, ragged_k: bool = False):
+                     stream=None, a_scale=None, b_scale=None, ragged_k: bool = False, fp4: bool = False):
     """One launch over all groups.
 
     Ragged rows (default): C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate)
     * up). A [A_rows, K]; B [G, N or 2N, K] (any strides with unit inner stride, e.g. a
     permuted view of transposed weights); C [M, N]; offsets int32 [G+1] (device); a_rows
     int32 [M]. MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale
-    [G, N_B, K/32] uint8 E8M0 bytes.
+    [G, N_B, K/32] uint8 E8M0 bytes. fp4 (MXFP4): A [A_rows, K/2] and B [G, N_B, K/2] uint8
+    hold E2M1 codes two per byte (K counts elements, strides are passed in elements).
     ragged_k: C [G, M, N], C[g] = A_g @ B_g^T over group g's offsets[g] .. offsets[g+1]-1
     blocks of 32 K elements, A, B, a_scale, b_scale being the column-wise quantiser's
     group-major output buffers (capacities [M, K], [N, K], [M, K/32], [N, K/32]).
@@ -173,12 +176,17 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
     else:
         G = B.shape[0]
         M, N = C.shape
-        K = A.shape[1]
+        per = 2 if fp4 else 1                # elements per stored byte
+        if fp4 and (A.dtype != torch.uint8 or B.dtype != torch.uint8):
+            raise TypeError("MXFP4 operands are uint8 tensors of packed E2M1 codes")
+        K = A.shape[1] * per
+        ab = MOE_E2M1 if fp4 else _dtype(A)
         args = MoeGemmArgs(
             G=G, offsets=offsets.data_ptr(), M=M, N=N, K=K,
-            A=A.data_ptr(), a_dtype=_dtype(A), lda=A.stride(0), A_rows=A.shape[0],
+            A=A.data_ptr(), a_dtype=ab, lda=A.stride(0) * per, A_rows=A.shape[0],
             a_rows=None if a_rows is None else a_rows.data_ptr(),
-            B=B.data_ptr(), b_dtype=_dtype(B), ldb=B.stride(1), b_group_stride=B.stride(0),
+            B=B.data_ptr(), b_dtype=MOE_E2M1 if fp4 else _dtype(B), ldb=B.stride(1) * per,
+            b_group_stride=B.stride(0) * per,
             C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
             epilogue=epilogue, aux=None if aux is None else aux.data_ptr(),
             ld_aux=0 if aux is None else aux.stride(0),
@@ -288,6 +296,19 @@ def moe_group_quant_mxfp8(x, q, scales, axis: int = 0, group_offsets=None, block
     _check("moe_group_quant_mxfp8", _lib.moe_group_quant_mxfp8(
         _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(row_index), in_rows, _ptr(group_offsets), G, axis,
         _ptr(q), q.stride(0), _ptr(scales), scales.stride(0), _ptr(block_start), ws, wsb, _stream(stream)))
+
+
+def moe_group_quant_mxfp4(x, q, scales, stream=None, row_index=None, rows=None):
+    """Row-wise MXFP4 quantisation of x (bf16 or fp32, [in_rows, cols]) into packed E2M1
+    codes q (uint8 [rows, >= cols/2], even element in the low nibble) and E8M0 scale bytes
+    (uint8 [rows, >= cols/32]). Logical row r reads x[row_index[r]] when row_index is given
+    (then `rows` defaults to row_index's length), else x[r]."""
+    in_rows, cols = x.shape
+    if rows is None:
+        rows = in_rows if row_index is None else row_index.numel()
+    _check("moe_group_quant_mxfp4", _lib.moe_group_quant_mxfp4(
+        _ptr(x), _dtype(x), rows, cols, x.stride(0), _ptr(row_index), in_rows, _ptr(q), q.stride(0),
+        _ptr(scales), scales.stride(0), _stream(stream)))
 
 
 def moe_group_quant_mxfp8_dual(x, q_row, s_row, q_col, s_col, group_offsets, block_start=None, workspace=None,

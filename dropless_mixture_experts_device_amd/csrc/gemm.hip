@@ -70,19 +70,27 @@ constexpr int kChunks = kRowBytes / 16;
                                   // slower on the DeepSeek-V3 and Mixtral shapes: longer tiles, worse tail)
 #endif
 
+// Operand formats of the MFMA path: bf16, E4M3 (MXFP8) and E2M1 (MXFP4, two per byte, the
+// even element in the low nibble). A stage holds 128 bytes of every A and B row: 64 bf16,
+// 128 E4M3 or 256 E2M1 values of K.
+constexpr int kBF16 = 0, kE4M3 = 1, kE2M1 = 2;
+
 // One LDS pipeline stage of a BM-row tile: BM A rows then kBN B rows of kRowBytes each, then
-// (MXFP8) one scale dword per A row and per B row. A scale rows are loaded 64 per wave
-// instruction, so their slot is rounded up to a multiple of 64 rows (a 16-row tile's scale
-// load still writes 64 dwords and must not reach the B scales). Tiles up to 128 rows keep a
-// 3-stage ring (a 4th stage for the 16/32-row tiles measured no faster on the expert
-// shapes); 256-row tiles (64 KiB of operands per stage) fit two.
-template <int BM>
+// (block-scaled formats) the E8M0 scale bytes of the stage's K slice per A row and per B row,
+// as dwords: one per row for E4M3 (4 blocks of 32), two for E2M1 (8 blocks), dword h of every
+// row together. A scale rows are loaded 64 per wave instruction, so their slot is rounded up
+// to a multiple of 64 rows (a 16-row tile's scale load still writes 64 dwords and must not
+// reach the B scales). Tiles up to 128 rows keep a 3-stage ring (a 4th stage for the 16/32-
+// row tiles measured no faster on the expert shapes); 256-row tiles (64 KiB of operands per
+// stage) fit two.
+template <int BM, int FMT = kE4M3>
 struct Stage {
+    static constexpr int kScaleDw = FMT == kE2M1 ? 2 : 1;   // scale dwords per row and stage
     static constexpr int kScaleRowsA = (BM + 63) / 64 * 64;
     static constexpr int kData = (BM + kBN) * kRowBytes;
     static constexpr int kScaleA = kData;
-    static constexpr int kScaleB = kData + kScaleRowsA * 4;
-    static constexpr int kBytes = kData + (kScaleRowsA + kBN) * 4;
+    static constexpr int kScaleB = kData + kScaleRowsA * 4 * kScaleDw;
+    static constexpr int kBytes = kData + (kScaleRowsA + kBN) * 4 * kScaleDw;
     static constexpr int kCount = BM == 256 ? 2 : 3;
 };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -90,6 +98,15 @@ constexpr int kPipeBytes = cmax(3 * Stage<128>::kBytes, 2 * Stage<256>::kBytes);
 constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+// E2M1 stages carry twice the scale bytes: the ring grows by 9 KiB, which leaves room for the
+// schedule's tile prefix of at most 1791 groups in the same 160 KiB
+template <int FMT>
+constexpr int pipe_bytes() { return FMT == kE2M1 ? 3 * Stage<128, kE2M1>::kBytes : kPipeBytes; }
+template <int FMT>
+constexpr int max_groups() { return FMT == kE2M1 ? (160 * 1024 - pipe_bytes<kE2M1>()) / 4 - 1 : kMaxGroups; }
+template <int FMT>
+constexpr int lds_bytes() { return pipe_bytes<FMT>() + (max_groups<FMT>() + 1) * 4; }
+static_assert(lds_bytes<kE2M1>() <= 160 * 1024 && max_groups<kE2M1>() == 1791, "E2M1 LDS budget");
 constexpr int kSuper = 4;         // column tiles per supertile
 // Ragged-K (weight-gradient) tiles write a 128 x 256 bf16 block each over a short K range, so
 // output stores weigh more than operand reuse: with 16 or more column tiles they take wider
@@ -333,11 +350,11 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, Is.
     (f(std::integral_constant<int, L0 + Is>{}), ...);
 }
 
-template <int MS, bool MX>
+template <int MS, int FMT>
 struct Mfma;
 
 template <>
-struct Mfma<16, false> {
+struct Mfma<16, kBF16> {
     using acc_t = f32x4;
     static constexpr int KS = 2;                                    // k-steps per stage
     static constexpr int NACC = 4;
@@ -349,7 +366,7 @@ struct Mfma<16, false> {
     static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
 };
 template <>
-struct Mfma<32, false> {
+struct Mfma<32, kBF16> {
     using acc_t = f32x16;
     static constexpr int KS = 4;
     static constexpr int NACC = 16;
@@ -368,7 +385,7 @@ struct Mfma<32, false> {
 // [64+16g, ...), scale lane 16b+r owns block b. frag_chunk is the first chunk, the second
 // follows kChunk2 chunks later.
 template <>
-struct Mfma<16, true> {
+struct Mfma<16, kE4M3> {
     using acc_t = f32x4;
     static constexpr int KS = 1;                                    // 16x16x128
     static constexpr int NACC = 4;
@@ -380,7 +397,7 @@ struct Mfma<16, true> {
     static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
 };
 template <>
-struct Mfma<32, true> {
+struct Mfma<32, kE4M3> {
     using acc_t = f32x16;
     static constexpr int KS = 2;                                    // 32x32x64
     static constexpr int NACC = 16;
@@ -391,49 +408,93 @@ struct Mfma<32, true> {
     static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
     static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
 };
+// fp4 (E2M1, measured on gfx950 with one-hot E2M1 operands against an E4M3 identity): a
+// lane's 16 bytes are 32 consecutive K values of its row, the even one in the low nibble,
+// i.e. one whole MX block, whose scale the lane passes. 32x32x64: lanes 32h+r hold K
+// [32h, 32h+32); 16x16x128: lanes 16g+r hold K [32g, 32g+32). One 16-byte chunk per
+// fragment, as for bf16.
+template <>
+struct Mfma<16, kE2M1> {
+    using acc_t = f32x4;
+    static constexpr int KS = 2;                                    // 16x16x128, 256 K per stage
+    static constexpr int NACC = 4;
+    static constexpr int kChunk2 = 0;
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 16; }
+    static constexpr __device__ __host__ int frag_block(int lane, int ks) { return ks * 4 + lane / 16; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 4 + lane / 16; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (lane / 16) * 4 + r; }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 16; }
+};
+template <>
+struct Mfma<32, kE2M1> {
+    using acc_t = f32x16;
+    static constexpr int KS = 4;                                    // 32x32x64, 256 K per stage
+    static constexpr int NACC = 16;
+    static constexpr int kChunk2 = 0;
+    static __device__ __forceinline__ int frag_row(int lane) { return lane % 32; }
+    static constexpr __device__ __host__ int frag_block(int lane, int ks) { return ks * 2 + lane / 32; }
+    static __device__ __forceinline__ int frag_chunk(int lane, int ks) { return ks * 2 + lane / 32; }
+    static __device__ __forceinline__ int out_row(int lane, int r) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
+    static __device__ __forceinline__ int out_col(int lane) { return lane % 32; }
+};
 
-template <int MS, bool MX>
+template <int MS, int FMT>
 struct Frag {
     using t = bf16x8;
 };
 template <int MS>
-struct Frag<MS, true> {
+struct Frag<MS, kE4M3> {
     using t = i32x8;
 };
+template <int MS>
+struct Frag<MS, kE2M1> {
+    using t = u32x4;
+};
 
-template <int MS, bool MX>
-__device__ __forceinline__ typename Frag<MS, MX>::t load_frag(const char* st, int off0, int off1) {
-    if constexpr (MX) {
+template <int MS, int FMT>
+__device__ __forceinline__ typename Frag<MS, FMT>::t load_frag(const char* st, int off0, int off1) {
+    if constexpr (FMT == kE4M3) {
         const u32x4 lo = *reinterpret_cast<const u32x4*>(st + off0);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(st + off1);
         return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else if constexpr (FMT == kE2M1) {
+        (void)off1;
+        return *reinterpret_cast<const u32x4*>(st + off0);
     } else {
         (void)off1;
         return *reinterpret_cast<const bf16x8*>(st + off0);
     }
 }
 
-// SEL: MXFP8 only, which byte of the scale registers sa / sb the instruction applies (op_sel)
-template <int MS, bool MX, int SEL = 0>
-__device__ __forceinline__ typename Mfma<MS, MX>::acc_t mfma(typename Frag<MS, MX>::t a, typename Frag<MS, MX>::t b,
-                                                             typename Mfma<MS, MX>::acc_t c, int sa, int sb) {
-    if constexpr (!MX) {
+// SEL: block-scaled formats only, which byte of the scale registers sa / sb the instruction
+// applies (op_sel)
+template <int MS, int FMT, int SEL = 0>
+__device__ __forceinline__ typename Mfma<MS, FMT>::acc_t mfma(typename Frag<MS, FMT>::t a, typename Frag<MS, FMT>::t b,
+                                                              typename Mfma<MS, FMT>::acc_t c, int sa, int sb) {
+    if constexpr (FMT == kBF16) {
         (void)sa;
         (void)sb;
         if constexpr (MS == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
         else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    } else {
+    } else if constexpr (FMT == kE4M3) {
         // format 0 = E4M3 for both operands; the scale byte SEL of each scale register
         if constexpr (MS == 32) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
         else return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
+    } else {
+        // format 4 = E2M1 for both operands, which take four registers each (the upper half of
+        // the eight-register operand is not read)
+        const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+        const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+        if constexpr (MS == 32) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SEL, sa, SEL, sb);
+        else return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, SEL, sa, SEL, sb);
     }
 }
 
-template <int MS, bool MX>
-__device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
-    typename Mfma<MS, MX>::acc_t z;
+template <int MS, int FMT>
+__device__ __forceinline__ typename Mfma<MS, FMT>::acc_t acc_zero() {
+    typename Mfma<MS, FMT>::acc_t z;
 #pragma unroll
-    for (int r = 0; r < Mfma<MS, MX>::NACC; ++r) z[r] = 0.f;
+    for (int r = 0; r < Mfma<MS, FMT>::NACC; ++r) z[r] = 0.f;
     return z;
 }
 
@@ -445,15 +506,19 @@ __device__ __forceinline__ typename Mfma<MS, MX>::acc_t acc_zero() {
 // offsets[g] .. offsets[g+1]-1 of 32 K elements, read from the group-major column-wise
 // layout (group g's A block [M, 32 n_g] at A + 32 M offsets[g], row stride 32 n_g; likewise
 // B with N rows and both scale blocks), and writes it at C + g * c_stride.
-template <int BM, bool SWIGLU, bool MX, bool RK>
+template <int BM, bool SWIGLU, int FMT, bool RK>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int r_off, int nt) {
-    constexpr int EB = MX ? 1 : 2;                      // operand element bytes
+    constexpr bool MX = FMT != kBF16;                   // block-scaled operands (E8M0 scales)
+    constexpr bool FP4 = FMT == kE2M1;
+    constexpr int EB = MX ? 1 : 2;                      // operand element bytes (E2M1: half a byte)
+    constexpr int KPS = FP4 ? 2 * kRowBytes : kRowBytes / EB;   // K elements per stage
     // wave grid WM x WN: 8 waves: 1x8 for 16 rows, else 2x4; 4 waves: 2x2 from 128 rows, else 1x4
     constexpr int WM = kWaves == 8 ? ((BM == 16) ? 1 : 2) : ((BM >= 128) ? 2 : 1);
     constexpr int WN = kWaves / WM;
     constexpr int MS = (BM / WM >= 32) ? 32 : 16;       // MFMA tile edge
-    using MF = Mfma<MS, MX>;
-    using FragT = typename Frag<MS, MX>::t;
+    using MF = Mfma<MS, FMT>;
+    using FragT = typename Frag<MS, FMT>::t;
+    using ST = Stage<BM, FP4 ? kE2M1 : kE4M3>;
     constexpr int NKS = MF::KS;                          // MFMA k-steps per stage
     constexpr int ROWS_PER_INSTR = 1024 / kRowBytes;     // LDS rows filled by one 1 KiB DMA instruction
     constexpr int WTM = BM / WM;                         // rows per wave
@@ -464,16 +529,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     constexpr int A_PER_WAVE = cdiv(A_INSTR, kLWaves);
     constexpr int B_PER_WAVE = kBN / ROWS_PER_INSTR / kLWaves;
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
-    constexpr int AS_INSTR = cdiv(BM, 64);               // MXFP8: scale dwords, 64 rows per instruction
-    constexpr int BS_INSTR = kBN / 64;
+    constexpr int SDW = ST::kScaleDw;                    // scale dwords per row and stage
+    constexpr int AS_GRP = cdiv(BM, 64);                 // 64-row groups of A (one scale instruction each)
+    constexpr int BS_GRP = kBN / 64;
+    constexpr int AS_INSTR = AS_GRP * SDW;               // scale dword instructions of a stage: A, then B
+    constexpr int BS_INSTR = BS_GRP * SDW;
     constexpr int SC_PER_WAVE = MX ? cdiv(AS_INSTR + BS_INSTR, kLWaves) : 0;   // scale instructions per wave
-    constexpr int NST = Stage<BM>::kCount;
-    constexpr int SB = Stage<BM>::kBytes;
-    static_assert(NST * SB <= kPipeBytes, "pipeline stages exceed the LDS ring");
+    constexpr int NST = ST::kCount;
+    constexpr int SB = ST::kBytes;
+    static_assert(NST * SB <= pipe_bytes<FMT>(), "pipeline stages exceed the LDS ring");
     static_assert(NST <= 4, "the wait counts cover at most two later stages in flight");
     static_assert(BM < 256 || (BM * (kBN * 2 + 16) <= kPipeBytes), "bf16 epilogue tile must fit in LDS");
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
-    static_assert(SC_PER_WAVE <= 2, "at most two scale loads per wave");
+    static_assert(SC_PER_WAVE <= 3, "at most three scale loads per wave");
 
     if constexpr (BM == 256) {
         if (p.c_f32) return;   // never scheduled: 256-row tiles are only chosen for 2-byte outputs
@@ -489,13 +557,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const bool producer = kPWaves > 0 && wave >= kWaves;
     const int lw = kPWaves ? wave - kWaves : wave;      // index among the load-issuing waves
     int row_begin, row_end;
-    int nk = p.K / (kRowBytes / EB);                      // K slices
+    int nk = p.K / KPS;                                   // K slices
     char* Cg = p.C;
     // operand bases and row strides (bytes); scale bases and row strides (scale bytes)
+    // row strides and offsets in bytes (E2M1: leading dimensions and strides counted in
+    // elements, two per byte)
+    auto bytes_of = [](int64_t elems) -> int64_t { return FP4 ? elems / 2 : elems * EB; };
     const char* a_base = p.A;
-    int64_t a_ld = p.lda * EB;
-    const char* b_base = p.B + (RK ? 0 : (int64_t)g * p.b_stride * EB);
-    int64_t b_ld = p.ldb * EB;
+    int64_t a_ld = bytes_of(p.lda);
+    const char* b_base = p.B + (RK ? 0 : bytes_of((int64_t)g * p.b_stride));
+    int64_t b_ld = bytes_of(p.ldb);
     const uint8_t* as_base = p.a_scale;
     int64_t as_ld = p.lda_scale;
     const uint8_t* bs_base = p.b_scale ? p.b_scale + (RK ? 0 : (int64_t)g * p.b_scale_stride) : nullptr;
@@ -521,7 +592,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     } else if (p.uniform_rows > 0) {
         row_begin = min(g * p.uniform_rows, p.M);
         row_end = min(row_begin + p.uniform_rows, p.M);
-        a_base = p.A + (int64_t)g * p.a_group_stride * EB;
+        a_base = p.A + bytes_of((int64_t)g * p.a_group_stride);
     } else {
         group_rows(p.offsets, g, p.M, row_begin, row_end);
     }
@@ -587,12 +658,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         for (int u = 0; u < SC_PER_WAVE; ++u) {
             const int q = lw + kLWaves * u;
             if (q < AS_INSTR) {
-                s_src[u] = as_base + a_row_of(q * 64 + lane) * as_ld;
-                s_lds[u] = Stage<BM>::kScaleA + q * 256;
+                // dword h = q / AS_GRP of the stage's scales of rows 64 (q % AS_GRP) + lane
+                const int h = q / AS_GRP, grp = q % AS_GRP;
+                s_src[u] = as_base + a_row_of(grp * 64 + lane) * as_ld + 4 * h;
+                s_lds[u] = ST::kScaleA + h * ST::kScaleRowsA * 4 + grp * 256;
             } else if (q < AS_INSTR + BS_INSTR) {
-                const int rho = (q - AS_INSTR) * 64 + lane;
-                s_src[u] = bs_base + (int64_t)b_row_of(rho) * bs_ld;
-                s_lds[u] = Stage<BM>::kScaleB + (q - AS_INSTR) * 256;
+                const int h = (q - AS_INSTR) / BS_GRP, grp = (q - AS_INSTR) % BS_GRP;
+                const int rho = grp * 64 + lane;
+                s_src[u] = bs_base + (int64_t)b_row_of(rho) * bs_ld + 4 * h;
+                s_lds[u] = ST::kScaleB + h * kBN * 4 + grp * 256;
             }
         }
     }
@@ -623,9 +697,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
             load_lds16(b_src[i] + koff, st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024);
 #endif
         } else {
-            // 4 scale bytes (the stage's 4 blocks of 32) per row
+            // 4 scale bytes (4 blocks of 32) per row and instruction; the stage's 4 * SDW blocks
             constexpr int u = l - A_PER_WAVE - B_PER_WAVE;
-            if (lw + kLWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4, st + s_lds[u]);
+            if (lw + kLWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4 * SDW, st + s_lds[u]);
         }
     };
     auto issue = [&](int kt) {
@@ -636,7 +710,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, MX>();
+        for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, FMT>();
 
     // Per-wave loads per stage differ (some waves issue no A or scale load); the wait count
     // uses the smallest, so every wave is sure its own loads of stage kt have landed.
@@ -664,24 +738,29 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     // matrix core works instead of all waves issuing them back to back after the barrier.
     auto compute = [&](int kt, int kn) {
         const char* st = lds + (kt % NST) * SB;
-        // MXFP8: this lane's rows' 4 scale bytes of the stage, shifted so that byte SEL of the
-        // register is the block of k-step ks for this lane (the instruction's op_sel picks it)
-        int sa_w[MI], sb_w[NI];
+        // block-scaled formats: this lane's rows' scale dwords of the stage, shifted so that byte
+        // SEL of dword DW is the block of k-step ks for this lane (the instruction's op_sel picks it)
+        int sa_w[MI][SDW], sb_w[NI][SDW];
         if constexpr (MX) {
-            const uint32_t sh0 = 8 * MF::frag_block(lane, 0);
+            const uint32_t sh0 = 8 * (MF::frag_block(lane, 0) - MF::frag_block(0, 0));
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                sa_w[i] = (int)(*reinterpret_cast<const uint32_t*>(
-                                    st + Stage<BM>::kScaleA + (wm * WTM + i * MS + MF::frag_row(lane)) * 4) >> sh0);
+            for (int h = 0; h < SDW; ++h) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j)
-                sb_w[j] = (int)(*reinterpret_cast<const uint32_t*>(
-                                    st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4) >> sh0);
+                for (int i = 0; i < MI; ++i)
+                    sa_w[i][h] = (int)(*reinterpret_cast<const uint32_t*>(
+                                           st + ST::kScaleA + h * ST::kScaleRowsA * 4 +
+                                           (wm * WTM + i * MS + MF::frag_row(lane)) * 4) >> sh0);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    sb_w[j][h] = (int)(*reinterpret_cast<const uint32_t*>(
+                                           st + ST::kScaleB + h * kBN * 4 + (wn * WTN + j * MS + MF::frag_row(lane)) * 4) >>
+                                       sh0);
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < MI; ++i) sa_w[i] = 0;
+            for (int i = 0; i < MI; ++i) sa_w[i][0] = 0;
 #pragma unroll
-            for (int j = 0; j < NI; ++j) sb_w[j] = 0;
+            for (int j = 0; j < NI; ++j) sb_w[j][0] = 0;
         }
         // Fragments are double-buffered in registers (the LDS reads of k-step ks+1 go out before
         // the MFMAs of k-step ks); MOE_GEMM_MX_FRAG_DB=0 loads the MXFP8 fragments (twice the
@@ -689,30 +768,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         constexpr bool DB = !MX || MOE_GEMM_MX_FRAG_DB;
         FragT af[DB ? 2 : 1][MI], bfr[DB ? 2 : 1][NI];
 #pragma unroll
-        for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
+        for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, FMT>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
+        for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, FMT>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
         static_for<0>(
             [&](auto ks_tag) {
                 constexpr int ks = decltype(ks_tag)::value;
                 constexpr int cur = DB ? (ks & 1) : 0, nxt = DB ? (cur ^ 1) : 0;
-                constexpr int SEL = MX ? MF::frag_block(0, ks) - MF::frag_block(0, 0) : 0;
+                // the k-step's block of this lane: dword DW, byte SEL after the per-lane shift
+                constexpr int DW = MX ? MF::frag_block(0, ks) / 4 : 0;
+                constexpr int SEL = MX ? MF::frag_block(0, ks) % 4 : 0;
+                static_assert(DW < SDW, "scale dword of the k-step");
                 if constexpr (!DB && ks > 0) {
 #pragma unroll
-                    for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[ks][0], a_off[ks][1]);
+                    for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, FMT>(st + i * FSTEP, a_off[ks][0], a_off[ks][1]);
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[ks][0], b_off[ks][1]);
+                    for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, FMT>(st + j * FSTEP, b_off[ks][0], b_off[ks][1]);
                 }
                 if constexpr (DB && ks + 1 < NKS) {
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
-                        af[nxt][i] = load_frag<MS, MX>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
+                        af[nxt][i] = load_frag<MS, FMT>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        bfr[nxt][j] = load_frag<MS, MX>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
+                        bfr[nxt][j] = load_frag<MS, FMT>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
-                acc[0][0] = mfma<MS, MX, SEL>(af[cur][0], bfr[cur][0], acc[0][0], sa_w[0], sb_w[0]);
+                acc[0][0] = mfma<MS, FMT, SEL>(af[cur][0], bfr[cur][0], acc[0][0], sa_w[0][DW], sb_w[0][DW]);
                 if (kn >= 0) {
                     __builtin_amdgcn_sched_barrier(0);
                     static_for<0>(
@@ -729,7 +811,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
                         if (i != 0 || j != 0)
-                            acc[i][j] = mfma<MS, MX, SEL>(af[cur][i], bfr[cur][j], acc[i][j], sa_w[i], sb_w[j]);
+                            acc[i][j] = mfma<MS, FMT, SEL>(af[cur][i], bfr[cur][j], acc[i][j], sa_w[i][DW], sb_w[j][DW]);
             },
             std::make_integer_sequence<int, NKS>{});
     };
@@ -868,8 +950,8 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
     constexpr int BM = 128, NST = Stage<BM>::kCount, SB = Stage<BM>::kBytes;
     constexpr int MS = 32, WM = 2, WN = kWaves / WM, WTM = BM / WM, WTN = kBN / WN;
     constexpr int MI = WTM / MS, NI = WTN / MS;
-    using MF = Mfma<MS, true>;
-    using FragT = typename Frag<MS, true>::t;
+    using MF = Mfma<MS, kE4M3>;
+    using FragT = typename Frag<MS, kE4M3>::t;
     constexpr int NKS = MF::KS;
     constexpr int ROWS_PER_INSTR = 1024 / kRowBytes, CH = kRowBytes / 16;
     constexpr int A_INSTR = BM / ROWS_PER_INSTR;
@@ -1004,7 +1086,7 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, true>();
+            for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, kE4M3>();
         for (int kt = 0; kt < nk; ++kt, ++q) {
             wait_vm_lgkm0<63>();   // this wave's LDS reads of the previous slice are done
             lds_barrier();
@@ -1018,19 +1100,19 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
                 sb_w[j] = *reinterpret_cast<const int*>(st + Stage<BM>::kScaleB + (wn * WTN + j * MS + MF::frag_row(lane)) * 4);
             FragT af[2][MI], bfr[2][NI];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, true>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
+            for (int i = 0; i < MI; ++i) af[0][i] = load_frag<MS, kE4M3>(st + i * FSTEP, a_off[0][0], a_off[0][1]);
 #pragma unroll
-            for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, true>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
+            for (int j = 0; j < NI; ++j) bfr[0][j] = load_frag<MS, kE4M3>(st + j * FSTEP, b_off[0][0], b_off[0][1]);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int cur = ks & 1, nxt = cur ^ 1;
                 if (ks + 1 < NKS) {
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
-                        af[nxt][i] = load_frag<MS, true>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
+                        af[nxt][i] = load_frag<MS, kE4M3>(st + i * FSTEP, a_off[ks + 1][0], a_off[ks + 1][1]);
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        bfr[nxt][j] = load_frag<MS, true>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
+                        bfr[nxt][j] = load_frag<MS, kE4M3>(st + j * FSTEP, b_off[ks + 1][0], b_off[ks + 1][1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const int sh = 8 * MF::frag_block(lane, ks);
@@ -1038,7 +1120,7 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        acc[i][j] = mfma<MS, true>(af[cur][i], bfr[cur][j], acc[i][j], (sa_w[i] >> sh) & 0xFF,
+                        acc[i][j] = mfma<MS, kE4M3>(af[cur][i], bfr[cur][j], acc[i][j], (sa_w[i] >> sh) & 0xFF,
                                                    (sb_w[j] >> sh) & 0xFF);
             }
         }
@@ -1068,7 +1150,7 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
     }
 }
 
-template <bool SWIGLU, bool MX, bool RK>
+template <bool SWIGLU, int FMT, bool RK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // XCD-aware slot: the hardware deals workgroups round-robin over the 8 XCDs, so give the
@@ -1090,7 +1172,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
             int mt, nt;
             if (p.NT >= kSuperRKMinNT) tile_coords<kSuperRK>(tile - g * per_group, p.MT, p.NT, mt, nt);
             else tile_coords(tile - g * per_group, p.MT, p.NT, mt, nt);
-            gemm_tile<128, false, true, true>(p, lds, g, mt * 128, nt);
+            gemm_tile<128, false, kE4M3, true>(p, lds, g, mt * 128, nt);
         }
         return;
     }
@@ -1099,7 +1181,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
     const bool uniform = p.uniform_rows > 0;
     const RowTiles rt_u = row_tiles(uniform ? p.uniform_rows : 0, false);
     const int per_group_u = rt_u.count() * p.NT;
-    int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
+    int32_t* ts = reinterpret_cast<int32_t*>(lds + pipe_bytes<FMT>());
     int total;
     if (uniform) {
         total = p.G * per_group_u;
@@ -1133,14 +1215,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
         tile_coords(L, rt.count(), p.NT, mt, nt);
         row_tile(rt, mt, r_off, bm);
         switch (bm) {
-            case 16: gemm_tile<16, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
-            case 32: gemm_tile<32, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
-            case 64: gemm_tile<64, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
-            case 128: gemm_tile<128, SWIGLU, MX, false>(p, lds, g, r_off, nt); break;
+            case 16: gemm_tile<16, SWIGLU, FMT, false>(p, lds, g, r_off, nt); break;
+            case 32: gemm_tile<32, SWIGLU, FMT, false>(p, lds, g, r_off, nt); break;
+            case 64: gemm_tile<64, SWIGLU, FMT, false>(p, lds, g, r_off, nt); break;
+            case 128: gemm_tile<128, SWIGLU, FMT, false>(p, lds, g, r_off, nt); break;
             default:
                 // 256-row tiles are bf16 only (the fp8 fragments of a 256-row tile do not fit
                 // the register budget next to its accumulators); never chosen for MXFP8
-                if constexpr (!MX && MOE_GEMM_TILE256) gemm_tile<256, SWIGLU, MX, false>(p, lds, g, r_off, nt);
+                if constexpr (FMT == kBF16 && MOE_GEMM_TILE256) gemm_tile<256, SWIGLU, FMT, false>(p, lds, g, r_off, nt);
                 break;
         }
     }
@@ -1193,22 +1275,23 @@ int num_cus() {
     return cached[dev];
 }
 
-template <bool SWIGLU, bool MX, bool RK>
+template <bool SWIGLU, int FMT, bool RK>
 bool set_lds_attr() {
     static bool done = false;
     if (!done) {
-        if (hipFuncSetAttribute((const void*)gemm_mfma_kernel<SWIGLU, MX, RK>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
+        if (hipFuncSetAttribute((const void*)gemm_mfma_kernel<SWIGLU, FMT, RK>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<FMT>()) != hipSuccess)
             return false;
         done = true;
     }
     return true;
 }
 
-template <bool SWIGLU, bool MX, bool RK = false>
+template <bool SWIGLU, int FMT, bool RK = false>
 moe_status_t launch(const GemmParams& p, int grid, hipStream_t s) {
-    if (!set_lds_attr<SWIGLU, MX, RK>()) return MOE_EHIP;
-    hipLaunchKernelGGL((gemm_mfma_kernel<SWIGLU, MX, RK>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, p);
+    if (!set_lds_attr<SWIGLU, FMT, RK>()) return MOE_EHIP;
+    hipLaunchKernelGGL((gemm_mfma_kernel<SWIGLU, FMT, RK>), dim3((unsigned)grid), dim3(kThreads), lds_bytes<FMT>(), s,
+                       p);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
@@ -1232,7 +1315,10 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->M > INT32_MAX / 2) return MOE_EINVAL;
     if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_EINVAL;
     if (a->a_dtype != a->b_dtype) return MOE_ENOTSUP;
-    if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3) return MOE_ENOTSUP;
+    if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3 && a->a_dtype != MOE_E2M1)
+        return MOE_ENOTSUP;
+    // E2M1 stages carry twice the scale bytes, which leaves LDS for the schedule of 1791 groups
+    if (a->a_dtype == MOE_E2M1 && (a->G > moe::max_groups<moe::kE2M1>() || a->ragged_k)) return MOE_ENOTSUP;
     if (a->c_dtype != MOE_BF16 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->a_dtype == MOE_F32 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->ragged_k != 0 && a->ragged_k != 1) return MOE_EINVAL;
@@ -1253,7 +1339,8 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->aux && (a->epilogue != MOE_EPI_SWIGLU || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
     if (!workspace || workspace_bytes < moe_gemm_workspace_bytes(a->G)) return MOE_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    const bool mx = a->a_dtype == MOE_E4M3;
+    const bool fp4 = a->a_dtype == MOE_E2M1;
+    const bool mx = a->a_dtype == MOE_E4M3 || fp4;
 
     moe::GemmParams p{};
     p.offsets = a->offsets;
@@ -1292,11 +1379,14 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         MOE_CHECK_LAUNCH();
         return MOE_OK;
     }
-    // MFMA paths: 128-byte K slices (64 bf16 or 128 fp8)
-    const int64_t eb = mx ? 1 : 2;
-    if (a->K % (moe::kRowBytes / eb) != 0) return MOE_EINVAL;
+    // MFMA paths: 128-byte K slices (64 bf16, 128 E4M3 or 256 E2M1 values); sizes in bytes
+    // (E2M1 packs two values per byte, so its element counts must be even)
+    const int64_t eb2 = fp4 ? 1 : mx ? 2 : 4;   // bytes per two elements
+    auto bytes = [eb2](int64_t elems) { return elems * eb2 / 2; };
+    if (fp4 && (a->lda % 2 || a->ldb % 2 || a->b_group_stride % 2)) return MOE_EINVAL;
+    if (a->K % (2 * moe::kRowBytes / eb2) != 0) return MOE_EINVAL;
     if (!moe_aligned16(a->A) || !moe_aligned16(a->B) || !moe_aligned16(a->C)) return MOE_EINVAL;
-    if ((a->lda * eb) % 16 || (a->ldb * eb) % 16 || a->ldc % 8 || (a->b_group_stride * eb) % 16) return MOE_EINVAL;
+    if (bytes(a->lda) % 16 || bytes(a->ldb) % 16 || a->ldc % 8 || bytes(a->b_group_stride) % 16) return MOE_EINVAL;
     if (a->aux && (!moe_aligned16(a->aux) || a->ld_aux % 8)) return MOE_EINVAL;
     if (mx) {
         if (!a->a_scale || !a->b_scale || !aligned4(a->a_scale) || !aligned4(a->b_scale)) return MOE_EINVAL;
@@ -1310,9 +1400,9 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         // buffer DMA adds 32-bit lane offsets to each tile's operand base: every operand region
         // a tile addresses (plus the K extent) must stay below 4 GiB
         const int64_t lim = (int64_t)1 << 32;
-        const int64_t kb = a->K * eb;
-        const int64_t a_span = a->ragged_k ? a->M * kb : a->A_rows * a->lda * eb;
-        const int64_t b_span = a->ragged_k ? a->N * kb : (swiglu ? 2 : 1) * a->N * a->ldb * eb;
+        const int64_t kb = bytes(a->K);
+        const int64_t a_span = a->ragged_k ? a->M * kb : a->A_rows * bytes(a->lda);
+        const int64_t b_span = a->ragged_k ? a->N * kb : (swiglu ? 2 : 1) * a->N * bytes(a->ldb);
         if (a_span + kb >= lim || b_span + kb >= lim) return MOE_ENOTSUP;
     }
     if (a->ragged_k) {
@@ -1322,7 +1412,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         const int64_t tiles = (int64_t)p.MT * p.NT * a->G;
         if (tiles > INT32_MAX) return MOE_EINVAL;
         const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), tiles);
-        return moe::launch<false, true, true>(p, grid, s);
+        return moe::launch<false, moe::kE4M3, true>(p, grid, s);
     }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
                        p.allow256, (int32_t*)workspace, (int32_t*)workspace + (a->G + 1));
@@ -1330,8 +1420,11 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;
     const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
-    if (swiglu) return mx ? moe::launch<true, true>(p, grid, s) : moe::launch<true, false>(p, grid, s);
-    return mx ? moe::launch<false, true>(p, grid, s) : moe::launch<false, false>(p, grid, s);
+    if (swiglu)
+        return fp4 ? moe::launch<true, moe::kE2M1>(p, grid, s)
+                   : mx ? moe::launch<true, moe::kE4M3>(p, grid, s) : moe::launch<true, moe::kBF16>(p, grid, s);
+    return fp4 ? moe::launch<false, moe::kE2M1>(p, grid, s)
+               : mx ? moe::launch<false, moe::kE4M3>(p, grid, s) : moe::launch<false, moe::kBF16>(p, grid, s);
 }
 
 // Internal entry (route.hip): a bf16 K-split projection as one launch over KS uniform groups,
@@ -1365,5 +1458,5 @@ moe_status_t moe_gemm_ksplit_f32(const void* x, const void* w, int64_t T, int64_
     const int64_t row_tiles = T <= 128 ? 1 : T / 128 + (T % 128 ? 1 : 0);
     const int64_t tiles = row_tiles * p.NT * KS;
     const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), tiles);
-    return moe::launch<false, false>(p, grid, s);
+    return moe::launch<false, moe::kBF16>(p, grid, s);
 }

@@ -112,6 +112,77 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict_
 // 128-element boundary (one K slice of the MXFP8 GEMM, its 4 scale bytes one aligned dword),
 // and one group's transposed block is contiguous in memory; blocks past the group's last row
 // are all-zero (codes 0, scale byte 0).
+// ---- MXFP4 ([OCP-MX] FP4 E2M1 elements: bias 1, one mantissa bit, values 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6; the block's shared exponent floor(log2 amax) - 2, 2 being E2M1's largest exponent)
+
+__device__ __forceinline__ uint32_t mx4_scale_byte(float amax) {
+    if (!(amax > 0.f)) return 0u;
+    int e2;
+    (void)frexpf(amax, &e2);                  // amax = m * 2^e2, m in [0.5, 1)
+    const int b = e2 - 1 - 2 + 127;
+    return (uint32_t)min(max(b, 0), 254);     // at most 252 for a finite amax
+}
+
+// E2M1 code of a scaled value: round to nearest, ties to the even mantissa (the comparisons
+// against the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 are strict where the tie goes down
+// to an even code and inclusive where it goes up to one), magnitudes above 6 saturate; the sign
+// in bit 3, also for a value that rounds to zero. The magnitude index is the code's low 3 bits.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+    const float m = fabsf(x);
+    const uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                         (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+    return ((__float_as_uint(x) >> 28) & 0x8u) | idx;
+}
+
+// Row-wise MXFP4: one thread per 32-element block; the block's 32 codes go out as 16 bytes
+// (two per byte, the even element in the low nibble), its scale as one byte.
+template <int ESIZE>
+__global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const char* __restrict__ in, int64_t rows, int cols,
+                                                             int64_t ld_in, const int32_t* __restrict__ row_index,
+                                                             int64_t in_rows, uint8_t* __restrict__ q, int64_t ld_q,
+                                                             uint8_t* __restrict__ sc, int64_t ld_sc) {
+    const int nb = cols / kBlock;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * nb) return;
+    const int64_t r = idx / nb;
+    const int b = (int)(idx % nb);
+    const char* src = in + (in_row(row_index, in_rows, r) * ld_in + (int64_t)b * kBlock) * ESIZE;
+    float v[kBlock];
+    if (ESIZE == 2) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[c * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+                v[c * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[c * 4 + i] = __uint_as_float(w[i]);
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t byte = mx4_scale_byte(amax);
+    const float inv = mx_inv_scale(byte);     // exact: the scaled values are v * 2^(127 - byte)
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[w * 8 + i] * inv) << (4 * i);
+        out[w] = word;
+    }
+    *reinterpret_cast<u32x4*>(q + r * ld_q + (int64_t)b * (kBlock / 2)) = out;
+    sc[r * ld_sc + b] = (uint8_t)byte;
+}
+
 __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t* __restrict__ offsets, int G,
                                                                   int64_t rows, int32_t* __restrict__ block_start) {
     __shared__ int wsum[16];
@@ -529,6 +600,30 @@ extern "C" moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int
     // axis 1: group-aware blocks of rows, transposed output
     return quant_colwise(in, dtype, rows, cols, ld_in, row_index, in_rows, group_offsets, G, q, ld_q, scales,
                          ld_scales, nullptr, 0, nullptr, 0, block_start, workspace, workspace_bytes, s);
+}
+
+extern "C" moe_status_t moe_group_quant_mxfp4(const void* in, int32_t dtype, int64_t rows, int64_t cols,
+                                              int64_t ld_in, const int32_t* row_index, int64_t in_rows, uint8_t* q,
+                                              int64_t ld_q, uint8_t* scales, int64_t ld_scales, void* stream) {
+    if (rows < 0 || cols <= 0 || cols > INT32_MAX / 2 || ld_in < cols || cols % moe::kBlock != 0) return MOE_EINVAL;
+    if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ENOTSUP;
+    if (!row_index) in_rows = rows;
+    else if (in_rows <= 0 && rows > 0) return MOE_EINVAL;
+    if (rows == 0) return MOE_OK;
+    const int esize = dtype == MOE_BF16 ? 2 : 4;
+    if (!in || !q || !scales || ld_q < cols / 2 || ld_scales < cols / moe::kBlock) return MOE_EINVAL;
+    if (!moe_aligned16(in) || !moe_aligned16(q) || (ld_in * esize) % 16 != 0 || ld_q % 16 != 0) return MOE_EINVAL;
+    const int64_t n = rows * (cols / moe::kBlock);
+    const dim3 grid((unsigned)moe::cdiv<int64_t>(n, 256));
+    hipStream_t s = (hipStream_t)stream;
+    if (esize == 2)
+        hipLaunchKernelGGL(moe::quant_rows_fp4_kernel<2>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
+                           row_index, in_rows, q, ld_q, scales, ld_scales);
+    else
+        hipLaunchKernelGGL(moe::quant_rows_fp4_kernel<4>, grid, dim3(256), 0, s, (const char*)in, rows, (int)cols, ld_in,
+                           row_index, in_rows, q, ld_q, scales, ld_scales);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
 }
 
 extern "C" moe_status_t moe_group_quant_mxfp8_dual(const void* in, int32_t dtype, int64_t rows, int64_t cols,

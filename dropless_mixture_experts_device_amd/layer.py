@@ -303,3 +303,68 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
                              d_x_perm_shared=b.dXp[tk:] if s.shared else None, d_w_router=b.dW_router,
                              d_bias=b.d_bias, workspace=b.ws_route_bwd)
         mark("unpermute_route_bwd")
+
+
+# --------------------------------------------------------------------------------------
+# MXFP4 forward ([Blog] "JAX plus Transformer Engine MoE training performance": a 4-bit
+# block-scaled format is the planned next precision; [Reading] contribution 3: FP8/FP4
+# recipes). Every GEMM operand is quantised row-wise along its contraction axis, as in the
+# MXFP8 forward, to E2M1 codes packed two per byte with an E8M0 scale per 32 elements.
+# --------------------------------------------------------------------------------------
+
+class Mx4Weights:
+    """Row-wise MXFP4 copies of the expert weights: W_gu [G, 2f, d] along d and W_down
+    [G, d, f] along f (codes [., ., K/2] bytes, scales [., ., K/32])."""
+
+    def __init__(self, s: LayerShape, device):
+        dev = torch.device(device)
+        G, d, f = s.groups, s.d, s.f
+        for n, k in (("d", d), ("f", f)):
+            if k % 256:
+                raise ValueError(f"MXFP4 GEMMs need {n} % 256 == 0 (got {k})")
+        self.shape = s
+        self.q_gu, self.s_gu = _u8((G, 2 * f, d // 2), dev), _u8((G, 2 * f, d // 32), dev)
+        self.q_dn, self.s_dn = _u8((G, d, f // 2), dev), _u8((G, d, f // 32), dev)
+
+    def quantise(self, w_gu, w_down):
+        s = self.shape
+        G, d, f = s.groups, s.d, s.f
+        L.moe_group_quant_mxfp4(w_gu.view(G * 2 * f, d), self.q_gu.view(G * 2 * f, d // 2),
+                                self.s_gu.view(G * 2 * f, d // 32))
+        L.moe_group_quant_mxfp4(w_down.view(G * d, f), self.q_dn.view(G * d, f // 2), self.s_dn.view(G * d, f // 32))
+
+
+class Mx4Buffers(LayerBuffers):
+    """The MXFP4 forward's intermediates: the bf16 ones of the layer plus the quantised x and H."""
+
+    def __init__(self, s: LayerShape, device):
+        super().__init__(s, device, fused_gather=True)
+        dev = torch.device(device)
+        self.q_x, self.s_x = _u8((s.T, s.d // 2), dev), _u8((s.T, s.d // 32), dev)
+        self.q_h, self.s_h = _u8((s.rows, s.f // 2), dev), _u8((s.rows, s.f // 32), dev)
+
+
+def forward_mx4(x, w_router, bias, mw: Mx4Weights, s: LayerShape, b: Mx4Buffers, routed: bool = False, mark=None):
+    """MXFP4 forward: route and permute as in bf16, x quantised once per token (GEMM 1 gathers
+    its code and scale rows through src_token), GEMM 1 + SwiGLU into bf16 H, H quantised,
+    GEMM 2, combine. mw must hold the quantised weights; routed=True keeps b.topk_idx and
+    b.topk_w as they are; mark(name), if given, is called after each stage."""
+    mark = mark or _nomark
+    if not routed:
+        route(x, w_router, bias, s, b)
+    mark("route")
+    permute(x, s, b)
+    mark("permute")
+    L.moe_group_quant_mxfp4(x, b.q_x, b.s_x)
+    mark("quant_x")
+    L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, workspace=b.ws_gemm1,
+                       a_scale=b.s_x, b_scale=mw.s_gu, fp4=True)
+    mark("gemm1_swiglu")
+    L.moe_group_quant_mxfp4(b.H, b.q_h, b.s_h)
+    mark("quant_h")
+    L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
+                       b_scale=mw.s_dn, fp4=True)
+    mark("gemm2")
+    combine(s, b)
+    mark("combine")
+    return b.out

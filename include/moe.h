@@ -45,7 +45,12 @@ typedef enum {
     MOE_EHIP = 4         /* a HIP launch failed                                        */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_E4M3 = 2,   /* MXFP8 element: OCP FP8 E4M3, one byte                                    */
+    MOE_E2M1 = 3    /* MXFP4 element: OCP FP4 E2M1, two per byte, the even element in bits 3..0 */
+} moe_dtype_t;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
 typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue_t;
 typedef enum {
@@ -206,9 +211,9 @@ typedef struct moe_gemm_args {
     const int32_t* offsets;     /* device [G+1], non-decreasing, offsets[G] <= M            */
     int64_t M;                  /* rows of C (and of a_rows); a host-known capacity         */
     int64_t N;                  /* output columns, N % 8 == 0                                */
-    int64_t K;                  /* contraction length: K % 64 == 0 (bf16), K % 128 == 0 (E4M3) */
+    int64_t K;                  /* contraction length: K % 64 == 0 (bf16), % 128 (E4M3), % 256 (E2M1) */
     const void* A;              /* [A_rows, K], leading dimension lda                        */
-    int32_t a_dtype;            /* MOE_BF16, MOE_F32 or MOE_E4M3 (MXFP8, with scales below)  */
+    int32_t a_dtype;            /* MOE_BF16, MOE_F32, MOE_E4M3 or MOE_E2M1 (scales below)   */
     int64_t lda;
     int64_t A_rows;             /* rows of A (gather indices are clamped to it)              */
     const int32_t* a_rows;      /* optional device [M] gather index                          */
@@ -224,7 +229,11 @@ typedef struct moe_gemm_args {
     int64_t ld_aux;
     /* MXFP8 operands (a_dtype = b_dtype = MOE_E4M3, K % 128 == 0): A and B hold E4M3 codes and
      * every 32 consecutive K elements of a row share one E8M0 scale byte s, the element value
-     * being code_value * 2^(s-127) ([OCP-MX]); products are exact and summed in fp32. */
+     * being code_value * 2^(s-127) ([OCP-MX]); products are exact and summed in fp32.
+     * MXFP4 operands (MOE_E2M1, K % 256 == 0, ragged_k = 0, G <= 1791): the same with E2M1
+     * codes packed two per byte (element 2i of a row in bits 3..0 of byte i, as
+     * moe_group_quant_mxfp4 writes them); lda, ldb and b_group_stride still count elements
+     * (even numbers), so a row starts lda/2 bytes after the previous one. */
     const uint8_t* a_scale;     /* [A_rows, K/32], leading dimension lda_scale (a_rows applies) */
     int64_t lda_scale;
     const uint8_t* b_scale;     /* group g: [N or 2N, K/32] at b_scale + g*b_scale_group_stride  */
@@ -235,8 +244,8 @@ typedef struct moe_gemm_args {
 } moe_gemm_args_t;
 
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
- * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047. A, B, C, aux 16-byte
- * aligned; A and B rows (lda, ldb, b_group_stride) 16-byte multiples; ldc, ld_aux multiples
+ * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047 (1791 for MXFP4). A, B, C,
+ * aux 16-byte aligned; A and B rows (lda, ldb, b_group_stride, in bytes) 16-byte multiples; ldc, ld_aux multiples
  * of 8; MXFP8 scale pointers and their strides 4-byte multiples. A (A_rows x lda) and one
  * group's B (N or 2N rows x ldb) must each span less than 4 GiB (MOE_ENOTSUP otherwise: the
  * loads use 32-bit offsets from the tile's base). The args struct is read on the host during
@@ -334,6 +343,33 @@ moe_status_t moe_group_quant_mxfp8(const void* in, int32_t dtype, int64_t rows, 
                                    const int32_t* group_offsets, int32_t G, int32_t axis,
                                    uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_scales,
                                    int32_t* block_start, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_group_quant_mxfp4 -- MXFP4 quantisation, row-wise: E2M1 element codes plus one E8M0
+ * scale byte per block of 32 consecutive elements of a row (the layout a forward GEMM
+ * contracting along the rows' length reads).
+ * [Blog] "JAX plus Transformer Engine MoE training performance": a 4-bit block-scaled format
+ * is the planned next precision; [Reading] contribution 3: FP8/FP4 recipes. [OCP-MX]: MXFP4
+ * is E2M1 elements (bias 1, one mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6) with an E8M0
+ * scale. Rule: for a block with largest magnitude amax, scale byte
+ *   s = clamp(floor(log2 amax) - 2 + 127, 0, 254)   (s = 0 for an all-zero block)
+ * and each element x becomes the E2M1 code of x / 2^(s-127) rounded to nearest, ties to the
+ * even mantissa, saturating at +-6; code bit 3 is the sign (kept for zero), bits 2..0 the
+ * magnitude index 0..7 of the values above.
+ *
+ *   in [rows (logical), cols] (MOE_BF16 or MOE_F32, leading dimension ld_in), cols % 32 == 0;
+ *   row_index / in_rows as moe_group_quant_mxfp8 (logical row r reads in row row_index[r],
+ *   clamped into [0, in_rows)).
+ *   q [rows, ld_q >= cols/2] bytes: element 2i of a row in bits 3..0 of byte i, element 2i+1
+ *   in bits 7..4 (the packing moe_grouped_gemm's MOE_E2M1 operands use);
+ *   scales [rows, ld_scales >= cols/32] bytes.
+ *   in and q 16-byte aligned, ld_q % 16 == 0, ld_in rows spanning multiples of 16 bytes.
+ *   Deterministic. Errors: MOE_EINVAL for bad sizes or pointers, MOE_ENOTSUP for another
+ *   dtype, MOE_EHIP for a failed launch.
+ */
+moe_status_t moe_group_quant_mxfp4(const void* in, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_in,
+                                   const int32_t* row_index, int64_t in_rows, uint8_t* q, int64_t ld_q,
+                                   uint8_t* scales, int64_t ld_scales, void* stream);
 
 /*
  * moe_group_quant_mxfp8_dual -- both MXFP8 copies of one operand from a single read of it:

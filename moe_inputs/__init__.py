@@ -171,6 +171,7 @@ class Workload:
     sigma_w: float = 0.02
     mxfp8: bool = False
     backward: bool = False
+    mxfp4: bool = False
 
 
 WORKLOADS = {
@@ -185,6 +186,9 @@ WORKLOADS = {
     # receiving 65,536 rows (about 2,048 each, the compute-bound regime), plus the GPU's own
     # shared expert over its 8,192 tokens; the dispatch that would deliver those rows from the
     # other GPUs is replaced by routing 8,192 local tokens 8 ways over the 32 experts
+    # the DeepSeek-V3 layer forward with MXFP4 expert GEMMs (d and f multiples of 256)
+    "dsv3_mxfp4": Workload("dsv3_mxfp4", 8192, 7168, 2048, 256, 8, "bf16", "sigmoid", ("zipf", 1.2, 1.0), 2048,
+                           seed=3, mxfp4=True),
     "dsv3_ep8": Workload("dsv3_ep8", 8192, 7168, 2048, 32, 8, "bf16", "sigmoid", None, 2048, seed=4),
     # reduced shapes the oracle finishes in seconds: several tiles, ragged tails, empty and
     # one-row groups, one hot group
@@ -197,6 +201,9 @@ WORKLOADS = {
     # GEMM, still small enough for the oracle to finish in seconds
     "mid_mxfp8": Workload("mid_mxfp8", 1024, 1024, 1024, 8, 2, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 1024,
                           seed=21, mxfp8=True, backward=True),
+    # the MXFP4 forward at a reduced shape
+    "small_mxfp4": Workload("small_mxfp4", 600, 512, 256, 12, 3, "bf16", "sigmoid", ("zipf", 1.2, 0.7), 256,
+                            seed=14, mxfp4=True),
 }
 
 

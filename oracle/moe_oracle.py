@@ -228,18 +228,21 @@ def expert_gate_up(X, w_gu_e):
     return X @ W[:f].T, X @ W[f:].T
 
 
-def expert_forward(X, w_gu_e, w_down_e, rnd=None, mx=False, return_gu=False):
+def expert_forward(X, w_gu_e, w_down_e, rnd=None, mx=False, return_gu=False, mx4=False):
     """H = rnd(silu(G) * U), Y = rnd(H W_down^T); returns (H, Y) (and (G, U) unrounded).
 
-    w_down_e is [d, f]. With `mx`, each GEMM operand first passes through the rowwise MX
-    quantiser along its contraction axis (X and W_gu along d, H and W_down along f).
+    w_down_e is [d, f]. With `mx` (MXFP8) or `mx4` (MXFP4), each GEMM operand first passes
+    through that format's rowwise quantiser along its contraction axis (X and W_gu along d,
+    H and W_down along f).
     """
     r = _rounder(rnd)
+    q = mx4_q_rows if mx4 else mx_q_rows
+    mx = mx or mx4
     if mx:
-        X, w_gu_e, w_down_e = mx_q_rows(X), mx_q_rows(w_gu_e), mx_q_rows(w_down_e)
+        X, w_gu_e, w_down_e = q(X), q(w_gu_e), q(w_down_e)
     G, U = expert_gate_up(X, w_gu_e)
     H = r(silu(G) * U)
-    Hq = mx_q_rows(H) if mx else H
+    Hq = q(H) if mx else H
     Y = r(Hq @ np.asarray(w_down_e, F64).T)
     if return_gu:
         return H, Y, (G, U)
@@ -311,7 +314,7 @@ def combine(Y, topk_w, row_of, y_shared=None, rnd=None):
 # --------------------------------------------------------------------------------------
 
 def layer_forward(x, w_router, bias, k, score, w_gu, w_down, E, shared=False, rnd=None,
-                  topk=None, mx=False):
+                  topk=None, mx=False, mx4=False):
     """One dropless MoE layer forward: route -> permute -> grouped SwiGLU MLP -> combine.
 
     w_gu(e) / w_down(e) return expert e's [2f, d] / [d, f] weights (e = E is the shared
@@ -335,7 +338,7 @@ def layer_forward(x, w_router, bias, k, score, w_gu, w_down, E, shared=False, rn
         lo, hi = int(offsets[g]), int(offsets[g + 1])
         if hi == lo:
             continue
-        H, Y = expert_forward(xp[lo:hi], w_gu(g), w_down(g), rnd, mx=mx)
+        H, Y = expert_forward(xp[lo:hi], w_gu(g), w_down(g), rnd, mx=mx, mx4=mx4)
         H_parts.append((lo, H))
         Y_parts.append((lo, Y))
         f = H.shape[1]

@@ -30,15 +30,19 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def stage_bytes(bm):
+def stage_bytes(bm, fp4=False):
+    sdw = 2 if fp4 else 1          # scale dwords per row and stage
     scale_rows_a = cdiv(bm, 64) * 64
     data = (bm + BN) * ROW_BYTES
-    return dict(data=data, scale_a=data, scale_b=data + scale_rows_a * 4,
-                bytes=data + (scale_rows_a + BN) * 4, count=2 if bm == 256 else 3)
+    return dict(data=data, scale_a=data, scale_b=data + scale_rows_a * 4 * sdw, sdw=sdw, scale_rows_a=scale_rows_a,
+                bytes=data + (scale_rows_a + BN) * 4 * sdw, count=2 if bm == 256 else 3)
 
 
 PIPE_BYTES = max(3 * stage_bytes(128)["bytes"], 2 * stage_bytes(256)["bytes"])
 LDS_BYTES = PIPE_BYTES + (MAX_GROUPS + 1) * 4
+PIPE_BYTES_FP4 = 3 * stage_bytes(128, True)["bytes"]
+MAX_GROUPS_FP4 = (160 * 1024 - PIPE_BYTES_FP4) // 4 - 1
+assert MAX_GROUPS_FP4 == 1791 and PIPE_BYTES_FP4 + (MAX_GROUPS_FP4 + 1) * 4 <= 160 * 1024
 
 
 def bm_of_rows(m):
@@ -139,6 +143,7 @@ class Launch:
     c_esize: int
     swiglu: bool
     mx: bool = False
+    fp4: bool = False       # E2M1 operands (implies mx): leading dimensions and strides in elements, two per byte
     uniform_rows: int = 0   # the router's K-split mode: group g owns C rows [g R, (g+1) R), no schedule
     a_group_stride: int = 0
     lda_scale: int = 0
@@ -153,16 +158,20 @@ def check_launch(la: Launch):
     """Replay the whole launch; raise AssertionError at the first access outside a buffer or
     at any output element not written exactly once. Returns a summary dict."""
     G = len(la.offsets) - 1
+    if la.fp4:
+        assert la.mx and G <= MAX_GROUPS_FP4 and la.lda % 2 == 0 and la.ldb % 2 == 0 and la.b_stride % 2 == 0
     eb = 1 if la.mx else 2
+    byt = (lambda e: e // 2) if la.fp4 else (lambda e: e * eb)
     assert 1 <= G <= MAX_GROUPS
     bn_out = BN // 2 if la.swiglu else BN
     NT = cdiv(la.N, bn_out)
-    assert la.K % (ROW_BYTES // eb) == 0
-    nk = la.K // (ROW_BYTES // eb)
-    a_bytes = la.A_rows * la.lda * eb
+    kps = 2 * ROW_BYTES if la.fp4 else ROW_BYTES // eb      # K elements per stage
+    assert la.K % kps == 0
+    nk = la.K // kps
+    a_bytes = la.A_rows * byt(la.lda)
     # the host's 4 GiB rule for 32-bit lane offsets
-    b_span = (2 if la.swiglu else 1) * la.N * la.ldb * eb
-    assert a_bytes + la.K * eb < 1 << 32 and b_span + la.K * eb < 1 << 32
+    b_span = (2 if la.swiglu else 1) * la.N * byt(la.ldb)
+    assert a_bytes + byt(la.K) < 1 << 32 and b_span + byt(la.K) < 1 << 32
     uniform = la.uniform_rows > 0
     if uniform:
         rt_u = row_tiles(la.uniform_rows)
@@ -204,7 +213,7 @@ def check_launch(la: Launch):
             assert 0 <= mt < rt_count(rt) and 0 <= nt < NT, (tile, g, mt, nt)
             r_off, bm = row_tile(rt, mt)
             assert bm in (16, 32, 64, 128)
-            _check_tile(la, g, rb, re, r_off, bm, nt, nk, eb, written)
+            _check_tile(la, g, rb, re, r_off, bm, nt, nk, byt, written)
     assert seen_tiles == total
     # every row of every group: each column tile written exactly once; other rows untouched
     live = np.zeros(la.M, bool)
@@ -220,7 +229,7 @@ def check_launch(la: Launch):
     return dict(grid=grid, tiles=total, nk=nk, NT=NT)
 
 
-def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
+def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written):
     lane = np.arange(WAVE)
     WM = 1 if bm == 16 else 2
     WN = 8 // WM
@@ -228,14 +237,15 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
     bn_out = BN // 2 if la.swiglu else BN
     r0 = row_begin + r_off
     n0 = nt * bn_out
-    st = stage_bytes(bm)
+    st = stage_bytes(bm, la.fp4)
     a_instr = bm // ROWS_PER_INSTR
     a_per_wave = cdiv(a_instr, L_WAVES)
     b_per_wave = BN // ROWS_PER_INSTR // L_WAVES
     k_extent = (nk - 1) * ROW_BYTES + 16        # bytes a lane reads past its offset over the K loop
-    assert st["count"] * st["bytes"] <= PIPE_BYTES
+    assert st["count"] * st["bytes"] <= (PIPE_BYTES_FP4 if la.fp4 else PIPE_BYTES)
 
-    a_base = g * la.a_group_stride * eb if la.uniform_rows else 0
+    a_base = byt(g * la.a_group_stride) if la.uniform_rows else 0
+    a_bytes = la.A_rows * byt(la.lda)
 
     def a_row_of(row):
         r = np.minimum(r0 + row, row_end - 1)
@@ -252,7 +262,7 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
             return half * la.N + np.minimum(n0 + wnb * (WTN // 2) + idx, la.N - 1)
         return np.minimum(n0 + rho, la.N - 1)
 
-    b_base = g * la.b_stride * eb
+    b_base = byt(g * la.b_stride)
     for lw in range(L_WAVES):
         for i in range(a_per_wave):
             instr = lw + L_WAVES * i
@@ -260,8 +270,8 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
                 continue
             row = instr * ROWS_PER_INSTR + lane // 8
             chunk = (lane % 8) ^ ((row >> 1) & 7)
-            voff = a_row_of(row) * la.lda * eb + chunk * 16
-            assert voff.min() >= 0 and a_base + voff.max() + k_extent <= la.A_rows * la.lda * eb, ("A", g, r0, bm)
+            voff = a_row_of(row) * byt(la.lda) + chunk * 16
+            assert voff.min() >= 0 and a_base + voff.max() + k_extent <= a_bytes, ("A", g, r0, bm)
             assert voff.max() + k_extent - 16 < 1 << 32
             lds = instr * 1024 + lane * 16
             assert lds.max() + 16 <= bm * ROW_BYTES, ("A LDS", bm)
@@ -269,26 +279,31 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, eb, written):
             instr = lw * b_per_wave + i
             rho = instr * ROWS_PER_INSTR + lane // 8
             chunk = (lane % 8) ^ ((rho >> 1) & 7)
-            voff = b_row_of(rho) * la.ldb * eb + chunk * 16
+            voff = b_row_of(rho) * byt(la.ldb) + chunk * 16
             assert voff.min() >= 0 and voff.max() + k_extent - 16 < 1 << 32
             assert b_base + voff.max() + k_extent <= la.b_bytes, ("B", g, nt)
             lds = bm * ROW_BYTES + instr * 1024 + lane * 16
             assert lds.max() + 16 <= st["data"], ("B LDS", bm)
         if la.mx:
-            as_instr, bs_instr = cdiv(bm, 64), BN // 64
+            sdw = st["sdw"]
+            as_grp, bs_grp = cdiv(bm, 64), BN // 64
+            as_instr, bs_instr = as_grp * sdw, bs_grp * sdw
             sc_per_wave = cdiv(as_instr + bs_instr, L_WAVES)
+            assert sc_per_wave <= 3
             for u in range(sc_per_wave):
                 q = lw + L_WAVES * u
                 if q < as_instr:
-                    off = a_row_of(q * 64 + lane) * la.lda_scale
-                    assert off.max() + (nk - 1) * 4 + 4 <= la.A_rows * la.lda_scale, ("A scale", g)
-                    lds = st["scale_a"] + q * 256 + lane * 4
+                    h, grp = divmod(q, as_grp)
+                    off = a_row_of(grp * 64 + lane) * la.lda_scale + 4 * h
+                    assert off.max() + (nk - 1) * 4 * sdw + 4 <= la.A_rows * la.lda_scale, ("A scale", g)
+                    lds = st["scale_a"] + h * st["scale_rows_a"] * 4 + grp * 256 + lane * 4
                     assert lds.max() + 4 <= st["scale_b"]
                 elif q < as_instr + bs_instr:
-                    rho = (q - as_instr) * 64 + lane
-                    off = g * la.b_scale_stride + b_row_of(rho) * la.ldb_scale
-                    assert off.max() + (nk - 1) * 4 + 4 <= la.b_scale_bytes, ("B scale", g)
-                    lds = st["scale_b"] + (q - as_instr) * 256 + lane * 4
+                    h, grp = divmod(q - as_instr, bs_grp)
+                    rho = grp * 64 + lane
+                    off = g * la.b_scale_stride + b_row_of(rho) * la.ldb_scale + 4 * h
+                    assert off.max() + (nk - 1) * 4 * sdw + 4 <= la.b_scale_bytes, ("B scale", g)
+                    lds = st["scale_b"] + h * BN * 4 + grp * 256 + lane * 4
                     assert lds.max() + 4 <= st["bytes"]
     # epilogue: LDS staging of the output tile, then 16-byte stores of valid rows and columns
     pitch = bn_out * la.c_esize + 16

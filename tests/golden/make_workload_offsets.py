@@ -1,5 +1,6 @@
 """Writes tests/golden/offsets_<workload>.txt: the expert group offsets of each full-size
-layer workload, from the oracle's routing and permutation of the workload's seeded inputs.
+layer workload and of the reduced workloads of the GPU layer tests, from the oracle's routing
+and permutation of the workload's seeded inputs.
 
 The host-side replay of the grouped GEMM's index math reads them, so the CPU tests check the
 launches the GPU path makes at these sizes without regenerating the inputs every run. Calls
@@ -18,7 +19,8 @@ import numpy as np  # noqa: E402
 import moe_inputs as mi  # noqa: E402
 from oracle import moe_oracle as O  # noqa: E402
 
-NAMES = ("dsv3", "dsv3_ep8", "mixtral", "qwen3")
+NAMES = ("dsv3", "dsv3_ep8", "mixtral", "qwen3", "small_softmax", "small_sigmoid", "small_mxfp8", "mid_mxfp8",
+         "small_mxfp4")
 
 
 def main():

@@ -196,6 +196,38 @@ def test_host_argument_errors_backward_and_quant(lib):
               None, 0, None) == L.MOE_ENOTSUP
 
 
+def test_host_argument_errors_mxfp4(lib):
+    """MXFP4 quantiser and E2M1 GEMM operands: every rejected argument returns its status
+    before anything is enqueued."""
+    from dropless_mixture_experts_device_amd import _lib as L
+    fake = ctypes.c_void_p(1 << 20)
+    q4 = L._lib.moe_group_quant_mxfp4
+    ok = [fake, L.MOE_BF16, 64, 256, 256, None, 0, fake, 128, fake, 8, None]
+    for i, v, want in ((3, 240, L.MOE_EINVAL), (4, 128, L.MOE_EINVAL), (1, L.MOE_E4M3, L.MOE_ENOTSUP),
+                       (8, 112, L.MOE_EINVAL), (10, 7, L.MOE_EINVAL), (7, None, L.MOE_EINVAL),
+                       (9, None, L.MOE_EINVAL), (0, None, L.MOE_EINVAL), (8, 136, L.MOE_EINVAL),
+                       (7, fake.value + 8, L.MOE_EINVAL), (5, fake, L.MOE_EINVAL), (2, -1, L.MOE_EINVAL)):
+        args = list(ok)
+        args[i] = v
+        assert q4(*args) == want, (i, v)
+    # nothing to do for zero rows, even with null buffers
+    assert q4(None, L.MOE_BF16, 0, 256, 256, None, 0, None, 128, None, 8, None) == L.MOE_OK
+    # E2M1 GEMM: K % 256, even element strides, no ragged-K mode, at most 1791 groups
+    a = L.MoeGemmArgs(G=4, offsets=fake.value, M=128, N=64, K=512, A=fake.value, a_dtype=L.MOE_E2M1, lda=512,
+                      A_rows=128, a_rows=None, B=fake.value, b_dtype=L.MOE_E2M1, ldb=512, b_group_stride=64 * 512,
+                      C=fake.value, c_dtype=L.MOE_BF16, ldc=64, epilogue=L.MOE_EPI_NONE, aux=None, ld_aux=0,
+                      a_scale=fake.value, lda_scale=16, b_scale=fake.value, ldb_scale=16,
+                      b_scale_group_stride=64 * 16, ragged_k=0, c_group_stride=0)
+    assert L._lib.moe_grouped_gemm(ctypes.byref(a), None, 0, None) == L.MOE_EWORKSPACE
+    for field, value, want in (("K", 384, L.MOE_EINVAL), ("lda", 513, L.MOE_EINVAL), ("ldb", 520, L.MOE_EINVAL),
+                               ("b_group_stride", 64 * 512 + 1, L.MOE_EINVAL), ("ragged_k", 1, L.MOE_ENOTSUP),
+                               ("G", 1792, L.MOE_ENOTSUP), ("a_scale", None, L.MOE_EINVAL),
+                               ("b_dtype", L.MOE_E4M3, L.MOE_ENOTSUP)):
+        bad = L.MoeGemmArgs.from_buffer_copy(a)
+        setattr(bad, field, value)
+        assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, field
+
+
 def test_binding_constants_match_header_enums():
     """Every enumerator of include/moe.h has the same value in the Python binding, and every
     workspace op id is answered (an unknown one returns 0)."""

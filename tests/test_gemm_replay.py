@@ -22,27 +22,30 @@ def _offsets(name):
     return np.array([int(v) for v in lines[0].split()], np.int64)
 
 
-def _gemm1(w, off, mx=False):
+def _gemm1(w, off, mx=False, fp4=False):
     """GEMM 1 (gate/up + SwiGLU) as layer.py launches it: A = x [T, d] through src_token, B =
-    W_gu [G, 2f, d] (MXFP8: the row-wise codes and scales), C = H [rows, f]."""
+    W_gu [G, 2f, d] (MXFP8 / MXFP4: the row-wise codes and scales), C = H [rows, f]."""
     G = len(off) - 1
     rows = int(off[-1])
-    eb = 1 if mx else 2
+    mx = mx or fp4
+    eb = 0.5 if fp4 else 1 if mx else 2
     a_rows = np.arange(rows, dtype=np.int64) % w.T      # any in-range gather index
     return Launch(offsets=off, M=rows, N=w.f, K=w.d, A_rows=w.T, lda=w.d, a_rows=a_rows, b_groups=G,
-                  ldb=w.d, b_stride=2 * w.f * w.d, b_bytes=G * 2 * w.f * w.d * eb, ldc=w.f, c_esize=2, swiglu=True,
-                  mx=mx, lda_scale=w.d // 32, ldb_scale=w.d // 32, b_scale_stride=2 * w.f * w.d // 32,
-                  b_scale_bytes=G * 2 * w.f * w.d // 32, aux_ld=2 * w.f if mx else 0)
+                  ldb=w.d, b_stride=2 * w.f * w.d, b_bytes=int(G * 2 * w.f * w.d * eb), ldc=w.f, c_esize=2,
+                  swiglu=True, mx=mx, fp4=fp4, lda_scale=w.d // 32, ldb_scale=w.d // 32,
+                  b_scale_stride=2 * w.f * w.d // 32, b_scale_bytes=G * 2 * w.f * w.d // 32,
+                  aux_ld=2 * w.f if mx else 0)
 
 
-def _gemm2(w, off, mx=False):
+def _gemm2(w, off, mx=False, fp4=False):
     """GEMM 2 (down): A = H [rows, f], B = W_down [G, d, f], C = Y [rows, d]."""
     G = len(off) - 1
     rows = int(off[-1])
-    eb = 1 if mx else 2
+    mx = mx or fp4
+    eb = 0.5 if fp4 else 1 if mx else 2
     return Launch(offsets=off, M=rows, N=w.d, K=w.f, A_rows=rows, lda=w.f, a_rows=None, b_groups=G, ldb=w.f,
-                  b_stride=w.d * w.f, b_bytes=G * w.d * w.f * eb, ldc=w.d, c_esize=2, swiglu=False, mx=mx,
-                  lda_scale=w.f // 32, ldb_scale=w.f // 32, b_scale_stride=w.d * w.f // 32,
+                  b_stride=w.d * w.f, b_bytes=int(G * w.d * w.f * eb), ldc=w.d, c_esize=2, swiglu=False, mx=mx,
+                  fp4=fp4, lda_scale=w.f // 32, ldb_scale=w.f // 32, b_scale_stride=w.d * w.f // 32,
                   b_scale_bytes=G * w.d * w.f // 32)
 
 
@@ -87,6 +90,30 @@ def test_replay_full_size_mxfp8_step_gemms():
         check_launch(la)
 
 
+@pytest.mark.parametrize("name", ["dsv3", "qwen3"])
+def test_replay_full_size_mxfp4_forward_gemms(name):
+    """E2M1 operands: 256 K values per stage, two scale dwords per row, the larger LDS ring."""
+    w = mi.WORKLOADS[name]
+    off = _offsets(name)
+    check_launch(_gemm1(w, off, fp4=True))
+    check_launch(_gemm2(w, off, fp4=True))
+
+
+@pytest.mark.parametrize("name", ["small_softmax", "small_sigmoid", "small_mxfp8", "mid_mxfp8", "small_mxfp4"])
+def test_replay_reduced_layer_workloads(name):
+    """The GEMMs of the GPU layer tests at their reduced shapes, in each workload's format
+    (bf16 forward, the MXFP8 step's four GEMMs, the MXFP4 forward)."""
+    w = mi.WORKLOADS[name]
+    off = _offsets(name)
+    assert off[-1] == w.T * w.k + (w.T if w.shared_f else 0)
+    if w.mxfp8:
+        launches = [_gemm1(w, off, mx=True), _gemm2(w, off, mx=True), _dgrad(w, off, 2), _dgrad(w, off, 1)]
+    else:
+        launches = [_gemm1(w, off, fp4=w.mxfp4), _gemm2(w, off, fp4=w.mxfp4)]
+    for la in launches:
+        check_launch(la)
+
+
 GPU_TEST_SIZES = [[0, 1, 17, 33, 0, 65, 129, 300, 16, 32, 64, 128, 2], [513], [0, 0, 5]]
 
 
@@ -110,7 +137,7 @@ def _fuzz_sizes(g):
     return sizes.astype(np.int64)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_replay_fuzz_ragged_groups(seed):
     """Seeded random group layouts: every tile height, empty and one-row groups, sizes not a
     multiple of 32, up to 300 groups, SwiGLU or plain, bf16 or MXFP8, with or without a gather."""
@@ -118,19 +145,20 @@ def test_replay_fuzz_ragged_groups(seed):
     sizes = _fuzz_sizes(g)
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     G = len(sizes)
-    mx = bool(g.integers(0, 2))
+    fmt = int(g.integers(0, 3))                          # bf16, MXFP8, MXFP4
+    mx, fp4 = fmt > 0, fmt == 2
     swiglu = bool(g.integers(0, 2))
     N = int(g.choice([128, 256, 384, 1152] if mx else [64, 128, 136, 256, 520, 1024]))
-    K = int(g.choice([128, 256, 512, 1024] if mx else [64, 128, 320, 1024]))
+    K = int(g.choice([256, 512, 1024, 2048] if fp4 else [128, 256, 512, 1024] if mx else [64, 128, 320, 1024]))
     extra = int(g.integers(0, 40))
     M = int(off[-1]) + extra
     gather = bool(g.integers(0, 2))
     A_rows = int(g.integers(1, 3000)) if gather else max(M, 1)
     a_rows = g.integers(-5, A_rows + 5, M) if gather else None      # out-of-range entries are clamped
-    eb = 1 if mx else 2
+    eb = 0.5 if fp4 else 1 if mx else 2
     nb = 2 * N if swiglu else N
     la = Launch(offsets=off, M=M, N=N, K=K, A_rows=A_rows, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
-                b_stride=nb * K, b_bytes=G * nb * K * eb, ldc=N, c_esize=2, swiglu=swiglu, mx=mx,
+                b_stride=nb * K, b_bytes=int(G * nb * K * eb), ldc=N, c_esize=2, swiglu=swiglu, mx=mx, fp4=fp4,
                 lda_scale=K // 32, ldb_scale=K // 32, b_scale_stride=nb * K // 32, b_scale_bytes=G * nb * K // 32,
                 aux_ld=2 * N if swiglu else 0)
     if M == 0:
@@ -148,3 +176,25 @@ def test_replay_catches_an_out_of_range_gather_without_clamp(monkeypatch):
     monkeypatch.setattr(R.np, "clip", lambda a, lo, hi: a)
     with pytest.raises(AssertionError):
         check_launch(la)
+
+
+MX4_GPU_TEST_LAUNCHES = [([0, 1, 17, 33, 65, 129, 300, 2], 256, 512, 2, 5), ([700], 192, 256, 2, 5),
+                         ([5, 0, 90], 520, 2048, 2, 5), ([33, 0, 260, 1], 384, 1024, 0, 0),
+                         ([40, 0, 1, 200, 7, 129, 513], 384, 1024, 0, 0)]
+
+
+@pytest.mark.parametrize("sizes,N,K,extra_m,extra_a", MX4_GPU_TEST_LAUNCHES)
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_replay_mx4_gpu_test_shapes(sizes, N, K, extra_m, extra_a, gather, swiglu):
+    """The MXFP4 GEMM launches of the GPU tests (C rows beyond the groups, A rows beyond C's)."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    M = int(off[-1]) + extra_m
+    A_rows = M + extra_a
+    G = len(sizes)
+    nb = 2 * N if swiglu else N
+    a_rows = np.random.Generator(np.random.PCG64(2)).integers(0, A_rows, M) if gather else None
+    check_launch(Launch(offsets=off, M=M, N=N, K=K, A_rows=A_rows, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
+                        b_stride=nb * K, b_bytes=G * nb * K // 2, ldc=N, c_esize=4, swiglu=swiglu, mx=True, fp4=True,
+                        lda_scale=K // 32, ldb_scale=K // 32, b_scale_stride=nb * K // 32,
+                        b_scale_bytes=G * nb * K // 32))

@@ -238,3 +238,108 @@ def test_mx_output_moves_past_6e2_when_one_intermediate_moves_one_bf16_ulp():
                 yp = O.round_bf16(q @ WdQ.T)
                 worst = max(worst, float(np.max(np.abs(yp - Y[i]) / np.maximum(np.abs(Y[i]), rms))))
     assert worst > 6e-2, worst
+
+
+# ---- MXFP4 forward ([OCP-MX] E2M1 elements, E8M0 scale floor(log2 amax) - 2)
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def q4_block(vals):
+    """One MXFP4 block by brute force: scale 2^(floor(log2 amax) - 2) read off the block's
+    largest magnitude with math.frexp, every element the nearest signed grid value by
+    exhaustive search (ties to the grid value whose index is even, i.e. the even mantissa),
+    magnitudes past 6 saturating."""
+    vals = [float(v) for v in vals]
+    amax = max(abs(v) for v in vals)
+    if amax == 0.0:
+        return np.zeros(len(vals))
+    e = math.frexp(amax)[1] - 1 - 2
+    X = 2.0 ** e
+    out = []
+    for v in vals:
+        a = abs(v) / X
+        dist = [abs(a - g) for g in E2M1_GRID]
+        best = min(dist)
+        idx = [i for i, dd in enumerate(dist) if dd == best]
+        i = idx[0] if len(idx) == 1 else [j for j in idx if j % 2 == 0][0]
+        out.append(math.copysign(E2M1_GRID[i] * X, v))
+    return np.array(out)
+
+
+def q4_vec(vec):
+    vec = np.asarray(vec, np.float64)
+    return np.concatenate([q4_block(vec[s:s + BLK]) for s in range(0, len(vec), BLK)])
+
+
+def brute_mx4_forward(c: Case, wrong: str = ""):
+    """H and Y of the MXFP4 expert forward, element by element: G and U contract over d (X
+    rows and W_gu rows blocked along d), Y over f (H rows and W_down rows blocked along f).
+    `wrong`: "G:Wgu" blocks W_gu along 2f, "Y:H" blocks H along the tokens, "Y:Wd" blocks
+    W_down along d."""
+    m, d, f = c.m, c.d, c.f
+    Xq = [q4_vec(c.X[i]) for i in range(m)]
+    if wrong == "G:Wgu":
+        cols = [q4_vec(c.Wgu[:, j]) for j in range(d)]
+        Wguq = [np.array([cols[j][r] for j in range(d)]) for r in range(2 * f)]
+    else:
+        Wguq = [q4_vec(c.Wgu[r]) for r in range(2 * f)]
+    G = np.array([[dot(Xq[i], Wguq[n]) for n in range(f)] for i in range(m)])
+    U = np.array([[dot(Xq[i], Wguq[f + n]) for n in range(f)] for i in range(m)])
+    H = np.array([[rnd(silu(G[i, n]) * U[i, n]) for n in range(f)] for i in range(m)])
+    if wrong == "Y:H":
+        hc = [q4_vec(H[:, n]) for n in range(f)]
+        Hq = [np.array([hc[n][i] for n in range(f)]) for i in range(m)]
+    else:
+        Hq = [q4_vec(H[i]) for i in range(m)]
+    if wrong == "Y:Wd":
+        wc = [q4_vec(c.Wd[:, n]) for n in range(f)]
+        Wdq = [np.array([wc[n][e] for n in range(f)]) for e in range(d)]
+    else:
+        Wdq = [q4_vec(c.Wd[e]) for e in range(d)]
+    Y = np.array([[rnd(dot(Hq[i], Wdq[e])) for e in range(d)] for i in range(m)])
+    return dict(H=H, Y=Y)
+
+
+@pytest.fixture(scope="module")
+def mx4_case():
+    c = Case(m=40, seed=11)
+    H, Y = O.expert_forward(c.X, c.Wgu, c.Wd, O.round_bf16, mx4=True)
+    return c, dict(H=H, Y=Y)
+
+
+def test_mx4_forward_composition_matches_blockwise_brute_force(mx4_case):
+    c, ref = mx4_case
+    bf = brute_mx4_forward(c)
+    np.testing.assert_array_equal(ref["H"], bf["H"])
+    np.testing.assert_array_equal(ref["Y"], bf["Y"])
+
+
+@pytest.mark.parametrize("wrong,tensor", [("G:Wgu", "H"), ("Y:H", "Y"), ("Y:Wd", "Y")])
+def test_mx4_forward_wrong_axis_is_detected(mx4_case, wrong, tensor):
+    c, ref = mx4_case
+    alt = brute_mx4_forward(c, wrong)
+    assert not np.array_equal(alt[tensor], ref[tensor]), f"{wrong} left {tensor} unchanged"
+
+
+def test_mx4_layer_forward_uses_the_fp4_quantiser():
+    """The layer forward's MXFP4 flag reaches every expert: its Y rows equal the per-expert
+    MXFP4 forward on the gathered rows, and differ from the MXFP8 layer's."""
+    g = np.random.Generator(np.random.PCG64(13))
+    T, d, f, E = 24, 64, 32, 3
+    X = O.round_bf16(g.standard_normal((T, d)))
+    Wgu = O.round_bf16(g.standard_normal((E, 2 * f, d)) * 0.02)
+    Wd = O.round_bf16(g.standard_normal((E, d, f)) * 0.02)
+    idx = (np.arange(T) % E).astype(np.int32)[:, None]
+    w = np.ones((T, 1))
+    kw = dict(rnd=O.round_bf16, topk=(idx, w))
+    f4 = O.layer_forward(X, None, None, 1, "softmax", lambda e: Wgu[e], lambda e: Wd[e], E, mx4=True, **kw)
+    f8 = O.layer_forward(X, None, None, 1, "softmax", lambda e: Wgu[e], lambda e: Wd[e], E, mx=True, **kw)
+    off = f4["offsets"]
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        c = Case.__new__(Case)
+        c.m, c.d, c.f = hi - lo, d, f
+        c.X, c.Wgu, c.Wd = X[f4["src_token"][lo:hi]], Wgu[e], Wd[e]
+        np.testing.assert_array_equal(f4["Y"][lo:hi], brute_mx4_forward(c)["Y"])
+    assert not np.array_equal(f4["Y"], f8["Y"])
