@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 
 
 def parse():
@@ -193,13 +194,14 @@ def gemm1_bytes(w, counts, fused):
 CPU_BUDGET_S = 25.0
 
 
-def cpu_baseline(w, w_gu_dev, w_down_dev):
+def cpu_baseline(w, w_gu_dev, w_down_dev, mx4=False):
     """The oracle's forward (fp64 numpy, as it stands) on the host cores: routing, the
     permutation and gather of all T tokens, then the SwiGLU experts one group at a time in a
     spread order (0, 16, 32, ..., then 8, 24, ...), the shared expert on all tokens, and the
     combine, until about CPU_BUDGET_S seconds of oracle time are spent. Each expert's weights
     are copied off the GPU (same generator, same values) outside the timed region. Reported
-    in useful TFLOPS of the groups it finished."""
+    in useful TFLOPS of the groups it finished. mx4: the oracle's MXFP4 forward (every GEMM
+    operand through its row-wise MXFP4 quantiser, the weights' quantisation included)."""
     import moe_inputs as mi
     from oracle import moe_oracle as O
     try:
@@ -229,7 +231,7 @@ def cpu_baseline(w, w_gu_dev, w_down_dev):
         gu = w_gu_dev[g].float().cpu().numpy()
         dn = w_down_dev[g].float().cpu().numpy()
         t0 = time.perf_counter()
-        _, Y[lo:hi] = O.expert_forward(xp[lo:hi], gu, dn, O.round_bf16)
+        _, Y[lo:hi] = O.expert_forward(xp[lo:hi], gu, dn, O.round_bf16, mx4=mx4)
         spent += time.perf_counter() - t0
         flops += 6.0 * (hi - lo) * w.d * (gu.shape[0] // 2)
     whole = done == len(groups)
@@ -243,7 +245,8 @@ def cpu_baseline(w, w_gu_dev, w_down_dev):
             f"{CPU_BUDGET_S:.0f} s; no combine")
     return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
             "seconds": round(spent, 2), "host": host_info(),
-            "sample": f"fp64 numpy oracle on {what}; value = useful FLOPs of the finished groups / oracle time"}
+            "sample": f"fp64 numpy {'MXFP4 ' if mx4 else ''}oracle on {what}; value = useful FLOPs of the "
+                      f"finished groups / oracle time"}
 
 
 def mx_gemm_work(w, rows, nonempty):
@@ -420,6 +423,133 @@ def main_mx(args, w):
     print(json.dumps(res), flush=True)
 
 
+def mx4_gemm_work(w, rows, nonempty):
+    """Algorithmic HBM bytes and FLOPs of the two MXFP4 GEMMs of the forward: E2M1 operands at
+    half a byte per element plus one scale byte per 32 (weights of non-empty groups and the
+    shared expert once, x once through the fused gather), bf16 outputs written once, the
+    gather index read once."""
+    d, f = w.d, w.f
+    q = 0.5 + 1.0 / 32.0
+    return {
+        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + rows * f * 2 + rows * 4, 2.0 * rows * d * 2 * f),
+        "gemm2": (nonempty * d * f * q + rows * f * q + rows * d * 2, 2.0 * rows * f * d),
+    }
+
+
+def main_mx4(args, w):
+    """The MXFP4 layer forward. The expert weights are quantised once before the timed steps
+    (a forward-only layer's weights do not change between calls); x and H are quantised
+    inside every step."""
+    import torch
+    import moe_inputs as mi
+    from dropless_mixture_experts_device_amd import _lib as L
+    from dropless_mixture_experts_device_amd import layer
+
+    torch.cuda.init()
+    dev = "cuda"
+    x = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.X, 0, w.T, w.d, w.sigma_x, w.dtype, dev, out=x)
+    wr = torch.empty((w.E, w.d), dtype=torch.bfloat16, device=dev)
+    mi.randn_torch(w.seed, mi.W_ROUTER, 0, w.E, w.d, w.sigma_w, w.dtype, dev, out=wr)
+    b0 = mi.expert_bias(w)
+    bias = None if b0 is None else torch.from_numpy(b0).to(dev)
+    n = w.E + (1 if w.shared_f else 0)
+    w_gu = torch.empty((n, 2 * w.f, w.d), dtype=torch.bfloat16, device=dev)
+    w_down = torch.empty((n, w.d, w.f), dtype=torch.bfloat16, device=dev)
+    mi.fill_weights_torch(w, w_gu, w_down, dev)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.Mx4Weights(s, dev)
+    b = layer.Mx4Buffers(s, dev)
+    stream = torch.cuda.current_stream()
+    # the weights' quantisation, timed on its own (not part of a step)
+    mw.quantise(w_gu, w_down)
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record(stream)
+    mw.quantise(w_gu, w_down)
+    q1.record(stream)
+    torch.cuda.synchronize()
+    wq_ms = q0.elapsed_time(q1)
+
+    def step(rec=None):
+        mark = None
+        if rec is not None:
+            def mark(name):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                rec.append((name, e))
+            mark("start")
+        layer.forward_mx4(x, wr, bias, mw, s, b, mark=mark)
+
+    flush = CacheFlush(dev)
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    recs = [[] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush()
+        step(recs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = [nm for nm, _ in recs[0][1:]]
+    per = np.array([[r[j][1].elapsed_time(r[j + 1][1]) for j in range(len(r) - 1)] for r in recs])
+    pm = dict(zip(names, np.median(per, axis=0)))
+    step_all = np.array([r[0][1].elapsed_time(r[-1][1]) for r in recs])
+    ms = float(np.median(step_all))
+    graph_ms = time_graph(step, args.steps, flush)
+    counts = np.diff(b.offsets.cpu().numpy())[:w.E]
+    flops = useful_flops(w, counts)
+    nonempty = int(np.count_nonzero(counts)) + (1 if w.shared_f else 0)
+    work = mx4_gemm_work(w, s.rows, nonempty)
+    dom = max(work, key=lambda k: pm[k])
+    by, fl = work[dom]
+    t = pm[dom] * 1e-3
+    t_hbm, t_mfma = by / (HBM_PEAK_GBS * 1e9), fl / (FP4_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(by / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fl / t / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": pmc_traffic(w.name, dom), "kernel": f"moe_grouped_gemm MXFP4 {dom}",
+                 "algorithmic_bytes": int(by), "algorithmic_flops": fl, "ms": round(pm[dom], 4),
+                 "mfma_frac": round(fl / t / 1e12 / FP4_PEAK_TFLOPS, 4),
+                 "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)})
+    gemm_ms = sum(pm[k] for k in work)
+    res = {
+        "metric": "MoE layer forward TFLOPS (useful FLOPs) + tokens/s, DSv3-shaped MXFP4 forward",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e2m1 (MXFP4, E8M0/32)",
+        "data": "synthetic (seeded hash-table normal inputs, Zipf expert-bias skew; random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "score": w.score,
+                   "shared_f": w.shared_f, "weights": "quantised to MXFP4 once, before the timed steps",
+                   "groups_nonempty": int(np.count_nonzero(counts)), "group_max": int(counts.max()),
+                   "group_min": int(counts.min()), "groups_empty": int((counts == 0).sum())},
+        "timing": ("median over the timed steps of HIP events on the launching stream; every timed step "
+                   f"starts after a {FLUSH_BYTES >> 20} MiB read of a scratch buffer outside the events"),
+        "step_ms": spread(step_all),
+        "wall_ms_per_step_incl_flush": round(wall_ms, 4),
+        "graph_ms_per_step": spread(graph_ms),
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "weight_quant_ms": round(wq_ms, 4),
+        "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: spread(per[:, j]) for j, k in enumerate(names)},
+        "gemm_tflops_by_stage": {k: round(work[k][1] / (pm[k] * 1e-3) / 1e12, 1) for k in work},
+        "gemm_gbs_by_stage": {k: round(work[k][0] / (pm[k] * 1e-3) / 1e9, 1) for k in work},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, w_gu, w_down, mx4=True)
+    print(json.dumps(res), flush=True)
+
+
 # Workloads that were benchmarked together in one GPU run that ended in a GPU memory fault;
 # which of them faulted, and why, is not known, so none of them is run until the cause is.
 HELD_WORKLOADS = ("dsv3_ep8", "mixtral", "qwen3")
@@ -444,6 +574,8 @@ def main():
     w = mi.WORKLOADS[args.workload]
     if w.mxfp8:
         return main_mx(args, w)
+    if w.mxfp4:
+        return main_mx4(args, w)
     assert w.dtype == "bf16", "bench times the bf16 layer workloads"
     torch.cuda.init()
     dev = "cuda"

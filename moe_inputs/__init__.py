@@ -213,6 +213,8 @@ def expert_bias(w: Workload) -> Optional[np.ndarray]:
     linear: beta * (e / (E - 1) - 1/2), a mild monotone skew.
     zipf:   -lam * s * ln(rank(e)), rank(e) in 1..E a seeded permutation of the experts, so
             exp(bias) follows a Zipf(s) law over expert rank; lam scales its strength.
+    dead:   -30 on a seeded set of n experts, 0 elsewhere: those experts are never selected
+            while at least k others remain (forced empty groups).
     """
     if w.bias is None:
         return None
@@ -224,9 +226,48 @@ def expert_bias(w: Workload) -> Optional[np.ndarray]:
         s, lam = w.bias[1], w.bias[2]
         rank = np.random.Generator(np.random.PCG64(w.seed + 1000)).permutation(w.E) + 1
         b = -lam * s * np.log(rank.astype(np.float64))
+    elif kind == "dead":
+        dead = np.random.Generator(np.random.PCG64(w.seed + 1000)).permutation(w.E)[:w.bias[1]]
+        b = np.zeros(w.E)
+        b[dead] = -30.0
     else:
         raise ValueError(kind)
     return b.astype(np.float32)
+
+
+def fuzz_workloads(n: int = 14, seed: int = 4242) -> list:
+    """A seeded sweep of layer shapes over the edges the method has: E in 1..256, k in
+    1..min(8, E), T in 1..9000 (log-uniform), softmax or sigmoid, with or without a shared
+    expert, skew-free, Zipf-skewed or with a forced set of experts that receive nothing (empty
+    groups); d and f multiples of 64; group sizes fall anywhere, mostly not multiples of 32.
+    One in seven shapes is fp32. Sizes stay small enough for the oracle to finish in seconds."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        E = int(g.choice([1, 2, 3, 5, 8, 13, 32, 64, 100, 128, 200, 256]))
+        k = int(g.integers(1, min(8, E) + 1))
+        T = int(round(math.exp(g.uniform(0.0, math.log(9000.0)))))
+        d = int(g.choice([64, 128, 192, 320, 512]))
+        f = int(g.choice([64, 128, 192, 256, 384]))
+        if T * k * d * f > 2e9:                       # keep the oracle's work to a few seconds
+            f = 64
+        score = "softmax" if g.integers(0, 2) == 0 else "sigmoid"
+        kind = int(g.integers(0, 3))
+        if kind == 1:
+            bias = ("zipf", float(g.uniform(0.8, 1.4)), float(g.uniform(0.5, 2.0)))
+        elif kind == 2 and E - k >= 1:
+            bias = ("dead", int(g.integers(1, E - k + 1)))
+        else:
+            bias = None
+        shared = f if g.integers(0, 2) == 0 else 0
+        dtype = "f32" if i % 7 == 6 else "bf16"
+        out.append(Workload(f"fuzz{i}", T, d, f, E, k, dtype, score, bias, shared, seed=100 + i))
+    # the ends of the ranges: one expert taking all 9000 tokens; one token; 256 experts with
+    # most of them dead, on the router's split-K path (T >= 256, E % 8 == 0, d % 256 == 0)
+    out.append(Workload("fuzz_e1", 9000, 128, 128, 1, 1, "bf16", "softmax", None, 0, seed=201))
+    out.append(Workload("fuzz_t1", 1, 64, 64, 64, 8, "bf16", "sigmoid", None, 64, seed=202))
+    out.append(Workload("fuzz_wide", 3000, 512, 128, 256, 8, "bf16", "sigmoid", ("dead", 200), 128, seed=203))
+    return out
 
 
 def x_np(w: Workload, rows=None) -> np.ndarray:

@@ -198,3 +198,19 @@ def test_replay_mx4_gpu_test_shapes(sizes, N, K, extra_m, extra_a, gather, swigl
                         b_stride=nb * K, b_bytes=G * nb * K // 2, ldc=N, c_esize=4, swiglu=swiglu, mx=True, fp4=True,
                         lda_scale=K // 32, ldb_scale=K // 32, b_scale_stride=nb * K // 32,
                         b_scale_bytes=G * nb * K // 32))
+
+
+@pytest.mark.parametrize("w", [w for w in mi.fuzz_workloads() if w.dtype == "bf16"], ids=lambda w: w.name)
+def test_replay_layer_sweep(w):
+    """The GEMM launches of the seeded layer-shape sweep run on the GPU (group offsets from the
+    oracle's routing of the same inputs, which the GPU's routing equals away from near-ties;
+    the fuzz above covers arbitrary layouts): both expert GEMMs and, where the router takes
+    the K-split path, its projection."""
+    from oracle import moe_oracle as O
+    idx, _, _ = O.route(mi.x_np(w), mi.w_router_np(w), mi.expert_bias(w), w.k, w.score)
+    off, _, _ = O.permutation(idx, w.E, w.T if w.shared_f else 0)
+    off = np.asarray(off, np.int64)
+    check_launch(_gemm1(w, off))
+    check_launch(_gemm2(w, off))
+    if w.T >= 256 and w.E % 8 == 0 and w.d % 256 == 0:
+        check_launch(_router(w))
