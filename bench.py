@@ -252,11 +252,12 @@ def cpu_baseline(w, w_gu_dev, w_down_dev, mx4=False):
 def mx_gemm_work(w, rows, nonempty):
     """Algorithmic HBM bytes and FLOPs of each MXFP8 GEMM of the step: E4M3 operands with one
     scale byte per 32 elements read once (weights of non-empty groups only), bf16 outputs
-    written once (GEMM 1 also writes the saved gate/up pre-activations)."""
+    written once; GEMM 1 writes the saved gate/up pre-activations and H's two MXFP8 copies
+    (row-wise and column-wise, quantised in its epilogue) instead of a bf16 H."""
     d, f, G = w.d, w.f, w.E + (1 if w.shared_f else 0)
     q = 33.0 / 32.0
     return {
-        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + rows * f * 2 + rows * 2 * f * 2 + rows * 4,
+        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + 2 * rows * f * q + rows * 2 * f * 2 + rows * 4,
                          2.0 * rows * d * 2 * f),
         "gemm2": (nonempty * d * f * q + rows * f * q + rows * d * 2, 2.0 * rows * f * d),
         "dgrad2": (nonempty * f * d * q + rows * d * q + rows * f * 2, 2.0 * rows * d * f),
@@ -349,7 +350,7 @@ def main_mx(args, w):
         mw.quantise(w_gu, w_down)
         if mark:
             mark("weight_quant")
-        layer.forward_mx(x, wr, bias, mw, s, b, mark=mark)
+        layer.forward_mx(x, wr, bias, mw, s, b, mark=mark, write_h=False)
         layer.backward_mx(x, d_out, mw, s, b, mark=mark, w_router=wr)
 
     flush = CacheFlush(dev)
@@ -426,12 +427,12 @@ def main_mx(args, w):
 def mx4_gemm_work(w, rows, nonempty):
     """Algorithmic HBM bytes and FLOPs of the two MXFP4 GEMMs of the forward: E2M1 operands at
     half a byte per element plus one scale byte per 32 (weights of non-empty groups and the
-    shared expert once, x once through the fused gather), bf16 outputs written once, the
-    gather index read once."""
+    shared expert once, x once through the fused gather), GEMM 1's output as the MXFP4 codes
+    its epilogue writes, GEMM 2's bf16 output once, the gather index read once."""
     d, f = w.d, w.f
     q = 0.5 + 1.0 / 32.0
     return {
-        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + rows * f * 2 + rows * 4, 2.0 * rows * d * 2 * f),
+        "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + rows * f * q + rows * 4, 2.0 * rows * d * 2 * f),
         "gemm2": (nonempty * d * f * q + rows * f * q + rows * d * 2, 2.0 * rows * f * d),
     }
 
@@ -479,7 +480,7 @@ def main_mx4(args, w):
                 e.record(stream)
                 rec.append((name, e))
             mark("start")
-        layer.forward_mx4(x, wr, bias, mw, s, b, mark=mark)
+        layer.forward_mx4(x, wr, bias, mw, s, b, mark=mark, write_h=False)
 
     flush = CacheFlush(dev)
     for _ in range(args.warmup):

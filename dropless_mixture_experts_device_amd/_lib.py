@@ -35,6 +35,8 @@ class MoeGemmArgs(ctypes.Structure):
         ("epilogue", _i32), ("aux", _vp), ("ld_aux", _i64),
         ("a_scale", _vp), ("lda_scale", _i64), ("b_scale", _vp), ("ldb_scale", _i64), ("b_scale_group_stride", _i64),
         ("ragged_k", _i32), ("c_group_stride", _i64),
+        ("q_dtype", _i32), ("q_row", _vp), ("ld_q_row", _i64), ("s_row", _vp), ("ld_s_row", _i64),
+        ("q_col", _vp), ("s_col", _vp), ("q_block_start", _vp), ("q_col_blocks", _i64),
     ]
 
 
@@ -147,7 +149,9 @@ def moe_permute(x, topk_idx, E: int, shared_group: bool, offsets, row_of, src_to
 
 
 def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None, aux=None, workspace=None,
-                     stream=None, a_scale=None, b_scale=None, ragged_k: bool = False, fp4: bool = False):
+                     stream=None, a_scale=None, b_scale=None, ragged_k: bool = False, fp4: bool = False,
+                     q_row=None, s_row=None, q_col=None, s_col=None, q_block_start=None, q_fp4: bool = False,
+                     out_shape=None):
     """One launch over all groups.
 
     Ragged rows (default): C[rows of g] = A[a_rows or rows of g] @ B[g]^T (SWIGLU: silu(gate)
@@ -156,6 +160,9 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
     int32 [M]. MXFP8: A and B are uint8 E4M3 codes with a_scale [A_rows, K/32] and b_scale
     [G, N_B, K/32] uint8 E8M0 bytes. fp4 (MXFP4): A [A_rows, K/2] and B [G, N_B, K/2] uint8
     hold E2M1 codes two per byte (K counts elements, strides are passed in elements).
+    Fused output quantisation: q_row / s_row (uint8) receive the row-wise MXFP8 (q_fp4: MXFP4,
+    packed) copy of the bf16 output, q_col / s_col / q_block_start the group-aware column-wise
+    MXFP8 copy (as moe_group_quant_mxfp8 axis 1). C may then be None, with out_shape = (M, N).
     ragged_k: C [G, M, N], C[g] = A_g @ B_g^T over group g's offsets[g] .. offsets[g+1]-1
     blocks of 32 K elements, A, B, a_scale, b_scale being the column-wise quantiser's
     group-major output buffers (capacities [M, K], [N, K], [M, K/32], [N, K/32]).
@@ -175,7 +182,7 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
             ragged_k=1, c_group_stride=C.stride(0))
     else:
         G = B.shape[0]
-        M, N = C.shape
+        M, N = C.shape if C is not None else out_shape
         per = 2 if fp4 else 1                # elements per stored byte
         if fp4 and (A.dtype != torch.uint8 or B.dtype != torch.uint8):
             raise TypeError("MXFP4 operands are uint8 tensors of packed E2M1 codes")
@@ -187,14 +194,21 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
             a_rows=None if a_rows is None else a_rows.data_ptr(),
             B=B.data_ptr(), b_dtype=MOE_E2M1 if fp4 else _dtype(B), ldb=B.stride(1) * per,
             b_group_stride=B.stride(0) * per,
-            C=C.data_ptr(), c_dtype=_dtype(C), ldc=C.stride(0),
+            C=None if C is None else C.data_ptr(), c_dtype=MOE_BF16 if C is None else _dtype(C),
+            ldc=N if C is None else C.stride(0),
             epilogue=epilogue, aux=None if aux is None else aux.data_ptr(),
             ld_aux=0 if aux is None else aux.stride(0),
             a_scale=None if a_scale is None else a_scale.data_ptr(),
             lda_scale=0 if a_scale is None else a_scale.stride(0),
             b_scale=None if b_scale is None else b_scale.data_ptr(),
             ldb_scale=0 if b_scale is None else b_scale.stride(1),
-            b_scale_group_stride=0 if b_scale is None else b_scale.stride(0), ragged_k=0, c_group_stride=0)
+            b_scale_group_stride=0 if b_scale is None else b_scale.stride(0), ragged_k=0, c_group_stride=0,
+            q_dtype=0 if q_row is None else (MOE_E2M1 if q_fp4 else MOE_E4M3),
+            q_row=None if q_row is None else q_row.data_ptr(), ld_q_row=0 if q_row is None else q_row.stride(0),
+            s_row=None if s_row is None else s_row.data_ptr(), ld_s_row=0 if s_row is None else s_row.stride(0),
+            q_col=None if q_col is None else q_col.data_ptr(), s_col=None if s_col is None else s_col.data_ptr(),
+            q_block_start=None if q_block_start is None else q_block_start.data_ptr(),
+            q_col_blocks=0 if s_col is None else s_col.shape[1])
     ws, wsb = _ws(workspace)
     _check("moe_grouped_gemm", _lib.moe_grouped_gemm(ctypes.byref(args), ws, wsb, _stream(stream)))
 

@@ -30,6 +30,7 @@
 #include <utility>
 
 #include "moe_internal.h"
+#include "mx_math.h"
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -217,6 +218,19 @@ struct GemmParams {
     // row index or schedule are read
     int uniform_rows;
     int64_t a_group_stride;
+    // fused output quantisation (ragged rows, bf16 C; 0 = off): the epilogue quantises the
+    // bf16-rounded tile it writes, row-wise into q_row / s_row and (E4M3, when q_col is given)
+    // group-aware column-wise into q_col / s_col at the blocks q_bs gives each group
+    int q_fmt;                   // 0, kE4M3 or kE2M1
+    uint8_t* q_row;
+    int64_t ld_q_row;            // bytes
+    uint8_t* s_row;
+    int64_t ld_s_row;
+    uint8_t* q_col;
+    uint8_t* s_col;
+    const int32_t* q_bs;         // [G+1] column-wise block prefix, written by the schedule kernel
+    int64_t q_col_blocks;        // capacity of q_col / s_col in blocks
+    int c_skip;                  // C is not written (only its quantised copies)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -232,7 +246,8 @@ struct GemmParams {
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
                                                              int NT, int allow256, int32_t* __restrict__ tile_start,
-                                                             int32_t* __restrict__ order) {
+                                                             int32_t* __restrict__ order,
+                                                             int32_t* __restrict__ block_start = nullptr) {
     __shared__ unsigned long long key[2048];
     __shared__ int tiles_of[2048];
     __shared__ int sorted[2048];
@@ -336,6 +351,36 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
         __syncthreads();
     }
     if (tid == 0) tile_start[G] = (int)carry_s;
+    if (block_start == nullptr) return;
+    // the column-wise quantisation's block prefix: group g owns 4 ceil(m_g / 128) blocks of 32
+    // rows starting at block_start[g] (group order, the layout of moe_group_quant_mxfp8 axis 1)
+    __syncthreads();
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int h = 0; h < 2; ++h) {
+        const int g = h * 1024 + tid;
+        int nb = 0;
+        if (g < G) {
+            int b, e;
+            group_rows(offsets, g, M, b, e);
+            nb = 4 * cdiv(e - b, 128);
+        }
+        int incl = nb;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += o;
+        }
+        if (lane == kWave - 1) wsum[wave] = (unsigned long long)incl;
+        __syncthreads();
+        int base = (int)carry_s;
+        for (int w = 0; w < wave; ++w) base += (int)wsum[w];
+        if (g < G) block_start[g] = base + incl - nb;
+        __syncthreads();
+        if (tid == 1023) carry_s = (unsigned long long)(base + incl);
+        __syncthreads();
+    }
+    if (tid == 0) block_start[G] = (int)carry_s;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -496,6 +541,119 @@ __device__ __forceinline__ typename Mfma<MS, FMT>::acc_t acc_zero() {
 #pragma unroll
     for (int r = 0; r < Mfma<MS, FMT>::NACC; ++r) z[r] = 0.f;
     return z;
+}
+
+// ---------------------------------------------------------------------------------------
+// fused output quantisation: the epilogue's bf16 tile (LDS, `pitch` bytes per row, rows
+// [0, rows_valid) valid, BN_OUT columns from n0) quantised as the standalone quantisers would
+// quantise the stored output: row-wise blocks of 32 columns (E4M3 codes or packed E2M1 codes,
+// one scale byte each) and, for E4M3 with q_col, the group-aware column-wise blocks of 32 rows.
+// A tile starts on a multiple of 128 rows of its group, so it owns whole column-wise blocks:
+// the 4 (BM <= 128) or 8 (BM = 256) blocks from r_off / 32, those past the group's last row
+// written as zeros (codes 0, scale 0), as the standalone pass writes them.
+// ---------------------------------------------------------------------------------------
+template <int BM, int BN_OUT>
+__device__ __forceinline__ void quant_epilogue(const GemmParams& p, const char* lds, int pitch, int g, int r0,
+                                               int r_off, int rows_valid, int n0, int tid) {
+    constexpr int RB = BN_OUT / 32;            // row-wise blocks per tile row
+    const bool fp4 = p.q_fmt == kE2M1;
+    for (int t = tid; t < BM * RB; t += kThreads) {
+        const int row = t / RB, blk = t % RB;
+        const int col = n0 + blk * 32;
+        if (row >= rows_valid || col >= p.N) continue;    // N % 32 == 0: a block is whole or absent
+        const char* src = lds + row * pitch + blk * 64;
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[c * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+                v[c * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const int64_t r = (int64_t)(r0 + row);
+        if (fp4) {
+            const uint32_t byte = mx4_scale_byte(amax);
+            const float inv = mx_inv_scale(byte);
+            u32x4 out;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) word |= e2m1_code(v[w * 8 + i] * inv) << (4 * i);
+                out[w] = word;
+            }
+            *reinterpret_cast<u32x4*>(p.q_row + r * p.ld_q_row + col / 2) = out;
+            p.s_row[r * p.ld_s_row + col / 32] = (uint8_t)byte;
+        } else {
+            const uint32_t byte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(byte);
+            u32x4 out[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* e = v + h * 16 + w * 4;
+                    out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+                }
+            uint8_t* dst = p.q_row + r * p.ld_q_row + col;
+            *reinterpret_cast<u32x4*>(dst) = out[0];
+            *reinterpret_cast<u32x4*>(dst + 16) = out[1];
+            p.s_row[r * p.ld_s_row + col / 32] = (uint8_t)byte;
+        }
+    }
+    if (fp4 || p.q_col == nullptr) return;
+    // column-wise: thread t takes block blk of the column pair cp (LDS reads of 4 bytes = two
+    // columns); the 4 (8) threads of one column pair are adjacent lanes, so a column's 128
+    // (256) code bytes go out as whole lines
+    constexpr int NBT = BM <= 128 ? 4 : 8;     // column-wise blocks the tile owns
+    const int bs0 = p.q_bs[g];
+    const int nbg = p.q_bs[g + 1] - bs0;
+    const int jb0 = r_off / 32;
+    if (bs0 < 0 || nbg < jb0 + NBT || (int64_t)bs0 + nbg > p.q_col_blocks) return;   // never for consistent offsets
+    const int64_t N = p.N;
+    uint8_t* qg = p.q_col + 32 * N * bs0;
+    uint8_t* sg = p.s_col + N * bs0;
+    for (int t = tid; t < (BN_OUT / 2) * NBT; t += kThreads) {
+        const int cp = t / NBT, blk = t % NBT;
+        const int col = n0 + 2 * cp;
+        if (col >= p.N) continue;                 // N even: both columns or neither
+        uint32_t pair[32];                         // rows' bf16 pairs (column col in the low half)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int row = blk * 32 + i;
+            pair[i] = row < rows_valid ? *reinterpret_cast<const uint32_t*>(lds + row * pitch + cp * 4) : 0u;
+        }
+        const int jb = jb0 + blk;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(half ? (pair[i] & 0xFFFF0000u) : (pair[i] << 16));
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            const uint32_t byte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(byte);
+            u32x4 out[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* e = v + h * 16 + w * 4;
+                    out[h][w] = pack4_e4m3(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+                }
+            const int64_t c = col + half;
+            uint8_t* dst = qg + c * 32 * nbg + (int64_t)jb * 32;
+            *reinterpret_cast<u32x4*>(dst) = out[0];
+            *reinterpret_cast<u32x4*>(dst + 16) = out[1];
+            sg[c * nbg + jb] = (uint8_t)byte;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -904,6 +1062,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     lds_barrier();
     const int chunks_per_row = BN_OUT * esize / 16;
     const int cols_per_chunk = 16 / esize;
+    // (block-scaled operand kernels only: the bf16 kernels' register budget has no room for it)
+    if constexpr (!RK && MX) {
+        if (p.q_fmt != 0) quant_epilogue<BM, BN_OUT>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid);
+        if (p.c_skip) return;
+    }
     for (int c = tid; c < BM * chunks_per_row; c += kThreads) {
         const int row = c / chunks_per_row, ch = c % chunks_per_row;
         const int col = n0 + ch * cols_per_chunk;
@@ -1332,10 +1495,36 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         if (a->lda != a->K || a->ldb != a->K || a->lda_scale != a->K / 32 || a->ldb_scale != a->K / 32)
             return MOE_EINVAL;
     }
+    // fused output quantisation: ragged rows, bf16 output, whole 32-column blocks
+    const bool quant = a->q_dtype != 0;
+    if (quant) {
+        if (a->q_dtype != MOE_E4M3 && a->q_dtype != MOE_E2M1) return MOE_ENOTSUP;
+        if (a->ragged_k || a->c_dtype != MOE_BF16 || (a->a_dtype != MOE_E4M3 && a->a_dtype != MOE_E2M1))
+            return MOE_ENOTSUP;
+        if (a->q_col && a->q_dtype != MOE_E4M3) return MOE_ENOTSUP;
+        if (a->N % 32 != 0) return MOE_EINVAL;
+    } else if (a->q_row || a->s_row || a->q_col || a->s_col || a->q_block_start) {
+        return MOE_EINVAL;
+    }
     if (a->M == 0) return MOE_OK;
-    if (!a->A || !a->B || !a->C || a->A_rows <= 0) return MOE_EINVAL;
+    if (!a->A || !a->B || (!a->C && !quant) || a->A_rows <= 0) return MOE_EINVAL;
+    if (quant) {
+        const int64_t row_bytes = a->q_dtype == MOE_E2M1 ? a->N / 2 : a->N;
+        if (!a->q_row || !a->s_row || !moe_aligned16(a->q_row) || a->ld_q_row < row_bytes || a->ld_q_row % 16 ||
+            a->ld_s_row < a->N / 32)
+            return MOE_EINVAL;
+        if (a->q_col) {
+            // capacity for every group's blocks, whatever the device offsets hold (as
+            // moe_group_quant_mxfp8's column-wise mode: 4 (ceil(M / 128) + G) blocks)
+            const int64_t need = 4 * (moe::cdiv<int64_t>(a->M, 128) + a->G);
+            if (!a->s_col || !a->q_block_start || !moe_aligned16(a->q_col) || a->q_col_blocks < need)
+                return MOE_EINVAL;
+        } else if (a->s_col || a->q_block_start) {
+            return MOE_EINVAL;
+        }
+    }
     // groups' B matrices are only read, so they may overlap (e.g. K slices of one matrix)
-    if (a->lda < a->K || a->ldb < a->K || a->ldc < a->N || a->b_group_stride < 0) return MOE_EINVAL;
+    if (a->lda < a->K || a->ldb < a->K || (a->C && a->ldc < a->N) || a->b_group_stride < 0) return MOE_EINVAL;
     if (a->aux && (a->epilogue != MOE_EPI_SWIGLU || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
     if (!workspace || workspace_bytes < moe_gemm_workspace_bytes(a->G)) return MOE_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -1369,6 +1558,16 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.order = (const int32_t*)workspace + (a->G + 1);
     p.c_stride = a->c_group_stride;
     p.allow256 = (MOE_GEMM_TILE256 && a->c_dtype != MOE_F32 && a->a_dtype == MOE_BF16) ? 1 : 0;
+    p.q_fmt = !quant ? 0 : a->q_dtype == MOE_E2M1 ? moe::kE2M1 : moe::kE4M3;
+    p.q_row = a->q_row;
+    p.ld_q_row = a->ld_q_row;
+    p.s_row = a->s_row;
+    p.ld_s_row = a->ld_s_row;
+    p.q_col = a->q_col;
+    p.s_col = a->s_col;
+    p.q_bs = a->q_block_start;
+    p.q_col_blocks = a->q_col_blocks;
+    p.c_skip = a->C == nullptr ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
     if (a->a_dtype == MOE_F32) {
@@ -1385,7 +1584,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     auto bytes = [eb2](int64_t elems) { return elems * eb2 / 2; };
     if (fp4 && (a->lda % 2 || a->ldb % 2 || a->b_group_stride % 2)) return MOE_EINVAL;
     if (a->K % (2 * moe::kRowBytes / eb2) != 0) return MOE_EINVAL;
-    if (!moe_aligned16(a->A) || !moe_aligned16(a->B) || !moe_aligned16(a->C)) return MOE_EINVAL;
+    if (!moe_aligned16(a->A) || !moe_aligned16(a->B) || (a->C && !moe_aligned16(a->C))) return MOE_EINVAL;
     if (bytes(a->lda) % 16 || bytes(a->ldb) % 16 || a->ldc % 8 || bytes(a->b_group_stride) % 16) return MOE_EINVAL;
     if (a->aux && (!moe_aligned16(a->aux) || a->ld_aux % 8)) return MOE_EINVAL;
     if (mx) {
@@ -1415,7 +1614,8 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         return moe::launch<false, moe::kE4M3, true>(p, grid, s);
     }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
-                       p.allow256, (int32_t*)workspace, (int32_t*)workspace + (a->G + 1));
+                       p.allow256, (int32_t*)workspace, (int32_t*)workspace + (a->G + 1),
+                       a->q_col ? a->q_block_start : nullptr);
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;

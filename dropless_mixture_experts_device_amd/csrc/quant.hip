@@ -9,6 +9,7 @@
 #include "moe_internal.h"
 #include "swiglu_math.h"
 #include "round_math.h"
+#include "mx_math.h"
 
 namespace moe {
 namespace {
@@ -21,33 +22,6 @@ __device__ __forceinline__ int64_t in_row(const int32_t* row_index, int64_t in_r
     if (!row_index) return r;
     const int64_t v = row_index[r];
     return v < 0 ? 0 : (v >= in_rows ? in_rows - 1 : v);
-}
-
-// E8M0 byte for a block whose largest magnitude is `amax` (0 for an all-zero block).
-__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
-    if (!(amax > 0.f)) return 0u;
-    int e2;
-    (void)frexpf(amax, &e2);                  // amax = m * 2^e2, m in [0.5, 1)
-    const int b = e2 - 1 - 8 + 127;
-    return (uint32_t)min(max(b, 0), 254);
-}
-
-// 2^(127 - byte): the exact multiplier that divides by the block scale. byte <= 246 for any
-// finite bf16/fp32 amax, so the result is a normal float.
-__device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
-
-// Four scaled values -> four E4M3 codes (OCP "FN": bias 7, 3 mantissa bits, subnormal step
-// 2^-9, max 448, no infinities), packed little-endian into one word. gfx950's v_cvt_pk_fp8_f32
-// converts to OCP E4M3 with round-to-nearest-even; clamping to +-448 first gives the MX rule's
-// saturation (the sign of zero passes through).
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-    a = fminf(fmaxf(a, -448.f), 448.f);
-    b = fminf(fmaxf(b, -448.f), 448.f);
-    c = fminf(fmaxf(c, -448.f), 448.f);
-    d = fminf(fmaxf(d, -448.f), 448.f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);         // bytes 2, 3
-    return (uint32_t)w;
 }
 
 __device__ __forceinline__ float load_val(const char* p, int esize) {
@@ -105,34 +79,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const char* __restrict_
     sc[r * ld_sc + b] = (uint8_t)byte;
 }
 
-// Group-aware column-wise, transposed, group-major output: group g owns nb_g = 4 ceil(m_g/128)
-// blocks j = block_start[g] + i (i < nb_g) of 32 of its rows; its codes form a [cols, 32 nb_g]
-// matrix at q + 32 cols block_start[g] (block i of column c at column offset 32 i) and its
-// scales a [cols, nb_g] matrix at sc + cols block_start[g]. Each group thus starts on a
-// 128-element boundary (one K slice of the MXFP8 GEMM, its 4 scale bytes one aligned dword),
-// and one group's transposed block is contiguous in memory; blocks past the group's last row
-// are all-zero (codes 0, scale byte 0).
 // ---- MXFP4 ([OCP-MX] FP4 E2M1 elements: bias 1, one mantissa bit, values 0, 0.5, 1, 1.5, 2,
 // 3, 4, 6; the block's shared exponent floor(log2 amax) - 2, 2 being E2M1's largest exponent)
-
-__device__ __forceinline__ uint32_t mx4_scale_byte(float amax) {
-    if (!(amax > 0.f)) return 0u;
-    int e2;
-    (void)frexpf(amax, &e2);                  // amax = m * 2^e2, m in [0.5, 1)
-    const int b = e2 - 1 - 2 + 127;
-    return (uint32_t)min(max(b, 0), 254);     // at most 252 for a finite amax
-}
-
-// E2M1 code of a scaled value: round to nearest, ties to the even mantissa (the comparisons
-// against the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 are strict where the tie goes down
-// to an even code and inclusive where it goes up to one), magnitudes above 6 saturate; the sign
-// in bit 3, also for a value that rounds to zero. The magnitude index is the code's low 3 bits.
-__device__ __forceinline__ uint32_t e2m1_code(float x) {
-    const float m = fabsf(x);
-    const uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                         (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
-    return ((__float_as_uint(x) >> 28) & 0x8u) | idx;
-}
 
 // Row-wise MXFP4: one thread per 32-element block; the block's 32 codes go out as 16 bytes
 // (two per byte, the even element in the low nibble), its scale as one byte.
@@ -183,6 +131,13 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const char* __restr
     sc[r * ld_sc + b] = (uint8_t)byte;
 }
 
+// Group-aware column-wise, transposed, group-major output: group g owns nb_g = 4 ceil(m_g/128)
+// blocks j = block_start[g] + i (i < nb_g) of 32 of its rows; its codes form a [cols, 32 nb_g]
+// matrix at q + 32 cols block_start[g] (block i of column c at column offset 32 i) and its
+// scales a [cols, nb_g] matrix at sc + cols block_start[g]. Each group thus starts on a
+// 128-element boundary (one K slice of the MXFP8 GEMM, its 4 scale bytes one aligned dword),
+// and one group's transposed block is contiguous in memory; blocks past the group's last row
+// are all-zero (codes 0, scale byte 0).
 __global__ __launch_bounds__(1024) void quant_block_prefix_kernel(const int32_t* __restrict__ offsets, int G,
                                                                   int64_t rows, int32_t* __restrict__ block_start) {
     __shared__ int wsum[16];

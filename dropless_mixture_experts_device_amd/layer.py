@@ -204,11 +204,15 @@ def _nomark(name):
     pass
 
 
-def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False, mark=None):
+def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, routed: bool = False, mark=None,
+               fuse_h_quant: bool = True, write_h: bool = True):
     """MXFP8 forward: route and permute as in bf16, x quantised row-wise once per token (the
     GEMM gathers codes and scale rows through src_token), GEMM 1 + SwiGLU saving G and U,
-    H quantised row-wise (and, in the same pass, column-wise for the backward's wgrad 2),
-    GEMM 2, combine. mw must hold this step's quantised weights.
+    H quantised row-wise (and column-wise for the backward's wgrad 2), GEMM 2, combine.
+    mw must hold this step's quantised weights.
+    fuse_h_quant (the default): GEMM 1's epilogue writes both quantised copies of H (the same
+    bytes as the standalone dual pass over the stored H, which fuse_h_quant=False runs);
+    write_h=False then leaves the bf16 H unwritten (the step reads only its quantised copies).
     routed=True skips the router: b.topk_idx and b.topk_w already hold the assignment.
     Otherwise the router's keys are kept in b.keys for its backward.
     mark(name), if given, is called after each stage (e.g. to record a timing event)."""
@@ -220,11 +224,17 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
     mark("permute")
     L.moe_group_quant_mxfp8(x, b.q_x, b.s_x, axis=0)
     mark("quant_x")
-    L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, aux=b.GU,
-                       workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu)
-    mark("gemm1_swiglu")
-    L.moe_group_quant_mxfp8_dual(b.H, b.q_h, b.s_h, b.qc_h, b.sc_h, b.offsets, block_start=b.bs)
-    mark("quant_h")
+    if fuse_h_quant:
+        L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H if write_h else None, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token,
+                           aux=b.GU, workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu, q_row=b.q_h, s_row=b.s_h,
+                           q_col=b.qc_h, s_col=b.sc_h, q_block_start=b.bs, out_shape=(s.rows, s.f))
+        mark("gemm1_swiglu")
+    else:
+        L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, aux=b.GU,
+                           workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu)
+        mark("gemm1_swiglu")
+        L.moe_group_quant_mxfp8_dual(b.H, b.q_h, b.s_h, b.qc_h, b.sc_h, b.offsets, block_start=b.bs)
+        mark("quant_h")
     L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
                        b_scale=mw.s_dn)
     mark("gemm2")
@@ -344,11 +354,13 @@ class Mx4Buffers(LayerBuffers):
         self.q_h, self.s_h = _u8((s.rows, s.f // 2), dev), _u8((s.rows, s.f // 32), dev)
 
 
-def forward_mx4(x, w_router, bias, mw: Mx4Weights, s: LayerShape, b: Mx4Buffers, routed: bool = False, mark=None):
+def forward_mx4(x, w_router, bias, mw: Mx4Weights, s: LayerShape, b: Mx4Buffers, routed: bool = False, mark=None,
+                fuse_h_quant: bool = True, write_h: bool = True):
     """MXFP4 forward: route and permute as in bf16, x quantised once per token (GEMM 1 gathers
-    its code and scale rows through src_token), GEMM 1 + SwiGLU into bf16 H, H quantised,
-    GEMM 2, combine. mw must hold the quantised weights; routed=True keeps b.topk_idx and
-    b.topk_w as they are; mark(name), if given, is called after each stage."""
+    its code and scale rows through src_token), GEMM 1 + SwiGLU with H quantised in its
+    epilogue (fuse_h_quant=False: bf16 H, then a separate quantiser pass; write_h=False: the
+    bf16 H is not written), GEMM 2, combine. mw must hold the quantised weights; routed=True
+    keeps b.topk_idx and b.topk_w as they are; mark(name), if given, is called after each stage."""
     mark = mark or _nomark
     if not routed:
         route(x, w_router, bias, s, b)
@@ -357,11 +369,17 @@ def forward_mx4(x, w_router, bias, mw: Mx4Weights, s: LayerShape, b: Mx4Buffers,
     mark("permute")
     L.moe_group_quant_mxfp4(x, b.q_x, b.s_x)
     mark("quant_x")
-    L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token, workspace=b.ws_gemm1,
-                       a_scale=b.s_x, b_scale=mw.s_gu, fp4=True)
-    mark("gemm1_swiglu")
-    L.moe_group_quant_mxfp4(b.H, b.q_h, b.s_h)
-    mark("quant_h")
+    if fuse_h_quant:
+        L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H if write_h else None, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token,
+                           workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu, fp4=True, q_row=b.q_h, s_row=b.s_h,
+                           q_fp4=True, out_shape=(s.rows, s.f))
+        mark("gemm1_swiglu")
+    else:
+        L.moe_grouped_gemm(b.q_x, mw.q_gu, b.H, b.offsets, L.MOE_EPI_SWIGLU, a_rows=b.src_token,
+                           workspace=b.ws_gemm1, a_scale=b.s_x, b_scale=mw.s_gu, fp4=True)
+        mark("gemm1_swiglu")
+        L.moe_group_quant_mxfp4(b.H, b.q_h, b.s_h)
+        mark("quant_h")
     L.moe_grouped_gemm(b.q_h, mw.q_dn, b.Y, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm2, a_scale=b.s_h,
                        b_scale=mw.s_dn, fp4=True)
     mark("gemm2")

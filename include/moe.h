@@ -241,6 +241,30 @@ typedef struct moe_gemm_args {
     int64_t b_scale_group_stride;
     int32_t ragged_k;           /* 0: groups partition the rows of A and C; 1: ragged-K mode  */
     int64_t c_group_stride;     /* ragged-K mode: elements between consecutive groups' C      */
+    /* Fused output quantisation ([Blog] "JAX plus Transformer Engine MoE training
+     * performance": quantisation fused into the GEMM is the planned next step; [Blog]
+     * "Optimisations dropless MoE needs": group-aware MXFP8). q_dtype 0: off. MOE_E4M3 or
+     * MOE_E2M1 (ragged rows only, MXFP8 or MXFP4 operands, c_dtype MOE_BF16, N % 32 == 0;
+     * MOE_ENOTSUP otherwise): the epilogue also quantises
+     * the bf16 values of C it forms, so the bytes equal those moe_group_quant_mxfp8 (axis 0,
+     * and axis 1 for q_col) or moe_group_quant_mxfp4 write when run on the stored C:
+     *   q_row [M, N] E4M3 codes or [M, N/2] packed E2M1 (leading dimension ld_q_row bytes,
+     *         16-byte aligned, ld_q_row % 16 == 0), s_row [M, N/32] scale bytes (ld_s_row);
+     *   q_col, s_col (MOE_E4M3 only, optional): the group-aware column-wise copy in
+     *         moe_group_quant_mxfp8's axis-1 layout, with capacity q_col_blocks >=
+     *         4 (ceil(M/128) + G) blocks (q_col [N, 32 q_col_blocks], s_col [N, q_col_blocks]);
+     *         the group block prefix is written to q_block_start [G+1].
+     * Rows outside the groups are not written. C may be NULL when q_dtype != 0 (only the
+     * quantised copies are written). */
+    int32_t q_dtype;
+    uint8_t* q_row;
+    int64_t ld_q_row;
+    uint8_t* s_row;
+    int64_t ld_s_row;
+    uint8_t* q_col;
+    uint8_t* s_col;
+    int32_t* q_block_start;
+    int64_t q_col_blocks;
 } moe_gemm_args_t;
 
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,

@@ -228,6 +228,58 @@ def test_host_argument_errors_mxfp4(lib):
         assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, field
 
 
+def test_host_argument_errors_fused_quant(lib):
+    """The GEMM's fused output quantisation: every rejected combination returns its status
+    before anything is enqueued; C may be omitted only when a quantised copy is asked for."""
+    from dropless_mixture_experts_device_amd import _lib as L
+    fake = ctypes.c_void_p(1 << 20)
+    M, N, K, G = 128, 64, 512, 4
+    cap = L.quant_col_blocks(M, G)
+    a = L.MoeGemmArgs(G=G, offsets=fake.value, M=M, N=N, K=K, A=fake.value, a_dtype=L.MOE_E4M3, lda=K, A_rows=M,
+                      a_rows=None, B=fake.value, b_dtype=L.MOE_E4M3, ldb=K, b_group_stride=2 * N * K, C=fake.value,
+                      c_dtype=L.MOE_BF16, ldc=N, epilogue=L.MOE_EPI_SWIGLU, aux=None, ld_aux=0, a_scale=fake.value,
+                      lda_scale=K // 32, b_scale=fake.value, ldb_scale=K // 32, b_scale_group_stride=2 * N * K // 32,
+                      ragged_k=0, c_group_stride=0, q_dtype=L.MOE_E4M3, q_row=fake.value, ld_q_row=N,
+                      s_row=fake.value, ld_s_row=N // 32, q_col=fake.value, s_col=fake.value,
+                      q_block_start=fake.value, q_col_blocks=cap)
+    assert L._lib.moe_grouped_gemm(ctypes.byref(a), None, 0, None) == L.MOE_EWORKSPACE
+    cases = (("q_dtype", 5, L.MOE_ENOTSUP), ("c_dtype", L.MOE_F32, L.MOE_ENOTSUP),
+             ("N", 48, L.MOE_EINVAL), ("q_row", None, L.MOE_EINVAL), ("ld_q_row", N - 16, L.MOE_EINVAL),
+             ("ld_q_row", N + 8, L.MOE_EINVAL), ("ld_s_row", 1, L.MOE_EINVAL), ("s_row", None, L.MOE_EINVAL),
+             ("s_col", None, L.MOE_EINVAL), ("q_block_start", None, L.MOE_EINVAL),
+             ("q_col_blocks", cap - 1, L.MOE_EINVAL), ("q_row", fake.value + 8, L.MOE_EINVAL))
+    for field, value, want in cases:
+        bad = L.MoeGemmArgs.from_buffer_copy(a)
+        setattr(bad, field, value)
+        if field == "N":
+            bad.ldc, bad.ld_q_row = 48, 48
+        assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, (field, value)
+    # bf16 operands, ragged-K mode and E2M1 column-wise copies are not offered
+    for fields, want in (({"a_dtype": L.MOE_BF16, "b_dtype": L.MOE_BF16}, L.MOE_ENOTSUP),
+                         ({"q_dtype": L.MOE_E2M1}, L.MOE_ENOTSUP)):
+        bad = L.MoeGemmArgs.from_buffer_copy(a)
+        for k_, v in fields.items():
+            setattr(bad, k_, v)
+        assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, fields
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.ragged_k, bad.epilogue, bad.b_group_stride, bad.b_scale_group_stride = 1, L.MOE_EPI_NONE, 0, 0
+    bad.c_group_stride = M * N
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_ENOTSUP
+    # quantised outputs given without q_dtype, and a missing C without them, are errors
+    bad = L.MoeGemmArgs.from_buffer_copy(a)
+    bad.q_dtype = 0
+    assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == L.MOE_EINVAL
+    plain = L.MoeGemmArgs.from_buffer_copy(a)
+    for f_ in ("q_row", "s_row", "q_col", "s_col", "q_block_start"):
+        setattr(plain, f_, None)
+    plain.q_dtype, plain.C = 0, None
+    assert L._lib.moe_grouped_gemm(ctypes.byref(plain), fake, 1 << 20, None) == L.MOE_EINVAL
+    # C omitted with a quantised copy requested passes the argument checks (stops at the workspace)
+    ok = L.MoeGemmArgs.from_buffer_copy(a)
+    ok.C = None
+    assert L._lib.moe_grouped_gemm(ctypes.byref(ok), None, 0, None) == L.MOE_EWORKSPACE
+
+
 def test_binding_constants_match_header_enums():
     """Every enumerator of include/moe.h has the same value in the Python binding, and every
     workspace op id is answered (an unknown one returns 0)."""

@@ -319,3 +319,30 @@ def test_mx_step_graph_replay_with_new_inputs(LY):
             torch.cuda.synchronize()
             for n in names:
                 np.testing.assert_array_equal(bits(getattr(b, n)), want[n], err_msg=f"{n}, replay {rep}")
+
+
+@pytest.mark.parametrize("name", ["small_mxfp8", "mid_mxfp8"])
+def test_mx_step_fused_h_quant_equals_two_pass(LY, name):
+    """H quantised in GEMM 1's epilogue (both MXFP8 copies, bf16 H not written) gives the same
+    step, bit for bit, as the bf16 H passed through the standalone dual quantiser: the
+    quantised copies of H, the block prefix, Y, the output and every gradient."""
+    L, layer = LY
+    w = mi.WORKLOADS[name]
+    dw = DeviceWorkload(w)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.MxWeights(s, "cuda")
+    mw.quantise(dw.w_gu, dw.w_down)
+    d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
+    names = ("q_h", "s_h", "qc_h", "sc_h", "bs", "Y", "out", "dx", "dW_gu", "dW_down", "dW_router", "d_bias")
+    got = []
+    for fused in (False, True):
+        b = layer.MxBuffers(s, "cuda")
+        for n in ("qc_h", "sc_h"):
+            getattr(b, n).fill_(0x5A)                    # capacity past the last group: untouched by both
+        layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, fuse_h_quant=fused, write_h=not fused)
+        layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router)
+        torch.cuda.synchronize()
+        got.append({n: bits(getattr(b, n)).copy() for n in names})
+    for n in names:
+        np.testing.assert_array_equal(got[1][n], got[0][n], err_msg=n)

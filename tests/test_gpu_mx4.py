@@ -307,3 +307,23 @@ def test_mx4_layer_forward_dsv3_sampled(LY):
     local = np.arange(need.size).reshape(len(toks), w.k)
     assert_close(pick(b.out, toks), O.combine(pick(b.Y, need), wt, local, pick(b.Y, w.T * w.k + toks),
                                               O.round_bf16), "bf16", "out")
+
+
+def test_mx4_forward_fused_h_quant_equals_two_pass(LY):
+    """H quantised to MXFP4 in GEMM 1's epilogue (bf16 H not written) gives the same codes,
+    scales, Y and output, bit for bit, as the bf16 H passed through moe_group_quant_mxfp4."""
+    L, layer = LY
+    w = mi.WORKLOADS["small_mxfp4"]
+    dw = DeviceWorkload(w)
+    s = layer.LayerShape(T=w.T, d=w.d, f=w.f, E=w.E, k=w.k, shared=bool(w.shared_f),
+                         score=L.MOE_SOFTMAX if w.score == "softmax" else L.MOE_SIGMOID)
+    mw = layer.Mx4Weights(s, "cuda")
+    mw.quantise(dw.w_gu, dw.w_down)
+    got = []
+    for fused in (False, True):
+        b = layer.Mx4Buffers(s, "cuda")
+        layer.forward_mx4(dw.x, dw.w_router, dw.bias, mw, s, b, fuse_h_quant=fused, write_h=not fused)
+        torch.cuda.synchronize()
+        got.append({n: getattr(b, n).view(torch.uint8).cpu().numpy().copy() for n in ("q_h", "s_h", "Y", "out")})
+    for n in got[0]:
+        np.testing.assert_array_equal(got[1][n], got[0][n], err_msg=n)

@@ -11,7 +11,7 @@ import torch
 
 import moe_inputs as mi
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, dev_i32, host
+from tests.gpu_util import assert_close, bits, dev_i32, host
 
 pytestmark = pytest.mark.gpu
 
@@ -150,3 +150,90 @@ def test_mx_wgrad_quantised_within_tolerance(L):
             assert np.all(got[g] == 0), "an empty group's weight gradient is written as zeros"
         else:
             assert_close(got[g], want, "bf16", f"wgrad group {g}")
+
+
+# ---- output quantisation fused into the epilogue
+
+def _sentinel(shape):
+    return torch.full(shape, 0xA5, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("sizes", [[0, 1, 17, 33, 0, 65, 129, 300, 16, 32, 64, 128, 2], [513, 0, 7]])
+@pytest.mark.parametrize("epi", ["swiglu", "none"])
+@pytest.mark.parametrize("fp4_in", [False, True])
+def test_fused_quant_e4m3_equals_two_pass(L, sizes, epi, fp4_in):
+    """GEMM with its output quantised in the epilogue (row-wise and group-aware column-wise
+    MXFP8) writes the same bytes as the GEMM's bf16 output passed through the standalone dual
+    quantiser: every code and scale byte, the block prefix, the untouched rows and padding;
+    with C omitted the quantised copies are unchanged."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G, N, K = int(off[-1]) + 3, len(sizes), 256, 512
+    nb = 2 * N if epi == "swiglu" else N
+    x = mi.randn_np(31, mi.X, 0, M + 4, K, 1.0, "bf16").astype(np.float64)
+    W = np.stack([mi.randn_np(31, mi.W_GATE, g, nb, K, 0.05, "bf16") for g in range(G)]).astype(np.float64)
+    if fp4_in:
+        from tests.test_gpu_mx4 import pack
+        A, As, _ = O.mx4_quantize_rowwise(x)
+        parts = [O.mx4_quantize_rowwise(W[g]) for g in range(G)]
+        A = pack(A)
+        B = np.stack([pack(p[0]) for p in parts])
+    else:
+        A, As, _ = O.mx_quantize_rowwise(x)
+        parts = [O.mx_quantize_rowwise(W[g]) for g in range(G)]
+        B = np.stack([p[0] for p in parts])
+    Bs = np.stack([p[1] for p in parts])
+    a_rows = np.random.Generator(np.random.PCG64(5)).integers(0, M + 4, M).astype(np.int32)
+    e = L.MOE_EPI_SWIGLU if epi == "swiglu" else L.MOE_EPI_NONE
+    offs, ar = dev_i32(off), dev_i32(a_rows)
+    cap = L.quant_col_blocks(M, G)
+    # two-pass: bf16 output, then the dual quantiser
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_grouped_gemm(_u8(A), _u8(B), C, offs, e, a_rows=ar, workspace=_ws(L, G), a_scale=_u8(As),
+                       b_scale=_u8(Bs), fp4=fp4_in)
+    q2, s2, qc2, sc2 = _sentinel((M, N)), _sentinel((M, N // 32)), _sentinel((N, 32 * cap)), _sentinel((N, cap))
+    bs2 = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8_dual(C, q2, s2, qc2, sc2, offs, block_start=bs2, rows=int(off[-1]))
+    outs = []
+    for keep_c in (True, False):
+        Cf = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda") if keep_c else None
+        q1, s1, qc1, sc1 = _sentinel((M, N)), _sentinel((M, N // 32)), _sentinel((N, 32 * cap)), _sentinel((N, cap))
+        bs1 = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+        L.moe_grouped_gemm(_u8(A), _u8(B), Cf, offs, e, a_rows=ar, workspace=_ws(L, G), a_scale=_u8(As),
+                           b_scale=_u8(Bs), fp4=fp4_in, q_row=q1, s_row=s1, q_col=qc1, s_col=sc1, q_block_start=bs1,
+                           out_shape=(M, N))
+        torch.cuda.synchronize()
+        if keep_c:
+            np.testing.assert_array_equal(bits(Cf), bits(C))
+        outs.append([t.cpu().numpy() for t in (q1, s1, qc1, sc1, bs1)])
+    torch.cuda.synchronize()
+    want = [t.cpu().numpy() for t in (q2, s2, qc2, sc2, bs2)]
+    for got in outs:
+        for name, a, b in zip(("q_row", "s_row", "q_col", "s_col", "block_start"), got, want):
+            np.testing.assert_array_equal(a, b, err_msg=name)
+    assert np.all(outs[0][0][off[-1]:] == 0xA5), "rows outside the groups are not written"
+
+
+def test_fused_quant_e2m1_equals_two_pass(L):
+    """MXFP4 output quantisation in the epilogue equals moe_group_quant_mxfp4 on the bf16 output."""
+    from tests.test_gpu_mx4 import pack
+    sizes = [0, 1, 17, 33, 65, 129, 300, 2, 128, 513]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G, N, K = int(off[-1]) + 2, len(sizes), 384, 1024
+    x = mi.randn_np(33, mi.X, 0, M, K, 1.0, "bf16").astype(np.float64)
+    W = np.stack([mi.randn_np(33, mi.W_GATE, g, 2 * N, K, 0.05, "bf16") for g in range(G)]).astype(np.float64)
+    A, As, _ = O.mx4_quantize_rowwise(x)
+    parts = [O.mx4_quantize_rowwise(W[g]) for g in range(G)]
+    B = np.stack([pack(p[0]) for p in parts])
+    Bs = np.stack([p[1] for p in parts])
+    offs = dev_i32(off)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_grouped_gemm(_u8(pack(A)), _u8(B), C, offs, L.MOE_EPI_SWIGLU, workspace=_ws(L, G), a_scale=_u8(As),
+                       b_scale=_u8(Bs), fp4=True)
+    q2, s2 = _sentinel((M, N // 2)), _sentinel((M, N // 32))
+    L.moe_group_quant_mxfp4(C[:int(off[-1])], q2[:int(off[-1])], s2[:int(off[-1])])
+    q1, s1 = _sentinel((M, N // 2)), _sentinel((M, N // 32))
+    L.moe_grouped_gemm(_u8(pack(A)), _u8(B), None, offs, L.MOE_EPI_SWIGLU, workspace=_ws(L, G), a_scale=_u8(As),
+                       b_scale=_u8(Bs), fp4=True, q_row=q1, s_row=s1, q_fp4=True, out_shape=(M, N))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q1.cpu().numpy(), q2.cpu().numpy())
+    np.testing.assert_array_equal(s1.cpu().numpy(), s2.cpu().numpy())
