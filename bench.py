@@ -253,14 +253,16 @@ def mx_gemm_work(w, rows, nonempty):
     """Algorithmic HBM bytes and FLOPs of each MXFP8 GEMM of the step: E4M3 operands with one
     scale byte per 32 elements read once (weights of non-empty groups only), bf16 outputs
     written once; GEMM 1 writes the saved gate/up pre-activations and H's two MXFP8 copies
-    (row-wise and column-wise, quantised in its epilogue) instead of a bf16 H."""
+    (row-wise and column-wise, quantised in its epilogue) instead of a bf16 H; dgrad 2 reads
+    the saved pre-activations and writes dGU's two MXFP8 copies (the SwiGLU backward in its
+    epilogue) instead of a bf16 dH."""
     d, f, G = w.d, w.f, w.E + (1 if w.shared_f else 0)
     q = 33.0 / 32.0
     return {
         "gemm1_swiglu": (nonempty * 2 * f * d * q + w.T * d * q + 2 * rows * f * q + rows * 2 * f * 2 + rows * 4,
                          2.0 * rows * d * 2 * f),
         "gemm2": (nonempty * d * f * q + rows * f * q + rows * d * 2, 2.0 * rows * f * d),
-        "dgrad2": (nonempty * f * d * q + rows * d * q + rows * f * 2, 2.0 * rows * d * f),
+        "dgrad2": (nonempty * f * d * q + rows * d * q + rows * 2 * f * 2 + 2 * rows * 2 * f * q, 2.0 * rows * d * f),
         "wgrad2": ((d + f) * rows * q + G * d * f * 2, 2.0 * rows * d * f),
         "dgrad1": (nonempty * d * 2 * f * q + rows * 2 * f * q + rows * d * 2, 2.0 * rows * 2 * f * d),
         "wgrad1": ((2 * f + d) * rows * q + G * 2 * f * d * 2, 2.0 * rows * 2 * f * d),

@@ -19,7 +19,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_E4M3, MOE_E2M1 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_QUANT, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_BWD_QUANT = 0, 1, 2, 3, 4, 5
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -183,6 +183,8 @@ def moe_grouped_gemm(A, B, C, offsets, epilogue: int = MOE_EPI_NONE, a_rows=None
     else:
         G = B.shape[0]
         M, N = C.shape if C is not None else out_shape
+        if epilogue == MOE_EPI_SWIGLU_BWD:
+            N //= 2                          # C holds [dg | du]
         per = 2 if fp4 else 1                # elements per stored byte
         if fp4 and (A.dtype != torch.uint8 or B.dtype != torch.uint8):
             raise TypeError("MXFP4 operands are uint8 tensors of packed E2M1 codes")

@@ -31,6 +31,7 @@
 
 #include "moe_internal.h"
 #include "mx_math.h"
+#include "swiglu_math.h"
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -231,6 +232,7 @@ struct GemmParams {
     const int32_t* q_bs;         // [G+1] column-wise block prefix, written by the schedule kernel
     int64_t q_col_blocks;        // capacity of q_col / s_col in blocks
     int c_skip;                  // C is not written (only its quantised copies)
+    int swb;                     // SwiGLU-backward epilogue: C = [dg | du] from dh and the saved aux
 };
 
 // ---------------------------------------------------------------------------------------
@@ -554,13 +556,14 @@ __device__ __forceinline__ typename Mfma<MS, FMT>::acc_t acc_zero() {
 // ---------------------------------------------------------------------------------------
 template <int BM, int BN_OUT>
 __device__ __forceinline__ void quant_epilogue(const GemmParams& p, const char* lds, int pitch, int g, int r0,
-                                               int r_off, int rows_valid, int n0, int tid) {
+                                               int r_off, int rows_valid, int n0, int tid, int col_end,
+                                               int64_t ncols) {
     constexpr int RB = BN_OUT / 32;            // row-wise blocks per tile row
     const bool fp4 = p.q_fmt == kE2M1;
     for (int t = tid; t < BM * RB; t += kThreads) {
         const int row = t / RB, blk = t % RB;
         const int col = n0 + blk * 32;
-        if (row >= rows_valid || col >= p.N) continue;    // N % 32 == 0: a block is whole or absent
+        if (row >= rows_valid || col >= col_end) continue;   // col_end % 32 == 0: whole blocks only
         const char* src = lds + row * pitch + blk * 64;
         float v[32];
 #pragma unroll
@@ -615,13 +618,13 @@ __device__ __forceinline__ void quant_epilogue(const GemmParams& p, const char* 
     const int nbg = p.q_bs[g + 1] - bs0;
     const int jb0 = r_off / 32;
     if (bs0 < 0 || nbg < jb0 + NBT || (int64_t)bs0 + nbg > p.q_col_blocks) return;   // never for consistent offsets
-    const int64_t N = p.N;
+    const int64_t N = ncols;
     uint8_t* qg = p.q_col + 32 * N * bs0;
     uint8_t* sg = p.s_col + N * bs0;
     for (int t = tid; t < (BN_OUT / 2) * NBT; t += kThreads) {
         const int cp = t / NBT, blk = t % NBT;
         const int col = n0 + 2 * cp;
-        if (col >= p.N) continue;                 // N even: both columns or neither
+        if (col >= col_end) continue;             // col_end even: both columns or neither
         uint32_t pair[32];                         // rows' bf16 pairs (column col in the low half)
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -653,6 +656,84 @@ __device__ __forceinline__ void quant_epilogue(const GemmParams& p, const char* 
             *reinterpret_cast<u32x4*>(dst + 16) = out[1];
             sg[c * nbg + jb] = (uint8_t)byte;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// SwiGLU-backward epilogue (the data-gradient GEMM dh = dY W_down^T): the tile's dh values,
+// already rounded to bf16 in LDS, meet the saved pre-activations g = aux[r, n] and
+// u = aux[r, N + n]; dg and du (rounded to bf16, as moe_swiglu_backward stores them) replace
+// dh in LDS and fill a second LDS tile, then go out as C = [dg | du] ([M, 2N], optional)
+// and/or their quantised copies (2N columns), as the standalone SwiGLU backward followed by
+// the quantisers would write them.
+// ---------------------------------------------------------------------------------------
+template <int BM>
+__device__ __forceinline__ void swb_epilogue(const GemmParams& p, char* lds, int pitch, int g, int r0, int r_off,
+                                             int rows_valid, int n0, int tid) {
+    constexpr int BN = kBN;                    // dh columns of the tile
+    constexpr int CH = BN / 8;                 // 16-byte chunks per tile row
+    static_assert(2 * BM * (BN * 2 + 16) <= kPipeBytes, "the dg and du tiles fit the operand ring");
+    char* lds_u = lds + BM * pitch;            // the du tile (both fit the operand ring)
+    // every g, u load of this thread goes out before the first is used (NB chunks per thread)
+    constexpr int NB = cdiv(BM * CH, kThreads);
+    u32x4 gv_all[NB], uv_all[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = tid + i * kThreads;
+        const int row = c / CH, ch = c % CH;
+        const int col = n0 + ch * 8;
+        gv_all[i] = u32x4{0u, 0u, 0u, 0u};
+        uv_all[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < BM * CH && row < rows_valid && col < p.N) {   // N % 8 == 0: a chunk is whole or absent
+            const int64_t r = r0 + row;
+            gv_all[i] = *reinterpret_cast<const u32x4*>(p.aux + (r * p.ld_aux + col) * 2);
+            uv_all[i] = *reinterpret_cast<const u32x4*>(p.aux + (r * p.ld_aux + p.N + col) * 2);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = tid + i * kThreads;
+        const int row = c / CH, ch = c % CH;
+        const int col = n0 + ch * 8;
+        if (c >= BM * CH || row >= rows_valid || col >= p.N) continue;
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(lds + row * pitch + ch * 16);
+        const u32x4 gv = gv_all[i], uv = uv_all[i];
+        u32x4 og, ou;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t pg = 0u, pu = 0u;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int sh = 16 * e;
+                const float hh = __uint_as_float(((hv[w] >> sh) & 0xFFFFu) << 16);
+                const float gg = __uint_as_float(((gv[w] >> sh) & 0xFFFFu) << 16);
+                const float uu = __uint_as_float(((uv[w] >> sh) & 0xFFFFu) << 16);
+                float dg, du;
+                swiglu_grad(hh, gg, uu, dg, du);
+                pg |= (uint32_t)f32_to_bf16(dg) << sh;
+                pu |= (uint32_t)f32_to_bf16(du) << sh;
+            }
+            og[w] = pg;
+            ou[w] = pu;
+        }
+        *reinterpret_cast<u32x4*>(lds + row * pitch + ch * 16) = og;
+        *reinterpret_cast<u32x4*>(lds_u + row * pitch + ch * 16) = ou;
+    }
+    lds_barrier();
+    if (!p.c_skip) {
+        for (int c = tid; c < 2 * BM * CH; c += kThreads) {
+            const int half = c / (BM * CH), cc = c % (BM * CH);
+            const int row = cc / CH, ch = cc % CH;
+            const int col = n0 + ch * 8;
+            if (row >= rows_valid || col >= p.N) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>((half ? lds_u : lds) + row * pitch + ch * 16);
+            *reinterpret_cast<u32x4*>(p.C + ((int64_t)(r0 + row) * p.ldc + half * p.N + col) * 2) = v;
+        }
+    }
+    if (p.q_fmt != 0) {
+        const int64_t ncols = 2 * (int64_t)p.N;
+        quant_epilogue<BM, BN>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid, p.N, ncols);
+        quant_epilogue<BM, BN>(p, lds_u, pitch, g, r0, r_off, rows_valid, p.N + n0, tid, 2 * p.N, ncols);
     }
 }
 
@@ -1063,8 +1144,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int chunks_per_row = BN_OUT * esize / 16;
     const int cols_per_chunk = 16 / esize;
     // (block-scaled operand kernels only: the bf16 kernels' register budget has no room for it)
+    if constexpr (!RK && MX && !SWIGLU) {
+        if (p.swb) {
+            swb_epilogue<BM>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid);
+            return;
+        }
+    }
     if constexpr (!RK && MX) {
-        if (p.q_fmt != 0) quant_epilogue<BM, BN_OUT>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid);
+        if (p.q_fmt != 0) quant_epilogue<BM, BN_OUT>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid, p.N, p.N);
         if (p.c_skip) return;
     }
     for (int c = tid; c < BM * chunks_per_row; c += kThreads) {
@@ -1476,7 +1563,16 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->M < 0 || a->N <= 0 || a->K <= 0 || a->N % 8 != 0 || a->N > (1 << 24) || a->K > (1 << 24))
         return MOE_EINVAL;
     if (a->M > INT32_MAX / 2) return MOE_EINVAL;
-    if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_EINVAL;
+    if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU && a->epilogue != MOE_EPI_SWIGLU_BWD)
+        return MOE_EINVAL;
+    const bool swb = a->epilogue == MOE_EPI_SWIGLU_BWD;
+    if (swb) {
+        // block-scaled operands, ragged rows, bf16 output; the saved pre-activations are read
+        if ((a->a_dtype != MOE_E4M3 && a->a_dtype != MOE_E2M1) || a->ragged_k || a->c_dtype != MOE_BF16)
+            return MOE_ENOTSUP;
+        if (!a->aux || a->ld_aux < 2 * a->N || a->ld_aux % 8 || !moe_aligned16(a->aux)) return MOE_EINVAL;
+        if (a->N > INT32_MAX / 2 || (a->C && a->ldc < 2 * a->N)) return MOE_EINVAL;
+    }
     if (a->a_dtype != a->b_dtype) return MOE_ENOTSUP;
     if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3 && a->a_dtype != MOE_E2M1)
         return MOE_ENOTSUP;
@@ -1509,9 +1605,10 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->M == 0) return MOE_OK;
     if (!a->A || !a->B || (!a->C && !quant) || a->A_rows <= 0) return MOE_EINVAL;
     if (quant) {
-        const int64_t row_bytes = a->q_dtype == MOE_E2M1 ? a->N / 2 : a->N;
+        const int64_t qn = swb ? 2 * a->N : a->N;   // columns of the quantised matrix
+        const int64_t row_bytes = a->q_dtype == MOE_E2M1 ? qn / 2 : qn;
         if (!a->q_row || !a->s_row || !moe_aligned16(a->q_row) || a->ld_q_row < row_bytes || a->ld_q_row % 16 ||
-            a->ld_s_row < a->N / 32)
+            a->ld_s_row < qn / 32)
             return MOE_EINVAL;
         if (a->q_col) {
             // capacity for every group's blocks, whatever the device offsets hold (as
@@ -1524,8 +1621,9 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
         }
     }
     // groups' B matrices are only read, so they may overlap (e.g. K slices of one matrix)
-    if (a->lda < a->K || a->ldb < a->K || (a->C && a->ldc < a->N) || a->b_group_stride < 0) return MOE_EINVAL;
-    if (a->aux && (a->epilogue != MOE_EPI_SWIGLU || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
+    if (a->lda < a->K || a->ldb < a->K || (a->C && a->ldc < (swb ? 2 : 1) * a->N) || a->b_group_stride < 0)
+        return MOE_EINVAL;
+    if (a->aux && (a->epilogue == MOE_EPI_NONE || a->ld_aux < 2 * a->N)) return MOE_EINVAL;
     if (!workspace || workspace_bytes < moe_gemm_workspace_bytes(a->G)) return MOE_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const bool fp4 = a->a_dtype == MOE_E2M1;
@@ -1568,6 +1666,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.q_bs = a->q_block_start;
     p.q_col_blocks = a->q_col_blocks;
     p.c_skip = a->C == nullptr ? 1 : 0;
+    p.swb = swb ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
     if (a->a_dtype == MOE_F32) {

@@ -244,7 +244,7 @@ def forward_mx(x, w_router, bias, mw: MxWeights, s: LayerShape, b: MxBuffers, ro
 
 
 def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None, w_router=None,
-                fuse_swiglu_quant: bool = True, fuse_combine_quant: bool = True):
+                fuse_swiglu_quant: bool = True, fuse_combine_quant: bool = True, swiglu_in_dgrad2: bool = True):
     """Backward of forward_mx given d_out [T, d]: fills b.dx, b.dw, b.dW_gu, b.dW_down and,
     when w_router is given (a forward that ran the router), b.dW_router and b.d_bias.
 
@@ -254,8 +254,10 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
     then the router's backward: the routing weights' gradient dw through the top-k
     normalisation to the keys, from there to W_router and the bias, and the router's share
     of the input gradient added into dx (its dx pass forms permute^T itself). With fuse_swiglu_quant (the default) the SwiGLU
-    backward is formed inside the quantiser that writes both MXFP8 copies of dGU, so b.dGU is
-    not written; otherwise it is written by its own kernel and then quantised. Likewise with
+    backward is not written out: with swiglu_in_dgrad2 (the default) dgrad 2's epilogue forms
+    dGU from its dH tile and the saved G, U and writes both MXFP8 copies of dGU (b.dH and b.dGU
+    are not written), else the quantiser that writes those copies forms dGU from the stored
+    dH; without fuse_swiglu_quant dGU is written by its own kernel and then quantised. Likewise with
     fuse_combine_quant (the default) dY is formed inside the quantiser from d_out and the
     routing weights, so b.dY is not written and the combine's transpose only computes dw."""
     mark = mark or _nomark
@@ -275,14 +277,22 @@ def backward_mx(x, d_out, mw: MxWeights, s: LayerShape, b: MxBuffers, mark=None,
         mark("quant_dy")
     # dgrad 2 and wgrad 2
     q_dnT, s_dnT = mw.dn_T()
-    L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
-                       b_scale=s_dnT)
+    in_dgrad2 = fuse_swiglu_quant and swiglu_in_dgrad2
+    if in_dgrad2:
+        L.moe_grouped_gemm(b.q_dy, q_dnT, None, b.offsets, L.MOE_EPI_SWIGLU_BWD, aux=b.GU, workspace=b.ws_gemm1,
+                           a_scale=b.s_dy, b_scale=s_dnT, q_row=b.q_dgu, s_row=b.s_dgu, q_col=b.qc_dgu, s_col=b.sc_dgu,
+                           q_block_start=b.bs, out_shape=(s.rows, 2 * s.f))
+    else:
+        L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
+                           b_scale=s_dnT)
     mark("dgrad2")
     L.moe_grouped_gemm(b.qc_dy, b.qc_h, b.dW_down, b.bs, L.MOE_EPI_NONE, workspace=b.ws_gemm3,
                        a_scale=b.sc_dy, b_scale=b.sc_h, ragged_k=True)
     mark("wgrad2")
     # SwiGLU backward, dgrad 1 and wgrad 1
-    if fuse_swiglu_quant:
+    if in_dgrad2:
+        pass
+    elif fuse_swiglu_quant:
         L.moe_swiglu_backward_quant_mxfp8_dual(b.dH, b.GU, b.q_dgu, b.s_dgu, b.qc_dgu, b.sc_dgu, b.offsets,
                                                block_start=b.bs)
         mark("swiglu_bwd_quant_dgu")

@@ -52,7 +52,7 @@ typedef enum {
     MOE_E2M1 = 3    /* MXFP4 element: OCP FP4 E2M1, two per byte, the even element in bits 3..0 */
 } moe_dtype_t;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
-typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue_t;
+typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_SWIGLU_BWD = 2 } moe_epilogue_t;
 typedef enum {
     MOE_OP_ROUTE = 0,
     MOE_OP_PERMUTE = 1,
@@ -185,6 +185,12 @@ moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t* topk_idx,
  *                    C[r, n] = silu(G) * U,  silu(z) = z / (1 + exp(-z))     n < N
  *                    (B_g has 2N rows: gate rows first, then up rows); when aux != NULL
  *                    also aux[r, n] = G and aux[r, N+n] = U (in c_dtype).
+ *   epilogue SWIGLU_BWD (the SwiGLU backward fused into the data-gradient GEMM dh = dY W_down^T;
+ *                    MXFP8/MXFP4 operands, bf16 C): dh = bf16(sum_k A[a(r),k] B_g[n,k]) and, with
+ *                    g = aux[r, n], u = aux[r, N+n] (the saved pre-activations, read), s = 1/(1+exp(-g)):
+ *                    C[r, n] = bf16(dh u s (1 + g (1 - s))), C[r, N+n] = bf16(dh g s)   n < N
+ *                    (C is [M, 2N]: the values moe_swiglu_backward writes from the stored dh;
+ *                    the fused quantisation below then covers all 2N columns).
  * with a(r) = a_rows[r] if a_rows != NULL (a fused gather) else r, and
  * B_g = B + g * b_group_stride elements (groups may share or overlap B: it is only read).
  * Accumulation is fp32; C is rounded once.
@@ -225,7 +231,7 @@ typedef struct moe_gemm_args {
     int32_t c_dtype;            /* MOE_BF16 or MOE_F32                                       */
     int64_t ldc;
     int32_t epilogue;           /* moe_epilogue_t                                            */
-    void* aux;                  /* SWIGLU only, optional [M, 2N] pre-activation save        */
+    void* aux;                  /* SWIGLU: optional [M, 2N] pre-activation save; SWIGLU_BWD: its input */
     int64_t ld_aux;
     /* MXFP8 operands (a_dtype = b_dtype = MOE_E4M3, K % 128 == 0): A and B hold E4M3 codes and
      * every 32 consecutive K elements of a row share one E8M0 scale byte s, the element value

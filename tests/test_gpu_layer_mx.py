@@ -38,8 +38,11 @@ def _step(L, layer, w, topk=None, fused=True):
     layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router if topk is None else None,
                       fuse_swiglu_quant=fused, fuse_combine_quant=fused)
     if fused:
-        # the stage checks read dY and dGU: the standalone kernels write the exact values the
-        # fused quantisers formed (equal bytes, checked in the quantiser tests)
+        # the stage checks read dY, dH and dGU: the standalone kernels write the exact values
+        # the fused epilogue and quantisers formed (equal bytes, checked in the fused tests)
+        q_dnT, s_dnT = mw.dn_T()
+        L.moe_grouped_gemm(b.q_dy, q_dnT, b.dH, b.offsets, L.MOE_EPI_NONE, workspace=b.ws_gemm1, a_scale=b.s_dy,
+                           b_scale=s_dnT)
         tk = w.T * w.k
         L.moe_combine_backward(d_out, b.topk_w, b.row_of, b.dY[:tk], dy_shared=b.dY[tk:] if s.shared else None)
         L.moe_swiglu_backward(b.dH, b.GU, b.dGU)
@@ -323,9 +326,11 @@ def test_mx_step_graph_replay_with_new_inputs(LY):
 
 @pytest.mark.parametrize("name", ["small_mxfp8", "mid_mxfp8"])
 def test_mx_step_fused_h_quant_equals_two_pass(LY, name):
-    """H quantised in GEMM 1's epilogue (both MXFP8 copies, bf16 H not written) gives the same
-    step, bit for bit, as the bf16 H passed through the standalone dual quantiser: the
-    quantised copies of H, the block prefix, Y, the output and every gradient."""
+    """The step with its fusions (H quantised in GEMM 1's epilogue, bf16 H not written; the
+    SwiGLU backward and dGU's quantisation in dgrad 2's epilogue; dY formed in its quantiser)
+    equals, bit for bit, the step with every intermediate written out and quantised by the
+    standalone kernels: the quantised copies of H and dGU, the block prefix, Y, the output,
+    dX_perm and every gradient."""
     L, layer = LY
     w = mi.WORKLOADS[name]
     dw = DeviceWorkload(w)
@@ -334,14 +339,16 @@ def test_mx_step_fused_h_quant_equals_two_pass(LY, name):
     mw = layer.MxWeights(s, "cuda")
     mw.quantise(dw.w_gu, dw.w_down)
     d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
-    names = ("q_h", "s_h", "qc_h", "sc_h", "bs", "Y", "out", "dx", "dW_gu", "dW_down", "dW_router", "d_bias")
+    names = ("q_h", "s_h", "qc_h", "sc_h", "bs", "Y", "out", "q_dgu", "s_dgu", "qc_dgu", "sc_dgu", "dXp", "dx",
+             "dW_gu", "dW_down", "dW_router", "d_bias")
     got = []
     for fused in (False, True):
         b = layer.MxBuffers(s, "cuda")
-        for n in ("qc_h", "sc_h"):
+        for n in ("qc_h", "sc_h", "qc_dgu", "sc_dgu"):
             getattr(b, n).fill_(0x5A)                    # capacity past the last group: untouched by both
         layer.forward_mx(dw.x, dw.w_router, dw.bias, mw, s, b, fuse_h_quant=fused, write_h=not fused)
-        layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router)
+        layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router, fuse_swiglu_quant=fused,
+                          fuse_combine_quant=fused, swiglu_in_dgrad2=fused)
         torch.cuda.synchronize()
         got.append({n: bits(getattr(b, n)).copy() for n in names})
     for n in names:

@@ -237,3 +237,56 @@ def test_fused_quant_e2m1_equals_two_pass(L):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(q1.cpu().numpy(), q2.cpu().numpy())
     np.testing.assert_array_equal(s1.cpu().numpy(), s2.cpu().numpy())
+
+
+@pytest.mark.parametrize("sizes", [[0, 1, 17, 33, 0, 65, 129, 300, 16, 32, 64, 128, 2], [513, 0, 7]])
+@pytest.mark.parametrize("fp4_in", [False, True])
+def test_swiglu_bwd_epilogue_equals_two_pass(L, sizes, fp4_in):
+    """The data-gradient GEMM with the SwiGLU backward in its epilogue writes the [dg | du]
+    that moe_swiglu_backward forms from the GEMM's stored bf16 dh, bit for bit, and the same
+    MXFP8 copies (row-wise and column-wise over all 2N columns, block prefix) as the dual
+    quantiser run on that result; with C omitted the copies are unchanged."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(off[-1])
+    M, G, N, K = R + 3, len(sizes), 256, 512
+    dy = mi.randn_np(41, mi.D_OUT, 0, M, K, 1.0, "bf16").astype(np.float64)
+    W = np.stack([mi.randn_np(41, mi.W_DOWN, g, N, K, 0.05, "bf16") for g in range(G)]).astype(np.float64)
+    if fp4_in:
+        from tests.test_gpu_mx4 import pack
+        A, As, _ = O.mx4_quantize_rowwise(dy)
+        parts = [O.mx4_quantize_rowwise(W[g]) for g in range(G)]
+        A = pack(A)
+        B = np.stack([pack(p[0]) for p in parts])
+    else:
+        A, As, _ = O.mx_quantize_rowwise(dy)
+        parts = [O.mx_quantize_rowwise(W[g]) for g in range(G)]
+        B = np.stack([p[0] for p in parts])
+    Bs = np.stack([p[1] for p in parts])
+    gu = torch.from_numpy(mi.randn_np(42, mi.X, 0, M, 2 * N, 2.0, "bf16")).to(torch.bfloat16).cuda()
+    offs = dev_i32(off)
+    cap = L.quant_col_blocks(M, G)
+    dh = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_grouped_gemm(_u8(A), _u8(B), dh, offs, L.MOE_EPI_NONE, workspace=_ws(L, G), a_scale=_u8(As),
+                       b_scale=_u8(Bs), fp4=fp4_in)
+    dgu = torch.full((M, 2 * N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_swiglu_backward(dh[:R], gu[:R], dgu[:R])
+    q2, s2, qc2, sc2 = (_sentinel((M, 2 * N)), _sentinel((M, 2 * N // 32)), _sentinel((2 * N, 32 * cap)),
+                        _sentinel((2 * N, cap)))
+    bs2 = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+    L.moe_group_quant_mxfp8_dual(dgu, q2, s2, qc2, sc2, offs, block_start=bs2, rows=R)
+    want = [t.cpu().numpy() for t in (q2, s2, qc2, sc2, bs2)]
+    for keep_c in (True, False):
+        C = torch.full((M, 2 * N), float("nan"), dtype=torch.bfloat16, device="cuda") if keep_c else None
+        q1, s1, qc1, sc1 = (_sentinel((M, 2 * N)), _sentinel((M, 2 * N // 32)), _sentinel((2 * N, 32 * cap)),
+                            _sentinel((2 * N, cap)))
+        bs1 = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+        L.moe_grouped_gemm(_u8(A), _u8(B), C, offs, L.MOE_EPI_SWIGLU_BWD, aux=gu, workspace=_ws(L, G),
+                           a_scale=_u8(As), b_scale=_u8(Bs), fp4=fp4_in, q_row=q1, s_row=s1, q_col=qc1, s_col=sc1,
+                           q_block_start=bs1, out_shape=(M, 2 * N))
+        torch.cuda.synchronize()
+        if keep_c:
+            np.testing.assert_array_equal(bits(C)[:R], bits(dgu)[:R])
+            assert np.all(np.isnan(host(C[R:]))), "rows outside the groups are not written"
+        for name, a, b in zip(("q_row", "s_row", "q_col", "s_col", "block_start"),
+                              [t.cpu().numpy() for t in (q1, s1, qc1, sc1, bs1)], want):
+            np.testing.assert_array_equal(a, b, err_msg=name)
