@@ -11,7 +11,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIB selects another build of the same library (the debug or host-ASan variants)
+_LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run dropless_mixture_experts_device_amd.build.build()")
 _lib = ctypes.CDLL(_LIB_PATH)

@@ -866,10 +866,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #if MOE_BUF_DMA
     // buffer resources over the tile's operand bases; lane offsets stay below 2^32 for every
     // operand the host lets through (checked there), the scalar offset carries the K slice
-    const __amdgpu_buffer_rsrc_t rsrc_a =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)0xFFFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsrc_b =
-        __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)0xFFFFFFFF, 0x00020000);
+#if MOE_DEBUG
+    // the tile's operand extents (the last row needs only the K bytes); the K slice moves into
+    // the range-checked lane offset below
+    const int64_t kbytes = bytes_of(p.K);
+    const int64_t a_rows_span = RK ? p.M : (p.uniform_rows > 0 ? p.uniform_rows : p.A_rows);
+    const int64_t b_rows_span = RK ? p.N : (SWIGLU ? 2 * (int64_t)p.N : (int64_t)p.N);
+    const int a_rec = (int)min<int64_t>((a_rows_span - 1) * a_ld + (RK ? a_ld : kbytes), 0xFFFFFFFFll);
+    const int b_rec = (int)min<int64_t>((b_rows_span - 1) * b_ld + (RK ? b_ld : kbytes), 0xFFFFFFFFll);
+#else
+    const int a_rec = (int)0xFFFFFFFF, b_rec = (int)0xFFFFFFFF;
+#endif
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, a_rec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, b_rec, 0x00020000);
     uint32_t a_voff[A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) a_voff[i] = (uint32_t)(a_src[i] - a_base);
@@ -921,8 +930,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
             const int instr = lw + kLWaves * l;
 #if MOE_BUF_DMA
             if (A_INSTR % kLWaves == 0 || instr < A_INSTR)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + instr * 1024), 16, a_voff[l],
-                                                         (uint32_t)koff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + instr * 1024), 16,
+                                                         a_voff[l] + (MOE_DEBUG ? (uint32_t)koff : 0u),
+                                                         MOE_DEBUG ? 0u : (uint32_t)koff, 0, 0);
 #else
             if constexpr (A_INSTR % kLWaves == 0) load_lds16(a_src[l] + koff, st + instr * 1024);
             else if (instr < A_INSTR) load_lds16(a_src[l] + koff, st + instr * 1024);
@@ -931,7 +941,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
             constexpr int i = l - A_PER_WAVE;
 #if MOE_BUF_DMA
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, MOE_LDS(st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024),
-                                                     16, b_voff[i], (uint32_t)koff, 0, 0);
+                                                     16, b_voff[i] + (MOE_DEBUG ? (uint32_t)koff : 0u),
+                                                     MOE_DEBUG ? 0u : (uint32_t)koff, 0, 0);
 #else
             load_lds16(b_src[i] + koff, st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024);
 #endif
@@ -1244,10 +1255,12 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
                 if (nk == 0) continue;
                 const int r0 = mt * BM, n0 = nt * kBN;
                 const int64_t ld = (int64_t)32 * nbe;
-                rsrc_a = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)32 * p.M * kb0), (short)0,
-                                                           (int)0xFFFFFFFF, 0x00020000);
-                rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)32 * p.N * kb0), (short)0,
-                                                           (int)0xFFFFFFFF, 0x00020000);
+                const int a_rec = MOE_DEBUG ? (int)min<int64_t>((int64_t)p.M * ld, 0xFFFFFFFFll) : (int)0xFFFFFFFF;
+                const int b_rec = MOE_DEBUG ? (int)min<int64_t>((int64_t)p.N * ld, 0xFFFFFFFFll) : (int)0xFFFFFFFF;
+                rsrc_a = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)32 * p.M * kb0), (short)0, a_rec,
+                                                           0x00020000);
+                rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)32 * p.N * kb0), (short)0, b_rec,
+                                                           0x00020000);
 #pragma unroll
                 for (int i = 0; i < A_PER_WAVE; ++i) {
                     const int row = (lw + kLWaves * i) * ROWS_PER_INSTR + lane / CH;
@@ -1285,13 +1298,15 @@ __device__ __forceinline__ void gemm_rk_stream(const GemmParams& p, char* lds, i
             const uint32_t koff = (uint32_t)(kt * kRowBytes);
 #pragma unroll
             for (int i = 0; i < A_PER_WAVE; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + (lw + kLWaves * i) * 1024), 16, a_voff[i],
-                                                         koff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + (lw + kLWaves * i) * 1024), 16,
+                                                         a_voff[i] + (MOE_DEBUG ? koff : 0u), MOE_DEBUG ? 0u : koff, 0,
+                                                         0);
 #pragma unroll
             for (int i = 0; i < B_PER_WAVE; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b,
                                                          MOE_LDS(st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024),
-                                                         16, b_voff[i], koff, 0, 0);
+                                                         16, b_voff[i] + (MOE_DEBUG ? koff : 0u), MOE_DEBUG ? 0u : koff,
+                                                         0, 0);
 #pragma unroll
             for (int u = 0; u < SC_PER_WAVE; ++u)
                 if (lw + kLWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4, st + s_lds[u]);
@@ -1669,6 +1684,23 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.swb = swb ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
 
+#if MOE_DEBUG
+    {
+        // the device index data, validated on the host: offsets non-decreasing within [0, M]
+        // (ragged K: [0, K/32] on multiples of 4 blocks), gather indices within [0, A_rows)
+        std::vector<int32_t> off, ar;
+        if (!moe_debug_fetch_i32(a->offsets, a->G + 1, s, off)) return MOE_EHIP;
+        const int64_t lim = a->ragged_k ? a->K / 32 : a->M;
+        for (int g = 0; g <= a->G; ++g)
+            if (off[g] < 0 || off[g] > lim || (g > 0 && off[g] < off[g - 1]) || (a->ragged_k && off[g] % 4))
+                return MOE_EINVAL;
+        if (a->a_rows) {
+            if (!moe_debug_fetch_i32(a->a_rows, a->M, s, ar)) return MOE_EHIP;
+            for (int64_t r = off[0]; r < off[a->G]; ++r)
+                if (ar[r] < 0 || ar[r] >= a->A_rows) return MOE_EINVAL;
+        }
+    }
+#endif
     if (a->a_dtype == MOE_F32) {
         p.NT = 0;
         const int64_t n = a->M * a->N;

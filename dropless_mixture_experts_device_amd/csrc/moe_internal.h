@@ -72,3 +72,21 @@ moe_status_t moe_gemm_ksplit_f32(const void* x, const void* w, int64_t T, int64_
                                  hipStream_t s);
 
 static inline bool moe_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// MOE_DEBUG builds (never the release library): the grouped GEMM's operand loads carry the
+// operand's real extent in their buffer descriptors, so the hardware returns zeros for any
+// load outside it instead of reading past the buffer, and the entry points copy the device
+// index data they are given (group offsets, gather indices, expert ids) to the host and
+// validate it before launching anything (a synchronising copy: not for graph capture).
+#ifndef MOE_DEBUG
+#define MOE_DEBUG 0
+#endif
+#if MOE_DEBUG
+#include <vector>
+static inline bool moe_debug_fetch_i32(const int32_t* dev, int64_t n, hipStream_t s, std::vector<int32_t>& out) {
+    out.assign((size_t)(n > 0 ? n : 0), 0);
+    if (n <= 0) return true;
+    if (hipMemcpyAsync(out.data(), dev, (size_t)n * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+    return hipStreamSynchronize(s) == hipSuccess;
+}
+#endif

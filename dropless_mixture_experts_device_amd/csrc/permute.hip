@@ -210,6 +210,20 @@ extern "C" moe_status_t moe_permute(const void* x, int32_t dtype, const int32_t*
     if (!workspace || workspace_bytes < moe_permute_workspace_bytes(T, E)) return MOE_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
+#if MOE_DEBUG
+    {
+        // expert ids within [0, E) and distinct within each token
+        std::vector<int32_t> ids;
+        if (!moe_debug_fetch_i32(topk_idx, T * k, s, ids)) return MOE_EHIP;
+        for (int64_t t = 0; t < T; ++t)
+            for (int j = 0; j < k; ++j) {
+                const int32_t e = ids[t * k + j];
+                if (e < 0 || e >= E) return MOE_EINVAL;
+                for (int i = 0; i < j; ++i)
+                    if (ids[t * k + i] == e) return MOE_EINVAL;
+            }
+    }
+#endif
     const int Ti = (int)T;
     moe::PermWs ws = moe::perm_ws(workspace, T, E);
     if (T > 0) {

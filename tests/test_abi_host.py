@@ -8,7 +8,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
-LIB = os.path.join(ROOT, "dropless_mixture_experts_device_amd", "libmoe.so")
+# MOE_LIB: the same tests against another build of the library (the host-ASan build)
+LIB = os.environ.get("MOE_LIB") or os.path.join(ROOT, "dropless_mixture_experts_device_amd", "libmoe.so")
 
 
 def _declared():
@@ -30,6 +31,21 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_debug_build_exports_every_symbol():
+    """The MOE_DEBUG build (libmoe_debug.so, built next to libmoe.so) exports the same entry
+    points and answers the same host-side argument checks."""
+    path = os.path.join(ROOT, "dropless_mixture_experts_device_amd", "libmoe_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe_debug.so is not built")
+    dbg = ctypes.CDLL(path)
+    for n in _declared():
+        assert hasattr(dbg, n), n
+    dbg.moe_combine.restype = ctypes.c_int
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake, 1, fake, fake, None, ctypes.c_int64(16), ctypes.c_int64(60), ctypes.c_int32(2), fake, None]
+    assert dbg.moe_combine(*args) == 1          # d % 8 != 0: MOE_EINVAL, as the release build
 
 
 def test_binding_covers_every_symbol():
