@@ -30,4 +30,10 @@ def run_mx_step():
     d_out = mi.randn_torch(w.seed, mi.D_OUT, 0, w.T, w.d, 1.0, "bf16", "cuda")
     layer.backward_mx(dw.x, d_out, mw, s, b, w_router=dw.w_router)
     torch.cuda.synchronize()
-    return {f"mx_{n}": bits(getattr(b, n)) for n in ("out", "dx", "dW_gu", "dW_down", "dW_router", "q_h", "qc_dgu")}
+    res = {f"mx_{n}": bits(getattr(b, n)) for n in ("out", "dx", "dW_gu", "dW_down", "dW_router", "q_h")}
+    # the column-wise copy is written group-major up to the block prefix's end (32 code bytes per
+    # column and block); the buffer's capacity past it is never written, so it is not compared
+    nblk = int(b.bs[-1].item())
+    res["mx_qc_dgu"] = b.qc_dgu.reshape(-1)[: 32 * b.qc_dgu.shape[0] * nblk].cpu().numpy()
+    res["mx_bs"] = b.bs.cpu().numpy()
+    return res
