@@ -67,6 +67,25 @@ constexpr int kChunks = kRowBytes / 16;
 #define MOE_BUF_DMA 0
 #endif
 
+#ifndef MOE_GEMM_SPLIT256
+#define MOE_GEMM_SPLIT256 1       // bf16 groups' full 256-row chunks as 256 x 256 tiles (gemm_split_kernel)
+#endif
+// smallest group whose 256-row chunks take 256 x 256 tiles: K below MOE_GEMM_SPLIT_LONGK, and
+// from it on. Measured on the DeepSeek-V3 group sizes (one MI355X; 257 groups, 73,728 rows):
+// the down projection (K = 2,048) 2.96 -> 2.65 ms with every group of 256 rows or more split;
+// the gate/up projection (K = 7,168) on unpermuted rows 5.47 ms unsplit, 5.58 / 5.48 / 5.35 ms
+// with groups from 256 / 512 / 1,024 rows split. With gathered A rows (the fused gather) the
+// gate/up projection ran 5.22 ms unsplit against 5.35-5.53 ms split at any threshold, so
+// launches with a row index do not split.
+#ifndef MOE_GEMM_SPLIT_MIN_ROWS
+#define MOE_GEMM_SPLIT_MIN_ROWS 256
+#endif
+#ifndef MOE_GEMM_SPLIT_LONGK
+#define MOE_GEMM_SPLIT_LONGK 4096
+#endif
+#ifndef MOE_GEMM_SPLIT_MIN_ROWS_LONGK
+#define MOE_GEMM_SPLIT_MIN_ROWS_LONGK 1024
+#endif
 #ifndef MOE_GEMM_TILE256
 #define MOE_GEMM_TILE256 0        // 256-row tiles for bf16 groups of >= 256 rows with a bf16 output (measured
                                   // slower on the DeepSeek-V3 and Mixtral shapes: longer tiles, worse tail)
@@ -178,6 +197,11 @@ __device__ __forceinline__ void row_tile(const RowTiles& t, int mt, int& r_off, 
     }
 }
 
+// Rows of a group of m rows that 256 x 256 tiles cover (its full 256-row chunks) when the
+// launch splits; its other row tiles start that many rows in.
+// split_min: the smallest group that gets them (0: the launch does not split; else >= 256).
+__device__ __forceinline__ int chunk256_rows(int m, int split_min) { return (split_min && m >= split_min) ? (m & ~255) : 0; }
+
 // Rows [begin, end) of group g, clamped into [0, M] so that inconsistent offsets can never
 // send a load or store outside the buffers.
 __device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int M, int& begin, int& end) {
@@ -233,6 +257,10 @@ struct GemmParams {
     int64_t q_col_blocks;        // capacity of q_col / s_col in blocks
     int c_skip;                  // C is not written (only its quantised copies)
     int swb;                     // SwiGLU-backward epilogue: C = [dg | du] from dh and the saved aux
+    // bf16 ragged rows (0 = off): the full 256-row chunks of every group of at least split256
+    // rows are 256 x 256 tiles, its first tiles in the schedule; the rows past them get the
+    // usual row tiles (gemm_split_kernel)
+    int split256;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -249,7 +277,8 @@ struct GemmParams {
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int G, int M,
                                                              int NT, int allow256, int32_t* __restrict__ tile_start,
                                                              int32_t* __restrict__ order,
-                                                             int32_t* __restrict__ block_start = nullptr) {
+                                                             int32_t* __restrict__ block_start = nullptr,
+                                                             int split256 = 0) {
     __shared__ unsigned long long key[2048];
     __shared__ int tiles_of[2048];
     __shared__ int sorted[2048];
@@ -269,7 +298,9 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
             int b, e;
             group_rows(offsets, g, M, b, e);
             rows_of[h] = e - b;
-            t = row_tiles(e - b, allow256 != 0).count() * NT;
+            // split: the full 256-row chunks' tiles, then the rest's
+            const int c256 = chunk256_rows(e - b, split256);
+            t = (c256 / 256 + row_tiles(e - b - c256, allow256 != 0).count()) * NT;
             small = (e - b) <= 128;
         }
         if (g < 2048) tiles_of[g] = t;
@@ -745,8 +776,12 @@ __device__ __forceinline__ void swb_epilogue(const GemmParams& p, char* lds, int
 // offsets[g] .. offsets[g+1]-1 of 32 K elements, read from the group-major column-wise
 // layout (group g's A block [M, 32 n_g] at A + 32 M offsets[g], row stride 32 n_g; likewise
 // B with N rows and both scale blocks), and writes it at C + g * c_stride.
-template <int BM, bool SWIGLU, int FMT, bool RK>
+// PW: producer waves of the calling kernel (kPWaves in gemm_mfma_kernel; 0 in the 8-wave
+// kernel that also runs 256-row tiles, whose MFMA waves issue their own loads)
+template <int BM, bool SWIGLU, int FMT, bool RK, int PW = kPWaves>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g, int r_off, int nt) {
+    constexpr int LW = PW ? PW : kWaves;          // waves that issue the DMA loads
+    constexpr int THR = (kWaves + PW) * kWave;    // threads of the workgroup
     constexpr bool MX = FMT != kBF16;                   // block-scaled operands (E8M0 scales)
     constexpr bool FP4 = FMT == kE2M1;
     constexpr int EB = MX ? 1 : 2;                      // operand element bytes (E2M1: half a byte)
@@ -765,15 +800,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     constexpr int MI = WTM / MS;
     constexpr int NI = WTN / MS;
     constexpr int A_INSTR = BM / ROWS_PER_INSTR;         // 1 KiB DMA instructions for the A slice
-    constexpr int A_PER_WAVE = cdiv(A_INSTR, kLWaves);
-    constexpr int B_PER_WAVE = kBN / ROWS_PER_INSTR / kLWaves;
+    constexpr int A_PER_WAVE = cdiv(A_INSTR, LW);
+    constexpr int B_PER_WAVE = kBN / ROWS_PER_INSTR / LW;
     constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
     constexpr int SDW = ST::kScaleDw;                    // scale dwords per row and stage
     constexpr int AS_GRP = cdiv(BM, 64);                 // 64-row groups of A (one scale instruction each)
     constexpr int BS_GRP = kBN / 64;
     constexpr int AS_INSTR = AS_GRP * SDW;               // scale dword instructions of a stage: A, then B
     constexpr int BS_INSTR = BS_GRP * SDW;
-    constexpr int SC_PER_WAVE = MX ? cdiv(AS_INSTR + BS_INSTR, kLWaves) : 0;   // scale instructions per wave
+    constexpr int SC_PER_WAVE = MX ? cdiv(AS_INSTR + BS_INSTR, LW) : 0;   // scale instructions per wave
     constexpr int NST = ST::kCount;
     constexpr int SB = ST::kBytes;
     static_assert(NST * SB <= pipe_bytes<FMT>(), "pipeline stages exceed the LDS ring");
@@ -781,6 +816,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     static_assert(BM < 256 || (BM * (kBN * 2 + 16) <= kPipeBytes), "bf16 epilogue tile must fit in LDS");
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
     static_assert(SC_PER_WAVE <= 3, "at most three scale loads per wave");
+    static_assert(!MX || PW == kPWaves, "block-scaled epilogues assume the persistent kernel's threads");
 
     if constexpr (BM == 256) {
         if (p.c_f32) return;   // never scheduled: 256-row tiles are only chosen for 2-byte outputs
@@ -793,8 +829,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
-    const bool producer = kPWaves > 0 && wave >= kWaves;
-    const int lw = kPWaves ? wave - kWaves : wave;      // index among the load-issuing waves
+    const bool producer = PW > 0 && wave >= kWaves;
+    const int lw = PW ? wave - kWaves : wave;      // index among the load-issuing waves
     int row_begin, row_end;
     int nk = p.K / KPS;                                   // K slices
     char* Cg = p.C;
@@ -858,7 +894,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     const char* a_src[A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
-        const int instr = lw + kLWaves * i;
+        const int instr = lw + LW * i;
         const int row = instr * ROWS_PER_INSTR + lane / kChunks;
         const int chunk = (lane % kChunks) ^ swz(row);
         a_src[i] = a_base + a_row_of(row) * a_ld + chunk * 16;
@@ -897,14 +933,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     for (int i = 0; i < B_PER_WAVE; ++i) b_voff[i] = (uint32_t)(b_src[i] - b_base);
 #endif
     // MXFP8 scale rows: scale instruction q (0 .. AS_INSTR+BS_INSTR-1) is issued by load wave
-    // q % kLWaves as its (q / kLWaves)-th scale load; instructions below AS_INSTR bring 64 A rows' scale
+    // q % LW as its (q / LW)-th scale load; instructions below AS_INSTR bring 64 A rows' scale
     // dwords, the others 64 B rows'
     const uint8_t* s_src[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
     int s_lds[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
     if constexpr (MX) {
 #pragma unroll
         for (int u = 0; u < SC_PER_WAVE; ++u) {
-            const int q = lw + kLWaves * u;
+            const int q = lw + LW * u;
             if (q < AS_INSTR) {
                 // dword h = q / AS_GRP of the stage's scales of rows 64 (q % AS_GRP) + lane
                 const int h = q / AS_GRP, grp = q % AS_GRP;
@@ -927,14 +963,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         char* st = lds + (kt % NST) * SB;
         const int64_t koff = (int64_t)kt * kRowBytes;
         if constexpr (l < A_PER_WAVE) {
-            const int instr = lw + kLWaves * l;
+            const int instr = lw + LW * l;
 #if MOE_BUF_DMA
-            if (A_INSTR % kLWaves == 0 || instr < A_INSTR)
+            if (A_INSTR % LW == 0 || instr < A_INSTR)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, MOE_LDS(st + instr * 1024), 16,
                                                          a_voff[l] + (MOE_DEBUG ? (uint32_t)koff : 0u),
                                                          MOE_DEBUG ? 0u : (uint32_t)koff, 0, 0);
 #else
-            if constexpr (A_INSTR % kLWaves == 0) load_lds16(a_src[l] + koff, st + instr * 1024);
+            if constexpr (A_INSTR % LW == 0) load_lds16(a_src[l] + koff, st + instr * 1024);
             else if (instr < A_INSTR) load_lds16(a_src[l] + koff, st + instr * 1024);
 #endif
         } else if constexpr (l < A_PER_WAVE + B_PER_WAVE) {
@@ -949,7 +985,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         } else {
             // 4 scale bytes (4 blocks of 32) per row and instruction; the stage's 4 * SDW blocks
             constexpr int u = l - A_PER_WAVE - B_PER_WAVE;
-            if (lw + kLWaves * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4 * SDW, st + s_lds[u]);
+            if (lw + LW * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4 * SDW, st + s_lds[u]);
         }
     };
     auto issue = [&](int kt) {
@@ -964,7 +1000,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 
     // Per-wave loads per stage differ (some waves issue no A or scale load); the wait count
     // uses the smallest, so every wave is sure its own loads of stage kt have landed.
-    constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / kLWaves;
+    constexpr int LOADS_MIN = B_PER_WAVE + A_INSTR / LW;
 
     // per-lane LDS byte offsets of the first A and B fragment (fixed for the whole tile).
     // Fragment i (j) sits MS*i rows further down; MS is a multiple of 16 and swz() reads only
@@ -1071,7 +1107,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     // pending (LOADS_MIN per stage); the barrier then makes every wave's loads of stage kt
     // visible and guarantees that the buffer refilled during compute(kt) (stage kt+NST-1,
     // last read in iteration kt-1) is no longer in use.
-    if (nk > 0 && kPWaves == 0) {    // only a ragged-K group with an empty range has no slice (C_g = 0)
+    if (nk > 0 && PW == 0) {    // only a ragged-K group with an empty range has no slice (C_g = 0)
         lds_barrier();   // the previous tile's epilogue may still read LDS
 #pragma unroll
         for (int s0 = 0; s0 < NST - 1; ++s0)
@@ -1165,7 +1201,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         if (p.q_fmt != 0) quant_epilogue<BM, BN_OUT>(p, lds, pitch, g, r0, r_off, rows_valid, n0, tid, p.N, p.N);
         if (p.c_skip) return;
     }
-    for (int c = tid; c < BM * chunks_per_row; c += kThreads) {
+    for (int c = tid; c < BM * chunks_per_row; c += THR) {
         const int row = c / chunks_per_row, ch = c % chunks_per_row;
         const int col = n0 + ch * cols_per_chunk;
         if (row < rows_valid && col < p.N) {
@@ -1494,6 +1530,240 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// 256 x 256 tiles for the full 256-row chunks of bf16 groups (bf16 output, ragged rows, no
+// G|U save), in gemm_split_kernel.
+//
+// A 128 x 256 tile asks L2 for 384 operand rows per 32,768 outputs, a 256 x 256 tile for 512
+// rows per 65,536: a third fewer line requests per FLOP. Inside the persistent kernel (waves
+// of 168 registers, two stages fed by the four load waves) 256-row tiles run slower; the
+// shape measured faster on one MI355X is a workgroup of 8 waves, each a 64 x 128 wave tile
+// (4 x 2), every wave issuing its own loads. Wave w brings 64 rows of a stage (A rows for
+// w < 4, B rows otherwise) as whole 128-byte lines (64 bf16 of K) through buffer_load ... lds
+// into a two-slot ring of 64 KiB stages; the loads of stage kt+2 leave right after the
+// barrier that frees stage kt's slot, and that barrier sits before the stage's last k-step,
+// so the next stage's first fragment reads hide under the MFMAs. Half-line (64-byte) K
+// slices in deeper rings, four waves of 128 x 128 and operands staged through registers all
+// measured slower. The K order and the MFMA (32x32x16 bf16, k-steps in ascending K within
+// each 64-element stage) are the 128-row tiles', so a row's outputs are bit-identical
+// whichever tile computes them.
+// ---------------------------------------------------------------------------------------
+constexpr int k256Threads = (kWaves + 0) * kWave;                  // 8 waves, no producer waves
+constexpr int k256Stage = 2 * 256 * kRowBytes;                      // 256 A rows, then 256 B rows
+static_assert(kWaves == 8, "the 256-row tile's wave grid is 4 x 2 waves of 64 x 128");
+static_assert(2 * k256Stage <= kPipeBytes && 256 * (kBN * 2 + 16) <= kPipeBytes, "256-row ring and staging fit");
+
+// rows [r0, r0 + 256) of group g (rows [gb, ge)), column tile nt
+template <bool SWIGLU>
+__device__ __forceinline__ void gemm256_tile(const GemmParams& p, char* lds, int g, int ge, int r0, int nt) {
+    constexpr int WN = 2, WTM = 64, WTN = 128, MI = 2, NI = 4, MS = 32;
+    constexpr int BN_OUT = SWIGLU ? kBN / 2 : kBN;
+    constexpr int NO = SWIGLU ? NI / 2 : NI;       // output fragments per wave row block
+    constexpr int WOUT = SWIGLU ? WTN / 2 : WTN;   // output columns per wave
+    constexpr int IPW = 64 / (1024 / kRowBytes);   // 1 KiB DMA instructions per wave and stage (64 rows)
+    using MF = Mfma<MS, kBF16>;
+    // the lane index is opaque per tile, so its per-lane offsets are derived here rather than
+    // kept live across the persistent tile loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / WN, wn = wave % WN;
+    const bool loads_a = wave < 4;
+    const int lrow0 = (wave % 4) * 64;             // first A (or B) row of this wave's loads
+    const int nk = p.K / (kRowBytes / 2);
+    const int64_t a_ld = p.lda * 2, b_ld = p.ldb * 2;
+    const int n0 = nt * BN_OUT;
+#if MOE_DEBUG
+    // range-checked operand extents; the K slice moves into the checked lane offset
+    const int64_t kbytes = (int64_t)p.K * 2;
+    const int a_rec = (int)min<int64_t>((p.A_rows - 1) * a_ld + kbytes, 0xFFFFFFFFll);
+    const int b_rec = (int)min<int64_t>(((SWIGLU ? 2 : 1) * (int64_t)p.N - 1) * b_ld + kbytes, 0xFFFFFFFFll);
+#else
+    const int a_rec = (int)0xFFFFFFFF, b_rec = (int)0xFFFFFFFF;
+#endif
+    // fragment offsets of a stage's four k-steps (as gemm_tile's)
+    int a_off[4], b_off[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int chunk = MF::frag_chunk(lane, ks);
+        const int ra = wm * WTM + MF::frag_row(lane), rb = 256 + wn * WTN + MF::frag_row(lane);
+        a_off[ks] = ra * kRowBytes + ((chunk ^ swz(ra)) << 4);
+        b_off[ks] = rb * kRowBytes + ((chunk ^ swz(rb)) << 4);
+    }
+    // this wave's DMA sources: lane l of instruction i fills LDS row lrow0 + 8 i + l / 8 of its
+    // operand, slot l % 8, with global chunk (l % 8) ^ swz(row)
+    const char* base = loads_a ? p.A : p.B + (int64_t)g * p.b_stride * 2;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, loads_a ? a_rec : b_rec, 0x00020000);
+    uint32_t voff[IPW];
+    if (loads_a) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int row = lrow0 + 8 * i + lane / 8;
+            const int r = min(r0 + row, ge - 1);
+            const int64_t ar = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
+            const int64_t ac = ar < 0 ? 0 : (ar >= p.A_rows ? p.A_rows - 1 : ar);
+            voff[i] = (uint32_t)(ac * a_ld + (((lane % 8) ^ swz(row)) << 4));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int row = lrow0 + 8 * i + lane / 8;
+            int br;
+            if (SWIGLU) {
+                // wave wn's 128 B rows: 64 gate rows, then the matching 64 up rows
+                const int wnb = row / WTN, within = row % WTN;
+                br = (within / (WTN / 2)) * p.N + min(n0 + wnb * (WTN / 2) + within % (WTN / 2), p.N - 1);
+            } else {
+                br = min(n0 + row, p.N - 1);
+            }
+            voff[i] = (uint32_t)((int64_t)br * b_ld + (((lane % 8) ^ swz(row)) << 4));
+        }
+    }
+    char* const dst0 = lds + (loads_a ? 0 : 256 * kRowBytes) + lrow0 * kRowBytes;
+    auto issue = [&](int kt) {
+        char* st = dst0 + (kt & 1) * k256Stage;
+        const uint32_t koff = (uint32_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(st + i * 1024), 16, voff[i] + (MOE_DEBUG ? koff : 0u),
+                                                     MOE_DEBUG ? 0u : koff, 0, 0);
+    };
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = acc_zero<MS, kBF16>();
+    bf16x8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+    auto frags = [&](int kt, int ks, bf16x8 (&fa)[MI], bf16x8 (&fb)[NI]) {
+        const char* st = lds + (kt & 1) * k256Stage;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + i * MS * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + j * MS * kRowBytes);
+    };
+    auto mfmas = [&](const bf16x8 (&fa)[MI], const bf16x8 (&fb)[NI]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // one LDS fragment read after each of the first six MFMAs of a k-step
+#define MOE_G256_ILV(grp)                                        \
+    for (int q = 0; q < 6; ++q) {                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, grp);     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, grp);     \
+    }                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, grp);
+    lds_barrier();   // the previous tile's epilogue is done with LDS
+    issue(0);
+    if (nk > 1) {
+        issue(1);
+        wait_vm_lgkm0<IPW>();
+    } else {
+        wait_vm_lgkm0<0>();
+    }
+    lds_barrier();
+    frags(0, 0, fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+        frags(kt, 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        MOE_G256_ILV(0)
+        frags(kt, 2, fa0, fb0);
+        mfmas(fa1, fb1);
+        MOE_G256_ILV(1)
+        frags(kt, 3, fa1, fb1);
+        mfmas(fa0, fb0);
+        MOE_G256_ILV(2)
+        // own fragment reads of stage kt and own loads of stage kt+1 done; after the barrier
+        // stage kt+1 is visible and nobody reads stage kt's slot, which stage kt+2 refills
+        wait_vm_lgkm0<0>();
+        lds_barrier();
+        if (kt + 2 < nk) issue(kt + 2);
+        frags(kt + 1, 0, fa0, fb0);   // after the last stage: a stale slot, never used
+        mfmas(fa1, fb1);
+        MOE_G256_ILV(3)
+    }
+#undef MOE_G256_ILV
+    // ---- epilogue: values -> LDS (bf16) -> 16-byte coalesced stores ----
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    constexpr int pitch = BN_OUT * 2 + 16;
+    const int rows_valid = min(256, ge - r0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int col = wn * WOUT + j * MS + MF::out_col(lane);
+#pragma unroll
+            for (int r = 0; r < MF::NACC; ++r) {
+                const int row = wm * WTM + i * MS + MF::out_row(lane, r);
+                const float v = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + NO][r] : acc[i][j][r];
+                *reinterpret_cast<uint16_t*>(lds + row * pitch + col * 2) = f32_to_bf16(v);
+            }
+        }
+    lds_barrier();
+    constexpr int chunks_per_row = BN_OUT * 2 / 16;
+    for (int c = tid; c < 256 * chunks_per_row; c += k256Threads) {
+        const int row = c / chunks_per_row, ch = c % chunks_per_row;
+        const int col = n0 + ch * 8;
+        if (row < rows_valid && col < p.N) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + ch * 16);
+            u32x4* cp = reinterpret_cast<u32x4*>(p.C + ((int64_t)(r0 + row) * p.ldc + col) * 2);
+            if (MOE_GEMM_C_NT == 2 || (MOE_GEMM_C_NT == 1 && !SWIGLU)) __builtin_nontemporal_store(v, cp);
+            else *cp = v;
+        }
+    }
+}
+
+// bf16 ragged-row launches with the split: one persistent walk over the schedule, a group's
+// first tiles being 256 x 256 over its full 256-row chunks and the rest the usual row tiles
+// (their loads issued by the MFMA waves themselves: this workgroup has no producer waves).
+template <bool SWIGLU>
+__global__ __launch_bounds__(k256Threads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_split_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int nxcd = (gridDim.x % 8 == 0) ? 8 : 1;   // XCD-aware slots, as gemm_mfma_kernel
+    const int per_xcd = gridDim.x / nxcd;
+    const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
+    int32_t* ts = reinterpret_cast<int32_t*>(lds + kPipeBytes);
+    for (int g = threadIdx.x; g <= p.G; g += k256Threads) ts[g] = p.tile_start[g];
+    __syncthreads();
+    const int total = ts[p.G];
+    for (int tile = slot; tile < total; tile += gridDim.x) {
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ts[mid] <= tile) lo = mid;
+            else hi = mid - 1;
+        }
+        const int g = min(max(p.order[lo], 0), p.G - 1);
+        const int L = tile - ts[lo];
+        int gb, ge;
+        group_rows(p.offsets, g, p.M, gb, ge);
+        const int c256 = chunk256_rows(ge - gb, p.split256);
+        const int t256 = (c256 / 256) * p.NT;
+        int mt, nt;
+        if (L < t256) {
+            tile_coords(L, c256 / 256, p.NT, mt, nt);
+            gemm256_tile<SWIGLU>(p, lds, g, ge, gb + 256 * mt, nt);
+            continue;
+        }
+        const RowTiles rt = row_tiles(ge - gb - c256, false);
+        int r_off, bm;
+        tile_coords(L - t256, rt.count(), p.NT, mt, nt);
+        row_tile(rt, mt, r_off, bm);
+        r_off += c256;
+        switch (bm) {
+            case 16: gemm_tile<16, SWIGLU, kBF16, false, 0>(p, lds, g, r_off, nt); break;
+            case 32: gemm_tile<32, SWIGLU, kBF16, false, 0>(p, lds, g, r_off, nt); break;
+            case 64: gemm_tile<64, SWIGLU, kBF16, false, 0>(p, lds, g, r_off, nt); break;
+            default: gemm_tile<128, SWIGLU, kBF16, false, 0>(p, lds, g, r_off, nt); break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // fp32 grouped GEMM: one thread per output element, sequential fp32 dot products.
 // Meant for small fp32 layers (correctness, not speed).
 // ---------------------------------------------------------------------------------------
@@ -1550,6 +1820,20 @@ bool set_lds_attr() {
         done = true;
     }
     return true;
+}
+
+template <bool SWIGLU>
+moe_status_t launch_split(const GemmParams& p, int grid, hipStream_t s) {
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)gemm_split_kernel<SWIGLU>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsBytes) != hipSuccess)
+            return MOE_EHIP;
+        attr = true;
+    }
+    hipLaunchKernelGGL((gemm_split_kernel<SWIGLU>), dim3((unsigned)grid), dim3(k256Threads), kLdsBytes, s, p);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
 }
 
 template <bool SWIGLU, int FMT, bool RK = false>
@@ -1683,6 +1967,13 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     p.c_skip = a->C == nullptr ? 1 : 0;
     p.swb = swb ? 1 : 0;
     const bool swiglu = a->epilogue == MOE_EPI_SWIGLU;
+    // bf16 operands and output, ragged rows, A read in row order, plain or SwiGLU epilogue
+    // without the G|U save: gemm_split_kernel, full 256-row chunks of large groups as 256 x 256
+    // tiles (none while M < 256)
+    const bool split = MOE_GEMM_SPLIT256 && a->a_dtype == MOE_BF16 && a->c_dtype == MOE_BF16 && !a->ragged_k &&
+                       !quant && !swb && !a->aux && !a->a_rows && p.allow256 == 0 && a->M >= 256;
+    p.split256 = !split ? 0 : a->K >= MOE_GEMM_SPLIT_LONGK ? std::max(MOE_GEMM_SPLIT_MIN_ROWS_LONGK, 256)
+                                                            : std::max(MOE_GEMM_SPLIT_MIN_ROWS, 256);
 
 #if MOE_DEBUG
     {
@@ -1746,11 +2037,12 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     }
     hipLaunchKernelGGL(moe::gemm_schedule_kernel, dim3(1), dim3(1024), 0, s, a->offsets, a->G, p.M, p.NT,
                        p.allow256, (int32_t*)workspace, (int32_t*)workspace + (a->G + 1),
-                       a->q_col ? a->q_block_start : nullptr);
+                       a->q_col ? a->q_block_start : nullptr, p.split256);
     MOE_CHECK_LAUNCH();
     // enough persistent workgroups to fill every CU, never more than the tile bound
     const int64_t bound = (a->M / 16 + a->G) * (int64_t)p.NT;
     const int grid = (int)std::min<int64_t>((int64_t)moe::num_cus(), std::max<int64_t>(bound, 1));
+    if (split) return swiglu ? moe::launch_split<true>(p, grid, s) : moe::launch_split<false>(p, grid, s);
     if (swiglu)
         return fp4 ? moe::launch<true, moe::kE2M1>(p, grid, s)
                    : mx ? moe::launch<true, moe::kE4M3>(p, grid, s) : moe::launch<true, moe::kBF16>(p, grid, s);

@@ -5,7 +5,10 @@ offsets: the schedule kernel's tile prefix and group order, the persistent workg
 over the tile list (XCD-aware slots, binary search of the prefix, row-tile and column-tile
 decomposition), and for every tile the byte ranges its load waves' DMA instructions read (A
 rows through the gather index, B rows of the group, MXFP8 scale dwords, over every K slice),
-the LDS bytes they fill, and the output elements the epilogue writes. It asserts that every
+the LDS bytes they fill, and the output elements the epilogue writes. bf16 launches that
+split (gemm_split_kernel) take each group's full 256-row chunks as 256 x 256 tiles first (8
+waves that each load 64 rows of a stage), then the usual row tiles with all 8 waves issuing
+loads. It asserts that every
 access stays inside its buffer and that every output element of every group is written by
 exactly one tile, so a launch shape can be cleared on the CPU before it runs on a GPU.
 
@@ -43,6 +46,24 @@ LDS_BYTES = PIPE_BYTES + (MAX_GROUPS + 1) * 4
 PIPE_BYTES_FP4 = 3 * stage_bytes(128, True)["bytes"]
 MAX_GROUPS_FP4 = (160 * 1024 - PIPE_BYTES_FP4) // 4 - 1
 assert MAX_GROUPS_FP4 == 1791 and PIPE_BYTES_FP4 + (MAX_GROUPS_FP4 + 1) * 4 <= 160 * 1024
+
+# 256 x 256 tiles: two 64 KiB stages (256 A rows, then 256 B rows) and the bf16 output tile
+# staged over them, all below the tile prefix
+STAGE256 = 2 * 256 * ROW_BYTES
+assert 2 * STAGE256 <= PIPE_BYTES and 256 * (BN * 2 + 16) <= PIPE_BYTES
+
+
+# the host's split thresholds: smallest group whose 256-row chunks take 256 x 256 tiles, for K
+# below SPLIT_LONGK and from it on
+SPLIT_MIN_ROWS = 256
+SPLIT_LONGK = 4096
+SPLIT_MIN_ROWS_LONGK = 1024
+
+
+def chunk256_rows(m, split_min):
+    """Rows of a group that 256 x 256 tiles cover (its full 256-row chunks) when the launch
+    splits (split_min: the smallest group that gets them; 0: no split)."""
+    return (m & ~255) if (split_min and m >= split_min) else 0
 
 
 def bm_of_rows(m):
@@ -91,15 +112,17 @@ def group_rows(offsets, g, M):
     return b, e
 
 
-def schedule(offsets, G, M, NT, allow256=False):
-    """tile_start [G+1] and order [G] as gemm_schedule_kernel writes them."""
+def schedule(offsets, G, M, NT, allow256=False, split=0):
+    """tile_start [G+1] and order [G] as gemm_schedule_kernel writes them (split: a group's
+    tiles are its 256-row chunks' tiles, then the row tiles of the rows past them)."""
     tiles = np.zeros(G, np.int64)
     small = np.zeros(G, bool)
     rows = np.zeros(G, np.int64)
     for g in range(G):
         b, e = group_rows(offsets, g, M)
         rows[g] = e - b
-        tiles[g] = rt_count(row_tiles(e - b, allow256)) * NT
+        c256 = chunk256_rows(e - b, split)
+        tiles[g] = (c256 // 256 + rt_count(row_tiles(e - b - c256, allow256))) * NT
         small[g] = (e - b) <= 128
     tot_small = int(tiles[small].sum())
     tot_large = int(tiles[~small].sum())
@@ -152,6 +175,18 @@ class Launch:
     b_scale_bytes: int = 0
     aux_ld: int = 0
     num_cus: int = 256
+    split256: int | None = None    # None: the host's rule (bf16, bf16 C, ragged rows, no row index,
+                                   # no G|U save, M >= 256)
+
+
+def splits(la) -> int:
+    """The launch's split256 parameter: 0, or the smallest group with 256 x 256 tiles."""
+    if la.split256 is not None:
+        return la.split256
+    if (not la.mx) and la.c_esize == 2 and la.uniform_rows == 0 and la.aux_ld == 0 and la.a_rows is None \
+            and la.M >= 256:
+        return max(SPLIT_MIN_ROWS_LONGK if la.K >= SPLIT_LONGK else SPLIT_MIN_ROWS, 256)
+    return 0
 
 
 def check_launch(la: Launch):
@@ -180,14 +215,16 @@ def check_launch(la: Launch):
         tiles = total
         grid = min(la.num_cus, tiles)
     else:
-        ts, order = schedule(la.offsets, G, la.M, NT)
+        split = splits(la)
+        ts, order = schedule(la.offsets, G, la.M, NT, split=split)
         total = int(ts[G])
         bound = (la.M // 16 + G) * NT
         grid = min(la.num_cus, max(bound, 1))
     nxcd = 8 if grid % 8 == 0 else 1
     per_xcd = grid // nxcd
     written = np.zeros((la.M, NT), np.int32)     # tiles covering each (row, column tile)
-    seen_tiles = 0
+    seen_tiles = total256 = 0
+    lwaves = 8 if (not uniform and split) else L_WAVES   # the split kernel has no producer waves
     for bid in range(grid):
         slot = (bid % nxcd) * per_xcd + bid // nxcd
         for tile in range(slot, total, grid):
@@ -208,12 +245,23 @@ def check_launch(la: Launch):
                 g = min(max(int(order[lo]), 0), G - 1)
                 L = tile - int(ts[lo])
                 rb, re = group_rows(la.offsets, g, la.M)
-                rt = row_tiles(re - rb)
+                c256 = chunk256_rows(re - rb, split)
+                t256 = c256 // 256 * NT
+                if L < t256:
+                    mt, nt = tile_coords(L, c256 // 256, NT)
+                    assert 0 <= mt < c256 // 256 and 0 <= nt < NT, (tile, g, mt, nt)
+                    _check_tile256(la, g, rb, re, rb + 256 * mt, nt, nk, written)
+                    total256 += 1
+                    continue
+                L -= t256
+                rt = row_tiles(re - rb - c256)
             mt, nt = tile_coords(L, rt_count(rt), NT)
             assert 0 <= mt < rt_count(rt) and 0 <= nt < NT, (tile, g, mt, nt)
             r_off, bm = row_tile(rt, mt)
+            if not uniform:
+                r_off += c256
             assert bm in (16, 32, 64, 128)
-            _check_tile(la, g, rb, re, r_off, bm, nt, nk, byt, written)
+            _check_tile(la, g, rb, re, r_off, bm, nt, nk, byt, written, lwaves)
     assert seen_tiles == total
     # every row of every group: each column tile written exactly once; other rows untouched
     live = np.zeros(la.M, bool)
@@ -226,10 +274,59 @@ def check_launch(la: Launch):
         live[b:e] = True
     assert np.all(written[live] == 1), "an output element of a group was not written exactly once"
     assert np.all(written[~live] == 0), "a row outside every group was written"
-    return dict(grid=grid, tiles=total, nk=nk, NT=NT)
+    return dict(grid=grid, tiles=total, nk=nk, NT=NT, tiles256=total256)
 
 
-def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written):
+def _check_tile256(la, g, row_begin, row_end, r0, nt, nk, written):
+    """One gemm256_kernel tile: waves 0-3 load A rows, 4-7 B rows, 64 per wave and stage in 8
+    instructions of 8 rows x 128 bytes; SwiGLU B rows pair 64 gate and 64 up rows per
+    128-row half; bf16 output staged in LDS."""
+    lane = np.arange(WAVE)
+    WTN = 128
+    bn_out = BN // 2 if la.swiglu else BN
+    n0 = nt * bn_out
+    k_extent = (nk - 1) * ROW_BYTES + 16
+    a_bytes = la.A_rows * la.lda * 2
+    b_base = g * la.b_stride * 2
+    for wave in range(8):
+        loads_a = wave < 4
+        lrow0 = (wave % 4) * 64
+        for i in range(8):
+            row = lrow0 + 8 * i + lane // 8
+            chunk = (lane % 8) ^ ((row >> 1) & 7)
+            if loads_a:
+                r = np.minimum(r0 + row, row_end - 1)
+                ar = la.a_rows[r].astype(np.int64) if la.a_rows is not None else r.astype(np.int64)
+                ar = np.clip(ar, 0, la.A_rows - 1)
+                voff = ar * la.lda * 2 + chunk * 16
+                assert voff.min() >= 0 and voff.max() + k_extent <= a_bytes, ("A256", g, r0)
+            else:
+                if la.swiglu:
+                    wnb, within = row // WTN, row % WTN
+                    br = (within // (WTN // 2)) * la.N + np.minimum(n0 + wnb * (WTN // 2) + within % (WTN // 2), la.N - 1)
+                else:
+                    br = np.minimum(n0 + row, la.N - 1)
+                voff = br.astype(np.int64) * la.ldb * 2 + chunk * 16
+                assert voff.min() >= 0 and b_base + voff.max() + k_extent <= la.b_bytes, ("B256", g, nt)
+            assert voff.max() + k_extent - 16 < 1 << 32
+            for slot in range(2):
+                lds = slot * STAGE256 + (0 if loads_a else 256 * ROW_BYTES) + lrow0 * ROW_BYTES + i * 1024 + lane * 16
+                lo_, hi_ = slot * STAGE256 + (0 if loads_a else 256 * ROW_BYTES), slot * STAGE256 + (256 if loads_a else 512) * ROW_BYTES
+                assert lds.min() >= lo_ and lds.max() + 16 <= hi_, ("LDS256", wave, i)
+    # epilogue
+    pitch = bn_out * 2 + 16
+    assert 256 * pitch <= PIPE_BYTES
+    rows_valid = min(256, row_end - r0)
+    assert rows_valid == 256, ("a 256-row chunk", g, r0)
+    cols = n0 + np.arange(0, bn_out, 8)
+    cols = cols[cols < la.N]
+    assert r0 + rows_valid <= la.M
+    assert ((r0 + rows_valid - 1) * la.ldc + cols.max()) * 2 + 16 <= la.M * la.ldc * la.c_esize, ("C256", g, r0)
+    assert cols[0] == n0 and cols.max() + 8 >= min(n0 + bn_out, la.N)
+    written[r0:r0 + rows_valid, nt] += 1
+
+
+def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written, lwaves=L_WAVES):
     lane = np.arange(WAVE)
     WM = 1 if bm == 16 else 2
     WN = 8 // WM
@@ -239,8 +336,8 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written):
     n0 = nt * bn_out
     st = stage_bytes(bm, la.fp4)
     a_instr = bm // ROWS_PER_INSTR
-    a_per_wave = cdiv(a_instr, L_WAVES)
-    b_per_wave = BN // ROWS_PER_INSTR // L_WAVES
+    a_per_wave = cdiv(a_instr, lwaves)
+    b_per_wave = BN // ROWS_PER_INSTR // lwaves
     k_extent = (nk - 1) * ROW_BYTES + 16        # bytes a lane reads past its offset over the K loop
     assert st["count"] * st["bytes"] <= (PIPE_BYTES_FP4 if la.fp4 else PIPE_BYTES)
 
@@ -263,10 +360,10 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written):
         return np.minimum(n0 + rho, la.N - 1)
 
     b_base = byt(g * la.b_stride)
-    for lw in range(L_WAVES):
+    for lw in range(lwaves):
         for i in range(a_per_wave):
-            instr = lw + L_WAVES * i
-            if not (a_instr % L_WAVES == 0 or instr < a_instr):
+            instr = lw + lwaves * i
+            if not (a_instr % lwaves == 0 or instr < a_instr):
                 continue
             row = instr * ROWS_PER_INSTR + lane // 8
             chunk = (lane % 8) ^ ((row >> 1) & 7)
@@ -288,10 +385,10 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written):
             sdw = st["sdw"]
             as_grp, bs_grp = cdiv(bm, 64), BN // 64
             as_instr, bs_instr = as_grp * sdw, bs_grp * sdw
-            sc_per_wave = cdiv(as_instr + bs_instr, L_WAVES)
+            sc_per_wave = cdiv(as_instr + bs_instr, lwaves)
             assert sc_per_wave <= 3
             for u in range(sc_per_wave):
-                q = lw + L_WAVES * u
+                q = lw + lwaves * u
                 if q < as_instr:
                     h, grp = divmod(q, as_grp)
                     off = a_row_of(grp * 64 + lane) * la.lda_scale + 4 * h

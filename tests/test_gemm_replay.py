@@ -129,6 +129,53 @@ def test_replay_gpu_test_shapes(sizes, N, K, gather):
                         b_stride=N * K, b_bytes=G * N * K * 2, ldc=N, c_esize=4, swiglu=False))
 
 
+GPU_TEST_SIZES_256 = [[300, 0, 256, 513, 1, 1024, 37, 255], [2048]]
+
+
+@pytest.mark.parametrize("sizes", GPU_TEST_SIZES_256)
+@pytest.mark.parametrize("N,K", [(256, 512), (264, 64), (512, 1024)])
+@pytest.mark.parametrize("gather", [False, True])
+def test_replay_gpu_test_shapes_bf16_out(sizes, N, K, gather):
+    """test_grouped_gemm_integer_exact_bf16_out's launches: bf16 C, so without a row index the
+    full 256-row chunks take 256 x 256 tiles."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    M = int(off[-1]) + 3
+    G = len(sizes)
+    a_rows = np.random.Generator(np.random.PCG64(4)).integers(0, M + 7, M) if gather else None
+    r = check_launch(Launch(offsets=off, M=M, N=N, K=K, A_rows=M + 7, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
+                            b_stride=N * K, b_bytes=G * N * K * 2, ldc=N, c_esize=2, swiglu=False))
+    assert (r["tiles256"] > 0) == (not gather)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("N,K", [(384, 1024), (200, 192)])
+def test_replay_split256_test_shapes(swiglu, N, K):
+    """test_split256_bit_identical_to_128_row_tiles's two launches: the split one and the same
+    rows in groups below 256 rows (nothing for gemm256_kernel)."""
+    sizes = [700, 0, 256, 1, 1300, 90, 512]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    M = int(off[-1])
+    T, a_rows = M, None                                  # rows in order: the launch splits
+    nb = 2 * N if swiglu else N
+    pieces = [0]
+    for g in range(len(sizes)):
+        r = int(off[g])
+        while r < off[g + 1]:
+            r = min(r + 255, int(off[g + 1]))
+            pieces.append(r)
+    for o in (off, np.array(pieces, np.int64)):
+        G = len(o) - 1
+        r = check_launch(Launch(offsets=o, M=M, N=N, K=K, A_rows=T, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
+                                b_stride=nb * K, b_bytes=G * nb * K * 2, ldc=N, c_esize=2, swiglu=swiglu))
+        assert (r["tiles256"] > 0) == (o is off)
+    if swiglu:   # the same launch with the G|U save: the persistent kernel with load waves
+        G = len(off) - 1
+        r = check_launch(Launch(offsets=off, M=M, N=N, K=K, A_rows=T, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
+                                b_stride=nb * K, b_bytes=G * nb * K * 2, ldc=N, c_esize=2, swiglu=True,
+                                aux_ld=2 * N))
+        assert r["tiles256"] == 0
+
+
 def _fuzz_sizes(g):
     G = int(g.integers(1, 301))
     kind = g.integers(0, 4, G)
@@ -140,7 +187,8 @@ def _fuzz_sizes(g):
 @pytest.mark.parametrize("seed", range(16))
 def test_replay_fuzz_ragged_groups(seed):
     """Seeded random group layouts: every tile height, empty and one-row groups, sizes not a
-    multiple of 32, up to 300 groups, SwiGLU or plain, bf16 or MXFP8, with or without a gather."""
+    multiple of 32, up to 300 groups, SwiGLU or plain, bf16 or MXFP8, with or without a gather
+    (bf16 launches without the G|U save also split off the 256-row chunks)."""
     g = np.random.Generator(np.random.PCG64(1000 + seed))
     sizes = _fuzz_sizes(g)
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
@@ -157,10 +205,11 @@ def test_replay_fuzz_ragged_groups(seed):
     a_rows = g.integers(-5, A_rows + 5, M) if gather else None      # out-of-range entries are clamped
     eb = 0.5 if fp4 else 1 if mx else 2
     nb = 2 * N if swiglu else N
+    save = bool(g.integers(0, 2))                        # bf16 SwiGLU without the G|U save splits
     la = Launch(offsets=off, M=M, N=N, K=K, A_rows=A_rows, lda=K, a_rows=a_rows, b_groups=G, ldb=K,
                 b_stride=nb * K, b_bytes=int(G * nb * K * eb), ldc=N, c_esize=2, swiglu=swiglu, mx=mx, fp4=fp4,
                 lda_scale=K // 32, ldb_scale=K // 32, b_scale_stride=nb * K // 32, b_scale_bytes=G * nb * K // 32,
-                aux_ld=2 * N if swiglu else 0)
+                aux_ld=2 * N if swiglu and (mx or save) else 0)
     if M == 0:
         return                                           # the host returns before launching anything
     check_launch(la)

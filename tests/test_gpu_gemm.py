@@ -57,6 +57,66 @@ def test_grouped_gemm_integer_exact(L, sizes, N, K, gather):
     assert np.all(np.isnan(got[off[-1]:]))
 
 
+# bf16 output: without a row index, groups' full 256-row chunks take 256 x 256 tiles and the
+# rest the smaller row tiles. Integer sums below 2^24 are exact in fp32, so C is the exact sum
+# rounded once to bf16.
+SIZES_256 = [[300, 0, 256, 513, 1, 1024, 37, 255], [2048]]
+
+
+@pytest.mark.parametrize("sizes", SIZES_256)
+@pytest.mark.parametrize("N,K", [(256, 512), (264, 64), (512, 1024)])
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_gemm_integer_exact_bf16_out(L, sizes, N, K, gather):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(off[-1]) + 3
+    G = len(sizes)
+    A = mi.integer_valued((M + 7, K), -2, 2, 0, N + K + 1)
+    B = mi.integer_valued((G, N, K), -2, 2, -3, G + 1)
+    a_rows = np.random.Generator(np.random.PCG64(4)).integers(0, M + 7, M).astype(np.int32) if gather else None
+    C, _ = _gemm(L, dev(A, "bf16"), dev(B, "bf16"), off, M, N, L.MOE_EPI_NONE, torch.bfloat16, a_rows)
+    want = O.grouped_gemm(A, B, off, a_row_index=a_rows, rnd=O.round_bf16)
+    got = host(C)
+    np.testing.assert_array_equal(got[:off[-1]], want)
+    assert np.all(np.isnan(got[off[-1]:]))
+
+
+def _split_rows(off, cap=255):
+    """The same rows cut into groups of at most `cap` rows, and each piece's parent group."""
+    new, parent = [0], []
+    for g in range(len(off) - 1):
+        r = int(off[g])
+        while r < off[g + 1]:
+            r = min(r + cap, int(off[g + 1]))
+            new.append(r)
+            parent.append(g)
+    return np.array(new, np.int32), np.array(parent, np.int64)
+
+
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+@pytest.mark.parametrize("N,K", [(384, 1024), (200, 192)])
+def test_split256_bit_identical_to_128_row_tiles(L, epi, N, K):
+    """256 x 256 tiles run the 128-row tiles' K order and MFMA: the same rows cut into groups
+    below 256 rows (weights copied per piece, so no 256-row chunk exists) give the same bits,
+    and so does the persistent kernel with load waves (SwiGLU with the G|U save)."""
+    sizes = [700, 0, 256, 1, 1300, 90, 512]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G = int(off[-1]), len(sizes)
+    nb = 2 * N if epi == "swiglu" else N
+    x = dev(mi.randn_np(5, mi.X, 0, M, K, 1.0, "bf16"), "bf16")
+    B = dev(np.stack([mi.randn_np(5, mi.W_GATE, g, nb, K, 0.05, "bf16") for g in range(G)]), "bf16")
+    a_rows = None                                        # a row index turns the split off
+    e = L.MOE_EPI_SWIGLU if epi == "swiglu" else L.MOE_EPI_NONE
+    C1, _ = _gemm(L, x, B, off, M, N, e, torch.bfloat16, a_rows)
+    off2, parent = _split_rows(off)
+    B2 = B[torch.from_numpy(parent).cuda()].contiguous()
+    C2, _ = _gemm(L, x, B2, off2, M, N, e, torch.bfloat16, a_rows)
+    np.testing.assert_array_equal(bits(C1), bits(C2))
+    if epi == "swiglu":
+        # with the G|U save the launch does not split: the persistent kernel with load waves
+        C3, _ = _gemm(L, x, B, off, M, N, e, torch.bfloat16, a_rows, aux=True)
+        np.testing.assert_array_equal(bits(C1), bits(C3))
+
+
 @pytest.mark.parametrize("sizes,N,K", [([40, 0, 1, 200, 7, 129], 384, 256), ([1000], 128, 320)])
 def test_grouped_swiglu_bf16(L, sizes, N, K):
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
