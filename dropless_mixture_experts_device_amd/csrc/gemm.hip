@@ -80,9 +80,6 @@ constexpr int kChunks = kRowBytes / 16;
 #ifndef MOE_GEMM_SPLIT_MIN_ROWS
 #define MOE_GEMM_SPLIT_MIN_ROWS 256
 #endif
-#ifndef MOE_GEMM_SPLIT_GATHER
-#define MOE_GEMM_SPLIT_GATHER 0       // 1: launches with a row index split too (measured slower, above)
-#endif
 #ifndef MOE_GEMM_SPLIT_LONGK
 #define MOE_GEMM_SPLIT_LONGK 4096
 #endif
@@ -1974,8 +1971,7 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     // without the G|U save: gemm_split_kernel, full 256-row chunks of large groups as 256 x 256
     // tiles (none while M < 256)
     const bool split = MOE_GEMM_SPLIT256 && a->a_dtype == MOE_BF16 && a->c_dtype == MOE_BF16 && !a->ragged_k &&
-                       !quant && !swb && !a->aux && (MOE_GEMM_SPLIT_GATHER || !a->a_rows) && p.allow256 == 0 &&
-                       a->M >= 256;
+                       !quant && !swb && !a->aux && !a->a_rows && p.allow256 == 0 && a->M >= 256;
     p.split256 = !split ? 0 : a->K >= MOE_GEMM_SPLIT_LONGK ? std::max(MOE_GEMM_SPLIT_MIN_ROWS_LONGK, 256)
                                                             : std::max(MOE_GEMM_SPLIT_MIN_ROWS, 256);
 
