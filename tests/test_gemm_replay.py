@@ -176,6 +176,26 @@ def test_replay_split256_test_shapes(swiglu, N, K):
         assert r["tiles256"] == 0
 
 
+def test_replay_split256_full_size_down_projection():
+    """test_split256_full_size_down_projection_bit_identical's two launches: the DeepSeek-V3
+    down projection split, and the same rows as 485 groups below 256 rows (no 256-row tile)."""
+    w = mi.WORKLOADS["dsv3"]
+    off = _offsets("dsv3")
+    pieces = [0]
+    for g in range(len(off) - 1):
+        r = int(off[g])
+        while r < off[g + 1]:
+            r = min(r + 255, int(off[g + 1]))
+            pieces.append(r)
+    rows = int(off[-1])
+    for o in (off, np.array(pieces, np.int64)):
+        G = len(o) - 1
+        r = check_launch(Launch(offsets=o, M=rows, N=w.d, K=w.f, A_rows=rows, lda=w.f, a_rows=None, b_groups=G,
+                                ldb=w.f, b_stride=w.d * w.f, b_bytes=G * w.d * w.f * 2, ldc=w.d, c_esize=2,
+                                swiglu=False))
+        assert (r["tiles256"] > 0) == (o is off)
+
+
 def _fuzz_sizes(g):
     G = int(g.integers(1, 301))
     kind = g.integers(0, 4, G)

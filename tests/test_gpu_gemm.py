@@ -117,6 +117,27 @@ def test_split256_bit_identical_to_128_row_tiles(L, epi, N, K):
         np.testing.assert_array_equal(bits(C1), bits(C3))
 
 
+def test_split256_full_size_down_projection_bit_identical(L):
+    """DeepSeek-V3-shaped down projection (the layer's GEMM 2: 257 groups, 73,728 rows,
+    d = 7168, f = 2048) with its 256-row chunks on 256 x 256 tiles, against the same rows cut
+    into groups below 256 rows: every one of the 528M outputs bit-identical."""
+    import os
+    w = mi.WORKLOADS["dsv3"]
+    with open(os.path.join(os.path.dirname(__file__), "golden", "offsets_dsv3.txt")) as fh:
+        off = np.array([int(v) for v in [ln for ln in fh if not ln.startswith("#")][0].split()], np.int32)
+    M, G = int(off[-1]), len(off) - 1
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    H = torch.randn((M, w.f), generator=gen, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((G, w.d, w.f), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    C1, _ = _gemm(L, H, W, off, M, w.d, L.MOE_EPI_NONE, torch.bfloat16)
+    off2, parent = _split_rows(off)
+    W2 = W[torch.from_numpy(parent).cuda()].contiguous()
+    del W
+    C2, _ = _gemm(L, H, W2, off2, M, w.d, L.MOE_EPI_NONE, torch.bfloat16)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    assert not torch.isnan(C1).any()
+
+
 @pytest.mark.parametrize("sizes,N,K", [([40, 0, 1, 200, 7, 129], 384, 256), ([1000], 128, 320)])
 def test_grouped_swiglu_bf16(L, sizes, N, K):
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
