@@ -15,6 +15,11 @@
 //  * Persistent workgroups (one per CU: 8 MFMA waves + 4 load waves) walk the tile list; tiles are ordered group
 //    by group, in supertiles of 4 column tiles x all row tiles, and handed out so the 32 CUs
 //    of one XCD work on consecutive tiles (shared A/B panels hit that XCD's L2).
+//  * bf16 launches whose A rows are read in order (no row index), with a bf16 output and no
+//    G|U save, run gemm_split_kernel instead: 8-wave workgroups that take each large group's
+//    full 256-row chunks as 256 x 256 tiles (every wave loads 64 operand rows per stage into a
+//    two-stage ring) and the rest of the rows as the row tiles below, with the MFMA waves
+//    issuing their own loads; outputs are bit-identical to the persistent kernel's.
 //  * Operands stream global -> LDS with 16-byte DMA loads (no VGPR staging) through a 3-stage
 //    ring of K slices (64 bf16 or 128 fp8 = 128 bytes per row). Four producer waves (one per
 //    SIMD) issue every load and wait for it; the MFMA waves only read LDS and multiply, so
@@ -1547,7 +1552,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmParams p) {
 // each 64-element stage) are the 128-row tiles', so a row's outputs are bit-identical
 // whichever tile computes them.
 // ---------------------------------------------------------------------------------------
-constexpr int k256Threads = (kWaves + 0) * kWave;                  // 8 waves, no producer waves
+constexpr int k256Threads = kWaves * kWave;                        // 8 waves, no producer waves
 constexpr int k256Stage = 2 * 256 * kRowBytes;                      // 256 A rows, then 256 B rows
 static_assert(kWaves == 8, "the 256-row tile's wave grid is 4 x 2 waves of 64 x 128");
 static_assert(2 * k256Stage <= kPipeBytes && 256 * (kBN * 2 + 16) <= kPipeBytes, "256-row ring and staging fit");
