@@ -1024,6 +1024,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         b_off[ks][1] = BM * kRowBytes + rb * kRowBytes + (((chunk + MF::kChunk2) ^ swz(rb)) << 4);
     }
     constexpr int FSTEP = MS * kRowBytes;   // bytes between consecutive fragments' rows
+    constexpr bool DB_BF16 = FMT == kBF16;  // bf16 fragments are double-buffered in registers
     // compute(kt, kn): multiply stage kt; when kn >= 0 also issue this wave's loads of stage kn,
     // a share after the first MFMA of every k-step, so the DMA instructions queue while the
     // matrix core works instead of all waves issuing them back to back after the barrier.
@@ -1130,6 +1131,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         // and multiply. One barrier per stage: producers reach barrier kt with their loads of
         // stage kt landed; the buffer they refill after it (stage kt+NST-1) was last read by
         // compute(kt-1), which the MFMA waves finished before the same barrier.
+        // bf16 (LATE): the MFMA waves cross barrier kt+1 before stage kt's last k-step, whose
+        // fragments are already in registers, and read stage kt+1's first fragments under its
+        // MFMAs, so no stage starts with the matrix core waiting on LDS reads. Barrier kt+1 then
+        // follows every LDS read of stage kt, which is all the producers need before refilling
+        // its slot; both roles pass nk + 1 barriers (the producers one more after their loop).
+        constexpr bool LATE = FMT == kBF16 && !RK && DB_BF16;
         lds_barrier();
         if (producer) {   // two separate loops so that neither role keeps the other's registers live
 #pragma unroll
@@ -1142,6 +1149,42 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
                 else wait_vm_lgkm0<0>();
                 lds_barrier();
                 if (kt + NST - 1 < nk) issue(kt + NST - 1);
+            }
+            if constexpr (LATE) lds_barrier();
+        } else if constexpr (LATE) {
+            static_assert(NKS >= 2 && (NKS - 1) % 2 == 1, "the last k-step uses fragment buffer 1");
+            FragT fa[2][MI], fb[2][NI];
+            auto rd = [&](int kt, int ks, int b) {
+                const char* st = lds + (kt % NST) * SB;
+#pragma unroll
+                for (int i = 0; i < MI; ++i) fa[b][i] = load_frag<MS, FMT>(st + i * FSTEP, a_off[ks][0], a_off[ks][1]);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) fb[b][j] = load_frag<MS, FMT>(st + j * FSTEP, b_off[ks][0], b_off[ks][1]);
+            };
+            auto mm = [&](int b) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j) acc[i][j] = mfma<MS, FMT, 0>(fa[b][i], fb[b][j], acc[i][j], 0, 0);
+            };
+            wait_vm_lgkm0<63>();
+            lds_barrier();                       // barrier 0: stage 0 has landed
+            rd(0, 0, 0);
+            for (int kt = 0; kt < nk; ++kt) {
+                static_for<0>(
+                    [&](auto ks_tag) {
+                        constexpr int ks = decltype(ks_tag)::value;
+                        rd(kt, ks + 1, (ks + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs below
+                        mm(ks & 1);
+                    },
+                    std::make_integer_sequence<int, NKS - 1>{});
+                __builtin_amdgcn_sched_barrier(0);   // the k-step's MFMAs issue before the wait
+                wait_vm_lgkm0<63>();             // this wave's LDS reads of stage kt are done
+                lds_barrier();                   // barrier kt+1: stage kt+1 has landed
+                rd(kt + 1, 0, 0);                // after the last stage: a stale slot, never used
+                __builtin_amdgcn_sched_barrier(0);
+                mm(1);
             }
         } else {
             for (int kt = 0; kt < nk; ++kt) {
