@@ -22,8 +22,11 @@ constexpr int kSub = 64;                 // tokens per mask word
 constexpr int kSubPerTile = 16;
 constexpr int kTile = kSub * kSubPerTile; // 1024 tokens per histogram tile
 constexpr int kPermThreads = 256;
+// 16-byte chunks of x[t] a lane holds before the stores: 14 covers a 7,168-column bf16 row
+// in one pass, so each of its copies goes out as one 14 KiB burst (the DeepSeek-V3 gather
+// 0.231 -> 0.224 ms against 4 chunks, 0.228 with 8)
 #ifndef MOE_PERMUTE_UNROLL
-#define MOE_PERMUTE_UNROLL 4
+#define MOE_PERMUTE_UNROLL 14
 #endif
 
 struct PermWs {
