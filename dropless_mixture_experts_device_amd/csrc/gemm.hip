@@ -124,15 +124,27 @@ constexpr int kPipeBytes = cmax(3 * Stage<128>::kBytes, 2 * Stage<256>::kBytes);
 constexpr int kMaxGroups = 2047;
 constexpr int kLdsBytes = kPipeBytes + (kMaxGroups + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-// E2M1 stages carry twice the scale bytes: the ring grows by 9 KiB, which leaves room for the
-// schedule's tile prefix of at most 1791 groups in the same 160 KiB
+// Block-scaled row tiles (MXFP8, MXFP4; not the ragged-K mode) keep their scales out of the
+// stages, in a ring of two batch slots: a batch holds 16 scale bytes (4 dwords, the scales of
+// 4 MXFP8 or 2 MXFP4 stages) of every A and B row, 16 bytes per row, and is fetched by 4-byte
+// DMA lanes of which 4 consecutive ones read one row's 16 contiguous bytes. One scale
+// instruction thus covers 16 rows of 4 stages in 16 line requests, where a per-stage dword per
+// row took 64 rows of one stage in 64. The operand stages then hold codes only (3 x 48 KiB),
+// the two slots 12 KiB, which leaves room for a tile prefix of 1024 entries.
+constexpr int kScBatchBytes = 16;                                   // scale bytes per row and batch
+constexpr int kScSlot = (Stage<128>::kScaleRowsA + kBN) * kScBatchBytes;   // 6 KiB (largest BM)
+constexpr int kMxData = 3 * Stage<128>::kData;                      // 144 KiB of operand stages
+constexpr int kMxPipe = kMxData + 2 * kScSlot;                      // 156 KiB
 template <int FMT>
-constexpr int pipe_bytes() { return FMT == kE2M1 ? 3 * Stage<128, kE2M1>::kBytes : kPipeBytes; }
+constexpr int pipe_bytes() { return FMT == kBF16 ? kPipeBytes : kMxPipe; }
+// groups of the row-tile schedule whose prefix fits past the ring (the ragged-K mode has no
+// schedule and takes up to kMaxGroups)
 template <int FMT>
-constexpr int max_groups() { return FMT == kE2M1 ? (160 * 1024 - pipe_bytes<kE2M1>()) / 4 - 1 : kMaxGroups; }
+constexpr int max_groups() { return FMT == kBF16 ? kMaxGroups : (160 * 1024 - kMxPipe) / 4 - 1; }
 template <int FMT>
 constexpr int lds_bytes() { return pipe_bytes<FMT>() + (max_groups<FMT>() + 1) * 4; }
-static_assert(lds_bytes<kE2M1>() <= 160 * 1024 && max_groups<kE2M1>() == 1791, "E2M1 LDS budget");
+static_assert(lds_bytes<kE4M3>() <= 160 * 1024 && max_groups<kE4M3>() == 1023, "block-scaled LDS budget");
+static_assert(lds_bytes<kE4M3>() >= kPipeBytes + 8 * 1024, "the ragged-K stream's ring and staging fit");
 constexpr int kSuper = 4;         // column tiles per supertile
 // Ragged-K (weight-gradient) tiles write a 128 x 256 bf16 block each over a short K range, so
 // output stores weigh more than operand reuse: with 16 or more column tiles they take wider
@@ -708,7 +720,7 @@ __device__ __forceinline__ void swb_epilogue(const GemmParams& p, char* lds, int
                                              int rows_valid, int n0, int tid) {
     constexpr int BN = kBN;                    // dh columns of the tile
     constexpr int CH = BN / 8;                 // 16-byte chunks per tile row
-    static_assert(2 * BM * (BN * 2 + 16) <= kPipeBytes, "the dg and du tiles fit the operand ring");
+    static_assert(2 * BM * (BN * 2 + 16) <= kMxData, "the dg and du tiles fit the operand stages");
     char* lds_u = lds + BM * pitch;            // the du tile (both fit the operand ring)
     // every g, u load of this thread goes out before the first is used (NB chunks per thread)
     constexpr int NB = cdiv(BM * CH, kThreads);
@@ -813,14 +825,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     constexpr int BS_GRP = kBN / 64;
     constexpr int AS_INSTR = AS_GRP * SDW;               // scale dword instructions of a stage: A, then B
     constexpr int BS_INSTR = BS_GRP * SDW;
-    constexpr int SC_PER_WAVE = MX ? cdiv(AS_INSTR + BS_INSTR, LW) : 0;   // scale instructions per wave
+    // row tiles: scale batches (SPB stages each) in the two ring slots past the stages; piece q
+    // of a batch brings 16 rows' 16 bytes (A rows for q < APC, then B rows)
+    constexpr bool SCB = MX && !RK;
+    constexpr int SPB = kScBatchBytes / (4 * SDW);        // stages per scale batch
+    constexpr int APC = ST::kScaleRowsA / 16, NPC = APC + kBN / 16;
+    constexpr int SC_PER_WAVE = !MX ? 0 : SCB ? cdiv(NPC, LW) : cdiv(AS_INSTR + BS_INSTR, LW);
     constexpr int NST = ST::kCount;
-    constexpr int SB = ST::kBytes;
+    constexpr int SB = SCB ? ST::kData : ST::kBytes;
+    static_assert(!SCB || (NST * SB <= kMxData && SPB >= 2 && (ST::kScaleRowsA + kBN) * kScBatchBytes <= kScSlot),
+                  "scale batch layout");
     static_assert(NST * SB <= pipe_bytes<FMT>(), "pipeline stages exceed the LDS ring");
     static_assert(NST <= 4, "the wait counts cover at most two later stages in flight");
     static_assert(BM < 256 || (BM * (kBN * 2 + 16) <= kPipeBytes), "bf16 epilogue tile must fit in LDS");
     static_assert(!SWIGLU || NI % 2 == 0, "SwiGLU needs gate and up fragments in every wave");
-    static_assert(SC_PER_WAVE <= 3, "at most three scale loads per wave");
+    static_assert(SC_PER_WAVE <= (SCB ? 6 : 3), "scale loads per wave");
     static_assert(!MX || PW == kPWaves, "block-scaled epilogues assume the persistent kernel's threads");
 
     if constexpr (BM == 256) {
@@ -940,9 +959,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
     // MXFP8 scale rows: scale instruction q (0 .. AS_INSTR+BS_INSTR-1) is issued by load wave
     // q % LW as its (q / LW)-th scale load; instructions below AS_INSTR bring 64 A rows' scale
     // dwords, the others 64 B rows'
-    const uint8_t* s_src[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
-    int s_lds[SC_PER_WAVE > 0 ? SC_PER_WAVE : 1] = {};
-    if constexpr (MX) {
+    // (row tiles: batch pieces, below, keep 32-bit row offsets from as_base / bs_base instead)
+    const uint8_t* s_src[SC_PER_WAVE > 0 && !SCB ? SC_PER_WAVE : 1] = {};
+    int s_lds[SC_PER_WAVE > 0 && !SCB ? SC_PER_WAVE : 1] = {};
+    uint32_t s_off[SCB ? SC_PER_WAVE : 1] = {};
+    if constexpr (SCB) {
+        // batch pieces: lane l reads dword l % 4 of the batch in row 16 q + l / 4 (clamped to
+        // the row's K range when the batch is issued) into slot byte 256 q + 4 l
+#pragma unroll
+        for (int u = 0; u < SC_PER_WAVE; ++u) {
+            const int q = lw + LW * u;
+            if (q < APC) s_off[u] = (uint32_t)(a_row_of(q * 16 + lane / 4) * as_ld);
+            else if (q < NPC) s_off[u] = (uint32_t)((int64_t)b_row_of((q - APC) * 16 + lane / 4) * bs_ld);
+        }
+    } else if constexpr (MX) {
 #pragma unroll
         for (int u = 0; u < SC_PER_WAVE; ++u) {
             const int q = lw + LW * u;
@@ -987,13 +1017,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
 #else
             load_lds16(b_src[i] + koff, st + BM * kRowBytes + (lw * B_PER_WAVE + i) * 1024);
 #endif
-        } else {
+        } else if constexpr (!SCB) {
             // 4 scale bytes (4 blocks of 32) per row and instruction; the stage's 4 * SDW blocks
             constexpr int u = l - A_PER_WAVE - B_PER_WAVE;
             if (lw + LW * u < AS_INSTR + BS_INSTR) load_lds4(s_src[u] + kt * 4 * SDW, st + s_lds[u]);
         }
     };
+    // Scale batch b (stages b SPB .. b SPB + SPB - 1) goes out with the loads of stage
+    // max(0, (b - 1) SPB + 2): the loads of a stage leave after barrier stage - 2, when the MFMA
+    // waves are done with stage - 3 and so with batch b - 2, the slot's previous batch; and
+    // before stage b SPB's own loads, so the waits for that stage cover it.
+    auto issue_scales = [&](int kt) {
+        if constexpr (SCB) {
+            int b = -1;
+            if (kt == 0) b = 0;
+            else if ((kt + SPB - 2) % SPB == 0) b = (kt + SPB - 2) / SPB;
+            if (b < 0 || b * SPB >= nk) return;
+            char* slot = lds + kMxData + (b & 1) * kScSlot;
+            const int dw = min(4 * b + lane % 4, nk * SDW - 1);   // the row's last dword at most
+#pragma unroll
+            for (int u = 0; u < SC_PER_WAVE; ++u) {
+                const int q = lw + LW * u;
+                if (q < NPC) load_lds4((q < APC ? as_base : bs_base) + s_off[u] + 4 * dw, slot + q * 256);
+            }
+        }
+    };
     auto issue = [&](int kt) {
+        issue_scales(kt);
         static_for<0>([&](auto l) { issue_one(kt, l); }, std::make_integer_sequence<int, NLOADS>{});
     };
 
@@ -1033,7 +1083,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, char* lds, int g,
         // block-scaled formats: this lane's rows' scale dwords of the stage, shifted so that byte
         // SEL of dword DW is the block of k-step ks for this lane (the instruction's op_sel picks it)
         int sa_w[MI][SDW], sb_w[NI][SDW];
-        if constexpr (MX) {
+        if constexpr (SCB) {
+            const uint32_t sh0 = 8 * (MF::frag_block(lane, 0) - MF::frag_block(0, 0));
+            const char* slot = lds + kMxData + ((kt / SPB) & 1) * kScSlot + 4 * SDW * (kt % SPB);
+#pragma unroll
+            for (int h = 0; h < SDW; ++h) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    sa_w[i][h] = (int)(*reinterpret_cast<const uint32_t*>(
+                                           slot + 4 * h + (wm * WTM + i * MS + MF::frag_row(lane)) * kScBatchBytes) >> sh0);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    sb_w[j][h] = (int)(*reinterpret_cast<const uint32_t*>(
+                                           slot + 4 * h + (ST::kScaleRowsA + wn * WTN + j * MS + MF::frag_row(lane)) *
+                                                              kScBatchBytes) >> sh0);
+            }
+        } else if constexpr (MX) {
             const uint32_t sh0 = 8 * (MF::frag_block(lane, 0) - MF::frag_block(0, 0));
 #pragma unroll
             for (int h = 0; h < SDW; ++h) {
@@ -1923,8 +1988,10 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->a_dtype != a->b_dtype) return MOE_ENOTSUP;
     if (a->a_dtype != MOE_BF16 && a->a_dtype != MOE_F32 && a->a_dtype != MOE_E4M3 && a->a_dtype != MOE_E2M1)
         return MOE_ENOTSUP;
-    // E2M1 stages carry twice the scale bytes, which leaves LDS for the schedule of 1791 groups
-    if (a->a_dtype == MOE_E2M1 && (a->G > moe::max_groups<moe::kE2M1>() || a->ragged_k)) return MOE_ENOTSUP;
+    // block-scaled row tiles: the scale ring leaves LDS for the schedule of 1023 groups
+    if (a->a_dtype == MOE_E2M1 && a->ragged_k) return MOE_ENOTSUP;
+    if ((a->a_dtype == MOE_E4M3 || a->a_dtype == MOE_E2M1) && !a->ragged_k && a->G > moe::max_groups<moe::kE4M3>())
+        return MOE_ENOTSUP;
     if (a->c_dtype != MOE_BF16 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->a_dtype == MOE_F32 && a->c_dtype != MOE_F32) return MOE_ENOTSUP;
     if (a->ragged_k != 0 && a->ragged_k != 1) return MOE_EINVAL;
@@ -2059,6 +2126,10 @@ extern "C" moe_status_t moe_grouped_gemm(const moe_gemm_args_t* a, void* workspa
     if (a->aux && (!moe_aligned16(a->aux) || a->ld_aux % 8)) return MOE_EINVAL;
     if (mx) {
         if (!a->a_scale || !a->b_scale || !aligned4(a->a_scale) || !aligned4(a->b_scale)) return MOE_EINVAL;
+        // row tiles address scale rows by 32-bit offsets from the scale bases
+        if (!a->ragged_k && (a->A_rows * a->lda_scale >= ((int64_t)1 << 32) ||
+                             (swiglu ? 2 : 1) * a->N * a->ldb_scale >= ((int64_t)1 << 32)))
+            return MOE_ENOTSUP;
         if (a->lda_scale < a->K / 32 || a->ldb_scale < a->K / 32 || a->lda_scale % 4 || a->ldb_scale % 4 ||
             a->b_scale_group_stride < 0 || a->b_scale_group_stride % 4)
             return MOE_EINVAL;

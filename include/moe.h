@@ -236,7 +236,7 @@ typedef struct moe_gemm_args {
     /* MXFP8 operands (a_dtype = b_dtype = MOE_E4M3, K % 128 == 0): A and B hold E4M3 codes and
      * every 32 consecutive K elements of a row share one E8M0 scale byte s, the element value
      * being code_value * 2^(s-127) ([OCP-MX]); products are exact and summed in fp32.
-     * MXFP4 operands (MOE_E2M1, K % 256 == 0, ragged_k = 0, G <= 1791): the same with E2M1
+     * MXFP4 operands (MOE_E2M1, K % 256 == 0, ragged_k = 0): the same with E2M1
      * codes packed two per byte (element 2i of a row in bits 3..0 of byte i, as
      * moe_group_quant_mxfp4 writes them); lda, ldb and b_group_stride still count elements
      * (even numbers), so a row starts lda/2 bytes after the previous one. */
@@ -274,11 +274,13 @@ typedef struct moe_gemm_args {
 } moe_gemm_args_t;
 
 /* Grouped GEMM (see moe_gemm_args_t). Workspace: moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
- * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047 (1791 for MXFP4). A, B, C,
+ * 0, 0, 0, 0, G) bytes (a device-built tile schedule), G <= 2047 (1023 for MXFP8 and MXFP4
+ * outside the ragged-K mode; MOE_ENOTSUP above it). A, B, C,
  * aux 16-byte aligned; A and B rows (lda, ldb, b_group_stride, in bytes) 16-byte multiples; ldc, ld_aux multiples
  * of 8; MXFP8 scale pointers and their strides 4-byte multiples. A (A_rows x lda) and one
  * group's B (N or 2N rows x ldb) must each span less than 4 GiB (MOE_ENOTSUP otherwise: the
- * loads use 32-bit offsets from the tile's base). The args struct is read on the host during
+ * loads use 32-bit offsets from the tile's base; MXFP8/MXFP4 outside the ragged-K mode: also
+ * A_rows x lda_scale and one group's N (2N) x ldb_scale). The args struct is read on the host during
  * the call only. */
 moe_status_t moe_grouped_gemm(const moe_gemm_args_t* args, void* workspace, size_t workspace_bytes,
                               void* stream);

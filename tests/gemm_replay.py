@@ -43,9 +43,16 @@ def stage_bytes(bm, fp4=False):
 
 PIPE_BYTES = max(3 * stage_bytes(128)["bytes"], 2 * stage_bytes(256)["bytes"])
 LDS_BYTES = PIPE_BYTES + (MAX_GROUPS + 1) * 4
-PIPE_BYTES_FP4 = 3 * stage_bytes(128, True)["bytes"]
-MAX_GROUPS_FP4 = (160 * 1024 - PIPE_BYTES_FP4) // 4 - 1
-assert MAX_GROUPS_FP4 == 1791 and PIPE_BYTES_FP4 + (MAX_GROUPS_FP4 + 1) * 4 <= 160 * 1024
+# block-scaled row tiles (MXFP8, MXFP4): operand stages of codes only, then two scale-batch
+# slots of 16 bytes per A and B row (the scales of 4 MXFP8 or 2 MXFP4 stages), then the prefix
+SC_BATCH_BYTES = 16
+SC_PIECE = 16 * SC_BATCH_BYTES           # LDS bytes per 16-row piece
+SC_SLOT = (cdiv(128, 64) * 64 + BN) // 16 * SC_PIECE
+MX_DATA = 3 * stage_bytes(128)["data"]
+MX_PIPE = MX_DATA + 2 * SC_SLOT
+MAX_GROUPS_MX = (160 * 1024 - MX_PIPE) // 4 - 1
+assert MAX_GROUPS_MX == 1023 and MX_PIPE + (MAX_GROUPS_MX + 1) * 4 <= 160 * 1024
+assert LDS_BYTES <= 160 * 1024 and PIPE_BYTES + 8 * 1024 <= MX_PIPE + (MAX_GROUPS_MX + 1) * 4
 
 # 256 x 256 tiles: two 64 KiB stages (256 A rows, then 256 B rows) and the bf16 output tile
 # staged over them, all below the tile prefix
@@ -194,7 +201,9 @@ def check_launch(la: Launch):
     at any output element not written exactly once. Returns a summary dict."""
     G = len(la.offsets) - 1
     if la.fp4:
-        assert la.mx and G <= MAX_GROUPS_FP4 and la.lda % 2 == 0 and la.ldb % 2 == 0 and la.b_stride % 2 == 0
+        assert la.mx and la.lda % 2 == 0 and la.ldb % 2 == 0 and la.b_stride % 2 == 0
+    if la.mx:
+        assert G <= MAX_GROUPS_MX
     eb = 1 if la.mx else 2
     byt = (lambda e: e // 2) if la.fp4 else (lambda e: e * eb)
     assert 1 <= G <= MAX_GROUPS
@@ -339,7 +348,7 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written, lwav
     a_per_wave = cdiv(a_instr, lwaves)
     b_per_wave = BN // ROWS_PER_INSTR // lwaves
     k_extent = (nk - 1) * ROW_BYTES + 16        # bytes a lane reads past its offset over the K loop
-    assert st["count"] * st["bytes"] <= (PIPE_BYTES_FP4 if la.fp4 else PIPE_BYTES)
+    assert st["count"] * st["data"] <= MX_DATA if la.mx else st["count"] * st["bytes"] <= PIPE_BYTES
 
     a_base = byt(g * la.a_group_stride) if la.uniform_rows else 0
     a_bytes = la.A_rows * byt(la.lda)
@@ -382,29 +391,41 @@ def _check_tile(la, g, row_begin, row_end, r_off, bm, nt, nk, byt, written, lwav
             lds = bm * ROW_BYTES + instr * 1024 + lane * 16
             assert lds.max() + 16 <= st["data"], ("B LDS", bm)
         if la.mx:
+            # scale batches: batch b (stages b spb .. b spb + spb - 1) is 16 bytes of every A and
+            # B row; piece q of a batch brings rows 16 q .. 16 q + 15 (A rows, then B rows), lane l
+            # dword l % 4 of row 16 q + l / 4, clamped to the row's last dword of the K range
             sdw = st["sdw"]
-            as_grp, bs_grp = cdiv(bm, 64), BN // 64
-            as_instr, bs_instr = as_grp * sdw, bs_grp * sdw
-            sc_per_wave = cdiv(as_instr + bs_instr, lwaves)
-            assert sc_per_wave <= 3
+            spb = SC_BATCH_BYTES // (4 * sdw)
+            apc = st["scale_rows_a"] // 16
+            npc = apc + BN // 16
+            sc_per_wave = cdiv(npc, lwaves)
+            assert sc_per_wave <= 6 and spb >= 2
+            last_dw = nk * sdw - 1
             for u in range(sc_per_wave):
                 q = lw + lwaves * u
-                if q < as_instr:
-                    h, grp = divmod(q, as_grp)
-                    off = a_row_of(grp * 64 + lane) * la.lda_scale + 4 * h
-                    assert off.max() + (nk - 1) * 4 * sdw + 4 <= la.A_rows * la.lda_scale, ("A scale", g)
-                    lds = st["scale_a"] + h * st["scale_rows_a"] * 4 + grp * 256 + lane * 4
-                    assert lds.max() + 4 <= st["scale_b"]
-                elif q < as_instr + bs_instr:
-                    h, grp = divmod(q - as_instr, bs_grp)
-                    rho = grp * 64 + lane
-                    off = g * la.b_scale_stride + b_row_of(rho) * la.ldb_scale + 4 * h
-                    assert off.max() + (nk - 1) * 4 * sdw + 4 <= la.b_scale_bytes, ("B scale", g)
-                    lds = st["scale_b"] + h * BN * 4 + grp * 256 + lane * 4
-                    assert lds.max() + 4 <= st["bytes"]
+                if q >= npc:
+                    continue
+                dws = np.stack([np.minimum(4 * b + lane % 4, last_dw) for b in range(cdiv(nk, spb))])
+                assert dws.min() >= 0
+                if q < apc:
+                    off = a_row_of(q * 16 + lane // 4) * la.lda_scale
+                    assert off.max() < 1 << 32
+                    assert off.max() + 4 * dws.max() + 4 <= la.A_rows * la.lda_scale, ("A scale", g)
+                else:
+                    roff = b_row_of((q - apc) * 16 + lane // 4) * la.ldb_scale
+                    assert roff.max() < 1 << 32
+                    off = g * la.b_scale_stride + roff
+                    assert off.max() + 4 * dws.max() + 4 <= la.b_scale_bytes, ("B scale", g)
+                for slot in (0, 1):
+                    lds = MX_DATA + slot * SC_SLOT + q * SC_PIECE + lane * 4
+                    assert lds.min() >= MX_DATA and lds.max() + 4 <= MX_DATA + (slot + 1) * SC_SLOT
+            # the rows the MFMA waves read lie inside the slot's A and B parts
+            assert bm <= st["scale_rows_a"] and npc * SC_PIECE <= SC_SLOT
     # epilogue: LDS staging of the output tile, then 16-byte stores of valid rows and columns
     pitch = bn_out * la.c_esize + 16
     assert bm * pitch <= PIPE_BYTES, ("epilogue LDS", bm)
+    if la.mx:   # staging (twice for the SwiGLU-backward epilogue) below the scale slots
+        assert 2 * bm * (BN * 2 + 16) <= MX_DATA, ("epilogue LDS", bm)
     rows_valid = min(bm, row_end - r0)
     assert rows_valid >= 1
     cols_per_chunk = 16 // la.c_esize

@@ -228,7 +228,8 @@ def test_host_argument_errors_mxfp4(lib):
         assert q4(*args) == want, (i, v)
     # nothing to do for zero rows, even with null buffers
     assert q4(None, L.MOE_BF16, 0, 256, 256, None, 0, None, 128, None, 8, None) == L.MOE_OK
-    # E2M1 GEMM: K % 256, even element strides, no ragged-K mode, at most 1791 groups
+    # E2M1 GEMM: K % 256, even element strides, no ragged-K mode, at most 1023 groups (the
+    # block-scaled row tiles' scale ring leaves LDS for a prefix of 1024 entries)
     a = L.MoeGemmArgs(G=4, offsets=fake.value, M=128, N=64, K=512, A=fake.value, a_dtype=L.MOE_E2M1, lda=512,
                       A_rows=128, a_rows=None, B=fake.value, b_dtype=L.MOE_E2M1, ldb=512, b_group_stride=64 * 512,
                       C=fake.value, c_dtype=L.MOE_BF16, ldc=64, epilogue=L.MOE_EPI_NONE, aux=None, ld_aux=0,
@@ -237,11 +238,17 @@ def test_host_argument_errors_mxfp4(lib):
     assert L._lib.moe_grouped_gemm(ctypes.byref(a), None, 0, None) == L.MOE_EWORKSPACE
     for field, value, want in (("K", 384, L.MOE_EINVAL), ("lda", 513, L.MOE_EINVAL), ("ldb", 520, L.MOE_EINVAL),
                                ("b_group_stride", 64 * 512 + 1, L.MOE_EINVAL), ("ragged_k", 1, L.MOE_ENOTSUP),
-                               ("G", 1792, L.MOE_ENOTSUP), ("a_scale", None, L.MOE_EINVAL),
+                               ("G", 1024, L.MOE_ENOTSUP), ("a_scale", None, L.MOE_EINVAL),
                                ("b_dtype", L.MOE_E4M3, L.MOE_ENOTSUP)):
         bad = L.MoeGemmArgs.from_buffer_copy(a)
         setattr(bad, field, value)
         assert L._lib.moe_grouped_gemm(ctypes.byref(bad), fake, 1 << 20, None) == want, field
+    # MXFP8 row tiles: the same 1023-group limit
+    a8 = L.MoeGemmArgs.from_buffer_copy(a)
+    a8.a_dtype = a8.b_dtype = L.MOE_E4M3
+    a8.lda, a8.ldb, a8.b_group_stride = 512, 512, 64 * 512
+    a8.G = 1024
+    assert L._lib.moe_grouped_gemm(ctypes.byref(a8), fake, 1 << 20, None) == L.MOE_ENOTSUP
 
 
 def test_host_argument_errors_fused_quant(lib):
