@@ -69,6 +69,29 @@ def test_mx_gemm_on_grid_bit_exact(L, sizes, N, K, gather):
     assert np.all(np.isnan(C[off[-1]:]))
 
 
+def test_mx_gemm_on_grid_max_groups(L):
+    """The largest block-scaled row-tile launch (1,023 groups: the tile prefix fills the LDS left
+    past the operand stages and the two scale-batch slots), with empty, one-row and ragged groups
+    and K = 640 (5 MXFP8 stages: a full scale batch, then one clamped to the rows' last dword):
+    bit-exact against the oracle; 1,024 groups are refused."""
+    G, N, K = 1023, 64, 640
+    sizes = np.random.Generator(np.random.PCG64(5)).integers(0, 4, G)
+    sizes[::97] = 0
+    sizes[5] = 130
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(off[-1])
+    A, As = _grid_operand((M, K), 31)
+    B, Bs = _grid_operand((G, N, K), 32)
+    C = host(_run(L, A, As, B, Bs, off, M, N, L.MOE_EPI_NONE, torch.float32))
+    np.testing.assert_array_equal(C, O.grouped_gemm(_dequant(A, As), _dequant(B, Bs), off))
+    off2 = np.concatenate([off, [M]]).astype(np.int32)
+    B2 = np.concatenate([B, B[:1]])
+    Bs2 = np.concatenate([Bs, Bs[:1]])
+    with pytest.raises(L.MoeError) as e:
+        _run(L, A, As, B2, Bs2, off2, M, N, L.MOE_EPI_NONE, torch.float32)
+    assert e.value.status == L.MOE_ENOTSUP
+
+
 @pytest.mark.parametrize("epi", ["none", "swiglu"])
 def test_mx_gemm_quantised_random_within_tolerance(L, epi):
     sizes = [40, 0, 1, 200, 7, 129, 513]
