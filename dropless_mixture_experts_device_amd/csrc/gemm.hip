@@ -27,9 +27,11 @@
 //    faster than MFMA waves that also issue the loads). LDS rows are XOR-swizzled so
 //    MFMA fragment reads are bank-conflict free; fragments are double-buffered in registers.
 //  * bf16: v_mfma_f32_32x32x16_bf16 (16x16x32 for 16/32-row tiles). MXFP8: E4M3 codes with one
-//    E8M0 scale per 32 K-elements; each stage also brings one dword (4 block scales) per row,
-//    and v_mfma_scale_f32_32x32x64_f8f6f4 (16x16x128) applies per-(row, 32-block) scales (the
-//    lane-to-block layout was measured; see the Mfma traits). Accumulation is fp32 in both.
+//    E8M0 scale per 32 K-elements; row tiles fetch each row's scales 16 bytes (4 MXFP8 or 2
+//    MXFP4 stages) at a time into a two-slot scale ring, the weight-gradient tiles one dword (4
+//    block scales) per row and stage, and v_mfma_scale_f32_32x32x64_f8f6f4 (16x16x128) applies
+//    per-(row, 32-block) scales (the lane-to-block layout was measured; see the Mfma traits).
+//    Accumulation is fp32 in both.
 //  * The epilogue (optional SwiGLU) goes through LDS so that C is written in 16-byte chunks.
 #include <algorithm>
 #include <utility>
@@ -128,8 +130,8 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 // stages, in a ring of two batch slots: a batch holds 16 scale bytes (4 dwords, the scales of
 // 4 MXFP8 or 2 MXFP4 stages) of every A and B row, 16 bytes per row, and is fetched by 4-byte
 // DMA lanes of which 4 consecutive ones read one row's 16 contiguous bytes. One scale
-// instruction thus covers 16 rows of 4 stages in 16 line requests, where a per-stage dword per
-// row took 64 rows of one stage in 64. The operand stages then hold codes only (3 x 48 KiB),
+// instruction thus covers 16 rows of a whole batch in 16 line requests, where a per-stage
+// dword per row took 64 rows of one stage in 64. The operand stages then hold codes only (3 x 48 KiB),
 // the two slots 12 KiB, which leaves room for a tile prefix of 1024 entries.
 constexpr int kScBatchBytes = 16;                                   // scale bytes per row and batch
 constexpr int kScSlot = (Stage<128>::kScaleRowsA + kBN) * kScBatchBytes;   // 6 KiB (largest BM)
