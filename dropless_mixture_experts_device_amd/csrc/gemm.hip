@@ -156,8 +156,10 @@ constexpr int kSuper = 4;         // column tiles per supertile
 constexpr int kSuperRK = 16;
 constexpr int kSuperRKMinNT = 16;
 #ifndef MOE_GEMM_C_NT
-#define MOE_GEMM_C_NT 1           // ragged-row C stores non-temporal: 0 never, 1 without SwiGLU (outputs
+#define MOE_GEMM_C_NT 2           // ragged-row C stores non-temporal: 0 never, 1 without SwiGLU (outputs
                                   // the next kernel streams once; GEMM 2 at DeepSeek-V3 size -1.3%), 2 always
+                                  // (H too, 302 MB at DeepSeek-V3 size, more than the MALL holds: GEMM 1
+                                  // 5.12 -> 5.09 ms, GEMM 2 2.74 -> 2.75, forward 8.14 -> 8.12 ms)
 #endif
 #ifndef MOE_GEMM_RK_C_NT
 #define MOE_GEMM_RK_C_NT 1        // weight-gradient (ragged-K) outputs stored non-temporally (never re-read
